@@ -1,0 +1,346 @@
+"""Float64 CPU oracle for one NOSA-style block-sparse decode step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check and the CPU-baseline leg
+of the benchmark use it.  It shares no code with the HIP library or its
+Python binding and imports neither.
+
+Everything is plain NumPy in float64, one (sequence b, KV head h) pair at a
+time, written the slow, definitional way:
+
+* per-token scores over *every* key (no summaries, no pooling shortcuts);
+* sub-block mean, then block max;
+* selection by explicit sorting of (score, index) pairs and Python sets;
+* softmax attention by its textbook definition over the selected tokens.
+
+Sources (web pages; cited by title and section):
+
+[NOSA]  "NOSA: Native and Offloadable Sparse Attention" technical summary
+        (gist.science, paper 2510.13602), Methodology part 1 "Algorithm:
+        NOSA" -- bullets *dual-selection mechanism*, *locality guarantee*,
+        *block-wise implementation*, *ED-DMA*; Methodology part 2 "System:
+        NOSI" -- bullet *optimised memory layout* (set differences for block
+        swapping).
+[SPIN]  "Unifying Sparse Attention with Hierarchical Memory for Scalable
+        Long-Context LLM Serving" summary (gist.science, 2604.26837),
+        section 2.A (five-operation pipeline), 2.B (per-head physical pages),
+        2.C (two-level index).
+[LAZY]  "LazyAttention" technical summary (gist.science, 2606.04302),
+        "Technical implementation -- 2. Decoding" and "Mathematical
+        equivalence".
+[NOVITA] Novita AI blog "How KV sparsity achieves 1.5x acceleration for
+        vLLM", "Key techniques -- 2. Attention modifications" (one-pass
+        FlashAttention, returning rowmax and l).
+
+Readings where the pages leave a step open are marked READING in the
+docstrings below; each is also listed in the design notes.
+
+Pinning status: every function here is pinned by the CPU tests in
+``tests/test_oracle_*.py`` (library routines, closed forms, brute force and
+invariants) except the selection *semantics* choices marked READING, whose
+agreement with the GPU is agreement on the reading: parity unpinned beyond
+the reading for those choices (disjoint budgets, initial state, new-block
+candidacy, no forced local window, tie order).
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Iterable
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64",
+    "num_blocks",
+    "block_token_range",
+    "subblock_token_ranges",
+    "query_token_scores",
+    "eviction_token_scores",
+    "pool_block_scores",
+    "top_by_score",
+    "select_blocks",
+    "swap_lists",
+    "tokens_of_blocks",
+    "split_chunks",
+    "attend",
+    "merge_partials",
+    "rope_inv_freq",
+    "rope_rotate",
+    "decode_step_bh",
+]
+
+
+# ---------------------------------------------------------------------------
+# Input decoding
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns (uint16) as float64.
+
+    A bfloat16 number is the upper 16 bits of an IEEE-754 binary32 word, so
+    widening the pattern into the high half of a 32-bit word and reading it
+    as float32 gives the exact value; float32 -> float64 is exact too.
+    """
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Blocks and sub-blocks  [NOSA, block-wise implementation]
+# ---------------------------------------------------------------------------
+
+def num_blocks(T: int, bs: int) -> int:
+    """Number of (possibly partial) blocks covering T tokens."""
+    return -(-int(T) // int(bs))
+
+
+def block_token_range(i: int, T: int, bs: int) -> range:
+    """Tokens of logical block i that are present: [i*bs, min((i+1)*bs, T))."""
+    return range(i * bs, min((i + 1) * bs, T))
+
+
+def subblock_token_ranges(i: int, T: int, bs: int, ss: int) -> list[range]:
+    """Non-empty sub-blocks of block i, each the present tokens of
+    [i*bs + j*ss, i*bs + (j+1)*ss).
+
+    READING: a partial sub-block is averaged over the tokens it has; an empty
+    one takes no part in the block maximum.
+    """
+    out = []
+    for j in range(bs // ss):
+        lo = i * bs + j * ss
+        hi = min(i * bs + (j + 1) * ss, T)
+        if lo < hi:
+            out.append(range(lo, hi))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Scores  [NOSA, dual selection + block-wise implementation + ED-DMA]
+# ---------------------------------------------------------------------------
+
+def query_token_scores(q_group: np.ndarray, K: np.ndarray) -> np.ndarray:
+    """Query-aware score of every token: the group mean of q_g . k / sqrt(D).
+
+    q_group: (G, D) float64, the query heads that share this KV head.
+    K:       (T, D) float64, every key of the sequence for this KV head.
+    Returns (T,) float64.
+    """
+    G, D = q_group.shape
+    per_head = np.empty((G, K.shape[0]), dtype=np.float64)
+    for g in range(G):
+        per_head[g] = (K @ q_group[g]) / math.sqrt(D)
+    return per_head.mean(axis=0)
+
+
+def eviction_token_scores(e: np.ndarray) -> np.ndarray:
+    """Query-agnostic score of every token: its eviction-head logit as is.
+
+    ED-DMA keeps the exponent out of selection, so the raw (pre-exp) logit
+    is what gets pooled.  READING: logits are unscaled and are never used as
+    an attention bias.
+    """
+    return np.asarray(e, dtype=np.float64)
+
+
+def pool_block_scores(token_scores: np.ndarray, T: int, bs: int, ss: int) -> np.ndarray:
+    """Two-stage pooling: mean inside each sub-block, then max over the
+    sub-blocks of a block.  Returns (nb,) float64 for nb = ceil(T / bs)."""
+    nb = num_blocks(T, bs)
+    out = np.empty(nb, dtype=np.float64)
+    for i in range(nb):
+        means = [float(np.mean(token_scores[r.start:r.stop]))
+                 for r in subblock_token_ranges(i, T, bs, ss)]
+        out[i] = max(means)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Selection  [NOSA, dual selection + locality guarantee]
+# ---------------------------------------------------------------------------
+
+def top_by_score(scores: np.ndarray, candidates: Iterable[int], k: int) -> list[int]:
+    """The k best candidates under the total order (score descending, index
+    ascending).  READING: ties are broken towards the lower block index."""
+    order = sorted(candidates, key=lambda i: (-float(scores[i]), int(i)))
+    return order[:max(0, int(k))]
+
+
+def select_blocks(S_q: np.ndarray, E: np.ndarray, nb: int, k_e: int, k_q: int,
+                  evicted: set[int]):
+    """One step of dual selection.
+
+    Eviction part: the candidates are the blocks that have never been
+    dropped; the k_e best by eviction score are kept and every other
+    candidate is dropped for good (a block left out once never comes back to
+    this part).  Query part: the k_q best by query-aware score among the
+    blocks the eviction part did not take.
+
+    READINGS: the two parts are disjoint, so the union has min(k_e+k_q, nb)
+    blocks; the never-return rule binds only the eviction part (the query
+    part may still fetch a dropped block); a block created this step starts
+    as a candidate.
+
+    Returns (gamma_e, gamma_q, gamma, evicted_after), the first three as
+    ascending lists, the last as a new set.
+    """
+    cand = [i for i in range(nb) if i not in evicted]
+    gamma_e = set(top_by_score(E, cand, min(k_e, len(cand))))
+    evicted_after = set(evicted) | (set(cand) - gamma_e)
+    rest = [i for i in range(nb) if i not in gamma_e]
+    gamma_q = set(top_by_score(S_q, rest, min(k_q, len(rest))))
+    gamma = sorted(gamma_e | gamma_q)
+    return sorted(gamma_e), sorted(gamma_q), gamma, evicted_after
+
+
+def swap_lists(prev: Iterable[int], cur: Iterable[int]):
+    """Set differences for block swapping [NOSA, NOSI memory layout]:
+    blocks to bring in (cur minus prev) and blocks to drop (prev minus cur),
+    both ascending."""
+    p, c = set(int(x) for x in prev), set(int(x) for x in cur)
+    return sorted(c - p), sorted(p - c)
+
+
+# ---------------------------------------------------------------------------
+# Attention  [NOVITA, attention modifications; split-K merge]
+# ---------------------------------------------------------------------------
+
+def tokens_of_blocks(blocks: Iterable[int], T: int, bs: int) -> np.ndarray:
+    """Present token indices of the given logical blocks, in block order."""
+    toks: list[int] = []
+    for i in blocks:
+        toks.extend(block_token_range(int(i), T, bs))
+    return np.asarray(toks, dtype=np.int64)
+
+
+def split_chunks(sel: list[int], P: int) -> list[list[int]]:
+    """Cut a selected-block list into P contiguous chunks of ceil(n/P)
+    blocks (trailing chunks may be empty).  READING: the split layout is
+    not on the pages; any contiguous partition merges to the same result."""
+    n = len(sel)
+    c = -(-n // P) if n else 0
+    return [list(sel[p * c:(p + 1) * c]) if c else [] for p in range(P)]
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """Softmax attention of each query row over the given keys/values.
+
+    s = scale * q . k; m = max s; l = sum exp(s - m); O = sum exp(s - m) v / l.
+    q: (G, D); K, V: (n, D).  Returns O (G, D), m (G,), l (G,).  With no
+    tokens: O = 0, m = -inf, l = 0.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    G, D = q.shape
+    n = K.shape[0]
+    if n == 0:
+        return np.zeros((G, D)), np.full(G, -np.inf), np.zeros(G)
+    s = (q @ np.asarray(K, dtype=np.float64).T) * scale
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    O = (p @ np.asarray(V, dtype=np.float64)) / l[:, None]
+    return O, m, l
+
+
+def merge_partials(o_parts: np.ndarray, m_parts: np.ndarray, l_parts: np.ndarray):
+    """Merge per-split (o, m, l) triples, o already divided by its own l.
+
+    m = max over splits with l > 0; w_p = l_p exp(m_p - m); l = sum w_p;
+    O = sum w_p o_p / l.  o_parts (P, D), m_parts (P,), l_parts (P,).
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    m_parts = np.asarray(m_parts, dtype=np.float64)
+    l_parts = np.asarray(l_parts, dtype=np.float64)
+    live = l_parts > 0
+    if not live.any():
+        return np.zeros(o_parts.shape[1]), -np.inf, 0.0
+    m = m_parts[live].max()
+    w = l_parts[live] * np.exp(m_parts[live] - m)
+    l = w.sum()
+    O = (w[:, None] * o_parts[live]).sum(axis=0) / l
+    return O, float(m), float(l)
+
+
+# ---------------------------------------------------------------------------
+# Rotary position embedding  [LAZY, decoding + mathematical equivalence]
+# ---------------------------------------------------------------------------
+
+def rope_inv_freq(D: int, base: float) -> np.ndarray:
+    """theta_i = base^(-2i/D), i < D/2 (rotate-half convention; READING)."""
+    return np.power(float(base), -(2.0 * np.arange(D // 2, dtype=np.float64)) / D)
+
+
+def rope_rotate(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """Rotate the last axis of x by position pos (scalar or broadcastable
+    over the leading axes): pairs (i, i + D/2) turn by angle pos * theta_i."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(D, base)
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., : D // 2], x[..., D // 2:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# One decode step for one (b, h) pair
+# ---------------------------------------------------------------------------
+
+def decode_step_bh(q_group, K, V, e, T, bs, ss, k_e, k_q, evicted, prev_sel,
+                   num_splits, scale, select_all=False, rope=None):
+    """The whole step for one (sequence, KV head), from already-appended
+    inputs, in the order the pages give: score, select, set differences,
+    attention.
+
+    q_group: (G, D) float64 query heads of this group.
+    K, V:    (>=T, D) float64 keys/values in logical token order; for the
+             deferred-RoPE case these are the *stored* keys.
+    e:       (>=T,) float64 eviction logits.
+    rope:    None, or dict(q_pos=n, block_start=(nb,) absolute start
+             position of the document holding each block, base=...).  Keys
+             are then materialised as Rot(doc start) k_stored and queries as
+             Rot(n) q (READING: stored keys carry their in-document
+             rotation).
+    select_all: skip scoring and take every block (deferred-RoPE workload).
+
+    Returns a dict with block scores, the selection, swap lists, per-split
+    partials and the merged (O, m, l).
+    """
+    nb = num_blocks(T, bs)
+    out: dict = {"nb": nb}
+    if select_all:
+        gamma_e, gamma_q, gamma = [], list(range(nb)), list(range(nb))
+        evicted_after = set(evicted)
+    else:
+        s_q = query_token_scores(q_group, K[:T])
+        s_e = eviction_token_scores(e[:T])
+        S_q = pool_block_scores(s_q, T, bs, ss)
+        E = pool_block_scores(s_e, T, bs, ss)
+        out["S_q"], out["E"] = S_q, E
+        gamma_e, gamma_q, gamma, evicted_after = select_blocks(S_q, E, nb, k_e, k_q, evicted)
+    load, drop = swap_lists(prev_sel, gamma)
+    out.update(gamma_e=gamma_e, gamma_q=gamma_q, sel=gamma, evicted=evicted_after,
+               load=load, evict=drop)
+
+    if rope is not None:
+        Kt = np.empty((T, K.shape[1]))
+        starts = np.asarray(rope["block_start"], dtype=np.float64)
+        for i in range(nb):
+            r = block_token_range(i, T, bs)
+            Kt[r.start:r.stop] = rope_rotate(K[r.start:r.stop], starts[i], rope["base"])
+        qt = rope_rotate(q_group, rope["q_pos"], rope["base"])
+    else:
+        Kt, qt = K[:T], q_group
+
+    parts = []
+    for chunk in split_chunks(gamma, num_splits):
+        toks = tokens_of_blocks(chunk, T, bs)
+        parts.append(attend(qt, Kt[toks], V[toks], scale))
+    G, D = qt.shape
+    part_o = np.stack([p[0] for p in parts], axis=1)   # (G, P, D)
+    part_m = np.stack([p[1] for p in parts], axis=1)   # (G, P)
+    part_l = np.stack([p[2] for p in parts], axis=1)
+    toks = tokens_of_blocks(gamma, T, bs)
+    O, m, l = attend(qt, Kt[toks], V[toks], scale)
+    out.update(part_o=part_o, part_m=part_m, part_l=part_l, O=O, m=m, l=l)
+    return out

@@ -1,0 +1,363 @@
+"""Pins for the float64 oracle: checks against things other than the oracle
+itself (a library routine, closed forms worked by hand, brute force over all
+subsets, invariants the pages state).
+
+Each ``check_*`` takes the oracle module ``O`` and raises AssertionError on a
+violation, so the same checks can be run against planted mistakes
+(``test_oracle_mutations.py``) to show that they catch them.
+"""
+
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import torch
+
+
+def _sdpa(q, K, V, scale):
+    """torch's CPU scaled-dot-product attention in float64 (library route)."""
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(K), t(V), scale=scale)[0, 0].numpy()
+
+
+# ---------------------------------------------------------------------------
+# attention + split merge
+# ---------------------------------------------------------------------------
+
+def check_attend_vs_sdpa(O, seed=0):
+    rng = np.random.default_rng(seed)
+    for G, n, D in [(1, 1, 4), (4, 7, 16), (8, 130, 64), (4, 257, 128)]:
+        q = rng.standard_normal((G, D))
+        K = rng.standard_normal((n, D)) * 2.0
+        V = rng.standard_normal((n, D))
+        scale = 1.0 / math.sqrt(D)
+        out, m, l = O.attend(q, K, V, scale)
+        ref = _sdpa(q, K, V, scale)
+        assert np.abs(out - ref).max() <= 1e-12, "O differs from SDPA"
+        s = torch.tensor(q) @ torch.tensor(K).T * scale
+        lse = torch.logsumexp(s, dim=1).numpy()
+        assert np.abs(m + np.log(l) - lse).max() <= 1e-12, "m + ln l differs from logsumexp"
+        smax = torch.max(s, dim=1).values.numpy()
+        assert np.abs(m - smax).max() <= 1e-12 * max(1.0, np.abs(smax).max()), "m is not the row max"
+    out, m, l = O.attend(np.ones((3, 8)), np.zeros((0, 8)), np.zeros((0, 8)), 0.5)
+    assert np.all(out == 0) and np.all(np.isneginf(m)) and np.all(l == 0), "empty token set"
+
+
+def check_merge_vs_sdpa(O, seed=1):
+    rng = np.random.default_rng(seed)
+    D = 32
+    for trial in range(20):
+        n = int(rng.integers(1, 90))
+        P = int(rng.integers(1, 9))
+        cuts = np.sort(rng.integers(0, n + 1, size=P - 1))
+        bounds = [0, *cuts.tolist(), n]
+        q = rng.standard_normal((1, D))
+        K = rng.standard_normal((n, D)) * 3.0
+        V = rng.standard_normal((n, D))
+        parts = [O.attend(q, K[a:b], V[a:b], 0.25) for a, b in zip(bounds[:-1], bounds[1:])]
+        o_p = np.stack([p[0][0] for p in parts])
+        m_p = np.array([p[1][0] for p in parts])
+        l_p = np.array([p[2][0] for p in parts])
+        Om, mm, lm = O.merge_partials(o_p, m_p, l_p)
+        ref = _sdpa(q, K, V, 0.25)[0]
+        assert np.abs(Om - ref).max() <= 1e-12, "merged O differs from SDPA"
+        s = torch.tensor(q[0]) @ torch.tensor(K).T * 0.25
+        assert abs(mm + math.log(lm) - float(torch.logsumexp(s, 0))) <= 1e-12, "merged LSE"
+        assert abs(mm - float(s.max())) <= 1e-12, "merged m is not the global max"
+    Om, mm, lm = O.merge_partials(np.zeros((3, D)), np.full(3, -np.inf), np.zeros(3))
+    assert np.all(Om == 0) and mm == -np.inf and lm == 0, "all-empty merge"
+
+
+def check_split_chunks(O):
+    for n in range(0, 40):
+        sel = list(range(100, 100 + n))
+        for P in range(1, 12):
+            ch = O.split_chunks(sel, P)
+            assert len(ch) == P
+            assert [x for c in ch for x in c] == sel, "chunks must tile the list in order"
+            c = -(-n // P) if n else 0
+            assert all(len(x) <= c for x in ch)
+
+
+# ---------------------------------------------------------------------------
+# pooling
+# ---------------------------------------------------------------------------
+
+# token scores worked by hand: bs = 8, ss = 4 (two sub-blocks per block)
+_F = [3, 1, 2, 2, 0, 0, 9, 3,      # block 0: sub means 2 and 3        -> 3
+      5, 5, 5, 5, 1, 1, 1, 1,      # block 1: sub means 5 and 1        -> 5
+      -2, -2, -2, -2, 7]           # block 2: sub means -2 and 7 (1 token) -> 7
+
+
+def _keys_for_scores(f, g_noise):
+    """D = 4, G = 2 keys/queries whose group-mean score q.k/sqrt(4) is f[t]:
+    heads (3, 5) and (1, -5) average to (2, 0); keys (f, noise)."""
+    T = len(f)
+    K = np.zeros((T, 4))
+    K[:, 0] = f
+    K[:, 1] = g_noise
+    q = np.array([[3.0, 5.0, 0.0, 0.0], [1.0, -5.0, 0.0, 0.0]])
+    return q, K
+
+
+def check_pool_closed_form(O, seed=2):
+    rng = np.random.default_rng(seed)
+    q, K = _keys_for_scores(_F, rng.standard_normal(len(_F)))
+    s = O.query_token_scores(q, K)
+    assert np.abs(s - np.array(_F, dtype=float)).max() <= 1e-12, "group-mean token score"
+    S = O.pool_block_scores(s, len(_F), 8, 4)
+    assert np.array_equal(S, [3.0, 5.0, 7.0]), S
+    # T = 17: block 2 is one token (-2); its empty second sub-block is ignored
+    S17 = O.pool_block_scores(s[:17], 17, 8, 4)
+    assert np.array_equal(S17, [3.0, 5.0, -2.0]), S17
+    # ss = 1 reduces to the per-token max, ss = bs to the block mean
+    f = rng.standard_normal(45)
+    S1 = O.pool_block_scores(f, 45, 8, 1)
+    Sb = O.pool_block_scores(f, 45, 8, 8)
+    for i in range(6):
+        seg = f[i * 8:min(i * 8 + 8, 45)]
+        assert S1[i] == seg.max(), "ss = 1 must be the max over tokens"
+        assert abs(Sb[i] - seg.sum() / len(seg)) <= 1e-15, "ss = bs must be the block mean"
+    assert len(S1) == 6 and len(Sb) == 6
+
+
+def check_pool_linearity(O, seed=3):
+    """Pooling the per-token scores equals scoring the sub-block mean keys
+    with the group-mean query (mean and dot product are both linear)."""
+    rng = np.random.default_rng(seed)
+    for G, D, T, bs, ss in [(4, 16, 200, 16, 4), (8, 32, 131, 32, 8), (1, 8, 64, 64, 16)]:
+        q = rng.standard_normal((G, D))
+        K = rng.standard_normal((T, D))
+        S = O.pool_block_scores(O.query_token_scores(q, K), T, bs, ss)
+        qbar = q.sum(axis=0) / G
+        nb = -(-T // bs)
+        ref = np.full(nb, -np.inf)
+        for t0 in range(0, T, ss):
+            kbar = K[t0:min(t0 + ss, T)].sum(axis=0) / (min(t0 + ss, T) - t0)
+            ref[t0 // bs] = max(ref[t0 // bs], float(kbar @ qbar) / math.sqrt(D))
+        assert np.abs(S - ref).max() <= 1e-12
+
+
+def check_eviction_pre_exp(O):
+    """ED-DMA: the block order comes from pooled raw logits.  Block 0 has
+    sub-block logits (10, -10) -> mean 0, block 1 has (1, 1) -> mean 1; mean
+    of exponentials would rank block 0 first instead."""
+    e = O.eviction_token_scores(np.array([10.0, -10.0, 1.0, 1.0]))
+    E = O.pool_block_scores(e, 4, 2, 2)
+    assert np.array_equal(E, [0.0, 1.0]), E
+    ge, gq, g, ev = O.select_blocks(np.zeros(2), E, 2, 1, 0, set())
+    assert ge == [1] and ev == {0}
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+def _best_subset(scores, cand, k):
+    """Brute force: among the k-subsets with the largest score sum, the
+    lexicographically first (== lowest indices among ties)."""
+    combos = list(itertools.combinations(sorted(cand), k))
+    best = max(sum(float(scores[i]) for i in c) for c in combos)
+    return set(min(c for c in combos if sum(float(scores[i]) for i in c) == best))
+
+
+def check_select_bruteforce(O, seed=4, trials=300, ties=False):
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        nb = int(rng.integers(1, 9))
+        k_e = int(rng.integers(0, nb + 2))
+        k_q = int(rng.integers(0, nb + 2))
+        if ties:
+            E = rng.integers(0, 3, nb).astype(float)
+            S = rng.integers(-1, 2, nb).astype(float)
+        else:
+            E = rng.standard_normal(nb)
+            S = rng.standard_normal(nb)
+        evicted = {i for i in range(nb) if rng.random() < 0.3}
+        ge, gq, g, ev = O.select_blocks(S, E, nb, k_e, k_q, set(evicted))
+        C = [i for i in range(nb) if i not in evicted]
+        ne = min(k_e, len(C))
+        assert set(ge) == _best_subset(E, C, ne), ("eviction part", nb, k_e, evicted)
+        assert len(ge) == ne
+        rest = [i for i in range(nb) if i not in ge]
+        nq = min(k_q, len(rest))
+        assert set(gq) == _best_subset(S, rest, nq), ("query part", nb, k_q)
+        assert g == sorted(set(ge) | set(gq))
+        assert len(g) == min(len(ge) + k_q, nb)
+        assert g == sorted(g) and len(set(g)) == len(g)
+        assert ev == set(evicted) | (set(C) - set(ge)), "every unkept candidate is evicted"
+
+
+def check_select_sizes(O, seed=5):
+    rng = np.random.default_rng(seed)
+    for _ in range(200):
+        nb = int(rng.integers(1, 60))
+        k_e, k_q = int(rng.integers(0, 20)), int(rng.integers(0, 20))
+        ge, gq, g, ev = O.select_blocks(rng.standard_normal(nb), rng.standard_normal(nb), nb, k_e, k_q, set())
+        assert len(ge) == min(k_e, nb), "|Gamma_e| = min(k_e, nb) from a fresh state"
+        assert len(g) == min(k_e + k_q, nb), "|Gamma| = min(k, nb): the parts are disjoint"
+        assert not set(ge) & set(gq)
+        if k_e + k_q >= nb:
+            assert g == list(range(nb)), "k >= nb selects every block"
+
+
+def check_trajectory_invariants(O, seed=6, steps=40):
+    """Monotone eviction and the locality bound over a synthetic trajectory:
+    blocks are created as tokens arrive; scores are redrawn every step."""
+    rng = np.random.default_rng(seed)
+    for k_e, k_q, bs, T0 in [(4, 4, 4, 64), (3, 5, 2, 20), (6, 2, 8, 200), (1, 1, 1, 5)]:
+        k = k_e + k_q
+        evicted, prev_e, prev = set(), None, None
+        for t in range(1, steps + 1):
+            T = T0 + t
+            nb = -(-T // bs)
+            nb_prev = -(-(T - 1) // bs)
+            new = set(range(nb_prev, nb)) if t > 1 else set(range(nb))
+            ge, gq, g, ev = O.select_blocks(rng.standard_normal(nb), rng.standard_normal(nb), nb, k_e, k_q, evicted)
+            assert evicted <= ev, "the evicted set never shrinks"
+            assert not set(ge) & evicted, "an evicted block never returns to the eviction part"
+            if prev_e is not None:
+                assert set(ge) <= set(prev_e) | new, "Gamma_e(t) within Gamma_e(t-1) and new blocks"
+                gamma = len(set(g) & set(prev)) / len(g)
+                bound = (k_e - len(new & set(ge))) / k
+                assert gamma >= bound - 1e-15, ("locality", gamma, bound)
+                if not new:
+                    assert gamma >= k_e / k - 1e-15
+            evicted, prev_e, prev = ev, ge, g
+
+
+def check_swap_lists(O, seed=7):
+    load, drop = O.swap_lists([1, 3, 5, 7], [3, 4, 5, 8])
+    assert load == [4, 8] and drop == [1, 7], (load, drop)
+    assert O.swap_lists([], [2, 0]) == ([0, 2], [])
+    rng = np.random.default_rng(seed)
+    for _ in range(200):
+        prev = sorted(set(rng.integers(0, 30, rng.integers(0, 12)).tolist()))
+        cur = sorted(set(rng.integers(0, 30, rng.integers(0, 12)).tolist()))
+        load, drop = O.swap_lists(prev, cur)
+        both = set(prev) & set(cur)
+        assert set(load) | both == set(cur) and not set(load) & both
+        assert set(drop) | both == set(prev) and not set(drop) & both
+        assert not set(load) & set(drop)
+        assert load == sorted(load) and drop == sorted(drop)
+
+
+# ---------------------------------------------------------------------------
+# rotary embedding and the deferred (lazy) rotation
+# ---------------------------------------------------------------------------
+
+def check_rope_complex(O, seed=8):
+    """Rotate-half RoPE is multiplication of z_i = x_i + i x_{i+D/2} by
+    exp(i pos theta_i); theta_0 = 1 and consecutive thetas have the constant
+    ratio base^(-2/D)."""
+    rng = np.random.default_rng(seed)
+    for D, base in [(8, 10000.0), (64, 500000.0), (128, 500000.0)]:
+        th = O.rope_inv_freq(D, base)
+        assert th[0] == 1.0 and len(th) == D // 2
+        assert np.abs(th[1:] / th[:-1] - base ** (-2.0 / D)).max() <= 1e-14
+        for pos in [0, 1, 7, 4096, 32768]:
+            x = rng.standard_normal(D)
+            z = (x[: D // 2] + 1j * x[D // 2:]) * np.exp(1j * pos * th)
+            ref = np.concatenate([z.real, z.imag])
+            assert np.abs(O.rope_rotate(x, pos, base) - ref).max() <= 1e-12
+
+
+def check_rope_identities(O, seed=9):
+    rng = np.random.default_rng(seed)
+    D, base = 128, 500000.0
+    x = rng.standard_normal((5, D))
+    assert np.array_equal(O.rope_rotate(x, 0, base), x), "Rot(0) = I"
+    for a, b in [(3, 4), (4096, 28672), (12345, 20423)]:
+        lhs = O.rope_rotate(O.rope_rotate(x, b, base), a, base)
+        assert np.abs(lhs - O.rope_rotate(x, a + b, base)).max() <= 1e-10, "Rot(a) Rot(b) = Rot(a+b)"
+        assert np.abs(np.linalg.norm(O.rope_rotate(x, a, base), axis=1) - np.linalg.norm(x, axis=1)).max() <= 1e-12
+        q, k = rng.standard_normal(D), rng.standard_normal(D)
+        lhs = O.rope_rotate(q, a + b, base) @ O.rope_rotate(k, b, base)
+        rhs = O.rope_rotate(q, a, base) @ k
+        assert abs(lhs - rhs) <= 1e-10, "score depends on the offset only"
+
+
+# ---------------------------------------------------------------------------
+# whole step (one (b, h)), special cases
+# ---------------------------------------------------------------------------
+
+def check_step_dense_equivalence(O, seed=10):
+    """With k >= nb the step is plain softmax attention over every token."""
+    rng = np.random.default_rng(seed)
+    G, D, T, bs, ss = 4, 32, 301, 16, 4
+    q = rng.standard_normal((G, D))
+    K = rng.standard_normal((T, D))
+    V = rng.standard_normal((T, D))
+    e = rng.standard_normal(T)
+    nb = -(-T // bs)
+    for k_e, k_q in [(nb, 0), (0, nb), (7, nb - 7), (nb, nb)]:
+        r = O.decode_step_bh(q, K, V, e, T, bs, ss, k_e, k_q, set(), [], 5, 1 / math.sqrt(D))
+        assert r["sel"] == list(range(nb))
+        assert np.abs(r["O"] - _sdpa(q, K, V, 1 / math.sqrt(D))).max() <= 1e-12
+        Om, mm, lm = O.merge_partials(r["part_o"][0], r["part_m"][0], r["part_l"][0])
+        assert np.abs(Om - r["O"][0]).max() <= 1e-12
+
+
+def check_step_sparse_subset(O, seed=11):
+    """With k < nb the output is exactly SDPA over the selected blocks'
+    tokens, and the swap lists are the differences to the previous set."""
+    rng = np.random.default_rng(seed)
+    G, D, T, bs, ss = 2, 16, 150, 16, 4
+    q = rng.standard_normal((G, D))
+    K = rng.standard_normal((T, D))
+    V = rng.standard_normal((T, D))
+    e = rng.standard_normal(T)
+    r = O.decode_step_bh(q, K, V, e, T, bs, ss, 2, 3, set(), [0, 9], 3, 0.25)
+    assert len(r["sel"]) == 5
+    toks = np.concatenate([np.arange(i * bs, min(i * bs + bs, T)) for i in r["sel"]])
+    assert np.abs(r["O"] - _sdpa(q, K[toks], V[toks], 0.25)).max() <= 1e-12
+    assert set(r["load"]) == set(r["sel"]) - {0, 9} and set(r["evict"]) == {0, 9} - set(r["sel"])
+
+
+def check_step_lazy_rope(O, seed=12):
+    """Deferred RoPE: materialised rotated keys and the lazy relative
+    rotation of the query (once per document) give the same attention."""
+    rng = np.random.default_rng(seed)
+    G, D, bs, base = 4, 64, 8, 500000.0
+    doc_blocks = 3
+    T = bs * doc_blocks * 4
+    nb = T // bs
+    starts = (np.arange(nb) // doc_blocks) * doc_blocks * bs
+    q = rng.standard_normal((G, D))
+    K = rng.standard_normal((T, D))
+    V = rng.standard_normal((T, D))
+    n = T
+    r = O.decode_step_bh(q, K, V, np.zeros(T), T, bs, bs, 0, nb, set(), [], 4, 1 / math.sqrt(D),
+                         select_all=True, rope=dict(q_pos=n, block_start=starts, base=base))
+    # lazy route: scores of block i use Rot(n - start_i) q against stored keys
+    s = np.empty((G, T))
+    for i in range(nb):
+        qr = O.rope_rotate(q, n - starts[i], base)
+        s[:, i * bs:(i + 1) * bs] = qr @ K[i * bs:(i + 1) * bs].T / math.sqrt(D)
+    lse = torch.logsumexp(torch.tensor(s), dim=1).numpy()
+    p = np.exp(s - lse[:, None])
+    assert np.abs(r["O"] - p @ V).max() <= 1e-10
+    assert np.abs(r["m"] + np.log(r["l"]) - lse).max() <= 1e-10
+    # no rotation (position 0, documents at 0) reduces to plain attention
+    r0 = O.decode_step_bh(q, K, V, np.zeros(T), T, bs, bs, 0, nb, set(), [], 4, 1 / math.sqrt(D),
+                          select_all=True, rope=dict(q_pos=0, block_start=np.zeros(nb), base=base))
+    assert np.abs(r0["O"] - _sdpa(q, K, V, 1 / math.sqrt(D))).max() <= 1e-12
+
+
+def check_bf16_decode(O):
+    """bf16 bit patterns decode to their exact values."""
+    bits = np.array([0x0000, 0x3F80, 0xBF80, 0x4000, 0x3F00, 0x7F7F, 0x0001, 0x4049], dtype=np.uint16)
+    want = [0.0, 1.0, -1.0, 2.0, 0.5, 3.3895313892515355e38, 2.0 ** -133, 3.140625]
+    assert O.bf16_to_f64(bits).tolist() == want
+
+
+ALL_CHECKS = [
+    check_attend_vs_sdpa, check_merge_vs_sdpa, check_split_chunks,
+    check_pool_closed_form, check_pool_linearity, check_eviction_pre_exp,
+    check_select_bruteforce, check_select_sizes, check_trajectory_invariants,
+    check_swap_lists, check_rope_complex, check_rope_identities,
+    check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
+    check_bf16_decode,
+]
