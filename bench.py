@@ -1,0 +1,264 @@
+"""Benchmark of one NOSA-style block-sparse decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splits P]
+
+A step is the whole hot path over one batch: append -> score -> select ->
+swap_diff -> sparse_decode (split-K) -> combine, for every sequence of the
+batch, on synthetic inputs resident in HBM before timing starts.  The
+default workload is the Llama-3-8B-shaped layer at 32K context.
+
+Timing (HIP events on the stream the kernels run on):
+  * cold: before every step a 1 GiB buffer is read so L2 and the Infinity
+    Cache hold none of the step's data; the step is bracketed by events;
+  * per-kernel: a second cold pass with an event between every launch;
+  * warm: back-to-back steps, for context.
+`value` is B / (cold step time): decode tokens per second.  HBM bandwidth
+counts algorithmic bytes: K and V of the tokens present in the selected
+blocks plus the block summaries (fp32 mean keys and logits) that scoring
+streams.  The CPU baseline times the float64 oracle on a bounded sample of
+(b, h) pairs of the same workload and scales it to the whole batch.
+
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_HBM_GBPS = 8000.0
+METRIC = "sparse decode attn tokens/s + achieved HBM GB/s (% peak), 8B shape @32K"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_llama3_8b_32k.json")
+DECODE_SRC = os.path.join(ROOT, "block_sparse_kv_score_amd", "csrc", "nosa_decode.hip")
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b_32k")
+    ap.add_argument("--splits", type=int, default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args(argv)
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(w, sel, sel_count, T):
+    """K+V bytes of the tokens present in the selected blocks, and the
+    summary bytes scoring streams (valid sub-blocks), for one step."""
+    import numpy as np
+    nb = -(-T // w.bs)
+    tail = T - (nb - 1) * w.bs
+    n_tok = 0
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            s = sel[b, h, :sel_count[b, h]]
+            n_tok += len(s) * w.bs - int(np.count_nonzero(s == nb - 1)) * (w.bs - tail)
+    kv = n_tok * w.D * 2 * 2
+    n_sub = (nb - 1) * w.nsub + -(-tail // w.ss)
+    summ = 0 if w.select_all else w.B * w.Hkv * n_sub * (w.D * 4 + 4)
+    return kv, summ
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """The oracle as it stands, on (b, h) pairs of decode step 1 until the
+    time budget is spent; scaled to the whole batch."""
+    import numpy as np
+    import oracle
+    from block_sparse_kv_score_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    pairs = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    rng = np.random.default_rng(0)
+    rng.shuffle(pairs)
+    t = 1
+    T = w.seq_len(t)
+    q = inp.q(t)
+    done, elapsed = 0, 0.0
+    for (b, h) in pairs:
+        t0 = time.perf_counter()
+        K = oracle.bf16_to_f64(inp.K[b, h, :T])
+        V = oracle.bf16_to_f64(inp.V[b, h, :T])
+        e = inp.e[b, h, :T].astype(np.float64)
+        qg = oracle.bf16_to_f64(q[b, h * w.G:(h + 1) * w.G])
+        rope = None
+        if w.select_all and w.rope_base:
+            rope = dict(q_pos=int(inp.q_pos[b]), block_start=synth.block_doc_start(w) * w.bs, base=w.rope_base)
+        oracle.decode_step_bh(qg, K, V, e, T, w.bs, w.ss, w.k_e, w.k_q, set(), [], w.splits,
+                              1.0 / math.sqrt(w.D), select_all=w.select_all, rope=rope)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= budget_s:
+            break
+    step_s = elapsed / done * len(pairs)
+    return {"value": w.B / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (b,h) pairs of decode step 1 ({elapsed:.1f} s), "
+                      f"scaled to the batch; float64 NumPy, BLAS threads = {threads}",
+            "sec_per_step": step_s}
+
+
+def main(argv=None) -> int:
+    args = parse(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the per-(b, h) work shards without communication, see the design notes.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from block_sparse_kv_score_amd import synth
+    from block_sparse_kv_score_amd.step import DecodeSession
+    from block_sparse_kv_score_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    K, W = args.steps, args.warmup
+    passes = 3
+    if w.append and W + passes * K > w.n_append:
+        raise SystemExit(f"at most {w.n_append} appended tokens: lower --steps/--warmup")
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = synth.generate(w, args.seed)
+    sess = DecodeSession(w, inp, splits=args.splits, poison=False)
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+
+    def flush():
+        flush_buf.sum()
+
+    def next_t():
+        return sess.step_index + 1 if w.append else 1
+
+    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
+    for _ in range(W):
+        flush()
+        sess.step(next_t())
+    torch.cuda.synchronize()
+
+    # pass 1: cold steps, events at the ends only (the headline)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    bytes_kv, bytes_sum = [], []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(K):
+        flush()
+        ev[k][0].record(stream)
+        t = sess.step(next_t())
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall_cold = time.perf_counter() - wall0
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    sel = sess.sel.cpu().numpy()
+    cnt = sess.sel_count.cpu().numpy()
+    kvb, sb = algorithmic_bytes(w, sel, cnt, w.seq_len(sess.step_index))
+    print(f"[bench] cold pass done: median {np.median(step_ms)*1e3:.1f} us", file=sys.stderr, flush=True)
+
+    # pass 2: cold steps with an event between every launch
+    names = (["append"] if w.append else []) + ([] if w.select_all else ["score", "select"]) + \
+            ["swap_diff", "decode", "combine"]
+    per = {n: [] for n in names}
+    for k in range(K):
+        flush()
+        t = next_t()
+        sess.use_buffers(t)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        evs[0].record(stream)
+        for j, n in enumerate(names):
+            if n == "append":
+                sess.append(t)
+            elif n == "score":
+                sess.score(t)
+            elif n == "select":
+                sess.select()
+            elif n == "swap_diff":
+                sess.swap_diff()
+            elif n == "decode":
+                sess.decode(t)
+            else:
+                sess.combine()
+            evs[j + 1].record(stream)
+        sess.step_index = t
+        torch.cuda.synchronize()
+        for j, n in enumerate(names):
+            per[n].append(evs[j].elapsed_time(evs[j + 1]))
+    kernels_us = {n: float(np.mean(v) * 1e3) for n, v in per.items()}
+
+    # pass 3: warm, back to back
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for k in range(K):
+        sess.step(next_t())
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / K
+    assert int(sess.err.cpu()[0]) == 0, "device contract flag raised"
+
+    t_step = float(np.median(step_ms)) / 1e3
+    total_bytes = kvb + sb
+    gbps = total_bytes / t_step / 1e9
+    dec_s = kernels_us["decode"] / 1e6
+    dec_gbps = kvb / dec_s / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("decode_source_sha256_16") == source_hash(DECODE_SRC) and tr.get("workload") == w.name \
+                and tr.get("splits") == sess.P:
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                "kernel": "nosa_sparse_decode (decode_kernel)",
+                "algorithmic_bytes_per_launch": int(kvb), "avg_launch_us": round(kernels_us["decode"], 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, inp, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC if w.name == "llama3_8b_32k" else f"sparse decode attn tokens/s ({w.name})",
+        "value": round(w.B / t_step, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
+                   "context": w.T0, "block": w.bs, "sub_block": w.ss, "k_e": w.k_e, "k_q": w.k_q,
+                   "splits": sess.P, "table": w.table, "parallelism": "single GPU"},
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes_per_step": int(total_bytes),
+        "bytes_kv": int(kvb), "bytes_summaries": int(sb),
+        "step_ms_p10_p90": [round(float(np.percentile(step_ms, 10)), 4), round(float(np.percentile(step_ms, 90)), 4)],
+        "ms_per_step_warm": round(warm_ms, 4),
+        "wall_ms_per_step_incl_flush": round(wall_cold / K * 1e3, 4),
+        "kernels_us": {k: round(v, 2) for k, v in kernels_us.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "seed": args.seed,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

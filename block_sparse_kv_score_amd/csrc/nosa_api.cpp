@@ -1,0 +1,176 @@
+// C-ABI entry points of libnosa: argument checks, then one launch each.
+// The checks are plain host logic and touch no HIP API, so a failing call
+// returns before anything is enqueued.
+
+#include <stdint.h>
+
+#include "nosa.h"
+#include "nosa_launch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+nosa_status check_dims(const nosa_dims* d) {
+  if (!d) return NOSA_ERR_ARG;
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 || d->block_size < 1 ||
+      d->sub_block < 1 || d->max_blocks < 1)
+    return NOSA_ERR_ARG;
+  if (d->n_q_heads % d->n_kv_heads != 0) return NOSA_ERR_ARG;
+  if (d->block_size % d->sub_block != 0) return NOSA_ERR_ARG;
+  if ((int64_t)d->batch * d->n_kv_heads > 65535) return NOSA_ERR_UNSUPPORTED;
+  if ((int64_t)d->batch * d->n_q_heads > (int64_t)1 << 30) return NOSA_ERR_UNSUPPORTED;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (!pow2(G) || G > 16) return NOSA_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return NOSA_ERR_UNSUPPORTED;
+  if (d->block_size != 64 && d->block_size != 128 && d->block_size != 256) return NOSA_ERR_UNSUPPORTED;
+  const int nsub = d->block_size / d->sub_block;
+  if (!pow2(nsub) || nsub > 64) return NOSA_ERR_UNSUPPORTED;
+  if (d->max_blocks > 8192) return NOSA_ERR_UNSUPPORTED;
+  return NOSA_OK;
+}
+
+// `need_pages`: the call reads or writes the page pools.
+nosa_status check_kv(const nosa_dims* d, const nosa_kv* kv, bool need_pages) {
+  if (!kv) return NOSA_ERR_ARG;
+  if (kv->num_pages < 1) return NOSA_ERR_ARG;
+  if (need_pages) {
+    if (!kv->k_pages || !kv->v_pages || !kv->e_pages) return NOSA_ERR_ARG;
+    if (!aligned16(kv->k_pages) || !aligned16(kv->v_pages) || !aligned16(kv->e_pages)) return NOSA_ERR_ARG;
+  }
+  switch (kv->kind) {
+    case NOSA_TABLE_FLAT:
+      if (!kv->table) return NOSA_ERR_ARG;
+      break;
+    case NOSA_TABLE_TWO_LEVEL: {
+      if (!kv->directory || !kv->segments || kv->num_segments < 1) return NOSA_ERR_ARG;
+      if (kv->seg_log2 < 0 || kv->seg_log2 > 20 || kv->blocks_log2 < kv->seg_log2 || kv->blocks_log2 > 24)
+        return NOSA_ERR_ARG;
+      if ((int64_t)d->max_blocks > ((int64_t)1 << kv->blocks_log2)) return NOSA_ERR_ARG;
+      const int64_t need = (((int64_t)d->batch * d->n_kv_heads) << kv->blocks_log2) >> kv->seg_log2;
+      if ((int64_t)kv->dir_entries < need) return NOSA_ERR_ARG;
+      break;
+    }
+    case NOSA_TABLE_PACKED_ROPE:
+      if (!kv->packed) return NOSA_ERR_ARG;
+      if (kv->num_pages > ((int64_t)1 << NOSA_PACK_PAGE_BITS)) return NOSA_ERR_ARG;
+      break;
+    default:
+      return NOSA_ERR_ARG;
+  }
+  return NOSA_OK;
+}
+
+nosa_status from_hip(hipError_t e) { return e == hipSuccess ? NOSA_OK : NOSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+nosa_status nosa_prefill_pages(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* k_src,
+                               const uint16_t* v_src, const float* e_src, int32_t src_tokens,
+                               const int32_t* seq_lens, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if ((st = check_kv(dims, kv, true)) != NOSA_OK) return st;
+  if (!k_src || !v_src || !e_src || !seq_lens || src_tokens < 0) return NOSA_ERR_ARG;
+  if (!aligned16(k_src)) return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_prefill(*dims, *kv, k_src, v_src, e_src, src_tokens, seq_lens, stream));
+}
+
+nosa_status nosa_build_summaries(const nosa_dims* dims, const nosa_kv* kv, const int32_t* seq_lens,
+                                 float* k_summary, float* e_summary, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if ((st = check_kv(dims, kv, true)) != NOSA_OK) return st;
+  if (!seq_lens || !k_summary || !e_summary || !aligned16(k_summary)) return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_build_summaries(*dims, *kv, seq_lens, k_summary, e_summary, stream));
+}
+
+nosa_status nosa_append(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* k_new,
+                        const uint16_t* v_new, const float* e_new, int32_t* seq_lens, float* k_summary,
+                        float* e_summary, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if ((st = check_kv(dims, kv, true)) != NOSA_OK) return st;
+  if (!k_new || !v_new || !e_new || !seq_lens || !k_summary || !e_summary) return NOSA_ERR_ARG;
+  if (!aligned16(k_new) || !aligned16(k_summary)) return NOSA_ERR_ARG;
+  if (dims->n_kv_heads > 16) return NOSA_ERR_UNSUPPORTED;
+  return from_hip(
+      nosa::launch_append(*dims, *kv, k_new, v_new, e_new, seq_lens, k_summary, e_summary, stream));
+}
+
+nosa_status nosa_score_blocks(const nosa_dims* dims, const uint16_t* q, const float* k_summary,
+                              const float* e_summary, const int32_t* seq_lens, float* score_q,
+                              float* score_e, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if (!q || !k_summary || !e_summary || !seq_lens || !score_q || !score_e) return NOSA_ERR_ARG;
+  if (!aligned16(k_summary)) return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_score(*dims, q, k_summary, e_summary, seq_lens, score_q, score_e, stream));
+}
+
+nosa_status nosa_select(const nosa_dims* dims, const float* score_q, const float* score_e,
+                        const int32_t* seq_lens, int32_t k_e, int32_t k_q, uint32_t* evicted, int32_t* sel,
+                        int32_t sel_cap, int32_t* sel_count, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if (!score_q || !score_e || !seq_lens || !evicted || !sel || !sel_count) return NOSA_ERR_ARG;
+  if (k_e < 0 || k_q < 0 || sel_cap < 1) return NOSA_ERR_ARG;
+  const int64_t k = (int64_t)k_e + k_q;
+  if ((int64_t)sel_cap < (k < dims->max_blocks ? k : (int64_t)dims->max_blocks)) return NOSA_ERR_ARG;
+  return from_hip(
+      nosa::launch_select(*dims, score_q, score_e, seq_lens, k_e, k_q, evicted, sel, sel_cap, sel_count, stream));
+}
+
+nosa_status nosa_swap_diff(const nosa_dims* dims, int32_t cap, const int32_t* prev, const int32_t* prev_count,
+                           const int32_t* cur, const int32_t* cur_count, int32_t* load, int32_t* load_count,
+                           int32_t* evict, int32_t* evict_count, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if (cap < 1 || !prev || !prev_count || !cur || !cur_count || !load || !load_count || !evict || !evict_count)
+    return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_swap_diff(*dims, cap, prev, prev_count, cur, cur_count, load, load_count, evict,
+                                         evict_count, stream));
+}
+
+nosa_status nosa_sparse_decode(const nosa_dims* dims, const uint16_t* q, const nosa_kv* kv, const int32_t* sel,
+                               const int32_t* sel_count, int32_t sel_cap, const int32_t* seq_lens,
+                               int32_t num_splits, float sm_scale, float* part_o, float* part_m,
+                               float* part_l, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if ((st = check_kv(dims, kv, true)) != NOSA_OK) return st;
+  if (!q || !sel || !sel_count || !seq_lens || !part_o || !part_m || !part_l) return NOSA_ERR_ARG;
+  if (!aligned16(q)) return NOSA_ERR_ARG;
+  if (sel_cap < 1 || num_splits < 1 || num_splits > 256) return NOSA_ERR_ARG;
+  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return NOSA_ERR_ARG;
+  if (kv->kind == NOSA_TABLE_PACKED_ROPE) {
+    if (!kv->q_pos || !(kv->rope_base > 1.f)) return NOSA_ERR_ARG;
+    if (dims->n_q_heads / dims->n_kv_heads > 8) return NOSA_ERR_UNSUPPORTED;
+  }
+  return from_hip(nosa::launch_decode(*dims, q, *kv, sel, sel_count, sel_cap, seq_lens, num_splits, sm_scale,
+                                      part_o, part_m, part_l, stream));
+}
+
+nosa_status nosa_combine(const nosa_dims* dims, int32_t num_splits, const float* part_o, const float* part_m,
+                         const float* part_l, float* o, float* m, float* l, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if (num_splits < 1 || num_splits > 256 || !part_o || !part_m || !part_l || !o || !m || !l)
+    return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_combine(*dims, num_splits, part_o, part_m, part_l, o, m, l, stream));
+}
+
+const char* nosa_status_string(nosa_status status) {
+  switch (status) {
+    case NOSA_OK: return "ok";
+    case NOSA_ERR_ARG: return "invalid argument";
+    case NOSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case NOSA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

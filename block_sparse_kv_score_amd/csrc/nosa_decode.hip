@@ -1,0 +1,446 @@
+// Split-K flash decoding over the selected pages, and the combine.
+//
+// Novita AI blog "How KV sparsity achieves 1.5x acceleration for vLLM",
+// Key techniques, 2. Attention modifications: FlashAttention walks the KV
+// blocks once, keeping O, the running row max and the running sum l, and
+// divides O by l at the end; the row max and l are cheap to return with O.
+// Here the pass runs only over the pages of the selected blocks (NOSA
+// summary, Methodology 1, dual selection; Spin summary 2.B, per-head
+// pages; 2.C, two-level index), split into contiguous chunks of the
+// selected list whose (o, m, l) partials the combine merges.
+//
+// Deferred RoPE (LazyAttention summary, Technical implementation,
+// 2. Decoding; Mathematical equivalence): stored keys carry only their
+// in-document rotation; the query is rotated by (query position - document
+// start) once per document, inside the loop, and the (page, document start)
+// pair comes from one packed 32-bit word, so the kernel still reads only K
+// and V.
+//
+// gfx950 mapping.  Workgroup = 4 waves = one (b, h) pair x one split.  The
+// work unit is a 64-token tile of a selected block; wave w takes tiles w,
+// w+4, ... and keeps its own online-softmax state, and the four states are
+// merged through LDS at the end.  Both products run on the matrix cores
+// (v_mfma_f32_16x16x32_bf16) with the GQA group packed block-diagonally:
+//   q . k:  A = keys (16 token rows x 32 k slots), B = the group's query,
+//           non-zero only where a column's token set owns the k slots, so
+//           every output column is a real (token set, head) pair and the
+//           softmax runs on useful lanes only.  The query stays in
+//           registers for the whole workgroup.
+//   P . V:  A = V^T (16 dims x 32 token slots), B = the tile's bf16
+//           probabilities (block diagonal again, one LDS round trip per
+//           tile); per-set partial outputs are summed once at the end.
+// Page layouts make every operand a single 16-byte load per lane:
+//   K page [D/8][bs][8] -> A rows of q.k (runs of 16 tokens x 16 bytes);
+//   V page [bs/8][D][8] -> A rows of P.V (8 tokens of one dim per load).
+// The step is HBM-bound (4 bytes of K+V per token-dim); the matrix cores keep
+// the arithmetic and operand broadcasts off the vector ALUs and out of the
+// register file, which is what lets two waves per SIMD stay resident.  The
+// query is exact bf16 and accumulation is fp32; probabilities enter P.V as
+// bf16 while l sums the fp32 values.  With deferred RoPE the rotated query
+// is split into bf16 hi + lo parts that fill spare head columns of the same
+// MFMA (|error| ~ 2^-16 relative).
+
+#include "nosa_launch.hpp"
+
+namespace nosa {
+
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = kDecWaves * kWave;
+constexpr int kTile = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct DecodeArgs {
+  Table t;
+  int Hq, bs, P, sel_cap;
+  float scale_log2;  // sm_scale * log2(e): scores kept in log2 units
+  float rope_base;
+  const uint16_t* q;
+  const uint16_t* k_pages;
+  const uint16_t* v_pages;
+  const int32_t* sel;
+  const int32_t* sel_count;
+  const int32_t* seq_lens;
+  const int32_t* q_pos;
+  float* part_o;
+  float* part_m;
+  float* part_l;
+};
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// D(16x16) += A(16x32) . B(32x16), bf16 inputs, fp32 accumulation.  Lane
+// l = 16 q + r supplies A row r and B column r for the eight k slots of lane
+// group q, and receives D rows 4q .. 4q+3 of column r.
+__device__ __forceinline__ floatx4 mfma_bf16(const uint4& a, const uint4& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// Columns of one MFMA: GE head slots per token set, 16 / GE token sets.  A
+// set's k slots are LPS lane groups, and the query operand is zero outside
+// its own set's slots (block diagonal), so one MFMA scores 16 * (16 / GE)
+// tokens against GE head slots with no padded output.  With deferred RoPE
+// head slots G .. 2G-1 carry the low bf16 part of the rotated query.
+template <int D, int G, bool ROPE>
+struct DecodeShape {
+  static constexpr int GR = ROPE ? 2 * G : G;  // head slots carrying data
+  static constexpr int GE = GR <= 8 ? 8 : 16;  // head slots per set
+  static constexpr int NC = 16 / GE;           // token sets per MFMA
+  static constexpr int LPS = 4 / NC;           // lane groups per set
+  static constexpr int TPM = 16 * NC;          // tokens per q.k MFMA
+  static constexpr int TH = kTile / TPM;       // token slices per tile
+  static constexpr int DPM = 8 * LPS;          // dims per q.k MFMA
+  static constexpr int NDS = D / DPM;          // q.k MFMAs per slice
+  static constexpr int NDT = D / 16;           // P.V dim tiles
+  static_assert(GR <= 16, "at most 16 head slots");
+};
+
+template <int D, int G, bool ROPE>
+struct DecodeSmem {
+  uint16_t p[kDecWaves][G][kTile];  // bf16 probabilities of the tile, per wave
+  float qf[ROPE ? G : 1][ROPE ? D : 1];
+  uint16_t qrot[ROPE ? kDecWaves : 1][ROPE ? 2 * G : 1][ROPE ? D : 8];  // rotated query, bf16 hi / lo rows
+  float mw[kDecWaves][G];
+  float lw[kDecWaves][G];
+  float ow[kDecWaves][G][D];
+};
+
+template <int D, int G, int KIND>
+__global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs a) {
+  constexpr bool ROPE = KIND == NOSA_TABLE_PACKED_ROPE;
+  using S = DecodeShape<D, G, ROPE>;
+  constexpr int GE = S::GE, LPS = S::LPS, TPM = S::TPM, TH = S::TH, NDS = S::NDS, NDT = S::NDT;
+  __shared__ DecodeSmem<D, G, ROPE> sh;
+
+  const int bh = blockIdx.x, p = blockIdx.y;
+  const int Hkv = a.t.Hkv;
+  const int b = bh / Hkv, h = bh % Hkv;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int lq = lane >> 4, lr = lane & 15;    // lane group, row/column
+  const int set_q = lq / LPS, dsub = lq % LPS;  // k slots of this lane group
+  const int cset = lr / GE, cg = lr % GE;       // column: token set, head slot
+  const bool qcol = cset == set_q && cg < S::GR; // query operand non-zero
+  const bool real = cg < G;                     // column of a real head
+
+  const int T = min(max(a.seq_lens[b], 0), a.t.max_blocks * a.bs);
+  const int nb = (T + a.bs - 1) / a.bs;
+  const int n = min(max(a.sel_count[bh], 0), a.sel_cap);
+  const int c = (n + a.P - 1) / a.P;
+  const int j0 = min(p * c, n), j1 = min(j0 + c, n);
+  const int tpb = a.bs / kTile;
+  const int ntiles = (j1 - j0) * tpb;
+  const uint16_t* qg = a.q + ((int64_t)b * a.Hq + (int64_t)h * G) * D;  // heads h*G.. are contiguous
+
+  // query operand of q.k, one 16-byte slice per d-step
+  uint4 qreg[NDS];
+  double theta = 0.0;
+  int64_t qpos = 0;
+  if constexpr (!ROPE) {
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const int o = ds * LPS + dsub;
+      qreg[ds] = qcol ? *reinterpret_cast<const uint4*>(qg + cg * D + 8 * o) : make_uint4(0, 0, 0, 0);
+    }
+  } else {
+    for (int k = threadIdx.x; k < G * D; k += kDecThreads) sh.qf[k / D][k % D] = bf16_to_f32(qg[k]);
+    if (lane < D / 2) theta = pow((double)a.rope_base, -2.0 * (double)lane / (double)D);
+    qpos = a.q_pos[b];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qreg[ds] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+  }
+  uint32_t cur_doc = 0xffffffffu;
+
+  float m_run = -INFINITY, l_run = 0.f;  // for head slot cg, log2 units
+  floatx4 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* selp = a.sel + (int64_t)bh * a.sel_cap;
+  for (int k = w; k < ntiles; k += kDecWaves) {
+    const int blk = j0 + k / tpb;
+    const int sub = k % tpb;
+    const int i = selp[blk];
+    if (i < 0 || i >= nb) {
+      if (lane == 0) flag_error(a.t.err);
+      continue;
+    }
+    uint32_t docb = 0;
+    const int64_t page = page_of<KIND>(a.t, bh, i, docb);
+    if (page < 0) {
+      if (lane == 0) flag_error(a.t.err);
+      continue;
+    }
+    const int ntok = min(kTile, T - (i * a.bs + sub * kTile));
+    if (ntok <= 0) continue;
+
+    // K as the A operand: row lr of token set set_q, octet ds*LPS + dsub
+    const uint4* kpg = reinterpret_cast<const uint4*>(a.k_pages + page * (int64_t)a.bs * D) + sub * kTile +
+                       16 * set_q + lr + (int64_t)dsub * a.bs;
+    uint4 kr[TH][NDS];
+#pragma unroll
+    for (int th = 0; th < TH; ++th)
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) kr[th][ds] = kpg[(int64_t)ds * LPS * a.bs + th * TPM];
+    // Slots past the end hold stale page data.  A row of the q.k MFMA mixes
+    // tokens of every token set (the query is zero outside a set's slots),
+    // and 0 * NaN would leak into valid scores, so zero those keys.
+    if (ntok < kTile) {
+#pragma unroll
+      for (int th = 0; th < TH; ++th)
+        if (th * TPM + 16 * set_q + lr >= ntok)
+#pragma unroll
+          for (int ds = 0; ds < NDS; ++ds) kr[th][ds] = make_uint4(0, 0, 0, 0);
+    }
+    // V^T as the A operand of P.V: dim 16 dt + lr, tokens 32 ks + 8 lq .. +8
+    const uint4* vpg = reinterpret_cast<const uint4*>(a.v_pages + page * (int64_t)a.bs * D) + (sub * 8 + lq) * D + lr;
+    uint4 vr[2][NDT];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vr[ks][dt] = vpg[ks * 4 * D + dt * 16];
+
+    if constexpr (ROPE) {
+      if (docb != cur_doc) {  // new document: query rotated by n - start
+        cur_doc = docb;
+        if (lane < D / 2) {
+          double sv, cv;
+          sincos((double)(qpos - (int64_t)docb * a.bs) * theta, &sv, &cv);
+          // pair (lane, lane + D/2): first half x1 c - x2 s, second x2 c + x1 s;
+          // bf16 hi part in rows 0..G-1, lo part in rows G..2G-1
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const double x1 = sh.qf[g][lane], x2 = sh.qf[g][lane + D / 2];
+            const float r1 = (float)(x1 * cv - x2 * sv);
+            const float r2 = (float)(x2 * cv + x1 * sv);
+            const uint16_t h1 = f32_to_bf16(r1), h2 = f32_to_bf16(r2);
+            sh.qrot[w][g][lane] = h1;
+            sh.qrot[w][g][lane + D / 2] = h2;
+            sh.qrot[w][G + g][lane] = f32_to_bf16(r1 - bf16_to_f32(h1));
+            sh.qrot[w][G + g][lane + D / 2] = f32_to_bf16(r2 - bf16_to_f32(h2));
+          }
+        }
+        wave_lds_sync();
+        const int slot = qcol ? cg : 0;
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+          const uint4 v = *reinterpret_cast<const uint4*>(&sh.qrot[w][slot][8 * (ds * LPS + dsub)]);
+          qreg[ds] = qcol ? v : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+
+    // scores: slice th, rows 4 lq + e of token set cset, head slot cg
+    float sv[TH][4];
+#pragma unroll
+    for (int th = 0; th < TH; ++th) {
+      floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) acc = mfma_bf16(kr[th][ds], qreg[ds], acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = acc[e];
+        if constexpr (ROPE) x += __shfl_xor(x, G, kWave);  // hi + lo parts
+        const int tok = th * TPM + 16 * cset + 4 * lq + e;
+        sv[th][e] = tok < ntok ? x * a.scale_log2 : -INFINITY;
+      }
+    }
+    // tile max per head slot: lanes sharing cg
+    float mx = -INFINITY;
+#pragma unroll
+    for (int th = 0; th < TH; ++th)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sv[th][e]);
+#pragma unroll
+    for (int off = GE; off < kWave; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+    const float mn = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - mn);
+    m_run = mn;
+    float psum = 0.f;
+#pragma unroll
+    for (int th = 0; th < TH; ++th) {
+      uint32_t pw[2];
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const float p0 = exp2f(sv[th][e] - mn), p1 = exp2f(sv[th][e + 1] - mn);
+        psum += p0 + p1;
+        pw[e / 2] = (uint32_t)f32_to_bf16(p0) | ((uint32_t)f32_to_bf16(p1) << 16);
+      }
+      if (real)
+        *reinterpret_cast<uint2*>(&sh.p[w][cg][th * TPM + 16 * cset + 4 * lq]) = make_uint2(pw[0], pw[1]);
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+
+    // tokens past the end hold stale page data: zero their V entries
+    if (ntok < kTile) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int nv = min(max(ntok - (32 * ks + 8 * lq), 0), 8);
+        uint32_t mk[4];
+#pragma unroll
+        for (int jd = 0; jd < 4; ++jd)
+          mk[jd] = (2 * jd < nv ? 0x0000ffffu : 0u) | (2 * jd + 1 < nv ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          vr[ks][dt].x &= mk[0];
+          vr[ks][dt].y &= mk[1];
+          vr[ks][dt].z &= mk[2];
+          vr[ks][dt].w &= mk[3];
+        }
+      }
+    }
+    wave_lds_sync();
+
+    // O^T(dims x head slots) += V^T . P, P block diagonal over token sets
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint4 pv = *reinterpret_cast<const uint4*>(&sh.p[w][real ? cg : 0][32 * ks + 8 * lq]);
+      const bool on = real && cset == set_q;
+      const uint4 pb = on ? pv : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma_bf16(vr[ks][dt], pb, oacc[dt]);
+    }
+    wave_lds_sync();
+  }
+
+  // per-wave totals: sum the token sets of each head slot, then the lanes
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int off = GE; off < 16; off <<= 1) oacc[dt][e] += __shfl_xor(oacc[dt][e], off, kWave);
+  float lsum = l_run;
+#pragma unroll
+  for (int off = GE; off < kWave; off <<= 1) lsum += __shfl_xor(lsum, off, kWave);
+  if (real && cset == 0) {
+    if (lq == 0) {
+      sh.mw[w][cg] = m_run;
+      sh.lw[w][cg] = lsum;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sh.ow[w][cg][16 * dt + 4 * lq + e] = oacc[dt][e];
+  }
+  __syncthreads();
+
+  for (int k = threadIdx.x; k < G * D; k += kDecThreads) {
+    const int g = k / D, d = k % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kDecWaves; ++ww)
+      if (sh.lw[ww][g] > 0.f) M = fmaxf(M, sh.mw[ww][g]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kDecWaves; ++ww) {
+      if (sh.lw[ww][g] > 0.f) {
+        const float f = exp2f(sh.mw[ww][g] - M);
+        L += sh.lw[ww][g] * f;
+        O += sh.ow[ww][g][d] * f;
+      }
+    }
+    const int64_t row = ((int64_t)b * a.Hq + (int64_t)h * G + g) * a.P + p;
+    a.part_o[row * D + d] = L > 0.f ? O / L : 0.f;
+    if (d == 0) {
+      a.part_m[row] = L > 0.f ? M * kLn2 : -INFINITY;
+      a.part_l[row] = L;
+    }
+  }
+}
+
+// One workgroup per (b, query head); thread per dim.
+__global__ void combine_kernel(int P, int D, const float* __restrict__ part_o, const float* __restrict__ part_m,
+                               const float* __restrict__ part_l, float* __restrict__ o, float* __restrict__ m,
+                               float* __restrict__ l) {
+  const int64_t row = blockIdx.x;
+  const float* pm = part_m + row * P;
+  const float* pl = part_l + row * P;
+  float M = -INFINITY;
+  for (int k = 0; k < P; ++k)
+    if (pl[k] > 0.f) M = fmaxf(M, pm[k]);
+  float L = 0.f;
+  for (int k = 0; k < P; ++k)
+    if (pl[k] > 0.f) L += pl[k] * expf(pm[k] - M);
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float acc = 0.f;
+    for (int k = 0; k < P; ++k)
+      if (pl[k] > 0.f) acc += pl[k] * expf(pm[k] - M) * part_o[(row * P + k) * D + d];
+    o[row * D + d] = L > 0.f ? acc / L : 0.f;
+  }
+  if (threadIdx.x == 0) {
+    m[row] = L > 0.f ? M : -INFINITY;
+    l[row] = L;
+  }
+}
+
+template <int D, int G>
+static void launch_decode_dg(dim3 grid, const DecodeArgs& a, int kind, hipStream_t stream) {
+  switch (kind) {
+    case NOSA_TABLE_FLAT:
+      decode_kernel<D, G, NOSA_TABLE_FLAT><<<grid, kDecThreads, 0, stream>>>(a);
+      break;
+    case NOSA_TABLE_TWO_LEVEL:
+      decode_kernel<D, G, NOSA_TABLE_TWO_LEVEL><<<grid, kDecThreads, 0, stream>>>(a);
+      break;
+    default:
+      if constexpr (G <= 8) decode_kernel<D, G, NOSA_TABLE_PACKED_ROPE><<<grid, kDecThreads, 0, stream>>>(a);
+      break;
+  }
+}
+
+template <int D>
+static void launch_decode_d(dim3 grid, const DecodeArgs& a, int G, int kind, hipStream_t stream) {
+  switch (G) {
+    case 1: launch_decode_dg<D, 1>(grid, a, kind, stream); break;
+    case 2: launch_decode_dg<D, 2>(grid, a, kind, stream); break;
+    case 4: launch_decode_dg<D, 4>(grid, a, kind, stream); break;
+    case 8: launch_decode_dg<D, 8>(grid, a, kind, stream); break;
+    default: launch_decode_dg<D, 16>(grid, a, kind, stream); break;
+  }
+}
+
+hipError_t launch_decode(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv,
+                         const int32_t* sel, const int32_t* sel_count, int32_t sel_cap,
+                         const int32_t* seq_lens, int32_t num_splits, float sm_scale,
+                         float* part_o, float* part_m, float* part_l, hipStream_t stream) {
+  DecodeArgs a;
+  a.t = make_table(d, kv);
+  a.Hq = d.n_q_heads;
+  a.bs = d.block_size;
+  a.P = num_splits;
+  a.sel_cap = sel_cap;
+  a.scale_log2 = sm_scale * kLog2e;
+  a.rope_base = kv.rope_base;
+  a.q = q;
+  a.k_pages = kv.k_pages;
+  a.v_pages = kv.v_pages;
+  a.sel = sel;
+  a.sel_count = sel_count;
+  a.seq_lens = seq_lens;
+  a.q_pos = kv.q_pos;
+  a.part_o = part_o;
+  a.part_m = part_m;
+  a.part_l = part_l;
+  const dim3 grid(d.batch * d.n_kv_heads, num_splits);
+  const int G = d.n_q_heads / d.n_kv_heads;
+  if (d.head_dim == 128)
+    launch_decode_d<128>(grid, a, G, kv.kind, stream);
+  else
+    launch_decode_d<64>(grid, a, G, kv.kind, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const nosa_dims& d, int32_t num_splits, const float* part_o,
+                          const float* part_m, const float* part_l, float* o, float* m, float* l,
+                          hipStream_t stream) {
+  combine_kernel<<<d.batch * d.n_q_heads, d.head_dim, 0, stream>>>(num_splits, d.head_dim, part_o, part_m,
+                                                                    part_l, o, m, l);
+  return hipGetLastError();
+}
+
+}  // namespace nosa

@@ -1,0 +1,49 @@
+// Internal launchers, one per kernel family.  Arguments are already checked
+// by the C-ABI layer (nosa_api.cpp); each launcher only picks the template
+// instance and enqueues the kernel on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nosa.h"
+#include "nosa_device.hpp"
+
+namespace nosa {
+
+Table make_table(const nosa_dims& d, const nosa_kv& kv);
+
+hipError_t launch_prefill(const nosa_dims& d, const nosa_kv& kv, const uint16_t* k_src,
+                          const uint16_t* v_src, const float* e_src, int32_t src_tokens,
+                          const int32_t* seq_lens, hipStream_t stream);
+
+hipError_t launch_build_summaries(const nosa_dims& d, const nosa_kv& kv, const int32_t* seq_lens,
+                                  float* k_summary, float* e_summary, hipStream_t stream);
+
+hipError_t launch_append(const nosa_dims& d, const nosa_kv& kv, const uint16_t* k_new,
+                         const uint16_t* v_new, const float* e_new, int32_t* seq_lens,
+                         float* k_summary, float* e_summary, hipStream_t stream);
+
+hipError_t launch_score(const nosa_dims& d, const uint16_t* q, const float* k_summary,
+                        const float* e_summary, const int32_t* seq_lens, float* score_q,
+                        float* score_e, hipStream_t stream);
+
+hipError_t launch_select(const nosa_dims& d, const float* score_q, const float* score_e,
+                         const int32_t* seq_lens, int32_t k_e, int32_t k_q, uint32_t* evicted,
+                         int32_t* sel, int32_t sel_cap, int32_t* sel_count, hipStream_t stream);
+
+hipError_t launch_swap_diff(const nosa_dims& d, int32_t cap, const int32_t* prev,
+                            const int32_t* prev_count, const int32_t* cur, const int32_t* cur_count,
+                            int32_t* load, int32_t* load_count, int32_t* evict,
+                            int32_t* evict_count, hipStream_t stream);
+
+hipError_t launch_decode(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv,
+                         const int32_t* sel, const int32_t* sel_count, int32_t sel_cap,
+                         const int32_t* seq_lens, int32_t num_splits, float sm_scale,
+                         float* part_o, float* part_m, float* part_l, hipStream_t stream);
+
+hipError_t launch_combine(const nosa_dims& d, int32_t num_splits, const float* part_o,
+                          const float* part_m, const float* part_l, float* o, float* m, float* l,
+                          hipStream_t stream);
+
+}  // namespace nosa

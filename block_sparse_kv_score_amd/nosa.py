@@ -1,0 +1,251 @@
+"""ctypes binding of libnosa (include/nosa.h), one Python function per C
+entry point, same names.  Argument marshalling only: every function checks
+that tensors live on the GPU with the expected dtype and contiguity, turns
+them into device pointers and calls the library on the current (or given)
+HIP stream.  There is no fallback: if libnosa.so is missing, every call
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnosa.so")
+
+NOSA_OK = 0
+NOSA_ERR_ARG = -1
+NOSA_ERR_UNSUPPORTED = -2
+NOSA_ERR_HIP = -3
+
+NOSA_TABLE_FLAT = 0
+NOSA_TABLE_TWO_LEVEL = 1
+NOSA_TABLE_PACKED_ROPE = 2
+NOSA_PACK_PAGE_BITS = 20
+
+ENTRY_POINTS = [
+    "nosa_prefill_pages",
+    "nosa_build_summaries",
+    "nosa_append",
+    "nosa_score_blocks",
+    "nosa_select",
+    "nosa_swap_diff",
+    "nosa_sparse_decode",
+    "nosa_combine",
+    "nosa_status_string",
+]
+
+
+class NosaError(RuntimeError):
+    def __init__(self, name: str, status: int):
+        super().__init__(f"{name} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+class nosa_dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("sub_block", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+    ]
+
+
+class nosa_kv(ctypes.Structure):
+    _fields_ = [
+        ("k_pages", ctypes.c_void_p),
+        ("v_pages", ctypes.c_void_p),
+        ("e_pages", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int64),
+        ("kind", ctypes.c_int32),
+        ("dir_entries", ctypes.c_int32),
+        ("table", ctypes.c_void_p),
+        ("directory", ctypes.c_void_p),
+        ("segments", ctypes.c_void_p),
+        ("num_segments", ctypes.c_int64),
+        ("seg_log2", ctypes.c_int32),
+        ("blocks_log2", ctypes.c_int32),
+        ("packed", ctypes.c_void_p),
+        ("q_pos", ctypes.c_void_p),
+        ("rope_base", ctypes.c_float),
+        ("err_flags", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_F32 = ctypes.c_float
+_DIMS = ctypes.POINTER(nosa_dims)
+_KV = ctypes.POINTER(nosa_kv)
+
+_SIGNATURES = {
+    "nosa_prefill_pages": [_DIMS, _KV, _P, _P, _P, _I32, _P, _P],
+    "nosa_build_summaries": [_DIMS, _KV, _P, _P, _P, _P],
+    "nosa_append": [_DIMS, _KV, _P, _P, _P, _P, _P, _P, _P],
+    "nosa_score_blocks": [_DIMS, _P, _P, _P, _P, _P, _P, _P],
+    "nosa_select": [_DIMS, _P, _P, _P, _I32, _I32, _P, _P, _I32, _P, _P],
+    "nosa_swap_diff": [_DIMS, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "nosa_sparse_decode": [_DIMS, _P, _KV, _P, _P, _I32, _P, _I32, _F32, _P, _P, _P, _P],
+    "nosa_combine": [_DIMS, _I32, _P, _P, _P, _P, _P, _P, _P],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_kv_score_amd.build_lib`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int32
+        L.nosa_status_string.argtypes = [ctypes.c_int32]
+        L.nosa_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().nosa_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _dev(t: torch.Tensor | None, name: str, dtypes, optional: bool = False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(lib(), name)(*args)
+    if st != NOSA_OK:
+        raise NosaError(name, st)
+
+
+def make_dims(B, Hq, Hkv, D, bs, ss, max_blocks) -> nosa_dims:
+    return nosa_dims(int(B), int(Hq), int(Hkv), int(D), int(bs), int(ss), int(max_blocks))
+
+
+def make_kv(k_pages, v_pages, e_pages, kind, *, table=None, directory=None, segments=None,
+            seg_log2=0, blocks_log2=0, packed=None, q_pos=None, rope_base=0.0,
+            err_flags=None) -> nosa_kv:
+    """Build the nosa_kv descriptor.  The tensors must outlive every call
+    that receives the descriptor."""
+    kv = nosa_kv()
+    kv.k_pages = _dev(k_pages, "k_pages", _BF16_LIKE)
+    kv.v_pages = _dev(v_pages, "v_pages", _BF16_LIKE)
+    kv.e_pages = _dev(e_pages, "e_pages", (torch.float32,))
+    kv.num_pages = int(k_pages.shape[0])
+    kv.kind = int(kind)
+    kv.table = _dev(table, "table", (torch.int32,), optional=True)
+    kv.directory = _dev(directory, "directory", (torch.int32,), optional=True)
+    kv.dir_entries = int(directory.numel()) if directory is not None else 0
+    kv.segments = _dev(segments, "segments", (torch.int32,), optional=True)
+    kv.num_segments = int(segments.shape[0]) if segments is not None else 0
+    kv.seg_log2 = int(seg_log2)
+    kv.blocks_log2 = int(blocks_log2)
+    kv.packed = _dev(packed, "packed", (torch.int32, torch.uint32), optional=True)
+    kv.q_pos = _dev(q_pos, "q_pos", (torch.int32,), optional=True)
+    kv.rope_base = float(rope_base)
+    kv.err_flags = _dev(err_flags, "err_flags", (torch.int32,), optional=True)
+    return kv
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def nosa_prefill_pages(dims, kv, k_src, v_src, e_src, seq_lens, stream=None):
+    src_tokens = int(k_src.shape[-2])
+    _call("nosa_prefill_pages", ctypes.byref(dims), ctypes.byref(kv),
+          _dev(k_src, "k_src", _BF16_LIKE), _dev(v_src, "v_src", _BF16_LIKE),
+          _dev(e_src, "e_src", (torch.float32,)), src_tokens,
+          _dev(seq_lens, "seq_lens", (torch.int32,)), _stream(stream))
+
+
+def nosa_build_summaries(dims, kv, seq_lens, k_summary, e_summary, stream=None):
+    _call("nosa_build_summaries", ctypes.byref(dims), ctypes.byref(kv),
+          _dev(seq_lens, "seq_lens", (torch.int32,)), _dev(k_summary, "k_summary", (torch.float32,)),
+          _dev(e_summary, "e_summary", (torch.float32,)), _stream(stream))
+
+
+def nosa_append(dims, kv, k_new, v_new, e_new, seq_lens, k_summary, e_summary, stream=None):
+    _call("nosa_append", ctypes.byref(dims), ctypes.byref(kv),
+          _dev(k_new, "k_new", _BF16_LIKE), _dev(v_new, "v_new", _BF16_LIKE),
+          _dev(e_new, "e_new", (torch.float32,)), _dev(seq_lens, "seq_lens", (torch.int32,)),
+          _dev(k_summary, "k_summary", (torch.float32,)), _dev(e_summary, "e_summary", (torch.float32,)),
+          _stream(stream))
+
+
+def nosa_score_blocks(dims, q, k_summary, e_summary, seq_lens, score_q, score_e, stream=None):
+    _call("nosa_score_blocks", ctypes.byref(dims), _dev(q, "q", _BF16_LIKE),
+          _dev(k_summary, "k_summary", (torch.float32,)), _dev(e_summary, "e_summary", (torch.float32,)),
+          _dev(seq_lens, "seq_lens", (torch.int32,)), _dev(score_q, "score_q", (torch.float32,)),
+          _dev(score_e, "score_e", (torch.float32,)), _stream(stream))
+
+
+def nosa_select(dims, score_q, score_e, seq_lens, k_e, k_q, evicted, sel, sel_count, stream=None):
+    _call("nosa_select", ctypes.byref(dims), _dev(score_q, "score_q", (torch.float32,)),
+          _dev(score_e, "score_e", (torch.float32,)), _dev(seq_lens, "seq_lens", (torch.int32,)),
+          int(k_e), int(k_q), _dev(evicted, "evicted", (torch.int32, torch.uint32)),
+          _dev(sel, "sel", (torch.int32,)), int(sel.shape[-1]),
+          _dev(sel_count, "sel_count", (torch.int32,)), _stream(stream))
+
+
+def nosa_swap_diff(dims, prev, prev_count, cur, cur_count, load, load_count, evict, evict_count,
+                   stream=None):
+    cap = int(prev.shape[-1])
+    for t, n in ((cur, "cur"), (load, "load"), (evict, "evict")):
+        if int(t.shape[-1]) != cap:
+            raise ValueError(f"{n} must have the same last dimension as prev ({cap})")
+    _call("nosa_swap_diff", ctypes.byref(dims), cap,
+          _dev(prev, "prev", (torch.int32,)), _dev(prev_count, "prev_count", (torch.int32,)),
+          _dev(cur, "cur", (torch.int32,)), _dev(cur_count, "cur_count", (torch.int32,)),
+          _dev(load, "load", (torch.int32,)), _dev(load_count, "load_count", (torch.int32,)),
+          _dev(evict, "evict", (torch.int32,)), _dev(evict_count, "evict_count", (torch.int32,)),
+          _stream(stream))
+
+
+def nosa_sparse_decode(dims, q, kv, sel, sel_count, seq_lens, num_splits, sm_scale,
+                       part_o, part_m, part_l, stream=None):
+    _call("nosa_sparse_decode", ctypes.byref(dims), _dev(q, "q", _BF16_LIKE), ctypes.byref(kv),
+          _dev(sel, "sel", (torch.int32,)), _dev(sel_count, "sel_count", (torch.int32,)),
+          int(sel.shape[-1]), _dev(seq_lens, "seq_lens", (torch.int32,)), int(num_splits),
+          float(sm_scale), _dev(part_o, "part_o", (torch.float32,)),
+          _dev(part_m, "part_m", (torch.float32,)), _dev(part_l, "part_l", (torch.float32,)),
+          _stream(stream))
+
+
+def nosa_combine(dims, num_splits, part_o, part_m, part_l, o, m, l, stream=None):
+    _call("nosa_combine", ctypes.byref(dims), int(num_splits),
+          _dev(part_o, "part_o", (torch.float32,)), _dev(part_m, "part_m", (torch.float32,)),
+          _dev(part_l, "part_l", (torch.float32,)), _dev(o, "o", (torch.float32,)),
+          _dev(m, "m", (torch.float32,)), _dev(l, "l", (torch.float32,)), _stream(stream))

@@ -1,0 +1,180 @@
+"""Device buffers for one decode-step workload and the call sequence of a
+step.  Marshalling only: every step of the path runs in libnosa's kernels;
+this module allocates buffers with PyTorch and calls the C-ABI entry points
+in order on one stream.
+
+Call sequence of decode step t (1-based):
+  nosa_append            (workloads that append a token per step)
+  nosa_score_blocks      (skipped when every block is selected)
+  nosa_select            ( "            "              " )
+  nosa_swap_diff         against the previous step's selection
+  nosa_sparse_decode     split-K over the selected pages
+  nosa_combine           -> O, rowmax m, l
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import nosa
+from .synth import Inputs
+from .workloads import TABLE_FLAT, TABLE_PACKED_ROPE, TABLE_TWO_LEVEL, Workload
+
+_KIND = {TABLE_FLAT: nosa.NOSA_TABLE_FLAT, TABLE_TWO_LEVEL: nosa.NOSA_TABLE_TWO_LEVEL,
+         TABLE_PACKED_ROPE: nosa.NOSA_TABLE_PACKED_ROPE}
+
+BF16_NAN = -1  # 0xFFFF as int16: a NaN bit pattern for never-written slots
+
+
+def _i32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int32))
+
+
+class DecodeSession:
+    """All device state of one workload: page pools, tables, summaries,
+    selection state and step outputs."""
+
+    def __init__(self, w: Workload, inp: Inputs, splits: int | None = None, device: str = "cuda",
+                 poison: bool = True, stream: torch.cuda.Stream | None = None):
+        self.w, self.inp = w, inp
+        self.P = int(splits or w.splits)
+        self.dev = torch.device(device)
+        self.stream = stream
+        self.step_index = 0
+        B, Hq, Hkv, D, bs, ss, MB = w.B, w.Hq, w.Hkv, w.D, w.bs, w.ss, w.max_blocks
+        self.dims = nosa.make_dims(B, Hq, Hkv, D, bs, ss, MB)
+        self.cap = MB if w.select_all else min(w.k, MB)
+        CS = MB * w.nsub
+        dev = self.dev
+        fill = float("nan") if poison else 0.0
+
+        # page pools (never-written slots hold NaN patterns when poisoned)
+        self.k_pages = torch.full((w.num_pages, bs * D), BF16_NAN if poison else 0, dtype=torch.int16, device=dev)
+        self.v_pages = torch.full_like(self.k_pages, BF16_NAN if poison else 0)
+        self.e_pages = torch.full((w.num_pages, bs), fill, dtype=torch.float32, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.table = self.directory = self.segments = self.packed = self.q_pos = None
+        if w.table == TABLE_FLAT:
+            self.table = torch.from_numpy(inp.pages).to(dev)
+        elif w.table == TABLE_TWO_LEVEL:
+            self.directory = torch.from_numpy(inp.directory).to(dev)
+            self.segments = torch.from_numpy(inp.segments).to(dev)
+        else:
+            self.packed = _i32(inp.packed).to(dev)
+            self.q_pos = torch.from_numpy(inp.q_pos).to(dev)
+        self.kv = nosa.make_kv(self.k_pages, self.v_pages, self.e_pages, _KIND[w.table],
+                               table=self.table, directory=self.directory, segments=self.segments,
+                               seg_log2=w.seg_log2, blocks_log2=w.blocks_log2, packed=self.packed,
+                               q_pos=self.q_pos, rope_base=w.rope_base, err_flags=self.err)
+
+        self.seq_lens = torch.full((B,), w.T0, dtype=torch.int32, device=dev)
+        self.k_summary = torch.full((B, Hkv, D // 4, CS, 4), fill, dtype=torch.float32, device=dev)
+        self.e_summary = torch.full((B, Hkv, CS), fill, dtype=torch.float32, device=dev)
+        self.score_q = torch.full((B, Hkv, MB), fill, dtype=torch.float32, device=dev)
+        self.score_e = torch.full_like(self.score_q, fill)
+        self.evicted = torch.zeros((B, Hkv, (MB + 31) // 32), dtype=torch.int32, device=dev)
+        # selections ping-pong between two buffers: step t writes buffer t % 2
+        # and diffs against buffer (t - 1) % 2 (both start empty)
+        self.sel_bufs = [torch.full((B, Hkv, self.cap), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.cnt_bufs = [torch.zeros((B, Hkv), dtype=torch.int32, device=dev) for _ in range(2)]
+        self.sel, self.sel_count = self.sel_bufs[0], self.cnt_bufs[0]
+        self.prev, self.prev_count = self.sel_bufs[1], self.cnt_bufs[1]
+        self.load = torch.full_like(self.sel, -1)
+        self.load_count = torch.zeros_like(self.sel_count)
+        self.evict = torch.full_like(self.sel, -1)
+        self.evict_count = torch.zeros_like(self.sel_count)
+        self.part_o = torch.full((B, Hq, self.P, D), fill, dtype=torch.float32, device=dev)
+        self.part_m = torch.full((B, Hq, self.P), fill, dtype=torch.float32, device=dev)
+        self.part_l = torch.full_like(self.part_m, fill)
+        self.o = torch.full((B, Hq, D), fill, dtype=torch.float32, device=dev)
+        self.m = torch.full((B, Hq), fill, dtype=torch.float32, device=dev)
+        self.l = torch.full_like(self.m, fill)
+
+        # per-step queries and appended tokens, resident before timing
+        n_steps = w.n_append if w.append else 1
+        self.q_all = torch.from_numpy(np.stack([inp.q(t).view(np.int16) for t in range(1, n_steps + 1)])).to(dev)
+        if w.append:
+            A = w.n_append
+            self.k_new = torch.from_numpy(np.ascontiguousarray(
+                inp.K[:, :, w.T0:w.T0 + A].transpose(2, 0, 1, 3)).view(np.int16)).to(dev)
+            self.v_new = torch.from_numpy(np.ascontiguousarray(
+                inp.V[:, :, w.T0:w.T0 + A].transpose(2, 0, 1, 3)).view(np.int16)).to(dev)
+            self.e_new = torch.from_numpy(np.ascontiguousarray(inp.e[:, :, w.T0:w.T0 + A].transpose(2, 0, 1))).to(dev)
+        if w.select_all:
+            # every block, fixed: the static list and an empty "previous" one
+            nb = -(-w.T0 // bs)
+            sel = np.full((B, Hkv, self.cap), -1, dtype=np.int32)
+            sel[:, :, :nb] = np.arange(nb, dtype=np.int32)
+            self.all_sel = torch.from_numpy(sel).to(dev)
+            self.all_count = torch.full((B, Hkv), nb, dtype=torch.int32, device=dev)
+        self.prefill()
+
+    # ------------------------------------------------------------------
+    def prefill(self):
+        """Write the context into pages and build the summaries (Index)."""
+        w, inp = self.w, self.inp
+        k_src = torch.from_numpy(inp.K.view(np.int16)).to(self.dev)
+        v_src = torch.from_numpy(inp.V.view(np.int16)).to(self.dev)
+        e_src = torch.from_numpy(inp.e).to(self.dev)
+        nosa.nosa_prefill_pages(self.dims, self.kv, k_src, v_src, e_src, self.seq_lens, self.stream)
+        nosa.nosa_build_summaries(self.dims, self.kv, self.seq_lens, self.k_summary, self.e_summary, self.stream)
+        torch.cuda.synchronize()
+        del k_src, v_src, e_src
+
+    def q(self, t: int) -> torch.Tensor:
+        return self.q_all[t - 1]
+
+    # ------------------------------------------------------------------
+    # individual stages (the step is their sequence)
+    def append(self, t: int):
+        nosa.nosa_append(self.dims, self.kv, self.k_new[t - 1], self.v_new[t - 1], self.e_new[t - 1],
+                         self.seq_lens, self.k_summary, self.e_summary, self.stream)
+
+    def score(self, t: int):
+        nosa.nosa_score_blocks(self.dims, self.q(t), self.k_summary, self.e_summary, self.seq_lens,
+                               self.score_q, self.score_e, self.stream)
+
+    def select(self):
+        nosa.nosa_select(self.dims, self.score_q, self.score_e, self.seq_lens, self.w.k_e, self.w.k_q,
+                         self.evicted, self.sel, self.sel_count, self.stream)
+
+    def swap_diff(self):
+        nosa.nosa_swap_diff(self.dims, self.prev, self.prev_count, self.sel, self.sel_count,
+                            self.load, self.load_count, self.evict, self.evict_count, self.stream)
+
+    def decode(self, t: int):
+        nosa.nosa_sparse_decode(self.dims, self.q(t), self.kv, self.sel, self.sel_count, self.seq_lens,
+                                self.P, self.w.sm_scale, self.part_o, self.part_m, self.part_l, self.stream)
+
+    def combine(self):
+        nosa.nosa_combine(self.dims, self.P, self.part_o, self.part_m, self.part_l, self.o, self.m, self.l,
+                          self.stream)
+
+    def use_buffers(self, t: int):
+        """Point sel / prev at the buffers of step t."""
+        if self.w.select_all:
+            self.sel, self.sel_count = self.all_sel, self.all_count
+            if t == 1:
+                self.prev, self.prev_count = self.sel_bufs[0], self.cnt_bufs[0]  # still empty
+            else:
+                self.prev, self.prev_count = self.all_sel, self.all_count
+        else:
+            self.sel, self.sel_count = self.sel_bufs[t % 2], self.cnt_bufs[t % 2]
+            self.prev, self.prev_count = self.sel_bufs[(t - 1) % 2], self.cnt_bufs[(t - 1) % 2]
+
+    def step(self, t: int | None = None):
+        """One whole decode step (all hot-path stages), enqueued on the stream."""
+        t = self.step_index + 1 if t is None else t
+        w = self.w
+        self.use_buffers(t)
+        if w.append:
+            self.append(t)
+        if not w.select_all:
+            self.score(t)
+            self.select()
+        self.swap_diff()
+        self.decode(t)
+        self.combine()
+        self.step_index = t
+        return t

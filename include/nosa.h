@@ -1,0 +1,240 @@
+/*
+ * nosa.h -- C ABI of libnosa: one decode step of NOSA-style block-sparse
+ * attention over a paged KV cache, on AMD Instinct MI355X (gfx950).
+ *
+ * The step, per (sequence b, KV head h):
+ *   append      -- write this step's key/value/eviction logit, refresh the
+ *                  summary of the sub-block it lands in           (support)
+ *   score       -- query-aware and eviction block scores by two-stage
+ *                  pooling (sub-block mean, then block max)
+ *   select      -- monotone eviction set (budget k_e) + query-aware set
+ *                  (budget k_q)
+ *   swap_diff   -- blocks to load / drop against the previous selection
+ *   decode      -- split-K flash decoding over the selected pages only
+ *   combine     -- merge of the split partials into (O, rowmax, l)
+ *
+ * Sources (web pages, cited by title and section):
+ *   [NOSA]   "NOSA: Native and Offloadable Sparse Attention" summary,
+ *            gist.science 2510.13602 -- Methodology 1 (Algorithm: NOSA):
+ *            dual selection, locality guarantee, block-wise two-stage
+ *            pooling, ED-DMA; Methodology 2 (System: NOSI): block-sized KV
+ *            layout and the set-difference kernel for block swapping.
+ *   [SPIN]   "Unifying Sparse Attention with Hierarchical Memory for
+ *            Scalable Long-Context LLM Serving" summary, gist.science
+ *            2604.26837 -- 2.A Index/Select/Attention split over a shared
+ *            page substrate; 2.B per-head physical pages; 2.C two-level
+ *            page index (small GPU directory -> segments).
+ *   [LAZY]   "LazyAttention" summary, gist.science 2606.04302 -- Technical
+ *            implementation, 2. Decoding (query rotated only when the
+ *            document changes, (block id, offset) bit-packed in one word,
+ *            K and V are the only traffic); Mathematical equivalence.
+ *   [NOVITA] Novita AI blog "How KV sparsity achieves 1.5x acceleration for
+ *            vLLM" -- Key techniques, 2. Attention modifications (one-pass
+ *            FlashAttention; rowmax and l returned with O).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless stated otherwise, owned by the
+ *     caller; the library allocates nothing and keeps no state between
+ *     calls.  Calls are asynchronous on `stream` and never synchronise.
+ *   - Host-side argument checks run before any launch; a failed check
+ *     returns NOSA_ERR_ARG / NOSA_ERR_UNSUPPORTED and launches nothing.
+ *     A failed launch returns NOSA_ERR_HIP.
+ *   - Device-data contract violations (a page id outside [0, num_pages), a
+ *     selected block outside [0, nb), a sequence longer than the capacity)
+ *     never fault: the offending block or token is skipped and bit 0 of
+ *     `nosa_kv.err_flags[0]` is set when that pointer is non-null.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Multi-index shapes are row-major; G = n_q_heads / n_kv_heads and
+ *     query head j reads KV head j / G.
+ *
+ * Page layouts (one page = one logical block of one (b, h) pair):
+ *   K page, bf16 [head_dim/8][block_size][8]: element (token t, dim d) at
+ *          ((d/8) * block_size + t) * 8 + d % 8.
+ *   V page, bf16 [block_size/8][head_dim][8]: element (t, d) at
+ *          ((t/8) * head_dim + d) * 8 + t % 8.
+ *   E page, fp32 [block_size]: eviction logit of token t.
+ * Summary layouts (CS = max_blocks * nsub, nsub = block_size / sub_block):
+ *   k_summary fp32 [B][Hkv][head_dim/4][CS][4]: mean key of sub-block s,
+ *          dim d, at ((bh * head_dim/4 + d/4) * CS + s) * 4 + d % 4.
+ *   e_summary fp32 [B][Hkv][CS]: mean eviction logit of sub-block s.
+ */
+#ifndef NOSA_H
+#define NOSA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t nosa_status;
+#define NOSA_OK               0
+#define NOSA_ERR_ARG         -1  /* null pointer, bad size or shape          */
+#define NOSA_ERR_UNSUPPORTED -2  /* valid but not built (head_dim, sizes)    */
+#define NOSA_ERR_HIP         -3  /* a HIP launch failed                      */
+
+#define NOSA_TABLE_FLAT        0 /* table[b][h][i] -> page                   */
+#define NOSA_TABLE_TWO_LEVEL   1 /* directory -> segment -> page  [SPIN 2.C] */
+#define NOSA_TABLE_PACKED_ROPE 2 /* packed (page, document start) + RoPE     */
+
+#define NOSA_PACK_PAGE_BITS 20   /* packed word: page id in bits 0..19,
+                                    document start (in blocks) in bits 20..31 */
+
+/* Sizes shared by every call.
+ *   head_dim    D: 64 or 128.
+ *   block_size  bs: tokens per block (= per page); 64, 128 or 256.
+ *   sub_block   ss: divides bs; nsub = bs / ss is a power of two <= 64.
+ *   max_blocks  logical block capacity per (b, h): 1..8192.  Sequences may
+ *               hold at most max_blocks * bs tokens.
+ *   n_q_heads % n_kv_heads == 0 and G = n_q_heads / n_kv_heads <= 16.    */
+typedef struct nosa_dims {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t sub_block;
+  int32_t max_blocks;
+} nosa_dims;
+
+/* The paged KV cache and its logical->physical page table [SPIN 2.B, 2.C].
+ *   k_pages, v_pages, e_pages: num_pages pages each (layouts above).
+ *   kind NOSA_TABLE_FLAT:       table int32 [B][Hkv][max_blocks].
+ *   kind NOSA_TABLE_TWO_LEVEL:  key = ((b*Hkv + h) << blocks_log2) | i;
+ *        seg = directory[key >> seg_log2] (int32 [dir_entries], -1 = none);
+ *        page = segments[(seg << seg_log2) | (key & (2^seg_log2 - 1))]
+ *        (int32 [num_segments << seg_log2]).  Requires
+ *        max_blocks <= 2^blocks_log2, seg_log2 <= blocks_log2 and
+ *        dir_entries >= (B*Hkv << blocks_log2) >> seg_log2.
+ *   kind NOSA_TABLE_PACKED_ROPE [LAZY 2. Decoding]: packed uint32
+ *        [B][Hkv][max_blocks]; page = word & 0xFFFFF, document start
+ *        position = (word >> 20) * block_size.  q_pos int32 [B] is the
+ *        query position n; stored keys carry the rotation of their position
+ *        inside their document, and decode scores block tokens with the
+ *        query rotated by n - document start (rotate-half RoPE,
+ *        theta_i = rope_base^(-2i/D)).  Only nosa_sparse_decode applies the
+ *        rotation; the other calls use the packed word for the page only.
+ *   err_flags: optional int32 [1]; bit 0 is set on a device-data contract
+ *        violation (see above).  Never cleared by the library.            */
+typedef struct nosa_kv {
+  uint16_t* k_pages;
+  uint16_t* v_pages;
+  float* e_pages;
+  int64_t num_pages;
+  int32_t kind;
+  int32_t dir_entries;
+  const int32_t* table;
+  const int32_t* directory;
+  const int32_t* segments;
+  int64_t num_segments;
+  int32_t seg_log2;
+  int32_t blocks_log2;
+  const uint32_t* packed;
+  const int32_t* q_pos;
+  float rope_base;
+  int32_t* err_flags;
+} nosa_kv;
+
+/* Index op [SPIN 2.A]: copy the first seq_lens[b] tokens of every (b, h)
+ * from contiguous sources into their pages.
+ *   k_src, v_src: bf16 [B][Hkv][src_tokens][D];  e_src: fp32 [B][Hkv][src_tokens].
+ *   seq_lens int32 [B], each <= min(src_tokens, max_blocks * bs).
+ * Page slots past seq_lens[b] are left as they are, except that unused
+ * token slots of a partially filled V group of 8 are written with zeros.   */
+nosa_status nosa_prefill_pages(const nosa_dims* dims, const nosa_kv* kv,
+                               const uint16_t* k_src, const uint16_t* v_src, const float* e_src,
+                               int32_t src_tokens, const int32_t* seq_lens, hipStream_t stream);
+
+/* Index op, pooling inputs [NOSA block-wise implementation; NOSI fused
+ * pooling]: the fp32 mean key and mean eviction logit of every non-empty
+ * sub-block of every (b, h), over its present tokens (sum in float64 in
+ * token order, one rounding to fp32).  Entries of empty sub-blocks are not
+ * written.  Layouts above.                                                  */
+nosa_status nosa_build_summaries(const nosa_dims* dims, const nosa_kv* kv, const int32_t* seq_lens,
+                                 float* k_summary, float* e_summary, hipStream_t stream);
+
+/* Decode-step append: token T = seq_lens[b] of every (b, h) gets
+ *   k_new, v_new: bf16 [B][Hkv][D];  e_new: fp32 [B][Hkv];
+ * the summary of the sub-block holding it is recomputed exactly as
+ * nosa_build_summaries would, and seq_lens[b] becomes T + 1 (in place).
+ * The page of the block holding token T must exist in the table.          */
+nosa_status nosa_append(const nosa_dims* dims, const nosa_kv* kv,
+                        const uint16_t* k_new, const uint16_t* v_new, const float* e_new,
+                        int32_t* seq_lens, float* k_summary, float* e_summary, hipStream_t stream);
+
+/* Select, scoring [NOSA dual selection, block-wise implementation, ED-DMA]:
+ * for block i < nb = ceil(T / bs), T = seq_lens[b],
+ *   score_q[b][h][i] = max over non-empty sub-blocks j of
+ *                      (qbar . kbar_ij) / sqrt(D),  qbar = mean of the G
+ *                      query heads of KV head h (the group-mean per-token
+ *                      score, mean-pooled, by linearity), float64
+ *                      accumulation, rounded once to fp32;
+ *   score_e[b][h][i] = max over non-empty sub-blocks of the mean eviction
+ *                      logit (raw logits, no exponent).
+ *   q: bf16 [B][Hq][D].  score_q, score_e: fp32 [B][Hkv][max_blocks];
+ * entries i >= nb are not written.                                         */
+nosa_status nosa_score_blocks(const nosa_dims* dims, const uint16_t* q,
+                              const float* k_summary, const float* e_summary, const int32_t* seq_lens,
+                              float* score_q, float* score_e, hipStream_t stream);
+
+/* Select, dual selection [NOSA dual selection, locality guarantee]:
+ *   candidates C = { i < nb : evicted bit i clear };
+ *   Gamma_e = the min(k_e, |C|) best of C by (score_e desc, i asc); every
+ *             other candidate gets its evicted bit set (never cleared);
+ *   Gamma_q = the min(k_q, nb - |Gamma_e|) best of the blocks not in
+ *             Gamma_e by (score_q desc, i asc);
+ *   sel[b][h][0 .. sel_count) = Gamma_e U Gamma_q, ascending.
+ * After the call Gamma_e = { i < nb : evicted bit i clear }.
+ *   evicted: uint32 [B][Hkv][ceil(max_blocks / 32)], bit i of word i/32;
+ *            in/out, all zero before the first step.
+ *   sel: int32 [B][Hkv][sel_cap], sel_cap >= min(k_e + k_q, max_blocks);
+ *   sel_count: int32 [B][Hkv].  k_e, k_q >= 0.                             */
+nosa_status nosa_select(const nosa_dims* dims, const float* score_q, const float* score_e,
+                        const int32_t* seq_lens, int32_t k_e, int32_t k_q, uint32_t* evicted,
+                        int32_t* sel, int32_t sel_cap, int32_t* sel_count, hipStream_t stream);
+
+/* Block-swap set differences [NOSA, NOSI set-difference kernel]:
+ *   load  = cur  minus prev (in cur's order),
+ *   evict = prev minus cur  (in prev's order),
+ * per (b, h), over lists int32 [B][Hkv][cap] with counts int32 [B][Hkv].
+ * Entries must lie in [0, max_blocks) and a list holds no duplicates;
+ * entries outside that range are skipped.  Outputs may not alias inputs. */
+nosa_status nosa_swap_diff(const nosa_dims* dims, int32_t cap,
+                           const int32_t* prev, const int32_t* prev_count,
+                           const int32_t* cur, const int32_t* cur_count,
+                           int32_t* load, int32_t* load_count,
+                           int32_t* evict, int32_t* evict_count, hipStream_t stream);
+
+/* Attention, split-K over the selected pages [NOVITA one-pass FlashAttention;
+ * LAZY decoding for NOSA_TABLE_PACKED_ROPE].  The selected list of (b, h)
+ * is cut into num_splits contiguous chunks of ceil(n / num_splits) blocks;
+ * for chunk p and query head j of the group,
+ *   s = sm_scale * q_j . k over the present tokens of the chunk's blocks,
+ *   part_m = max s, part_l = sum exp(s - part_m),
+ *   part_o = sum exp(s - part_m) v / part_l;
+ * an empty chunk gives part_m = -inf, part_l = 0, part_o = 0.
+ *   q: bf16 [B][Hq][D];  sel: int32 [B][Hkv][sel_cap];  sel_count [B][Hkv];
+ *   part_o fp32 [B][Hq][num_splits][D];  part_m, part_l fp32 [B][Hq][num_splits].
+ * 1 <= num_splits <= 256.                                                  */
+nosa_status nosa_sparse_decode(const nosa_dims* dims, const uint16_t* q, const nosa_kv* kv,
+                               const int32_t* sel, const int32_t* sel_count, int32_t sel_cap,
+                               const int32_t* seq_lens, int32_t num_splits, float sm_scale,
+                               float* part_o, float* part_m, float* part_l, hipStream_t stream);
+
+/* Attention, combine [NOVITA: return rowmax and l with O]:
+ *   m = max_p part_m (over p with part_l > 0), l = sum_p part_l e^(part_m - m),
+ *   O = sum_p part_l e^(part_m - m) part_o / l;  all empty: O = 0, m = -inf, l = 0.
+ *   o fp32 [B][Hq][D];  m, l fp32 [B][Hq] (natural-log units of s).        */
+nosa_status nosa_combine(const nosa_dims* dims, int32_t num_splits,
+                         const float* part_o, const float* part_m, const float* part_l,
+                         float* o, float* m, float* l, hipStream_t stream);
+
+/* Static description of a status code (never null). Host only.           */
+const char* nosa_status_string(nosa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NOSA_H */

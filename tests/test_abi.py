@@ -1,0 +1,128 @@
+"""The C-ABI library loads on the CPU host, exports every symbol the header
+declares, and rejects bad arguments in its host-side checks (these return
+before anything touches HIP, so they run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nosa.h")
+
+pytestmark = pytest.mark.skipif(
+    not os.path.exists(os.path.join(ROOT, "block_sparse_kv_score_amd", "libnosa.so")),
+    reason="libnosa.so not built (run __graft_entry__.build())")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:nosa_status|const char\*)\s+(nosa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_step_calls():
+    names = declared_symbols()
+    for n in ["nosa_score_blocks", "nosa_select", "nosa_swap_diff", "nosa_sparse_decode", "nosa_combine",
+              "nosa_append", "nosa_build_summaries", "nosa_prefill_pages", "nosa_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    from block_sparse_kv_score_amd import nosa
+    L = nosa.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    assert sorted(nosa.ENTRY_POINTS) == declared_symbols()
+
+
+def test_status_strings():
+    from block_sparse_kv_score_amd import nosa
+    assert nosa.status_string(0) == "ok"
+    assert "invalid" in nosa.status_string(-1)
+    assert "unsupported" in nosa.status_string(-2)
+    assert nosa.status_string(12345) == "unknown status"
+
+
+def _good_dims(nosa):
+    return nosa.make_dims(2, 8, 2, 128, 64, 16, 40)
+
+
+def test_host_checks_reject_bad_arguments():
+    from block_sparse_kv_score_amd import nosa
+    L = nosa.lib()
+    P = ctypes.c_void_p
+    fake = P(256)  # never dereferenced: every call below fails its checks first
+    d = _good_dims(nosa)
+    D = ctypes.byref
+    # null dims
+    assert L.nosa_combine(None, 4, fake, fake, fake, fake, fake, fake, None) == nosa.NOSA_ERR_ARG
+    # splits out of range, null outputs
+    assert L.nosa_combine(D(d), 0, fake, fake, fake, fake, fake, fake, None) == nosa.NOSA_ERR_ARG
+    assert L.nosa_combine(D(d), 257, fake, fake, fake, fake, fake, fake, None) == nosa.NOSA_ERR_ARG
+    assert L.nosa_combine(D(d), 4, fake, fake, fake, None, fake, fake, None) == nosa.NOSA_ERR_ARG
+    # shapes
+    for field, value, want in [("n_q_heads", 7, nosa.NOSA_ERR_ARG),        # Hq % Hkv != 0
+                               ("n_q_heads", 12, nosa.NOSA_ERR_UNSUPPORTED),  # G = 6
+                               ("head_dim", 96, nosa.NOSA_ERR_UNSUPPORTED),
+                               ("block_size", 56, nosa.NOSA_ERR_ARG),       # 56 % 16 != 0
+                               ("block_size", 32, nosa.NOSA_ERR_UNSUPPORTED),
+                               ("sub_block", 3, nosa.NOSA_ERR_ARG),
+                               ("sub_block", 64 // 3 + 1, nosa.NOSA_ERR_ARG),
+                               ("max_blocks", 0, nosa.NOSA_ERR_ARG),
+                               ("max_blocks", 9000, nosa.NOSA_ERR_UNSUPPORTED),
+                               ("batch", 0, nosa.NOSA_ERR_ARG)]:
+        bad = _good_dims(nosa)
+        setattr(bad, field, value)
+        assert L.nosa_combine(D(bad), 4, fake, fake, fake, fake, fake, fake, None) == want, field
+    # nsub = 64 / 2 = 32 is fine, 64 / 1 = 64 too; block 128 / sub 1 = 128 is not
+    bad = _good_dims(nosa)
+    bad.block_size, bad.sub_block = 128, 1
+    assert L.nosa_combine(D(bad), 4, fake, fake, fake, fake, fake, fake, None) == nosa.NOSA_ERR_UNSUPPORTED
+    # select: negative budgets, selection capacity too small
+    assert L.nosa_select(D(d), fake, fake, fake, -1, 4, fake, fake, 8, fake, None) == nosa.NOSA_ERR_ARG
+    assert L.nosa_select(D(d), fake, fake, fake, 4, 4, fake, fake, 7, fake, None) == nosa.NOSA_ERR_ARG
+    # swap_diff capacity
+    assert L.nosa_swap_diff(D(d), 0, fake, fake, fake, fake, fake, fake, fake, fake, None) == nosa.NOSA_ERR_ARG
+    # decode: descriptor checks
+    kv = nosa.nosa_kv()
+    assert L.nosa_sparse_decode(D(d), fake, D(kv), fake, fake, 8, fake, 4, 0.1, fake, fake, fake,
+                                None) == nosa.NOSA_ERR_ARG  # no pages
+    kv.k_pages = kv.v_pages = kv.e_pages = ctypes.c_void_p(4096)
+    kv.num_pages = 10
+    kv.kind = nosa.NOSA_TABLE_FLAT
+    assert L.nosa_sparse_decode(D(d), fake, D(kv), fake, fake, 8, fake, 4, 0.1, fake, fake, fake,
+                                None) == nosa.NOSA_ERR_ARG  # flat table missing
+    kv.kind = 7
+    assert L.nosa_sparse_decode(D(d), fake, D(kv), fake, fake, 8, fake, 4, 0.1, fake, fake, fake,
+                                None) == nosa.NOSA_ERR_ARG  # unknown kind
+    kv.kind = nosa.NOSA_TABLE_TWO_LEVEL
+    kv.directory = kv.segments = ctypes.c_void_p(4096)
+    kv.num_segments, kv.seg_log2, kv.blocks_log2, kv.dir_entries = 4, 10, 12, 15  # needs 16 entries
+    assert L.nosa_sparse_decode(D(d), fake, D(kv), fake, fake, 8, fake, 4, 0.1, fake, fake, fake,
+                                None) == nosa.NOSA_ERR_ARG
+    kv.kind = nosa.NOSA_TABLE_PACKED_ROPE
+    kv.packed = ctypes.c_void_p(4096)
+    kv.rope_base = 10000.0
+    assert L.nosa_sparse_decode(D(d), fake, D(kv), fake, fake, 8, fake, 4, 0.1, fake, fake, fake,
+                                None) == nosa.NOSA_ERR_ARG  # q_pos missing
+    kv.q_pos = ctypes.c_void_p(4096)
+    assert L.nosa_sparse_decode(D(d), fake, D(kv), fake, fake, 8, fake, 0, 0.1, fake, fake, fake,
+                                None) == nosa.NOSA_ERR_ARG  # zero splits
+    assert L.nosa_sparse_decode(D(d), fake, D(kv), fake, fake, 8, fake, 4, -1.0, fake, fake, fake,
+                                None) == nosa.NOSA_ERR_ARG  # bad scale
+    g16 = nosa.make_dims(2, 32, 2, 128, 64, 16, 40)
+    assert L.nosa_sparse_decode(D(g16), fake, D(kv), fake, fake, 8, fake, 4, 0.1, fake, fake, fake,
+                                None) == nosa.NOSA_ERR_UNSUPPORTED  # deferred RoPE with G = 16
+    # misaligned 16-byte operands
+    assert L.nosa_score_blocks(D(d), fake, ctypes.c_void_p(4100), fake, fake, fake, fake,
+                               None) == nosa.NOSA_ERR_ARG
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    from block_sparse_kv_score_amd import nosa
+    d = _good_dims(nosa)
+    x = torch.zeros(4)
+    with pytest.raises(ValueError):
+        nosa.nosa_combine(d, 4, x, x, x, x, x, x)

@@ -1,0 +1,187 @@
+"""HIP path vs the float64 oracle, through the C-ABI, on the five workloads.
+
+Small variants compare every (b, h) pair at every step; the full-size runs
+(in the launch configuration the benchmark uses) compare sampled pairs and
+check the invariants on every pair.  Each case prints its name before it
+touches the GPU.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_kv_score_amd import synth
+from block_sparse_kv_score_amd.workloads import WORKLOADS
+
+from parity import (Gpu, PairState, bitmap_set, check_attention, compare_pair, logical_pair)
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg: str):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def session(w, inp, **kw):
+    from block_sparse_kv_score_amd.step import DecodeSession
+    return DecodeSession(w, inp, **kw)
+
+
+def force_pair(sess, b: int, h: int, r: dict):
+    """After a logged near-tie, hand the oracle's state for this pair to the
+    GPU (an input to the HIP path) so later steps stay comparable."""
+    w = sess.w
+    words = sess.evicted.shape[-1]
+    bits = np.zeros(words * 32, dtype=np.uint8)
+    for i in r["evicted"]:
+        bits[i] = 1
+    packed = np.packbits(bits, bitorder="little").view(np.uint32).view(np.int32)
+    sess.evicted[b, h] = torch.from_numpy(packed.copy()).to(sess.dev)
+    sel = np.full(sess.cap, -1, dtype=np.int32)
+    sel[:len(r["sel"])] = r["sel"]
+    sess.sel[b, h] = torch.from_numpy(sel).to(sess.dev)
+    sess.sel_count[b, h] = len(r["sel"])
+    torch.cuda.synchronize()
+
+
+def gpu_invariants(w, t, g: Gpu, prev: Gpu | None):
+    """Checks on the GPU trajectory itself, every pair."""
+    T = w.seq_len(t)
+    nb = -(-T // w.bs)
+    want = min(w.k, nb)
+    assert np.all(g.sel_count == want), ("selection size", np.unique(g.sel_count), want)
+    assert np.all(g.seq_lens == T)
+    if prev is None:
+        return
+    nb_prev = -(-(T - 1) // w.bs) if w.append else nb
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            ev_now, ev_before = bitmap_set(g.evicted[b, h], nb), bitmap_set(prev.evicted[b, h], nb)
+            assert ev_before <= ev_now, "evicted set shrank"
+            ge = set(range(nb)) - ev_now
+            ge_prev = set(range(nb_prev)) - ev_before
+            new = set(range(nb_prev, nb))
+            assert ge <= ge_prev | new, "an evicted block returned to the eviction set"
+            cur = set(g.sel[b, h, :g.sel_count[b, h]].tolist())
+            old = set(prev.sel[b, h, :prev.sel_count[b, h]].tolist())
+            gamma = len(cur & old) / len(cur)
+            assert gamma >= (w.k_e - len(new & ge)) / w.k - 1e-12, ("locality", gamma)
+
+
+def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=True):
+    announce(f"trajectory {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T0={w.T0} steps={steps or w.steps} "
+             f"P={splits or w.splits} pairs={'all' if pairs is None else pairs} seed={seed}")
+    inp = synth.generate(w, seed)
+    sess = session(w, inp, splits=splits)
+    pairs = pairs or [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    lgs = {p: logical_pair(inp, *p) for p in pairs}
+    states = {p: PairState() for p in pairs}
+    log: list[str] = []
+    prev_g = None
+    for t in range(1, (steps or w.steps) + 1):
+        sess.step(t)
+        torch.cuda.synchronize()
+        g = Gpu(sess)
+        assert g.err == 0, "device contract flag raised"
+        if not w.select_all:
+            gpu_invariants(w, t, g, prev_g)
+        forced = False
+        for (b, h) in pairs:
+            r = compare_pair(w, inp, lgs[(b, h)], g, b, h, t, states[(b, h)], sess.P, log, check_scores)
+            n = int(g.sel_count[b, h])
+            if g.sel[b, h, :n].tolist() != r["sel"] or bitmap_set(g.evicted[b, h], r["nb"]) != r["evicted"]:
+                force_pair(sess, b, h, r)
+                forced = True
+            states[(b, h)] = PairState(set(r["evicted"]), list(r["sel"]))
+        prev_g = Gpu(sess) if forced else g
+    for line in log:
+        print("near-tie:", line)
+    return log
+
+
+# ---------------------------------------------------------------------------
+# small variants: every pair, every step
+# ---------------------------------------------------------------------------
+
+def test_tiny_nosa_16_steps():
+    run_trajectory(WORKLOADS["tiny_nosa"])
+
+
+def test_8b_shape_small_ragged():
+    # T0 not a multiple of the block size: block creation at step 4,
+    # partial sub-blocks, 3 splits over 64 selected blocks
+    w = WORKLOADS["llama3_8b_32k"].scaled(B=2, Hq=8, Hkv=2, T0=4096 + 61)
+    run_trajectory(w, seed=1, splits=3)
+
+
+def test_70b_shape_small_two_level():
+    w = WORKLOADS["llama31_70b_256k"].scaled(B=2, Hq=16, Hkv=2, T0=16384 + 100, dir_entries=64)
+    run_trajectory(w, seed=2)
+
+
+def test_dense_small_many_splits():
+    # k = every block, more splits than blocks per split: empty splits
+    w = WORKLOADS["dense_8b_8k"].scaled(B=2, Hq=8, Hkv=2, T0=1000)
+    run_trajectory(w, seed=3, splits=37)
+
+
+def test_lazy_rope_small():
+    w = WORKLOADS["lazy_rope_32k"].scaled(B=2, Hq=8, Hkv=2, T0=8 * 512, doc_len=512)
+    run_trajectory(w, seed=4)
+
+
+def test_lazy_rope_g8_and_g1():
+    for hq in (16, 2):
+        w = WORKLOADS["lazy_rope_32k"].scaled(B=1, Hq=hq, Hkv=2, T0=4 * 256, doc_len=256, n_docs=4)
+        run_trajectory(w, seed=5)
+
+
+def test_group_sizes_and_head_dim_64():
+    base = WORKLOADS["tiny_nosa"]
+    for hq, hkv, d in [(2, 2, 64), (4, 2, 64), (16, 2, 64), (8, 1, 128), (16, 1, 128), (1, 1, 128)]:
+        w = base.scaled(B=2, Hq=hq, Hkv=hkv, D=d, T0=700, k_e=3, k_q=5)
+        run_trajectory(w, seed=6, steps=3, splits=2)
+
+
+def test_block_128_sub_1_and_256():
+    base = WORKLOADS["tiny_nosa"]
+    run_trajectory(base.scaled(B=1, Hq=4, Hkv=1, bs=128, ss=2, T0=1500, k_e=2, k_q=3), seed=7, steps=3)
+    run_trajectory(base.scaled(B=1, Hq=4, Hkv=1, bs=256, ss=64, T0=1500, k_e=1, k_q=2), seed=8, steps=3)
+
+
+def test_fewer_blocks_than_budget():
+    # nb < k_e: every block kept, no eviction
+    w = WORKLOADS["tiny_nosa"].scaled(B=1, T0=100, k_e=4, k_q=4)
+    run_trajectory(w, seed=9, steps=4)
+
+
+# ---------------------------------------------------------------------------
+# full sizes, launch configuration of the benchmark
+# ---------------------------------------------------------------------------
+
+def test_dense_8b_8k_full():
+    w = WORKLOADS["dense_8b_8k"]
+    run_trajectory(w, seed=0, check_scores=False,
+                   pairs=[(b, h) for b in range(w.B) for h in range(w.Hkv) if (b * w.Hkv + h) % 4 == 0])
+
+
+def test_8b_32k_full_sampled():
+    w = WORKLOADS["llama3_8b_32k"]
+    run_trajectory(w, seed=0, pairs=[(0, 0), (5, 3), (17, 7), (31, 2)])
+
+
+def test_70b_256k_full_sampled():
+    w = WORKLOADS["llama31_70b_256k"]
+    run_trajectory(w, seed=0, pairs=[(0, 0), (3, 5), (7, 7)])
+
+
+def test_lazy_rope_32k_full_sampled():
+    w = WORKLOADS["lazy_rope_32k"]
+    run_trajectory(w, seed=0, pairs=[(0, 0), (21, 4), (63, 7)])
