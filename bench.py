@@ -48,6 +48,8 @@ def parse(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with one plain 1 GiB device copy, a known-size kernel for counter calibration")
     return ap.parse_args(argv)
 
 
@@ -222,6 +224,14 @@ def main(argv=None) -> int:
                 "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
                 "kernel": "nosa_sparse_decode (decode_kernel)",
                 "algorithmic_bytes_per_launch": int(kvb), "avg_launch_us": round(kernels_us["decode"], 2)}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

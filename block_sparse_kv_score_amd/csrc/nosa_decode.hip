@@ -69,6 +69,15 @@ struct DecodeArgs {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Page data is read once per step: non-temporal loads stream it past the
+// caches (on gfx950 these sustain far more HBM bandwidth than ordinary
+// loads for this access pattern).
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // D(16x16) += A(16x32) . B(32x16), bf16 inputs, fp32 accumulation.  Lane
 // l = 16 q + r supplies A row r and B column r for the eight k slots of lane
@@ -159,31 +168,66 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int32_t* selp = a.sel + (int64_t)bh * a.sel_cap;
-  for (int k = w; k < ntiles; k += kDecWaves) {
-    const int blk = j0 + k / tpb;
-    const int sub = k % tpb;
-    const int i = selp[blk];
-    if (i < 0 || i >= nb) {
-      if (lane == 0) flag_error(a.t.err);
-      continue;
+  // Tile k of this split: block sel[j0 + k / tpb], 64-token slice k % tpb.
+  // Returns the next tile >= k with data, skipping (and flagging) entries the
+  // table cannot resolve; ntiles when there is none.
+  auto next_tile = [&](int k, int64_t& page, int& ntok, uint32_t& docb, int& sub) -> int {
+    for (; k < ntiles; k += kDecWaves) {
+      const int i = selp[j0 + k / tpb];
+      sub = k % tpb;
+      if (i < 0 || i >= nb) {
+        if (lane == 0) flag_error(a.t.err);
+        continue;
+      }
+      page = page_of<KIND>(a.t, bh, i, docb);
+      if (page < 0) {
+        if (lane == 0) flag_error(a.t.err);
+        continue;
+      }
+      ntok = min(kTile, T - (i * a.bs + sub * kTile));
+      if (ntok > 0) return k;
     }
-    uint32_t docb = 0;
-    const int64_t page = page_of<KIND>(a.t, bh, i, docb);
-    if (page < 0) {
-      if (lane == 0) flag_error(a.t.err);
-      continue;
-    }
-    const int ntok = min(kTile, T - (i * a.bs + sub * kTile));
-    if (ntok <= 0) continue;
+    return ntiles;
+  };
+  // K as the A operand: row lr of token set set_q, octet ds*LPS + dsub;
+  // V^T as the A operand of P.V: dim 16 dt + lr, tokens 32 ks + 8 lq .. +8
+  auto k_ptr = [&](int64_t page, int sub) {
+    return reinterpret_cast<const uint4*>(a.k_pages + page * (int64_t)a.bs * D) + sub * kTile + 16 * set_q + lr +
+           (int64_t)dsub * a.bs;
+  };
+  auto v_ptr = [&](int64_t page, int sub) {
+    return reinterpret_cast<const uint4*>(a.v_pages + page * (int64_t)a.bs * D) + (sub * 8 + lq) * D + lr;
+  };
 
-    // K as the A operand: row lr of token set set_q, octet ds*LPS + dsub
-    const uint4* kpg = reinterpret_cast<const uint4*>(a.k_pages + page * (int64_t)a.bs * D) + sub * kTile +
-                       16 * set_q + lr + (int64_t)dsub * a.bs;
-    uint4 kr[TH][NDS];
+  uint4 kr[TH][NDS];
+  uint4 vr[2][NDT];
+  int64_t page = 0;
+  int ntok = 0, sub = 0;
+  uint32_t docb = 0;
+  int k = next_tile(w, page, ntok, docb, sub);
+  if (k < ntiles) {
+    const uint4* kpg = k_ptr(page, sub);
 #pragma unroll
     for (int th = 0; th < TH; ++th)
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) kr[th][ds] = kpg[(int64_t)ds * LPS * a.bs + th * TPM];
+      for (int ds = 0; ds < NDS; ++ds) kr[th][ds] = load_stream(kpg + (int64_t)ds * LPS * a.bs + th * TPM);
+    const uint4* vpg = v_ptr(page, sub);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vr[ks][dt] = load_stream(vpg + ks * 4 * D + dt * 16);
+  }
+
+  // Software pipeline: once q.k has consumed this tile's keys the key
+  // registers receive the next tile's keys, and once P.V has consumed the
+  // values they receive the next values, so every wave keeps a tile of
+  // loads in flight while it computes.
+  while (k < ntiles) {
+    int64_t npage = 0;
+    int nntok = 0, nsub = 0;
+    uint32_t ndocb = 0;
+    const int nk = next_tile(k + kDecWaves, npage, nntok, ndocb, nsub);
+
     // Slots past the end hold stale page data.  A row of the q.k MFMA mixes
     // tokens of every token set (the query is zero outside a set's slots),
     // and 0 * NaN would leak into valid scores, so zero those keys.
@@ -194,13 +238,6 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
 #pragma unroll
           for (int ds = 0; ds < NDS; ++ds) kr[th][ds] = make_uint4(0, 0, 0, 0);
     }
-    // V^T as the A operand of P.V: dim 16 dt + lr, tokens 32 ks + 8 lq .. +8
-    const uint4* vpg = reinterpret_cast<const uint4*>(a.v_pages + page * (int64_t)a.bs * D) + (sub * 8 + lq) * D + lr;
-    uint4 vr[2][NDT];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) vr[ks][dt] = vpg[ks * 4 * D + dt * 16];
 
     if constexpr (ROPE) {
       if (docb != cur_doc) {  // new document: query rotated by n - start
@@ -247,6 +284,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
         sv[th][e] = tok < ntok ? x * a.scale_log2 : -INFINITY;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (nk < ntiles) {  // prefetch the next tile's keys
+      const uint4* kpg = k_ptr(npage, nsub);
+#pragma unroll
+      for (int th = 0; th < TH; ++th)
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) kr[th][ds] = load_stream(kpg + (int64_t)ds * LPS * a.bs + th * TPM);
+    }
+
     // tile max per head slot: lanes sharing cg
     float mx = -INFINITY;
 #pragma unroll
@@ -305,6 +351,19 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
       for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma_bf16(vr[ks][dt], pb, oacc[dt]);
     }
     wave_lds_sync();
+    __builtin_amdgcn_sched_barrier(0);
+    if (nk < ntiles) {  // prefetch the next tile's values
+      const uint4* vpg = v_ptr(npage, nsub);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) vr[ks][dt] = load_stream(vpg + ks * 4 * D + dt * 16);
+    }
+    k = nk;
+    page = npage;
+    ntok = nntok;
+    sub = nsub;
+    docb = ndocb;
   }
 
   // per-wave totals: sum the token sets of each head slot, then the lanes
@@ -353,23 +412,45 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
   }
 }
 
-// One workgroup per (b, query head); thread per dim.
+// One workgroup per (b, query head); thread per dim.  Split weights are
+// formed once in LDS; partial outputs are loaded eight splits at a time.
 __global__ void combine_kernel(int P, int D, const float* __restrict__ part_o, const float* __restrict__ part_m,
                                const float* __restrict__ part_l, float* __restrict__ o, float* __restrict__ m,
                                float* __restrict__ l) {
+  __shared__ float wgt[256];
+  __shared__ float stat[2];
   const int64_t row = blockIdx.x;
   const float* pm = part_m + row * P;
   const float* pl = part_l + row * P;
-  float M = -INFINITY;
-  for (int k = 0; k < P; ++k)
-    if (pl[k] > 0.f) M = fmaxf(M, pm[k]);
-  float L = 0.f;
-  for (int k = 0; k < P; ++k)
-    if (pl[k] > 0.f) L += pl[k] * expf(pm[k] - M);
+  if (threadIdx.x < kWave) {
+    float M = -INFINITY;
+    for (int k = threadIdx.x; k < P; k += kWave)
+      if (pl[k] > 0.f) M = fmaxf(M, pm[k]);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int k = threadIdx.x; k < P; k += kWave) {
+      const float wk = pl[k] > 0.f ? pl[k] * expf(pm[k] - M) : 0.f;
+      wgt[k] = wk;
+      L += wk;
+    }
+    L = wave_sum(L);
+    if (threadIdx.x == 0) {
+      stat[0] = M;
+      stat[1] = L;
+    }
+  }
+  __syncthreads();
+  const float M = stat[0], L = stat[1];
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float acc = 0.f;
-    for (int k = 0; k < P; ++k)
-      if (pl[k] > 0.f) acc += pl[k] * expf(pm[k] - M) * part_o[(row * P + k) * D + d];
+    for (int k0 = 0; k0 < P; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = k0 + j < P ? part_o[(row * P + k0 + j) * D + d] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < P) acc += wgt[k0 + j] * v[j];
+    }
     o[row * D + d] = L > 0.f ? acc / L : 0.f;
   }
   if (threadIdx.x == 0) {

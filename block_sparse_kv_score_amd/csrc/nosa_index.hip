@@ -93,21 +93,42 @@ __global__ __launch_bounds__(256) void prefill_kernel(Table t, int bs, const uin
 }
 
 // ---------------------------------------------------------------------------
-// Mean of one sub-block's present tokens [lo, hi) (page-relative), for the
-// d-quad u, from a K page; float64 sums in ascending token order.
+// Sums over a sub-block's present tokens [lo, hi) (page-relative), float64,
+// ascending token order.  Loads go out in batches of 16 (padding slots add
+// +0.0, which leaves a float64 sum unchanged), so build_summaries and append
+// produce identical sums for identical tokens.
 // ---------------------------------------------------------------------------
+constexpr int kSumBatch = 16;
+
 template <int D>
 __device__ __forceinline__ void sum_key_quad(const uint16_t* kpage, int bs, int u, int lo, int hi,
                                              double& a0, double& a1, double& a2, double& a3) {
   // quad u = dims 4u..4u+3 = half (u & 1) of octet u >> 1
   const uint2* base = reinterpret_cast<const uint2*>(kpage) + ((u >> 1) * bs) * 2 + (u & 1);
-  for (int tok = lo; tok < hi; ++tok) {
-    const uint2 v = base[tok * 2];
-    a0 += (double)bf16_lo(v.x);
-    a1 += (double)bf16_hi(v.x);
-    a2 += (double)bf16_lo(v.y);
-    a3 += (double)bf16_hi(v.y);
+  for (int t0 = lo; t0 < hi; t0 += kSumBatch) {
+    uint2 v[kSumBatch];
+#pragma unroll
+    for (int j = 0; j < kSumBatch; ++j) v[j] = t0 + j < hi ? base[(t0 + j) * 2] : make_uint2(0u, 0u);
+#pragma unroll
+    for (int j = 0; j < kSumBatch; ++j) {
+      a0 += (double)bf16_lo(v[j].x);
+      a1 += (double)bf16_hi(v[j].x);
+      a2 += (double)bf16_lo(v[j].y);
+      a3 += (double)bf16_hi(v[j].y);
+    }
   }
+}
+
+__device__ __forceinline__ double sum_logits(const float* ep, int lo, int hi) {
+  double a = 0;
+  for (int t0 = lo; t0 < hi; t0 += kSumBatch) {
+    float v[kSumBatch];
+#pragma unroll
+    for (int j = 0; j < kSumBatch; ++j) v[j] = t0 + j < hi ? ep[t0 + j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kSumBatch; ++j) a += (double)v[j];
+  }
+  return a;
 }
 
 // build_summaries: one thread per (sub-block, d-quad); threads with u == 0
@@ -149,9 +170,7 @@ __global__ __launch_bounds__(256) void summaries_kernel(Table t, int bs, int ss,
   r.w = (float)(a3 * inv_n);
   reinterpret_cast<float4*>(k_summary)[((int64_t)bh * NQ + u) * CS + s] = r;
   if (u == 0) {
-    double ae = 0;
-    const float* ep = e_pages + page * bs;
-    for (int tok = lo - i * bs; tok < hi - i * bs; ++tok) ae += (double)ep[tok];
+    const double ae = sum_logits(e_pages + page * bs, lo - i * bs, hi - i * bs);
     e_summary[(int64_t)bh * CS + s] = (float)(ae * inv_n);
   }
 }
@@ -212,10 +231,8 @@ __global__ void append_kernel(Table t, int bs, int ss, const uint16_t* __restric
         o.w = (float)(a3 * inv_n);
         reinterpret_cast<float4*>(k_summary)[((int64_t)bh * NQ + lane) * CS + s] = o;
       }
-      if (lane == 0) {
-        double ae = 0;
-        const float* ep = e_pages + page * bs;
-        for (int tok = lo; tok < r; ++tok) ae += (double)ep[tok];
+      if (lane == NQ) {  // the logit mean runs beside the key quads
+        double ae = sum_logits(e_pages + page * bs, lo, r);
         ae += (double)e_new[bh];
         e_summary[(int64_t)bh * CS + s] = (float)(ae * inv_n);
       }

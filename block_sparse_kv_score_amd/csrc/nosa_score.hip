@@ -46,6 +46,23 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(int Hq, int Hkv, i
   const int s0 = blockIdx.x * kScoreThreads;
   if (s0 >= nb * nsub) return;  // whole workgroup past the last block
 
+  const int s = s0 + threadIdx.x;
+  const int i = s / nsub, j = s % nsub;
+  const bool valid = i < nb && i * bs + j * ss < T;
+
+  // issue every load of the row first: D/4 independent 16-byte loads per
+  // lane (each a 1 KiB contiguous run per wave) keep the HBM queues full
+  // while the group-mean query is formed
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  f4 v[NQ];
+  float ev = -INFINITY;
+  if (valid) {
+    const f4* kp = reinterpret_cast<const f4*>(k_summary) + (int64_t)bh * NQ * CS + s;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) v[u] = __builtin_nontemporal_load(kp + (int64_t)u * CS);
+    ev = e_summary[(int64_t)bh * CS + s];
+  }
+
   __shared__ double qbar[D];
   for (int d = threadIdx.x; d < D; d += kScoreThreads) {
     const uint16_t* qh = q + ((int64_t)b * Hq + (int64_t)h * G) * D + d;
@@ -55,24 +72,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(int Hq, int Hkv, i
   }
   __syncthreads();
 
-  const int s = s0 + threadIdx.x;
-  const int i = s / nsub, j = s % nsub;
-  const bool valid = i < nb && i * bs + j * ss < T;
   double dot = -INFINITY;
-  float ev = -INFINITY;
   if (valid) {
-    const float4* kp = reinterpret_cast<const float4*>(k_summary) + (int64_t)bh * NQ * CS + s;
-    double a = 0;
-#pragma unroll 8
+    double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+#pragma unroll
     for (int u = 0; u < NQ; ++u) {
-      const float4 v = kp[(int64_t)u * CS];
-      a = fma((double)v.x, qbar[4 * u + 0], a);
-      a = fma((double)v.y, qbar[4 * u + 1], a);
-      a = fma((double)v.z, qbar[4 * u + 2], a);
-      a = fma((double)v.w, qbar[4 * u + 3], a);
+      a0 = fma((double)v[u].x, qbar[4 * u + 0], a0);
+      a1 = fma((double)v[u].y, qbar[4 * u + 1], a1);
+      a2 = fma((double)v[u].z, qbar[4 * u + 2], a2);
+      a3 = fma((double)v[u].w, qbar[4 * u + 3], a3);
     }
-    dot = a;
-    ev = e_summary[(int64_t)bh * CS + s];
+    dot = (a0 + a1) + (a2 + a3);
   }
   // max over the nsub lanes of each block (nsub is a power of two <= 64 and
   // kScoreThreads is a multiple of 64, so a block never straddles a wave)

@@ -14,9 +14,11 @@
 // starts as an eviction candidate.
 //
 // One workgroup per (b, h).  Top-k is a most-significant-digit radix select
-// over order-preserving 32-bit keys of the fp32 scores (four 8-bit passes,
-// each an LDS histogram plus a workgroup suffix scan), followed by a
-// lowest-index-first pick among blocks whose key equals the threshold.
+// over order-preserving 32-bit keys of the fp32 scores with 4-bit digits:
+// each pass counts the 16 digit values with wave ballots (no LDS atomics,
+// which would serialise on the few crowded bins), sums the four waves'
+// counts through LDS and picks the bin holding the k-th key; it stops as
+// soon as that bin is taken whole.  Exact key ties go to the lowest index.
 // Outputs are compacted in index order with wave ballots, so they come out
 // ascending without a sort.
 
@@ -36,7 +38,7 @@ constexpr uint8_t F_IN_Q = 4;     // in Gamma_q
 struct SelShared {
   uint32_t key[kMaxBlocks];
   uint8_t flag[kMaxBlocks];
-  uint32_t hist[256];
+  int32_t cnt[kSelWaves][16];
   int32_t wave_tot[kSelWaves];
   int32_t bcast[4];
 };
@@ -61,53 +63,54 @@ __device__ __forceinline__ int block_count_excl(bool pred, int& total, SelShared
   return before + below;
 }
 
-// Inclusive scan of one int per thread, in thread order.
-__device__ __forceinline__ int block_scan_incl(int v, SelShared& sh) {
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
-  if (lane == kWave - 1) sh.wave_tot[w] = v;
-  __syncthreads();
-  int before = 0;
-#pragma unroll
-  for (int k = 0; k < kSelWaves; ++k) before += k < w ? sh.wave_tot[k] : 0;
-  __syncthreads();
-  return v + before;
-}
-
 // Marks with `mark` the k best of the candidates (flag & cmask) == cval
 // under (key desc, index asc).  Requires 0 < k < number of candidates.
 __device__ void radix_top_k(int n, int k, uint8_t cmask, uint8_t cval, uint8_t mark, SelShared& sh) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   uint32_t prefix = 0, pmask = 0;
-  int rem = k;       // still to take among keys matching the prefix
-  int n_eq = 0;      // candidates whose key equals the final threshold
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    sh.hist[threadIdx.x] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kSelThreads) {
-      const uint32_t key = sh.key[i];
-      if ((sh.flag[i] & cmask) == cval && (key & pmask) == prefix)
-        atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+  int rem = k;   // still to take among keys matching the prefix
+  int n_eq = 0;  // candidates matching the prefix
+  for (int shift = 28; shift >= 0; shift -= 4) {
+    int cnt[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) cnt[d] = 0;
+    for (int base = 0; base < n; base += kSelThreads) {
+      const int i = base + threadIdx.x;
+      const uint32_t key = i < n ? sh.key[i] : 0u;
+      const bool in = i < n && (sh.flag[i] & cmask) == cval && (key & pmask) == prefix;
+      const uint32_t dg = (key >> shift) & 15u;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) cnt[d] += __popcll(__ballot(in && dg == (uint32_t)d));
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int d = 0; d < 16; ++d) sh.cnt[w][d] = cnt[d];
     }
     __syncthreads();
-    // suffix counts: thread t owns digit 255 - t
-    const int cnt = (int)sh.hist[255 - threadIdx.x];
-    const int cum = block_scan_incl(cnt, sh);  // #keys with digit >= 255 - t
-    if (cum >= rem && cum - cnt < rem) {
-      sh.bcast[0] = 255 - threadIdx.x;
-      sh.bcast[1] = cum - cnt;
-      sh.bcast[2] = cnt;
+    // lanes 0..15 of every wave take one digit each: total over the waves,
+    // suffix sum from the top digit, and the lane whose range holds the
+    // rem-th key names the digit (every wave computes the same answer)
+    int c = 0;
+    if (lane < 16) {
+#pragma unroll
+      for (int ww = 0; ww < kSelWaves; ++ww) c += sh.cnt[ww][lane];
     }
+    int suf = c;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int t = __shfl_down(suf, off, kWave);
+      if (lane + off < 16) suf += t;
+    }
+    const uint64_t hit = __ballot(lane < 16 && suf >= rem && suf - c < rem);
+    const int digit = __ffsll((unsigned long long)hit) - 1;
+    const int above = __shfl(suf - c, digit, kWave);
+    const int bin = __shfl(c, digit, kWave);
+    rem -= above;
+    n_eq = bin;
+    prefix |= (uint32_t)digit << shift;
+    pmask |= 15u << shift;
     __syncthreads();
-    const uint32_t digit = (uint32_t)sh.bcast[0];
-    rem -= sh.bcast[1];
-    n_eq = sh.bcast[2];
-    prefix |= digit << shift;
-    pmask |= 255u << shift;
-    __syncthreads();
+    if (rem == n_eq) break;  // the whole bin is taken: prefix is the threshold
   }
   const uint32_t thr = prefix;
   if (rem == n_eq) {
@@ -116,7 +119,7 @@ __device__ void radix_top_k(int n, int k, uint8_t cmask, uint8_t cval, uint8_t m
     __syncthreads();
     return;
   }
-  // take the rem lowest indices among the keys equal to thr
+  // exact key ties: take the rem lowest indices among keys equal to thr
   int carry = 0;
   for (int base = 0; base < n; base += kSelThreads) {
     const int i = base + threadIdx.x;
