@@ -13,14 +13,12 @@
 // part only, ties go to the lower block index, and a newly created block
 // starts as an eviction candidate.
 //
-// One workgroup per (b, h).  Top-k is a most-significant-digit radix select
-// over order-preserving 32-bit keys of the fp32 scores with 4-bit digits:
-// each pass counts the 16 digit values with wave ballots (no LDS atomics,
-// which would serialise on the few crowded bins), sums the four waves'
-// counts through LDS and picks the bin holding the k-th key; it stops as
-// soon as that bin is taken whole.  Exact key ties go to the lowest index.
-// Outputs are compacted in index order with wave ballots, so they come out
-// ascending without a sort.
+// One workgroup per (b, h); each thread keeps its blocks' keys in registers
+// (block i = r * 256 + thread).  Top-k is a most-significant-digit radix
+// select over order-preserving 32-bit keys of the fp32 scores (see
+// radix_top_k); exact key ties go to the lowest index.  Outputs are
+// compacted in index order with wave ballots, so they come out ascending
+// without a sort, and the eviction bitmap words are rebuilt from ballots.
 
 #include "nosa_launch.hpp"
 
@@ -30,110 +28,149 @@ constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kMaxBlocks = 8192;
 
-// flag bits per block in LDS
-constexpr uint8_t F_EVICTED = 1;  // evicted before or during this call
-constexpr uint8_t F_IN_E = 2;     // in Gamma_e
-constexpr uint8_t F_IN_Q = 4;     // in Gamma_q
-
+// Per-workgroup scratch in LDS; small slots are double-buffered by phase so
+// one barrier per exchange suffices.
 struct SelShared {
-  uint32_t key[kMaxBlocks];
-  uint8_t flag[kMaxBlocks];
-  int32_t cnt[kSelWaves][16];
-  int32_t wave_tot[kSelWaves];
-  int32_t bcast[4];
+  uint32_t hist[kSelWaves][256];  // per-wave digit histograms
+  int32_t tot[2][kSelWaves];
+  int32_t bc[2][4];
+  uint32_t mm[2][kSelWaves][2];
+  int32_t pos[32][kSelWaves];
 };
 
-// Exclusive count of `pred` over the workgroup in thread order, plus the
-// total.  Every thread must call it.
-__device__ __forceinline__ int block_count_excl(bool pred, int& total, SelShared& sh) {
+// Workgroup sum of one int per wave (lane 0's value); one barrier.
+__device__ __forceinline__ int block_sum(int v, int& phase, SelShared& sh) {
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  const uint64_t m = __ballot(pred);
-  const int below = lanes_below(m);
-  if (lane == 0) sh.wave_tot[w] = __popcll(m);
+  const int ph = phase++ & 1;
+  if (lane == 0) sh.tot[ph][w] = v;
   __syncthreads();
-  int before = 0;
-  total = 0;
+  int t = 0;
 #pragma unroll
-  for (int k = 0; k < kSelWaves; ++k) {
-    const int c = sh.wave_tot[k];
-    before += k < w ? c : 0;
-    total += c;
-  }
-  __syncthreads();
-  return before + below;
+  for (int k = 0; k < kSelWaves; ++k) t += sh.tot[ph][k];
+  return t;
 }
 
-// Marks with `mark` the k best of the candidates (flag & cmask) == cval
-// under (key desc, index asc).  Requires 0 < k < number of candidates.
-__device__ void radix_top_k(int n, int k, uint8_t cmask, uint8_t cval, uint8_t mark, SelShared& sh) {
+// Element r of this thread is block i = r * kSelThreads + threadIdx.x; the
+// thread's R elements live in registers (keys) and bit masks (bit r).
+// Marks in `out` the k best of the elements in `cand` under (key desc,
+// index asc).  Requires 0 < k < number of candidates.
+//
+// Radix select over 8-bit digits.  The first digit starts at the highest
+// bit where the candidates' smallest and largest keys differ (the bits above
+// are common to all of them), so no pass is spent on a shared exponent.
+// Digits are counted in per-wave LDS histograms; a workgroup scan over the
+// 256 bins finds the bin holding the k-th key; the select stops as soon as
+// that bin is taken whole.
+template <int R>
+__device__ void radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k, uint32_t& out, int& phase,
+                            SelShared& sh) {
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  uint32_t prefix = 0, pmask = 0;
-  int rem = k;   // still to take among keys matching the prefix
-  int n_eq = 0;  // candidates matching the prefix
-  for (int shift = 28; shift >= 0; shift -= 4) {
-    int cnt[16];
+  // range of the candidate keys
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
-    for (int d = 0; d < 16; ++d) cnt[d] = 0;
-    for (int base = 0; base < n; base += kSelThreads) {
-      const int i = base + threadIdx.x;
-      const uint32_t key = i < n ? sh.key[i] : 0u;
-      const bool in = i < n && (sh.flag[i] & cmask) == cval && (key & pmask) == prefix;
-      const uint32_t dg = (key >> shift) & 15u;
-#pragma unroll
-      for (int d = 0; d < 16; ++d) cnt[d] += __popcll(__ballot(in && dg == (uint32_t)d));
+  for (int r = 0; r < R; ++r)
+    if ((cand >> r) & 1u) {
+      kmin = min(kmin, key[r]);
+      kmax = max(kmax, key[r]);
     }
-    if (lane == 0) {
 #pragma unroll
-      for (int d = 0; d < 16; ++d) sh.cnt[w][d] = cnt[d];
-    }
-    __syncthreads();
-    // lanes 0..15 of every wave take one digit each: total over the waves,
-    // suffix sum from the top digit, and the lane whose range holds the
-    // rem-th key names the digit (every wave computes the same answer)
-    int c = 0;
-    if (lane < 16) {
-#pragma unroll
-      for (int ww = 0; ww < kSelWaves; ++ww) c += sh.cnt[ww][lane];
-    }
-    int suf = c;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const int t = __shfl_down(suf, off, kWave);
-      if (lane + off < 16) suf += t;
-    }
-    const uint64_t hit = __ballot(lane < 16 && suf >= rem && suf - c < rem);
-    const int digit = __ffsll((unsigned long long)hit) - 1;
-    const int above = __shfl(suf - c, digit, kWave);
-    const int bin = __shfl(c, digit, kWave);
-    rem -= above;
-    n_eq = bin;
-    prefix |= (uint32_t)digit << shift;
-    pmask |= 15u << shift;
-    __syncthreads();
-    if (rem == n_eq) break;  // the whole bin is taken: prefix is the threshold
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
   }
-  const uint32_t thr = prefix;
-  if (rem == n_eq) {
-    for (int i = threadIdx.x; i < n; i += kSelThreads)
-      if ((sh.flag[i] & cmask) == cval && sh.key[i] >= thr) sh.flag[i] |= mark;
+  {
+    const int ph = phase++ & 1;
+    if (lane == 0) {
+      sh.mm[ph][w][0] = kmin;
+      sh.mm[ph][w][1] = kmax;
+    }
     __syncthreads();
+#pragma unroll
+    for (int ww = 0; ww < kSelWaves; ++ww) {
+      kmin = min(kmin, sh.mm[ph][ww][0]);
+      kmax = max(kmax, sh.mm[ph][ww][1]);
+    }
+  }
+  int hi = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);  // bits [hi, 32) are shared
+  uint32_t prefix = hi >= 32 ? 0u : kmin & ~((1u << hi) - 1u);
+  uint32_t pmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
+  int rem = k, n_eq = 0;
+  bool done = false;
+  while (hi > 0 && !done) {
+    const int lo = hi > 8 ? hi - 8 : 0;
+    const uint32_t dmask = (1u << (hi - lo)) - 1u;
+    // per-wave histogram of this digit among the keys matching the prefix
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sh.hist[w][lane + 64 * j] = 0u;
+    wave_lds_sync();
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (((cand >> r) & 1u) && (key[r] & pmask) == prefix) atomicAdd(&sh.hist[w][(key[r] >> lo) & dmask], 1u);
+    __syncthreads();
+    // thread t owns digit 255 - t: inclusive scan gives the count of keys
+    // with a digit >= 255 - t
+    const int dg = 255 - (int)threadIdx.x;
+    int c = 0;
+#pragma unroll
+    for (int ww = 0; ww < kSelWaves; ++ww) c += (int)sh.hist[ww][dg];
+    int cum = c;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int t = __shfl_up(cum, off, kWave);
+      if (lane >= off) cum += t;
+    }
+    const int ph = phase++ & 1;
+    if (lane == kWave - 1) sh.tot[ph][w] = cum;
+    __syncthreads();
+#pragma unroll
+    for (int ww = 0; ww < kSelWaves; ++ww) cum += ww < w ? sh.tot[ph][ww] : 0;
+    if (c > 0 && cum >= rem && cum - c < rem) {
+      sh.bc[ph][0] = dg;
+      sh.bc[ph][1] = cum - c;
+      sh.bc[ph][2] = c;
+    }
+    __syncthreads();
+    const uint32_t digit = (uint32_t)sh.bc[ph][0];
+    rem -= sh.bc[ph][1];
+    n_eq = sh.bc[ph][2];
+    prefix |= digit << lo;
+    pmask |= dmask << lo;
+    hi = lo;
+    done = rem == n_eq;  // the whole bin is taken: prefix is the threshold
+  }
+  if (rem == n_eq) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (((cand >> r) & 1u) && (key[r] & pmask) >= prefix) out |= 1u << r;
     return;
   }
-  // exact key ties: take the rem lowest indices among keys equal to thr
-  int carry = 0;
-  for (int base = 0; base < n; base += kSelThreads) {
-    const int i = base + threadIdx.x;
-    const bool cand = i < n && (sh.flag[i] & cmask) == cval;
-    const uint32_t key = cand ? sh.key[i] : 0u;
-    const bool eq = cand && key == thr;
-    int total;
-    const int rank = carry + block_count_excl(eq, total, sh);
-    if (cand && (key > thr || (eq && rank < rem))) sh.flag[i] |= mark;
-    carry += total;
+  // exact key ties at the threshold: the rem lowest block indices win
+  uint64_t eqm[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) eqm[r] = __ballot(((cand >> r) & 1u) && key[r] == prefix);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) sh.pos[r][w] = __popcll(eqm[r]);
   }
   __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int rank = before + lanes_below(eqm[r]);
+#pragma unroll
+    for (int ww = 0; ww < kSelWaves; ++ww) {
+      const int c = sh.pos[r][ww];
+      rank += ww < w ? c : 0;
+      before += c;
+    }
+    if ((cand >> r) & 1u) {
+      if (key[r] > prefix || (key[r] == prefix && rank < rem)) out |= 1u << r;
+    }
+  }
+  __syncthreads();  // sh.pos is reused by the caller
 }
 
+template <int R>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(int Hkv, int bs, int max_blocks,
                                                              const float* __restrict__ score_q,
                                                              const float* __restrict__ score_e,
@@ -143,6 +180,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int Hkv, int bs, in
                                                              int32_t* __restrict__ sel, int sel_cap,
                                                              int32_t* __restrict__ sel_count) {
   __shared__ SelShared sh;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int bh = blockIdx.x;
   const int b = bh / Hkv;
   const int T = min(max(seq_lens[b], 0), max_blocks * bs);
@@ -152,65 +190,85 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int Hkv, int bs, in
   const float* se = score_e + (int64_t)bh * max_blocks;
   const float* sq = score_q + (int64_t)bh * max_blocks;
 
-  // --- eviction part ------------------------------------------------------
-  for (int i = threadIdx.x; i < nb; i += kSelThreads) {
-    sh.flag[i] = ((ev[i >> 5] >> (i & 31)) & 1u) ? F_EVICTED : 0;
-    sh.key[i] = order_key(se[i]);
+  // every load up front, over the whole capacity so they need not wait for
+  // seq_lens; blocks >= nb are masked out afterwards
+  uint32_t ke[R], kq[R], ew[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = r * kSelThreads + threadIdx.x;
+    ke[r] = kq[r] = ew[r] = 0u;
+    if (i < max_blocks) {
+      ke[r] = order_key(se[i]);
+      kq[r] = order_key(sq[i]);
+      ew[r] = ev[i >> 5];
+    }
   }
-  __syncthreads();
-  int n_cand = 0;
-  for (int base = 0; base < nb; base += kSelThreads) {
-    const int i = base + threadIdx.x;
-    int total;
-    block_count_excl(i < nb && !(sh.flag[i] & F_EVICTED), total, sh);
-    n_cand += total;
+  uint32_t valid = 0, evm = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = r * kSelThreads + threadIdx.x;
+    if (i < nb) {
+      valid |= 1u << r;
+      evm |= ((ew[r] >> (i & 31)) & 1u) << r;
+    }
   }
-  const int n_e = min(k_e, n_cand);
-  if (n_e == n_cand) {
-    for (int i = threadIdx.x; i < nb; i += kSelThreads)
-      if (!(sh.flag[i] & F_EVICTED)) sh.flag[i] |= F_IN_E;
-  } else if (n_e > 0) {
-    radix_top_k(nb, n_e, F_EVICTED, 0, F_IN_E, sh);
-  }
-  __syncthreads();
-  // every candidate left out is evicted for good
-  for (int i = threadIdx.x; i < nb; i += kSelThreads)
-    if (!(sh.flag[i] & (F_EVICTED | F_IN_E))) sh.flag[i] |= F_EVICTED;
-  __syncthreads();
+  int phase = 0;
 
-  // --- query part ---------------------------------------------------------
-  for (int i = threadIdx.x; i < nb; i += kSelThreads) sh.key[i] = order_key(sq[i]);
-  __syncthreads();
+  // --- eviction part: candidates are the never-evicted blocks ------------
+  const uint32_t cand_e = valid & ~evm;
+  int wave_cand = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) wave_cand += __popcll(__ballot((cand_e >> r) & 1u));
+  const int n_cand = block_sum(wave_cand, phase, sh);
+  const int n_e = min(k_e, n_cand);
+  uint32_t in_e = 0;
+  if (n_e == n_cand) in_e = cand_e;
+  else if (n_e > 0) radix_top_k<R>(ke, cand_e, n_e, in_e, phase, sh);
+  evm |= cand_e & ~in_e;  // every candidate left out is evicted for good
+
+  // --- query part: best of the blocks the eviction part did not take ----
+  const uint32_t cand_q = valid & ~in_e;
   const int rest = nb - n_e;
   const int n_q = min(k_q, rest);
-  if (n_q == rest) {
-    for (int i = threadIdx.x; i < nb; i += kSelThreads)
-      if (!(sh.flag[i] & F_IN_E)) sh.flag[i] |= F_IN_Q;
-  } else if (n_q > 0) {
-    radix_top_k(nb, n_q, F_IN_E, 0, F_IN_Q, sh);
+  uint32_t in_q = 0;
+  if (n_q == rest) in_q = cand_q;
+  else if (n_q > 0) radix_top_k<R>(kq, cand_q, n_q, in_q, phase, sh);
+
+  // --- outputs: ascending union via ballots, eviction bitmap words ------
+  const uint32_t pick = in_e | in_q;
+  uint64_t pm[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    pm[r] = __ballot((pick >> r) & 1u);
+    const uint64_t em = __ballot((evm >> r) & 1u);
+    const uint64_t vm = __ballot((valid >> r) & 1u);
+    // lanes 0 and 32 own the two 32-bit words this wave covers at element r
+    const int i0 = r * kSelThreads + w * kWave + (lane & 32);
+    if ((lane & 31) == 0 && i0 < nb) {  // this lane loaded that word at the start
+      const uint32_t e32 = (uint32_t)(em >> (lane & 32));
+      const uint32_t v32 = (uint32_t)(vm >> (lane & 32));
+      ev[i0 >> 5] = (ew[r] & ~v32) | e32;
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) sh.pos[r][w] = __popcll(pm[r]);
   }
   __syncthreads();
-
-  // --- outputs: ascending union, evicted bitmap ----------------------------
-  int carry = 0;
   int32_t* out = sel + (int64_t)bh * sel_cap;
-  for (int base = 0; base < nb; base += kSelThreads) {
-    const int i = base + threadIdx.x;
-    const bool pick = i < nb && (sh.flag[i] & (F_IN_E | F_IN_Q));
-    int total;
-    const int pos = carry + block_count_excl(pick, total, sh);
-    if (pick && pos < sel_cap) out[pos] = i;
-    carry += total;
-  }
-  if (threadIdx.x == 0) sel_count[bh] = min(carry, sel_cap);
-  for (int w = threadIdx.x; w < (nb + 31) / 32; w += kSelThreads) {
-    uint32_t bits = 0;
-    for (int k = 0; k < 32; ++k) {
-      const int i = w * 32 + k;
-      if (i < nb && (sh.flag[i] & F_EVICTED)) bits |= 1u << k;
+  int before = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int pos = before + lanes_below(pm[r]);
+#pragma unroll
+    for (int ww = 0; ww < kSelWaves; ++ww) {
+      const int c = sh.pos[r][ww];
+      pos += ww < w ? c : 0;
+      before += c;
     }
-    ev[w] |= bits;
+    if (((pick >> r) & 1u) && pos < sel_cap) out[pos] = r * kSelThreads + threadIdx.x;
   }
+  if (threadIdx.x == 0) sel_count[bh] = min(before, sel_cap);
 }
 
 // One wave per (b, h); membership through an LDS bitmap, order-preserving
@@ -263,9 +321,18 @@ __global__ __launch_bounds__(kWave) void swap_diff_kernel(int max_blocks, int ca
 hipError_t launch_select(const nosa_dims& d, const float* score_q, const float* score_e,
                          const int32_t* seq_lens, int32_t k_e, int32_t k_q, uint32_t* evicted,
                          int32_t* sel, int32_t sel_cap, int32_t* sel_count, hipStream_t stream) {
-  select_kernel<<<d.batch * d.n_kv_heads, kSelThreads, 0, stream>>>(
-      d.n_kv_heads, d.block_size, d.max_blocks, score_q, score_e, seq_lens, k_e, k_q, evicted, sel,
-      sel_cap, sel_count);
+  const int R = (d.max_blocks + kSelThreads - 1) / kSelThreads;  // elements per thread
+  const dim3 grid(d.batch * d.n_kv_heads);
+#define NOSA_SELECT(RR)                                                                              \
+  select_kernel<RR><<<grid, kSelThreads, 0, stream>>>(d.n_kv_heads, d.block_size, d.max_blocks, score_q, \
+                                                      score_e, seq_lens, k_e, k_q, evicted, sel, sel_cap, \
+                                                      sel_count)
+  if (R <= 2) NOSA_SELECT(2);
+  else if (R <= 4) NOSA_SELECT(4);
+  else if (R <= 8) NOSA_SELECT(8);
+  else if (R <= 16) NOSA_SELECT(16);
+  else NOSA_SELECT(32);
+#undef NOSA_SELECT
   return hipGetLastError();
 }
 
