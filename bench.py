@@ -4,7 +4,9 @@
 
 A step is the whole hot path over one batch: append -> score -> select ->
 swap_diff -> sparse_decode (split-K) -> combine, for every sequence of the
-batch, on synthetic inputs resident in HBM before timing starts.  The
+batch, on synthetic inputs resident in HBM before timing starts.  By default
+select + swap_diff run as one launch (nosa_select_swap) and decode + combine
+as one (nosa_sparse_decode_combine); --unfused times the six separate calls.  The
 default workload is the Llama-3-8B-shaped layer at 32K context.
 
 Timing (HIP events on the stream the kernels run on):
@@ -48,6 +50,7 @@ def parse(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true", help="time the six separate entry points")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with one plain 1 GiB device copy, a known-size kernel for counter calibration")
     return ap.parse_args(argv)
@@ -134,7 +137,7 @@ def main(argv=None) -> int:
         raise SystemExit(f"at most {w.n_append} appended tokens: lower --steps/--warmup")
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = synth.generate(w, args.seed)
-    sess = DecodeSession(w, inp, splits=args.splits, poison=False)
+    sess = DecodeSession(w, inp, splits=args.splits, poison=False, fused=not args.unfused)
     stream = torch.cuda.current_stream()
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
 
@@ -169,8 +172,13 @@ def main(argv=None) -> int:
     print(f"[bench] cold pass done: median {np.median(step_ms)*1e3:.1f} us", file=sys.stderr, flush=True)
 
     # pass 2: cold steps with an event between every launch
-    names = (["append"] if w.append else []) + ([] if w.select_all else ["score", "select"]) + \
-            ["swap_diff", "decode", "combine"]
+    fused = sess.fused
+    names = (["append"] if w.append else []) + ([] if w.select_all else ["score"])
+    if fused:
+        names += (["swap_diff"] if w.select_all else ["select_swap"]) + ["decode_combine"]
+    else:
+        names += ([] if w.select_all else ["select"]) + ["swap_diff", "decode", "combine"]
+    dec_name = "decode_combine" if fused else "decode"
     per = {n: [] for n in names}
     for k in range(K):
         flush()
@@ -185,6 +193,10 @@ def main(argv=None) -> int:
                 sess.score(t)
             elif n == "select":
                 sess.select()
+            elif n == "select_swap":
+                sess.select_swap()
+            elif n == "decode_combine":
+                sess.decode_combine(t)
             elif n == "swap_diff":
                 sess.swap_diff()
             elif n == "decode":
@@ -212,7 +224,7 @@ def main(argv=None) -> int:
     t_step = float(np.median(step_ms)) / 1e3
     total_bytes = kvb + sb
     gbps = total_bytes / t_step / 1e9
-    dec_s = kernels_us["decode"] / 1e6
+    dec_s = kernels_us[dec_name] / 1e6
     dec_gbps = kvb / dec_s / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -222,8 +234,8 @@ def main(argv=None) -> int:
             traffic = tr.get("bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                "kernel": "nosa_sparse_decode (decode_kernel)",
-                "algorithmic_bytes_per_launch": int(kvb), "avg_launch_us": round(kernels_us["decode"], 2)}
+                "kernel": ("nosa_sparse_decode_combine" if fused else "nosa_sparse_decode") + " (decode_kernel)",
+                "algorithmic_bytes_per_launch": int(kvb), "avg_launch_us": round(kernels_us[dec_name], 2)}
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -253,7 +265,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
                    "context": w.T0, "block": w.bs, "sub_block": w.ss, "k_e": w.k_e, "k_q": w.k_q,
-                   "splits": sess.P, "table": w.table, "parallelism": "single GPU"},
+                   "splits": sess.P, "table": w.table, "fused": fused, "parallelism": "single GPU"},
         "hbm_gbps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": int(total_bytes),

@@ -124,6 +124,25 @@ nosa_status nosa_select(const nosa_dims* dims, const float* score_q, const float
       nosa::launch_select(*dims, score_q, score_e, seq_lens, k_e, k_q, evicted, sel, sel_cap, sel_count, stream));
 }
 
+nosa_status nosa_select_swap(const nosa_dims* dims, const float* score_q, const float* score_e,
+                             const int32_t* seq_lens, int32_t k_e, int32_t k_q, uint32_t* evicted, int32_t* sel,
+                             int32_t sel_cap, int32_t* sel_count, const int32_t* prev, const int32_t* prev_count,
+                             int32_t* load, int32_t* load_count, int32_t* evict, int32_t* evict_count,
+                             hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if (!score_q || !score_e || !seq_lens || !evicted || !sel || !sel_count) return NOSA_ERR_ARG;
+  if (!prev || !prev_count || !load || !load_count || !evict || !evict_count) return NOSA_ERR_ARG;
+  if (k_e < 0 || k_q < 0 || sel_cap < 1) return NOSA_ERR_ARG;
+  const int64_t k = (int64_t)k_e + k_q;
+  if ((int64_t)sel_cap < (k < dims->max_blocks ? k : (int64_t)dims->max_blocks)) return NOSA_ERR_ARG;
+  if (sel_cap > dims->max_blocks) return NOSA_ERR_ARG;
+  if (prev == sel || load == sel || evict == sel || load == evict) return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_select_swap(*dims, score_q, score_e, seq_lens, k_e, k_q, evicted, sel, sel_cap,
+                                           sel_count, prev, prev_count, load, load_count, evict, evict_count,
+                                           stream));
+}
+
 nosa_status nosa_swap_diff(const nosa_dims* dims, int32_t cap, const int32_t* prev, const int32_t* prev_count,
                            const int32_t* cur, const int32_t* cur_count, int32_t* load, int32_t* load_count,
                            int32_t* evict, int32_t* evict_count, hipStream_t stream) {
@@ -151,7 +170,28 @@ nosa_status nosa_sparse_decode(const nosa_dims* dims, const uint16_t* q, const n
     if (dims->n_q_heads / dims->n_kv_heads > 8) return NOSA_ERR_UNSUPPORTED;
   }
   return from_hip(nosa::launch_decode(*dims, q, *kv, sel, sel_count, sel_cap, seq_lens, num_splits, sm_scale,
-                                      part_o, part_m, part_l, stream));
+                                      part_o, part_m, part_l, nullptr, nullptr, nullptr, nullptr, stream));
+}
+
+nosa_status nosa_sparse_decode_combine(const nosa_dims* dims, const uint16_t* q, const nosa_kv* kv,
+                                       const int32_t* sel, const int32_t* sel_count, int32_t sel_cap,
+                                       const int32_t* seq_lens, int32_t num_splits, float sm_scale,
+                                       float* part_o, float* part_m, float* part_l, int32_t* counters,
+                                       float* o, float* m, float* l, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if ((st = check_kv(dims, kv, true)) != NOSA_OK) return st;
+  if (!q || !sel || !sel_count || !seq_lens || !part_o || !part_m || !part_l) return NOSA_ERR_ARG;
+  if (!counters || !o || !m || !l) return NOSA_ERR_ARG;
+  if (!aligned16(q)) return NOSA_ERR_ARG;
+  if (sel_cap < 1 || num_splits < 1 || num_splits > 256) return NOSA_ERR_ARG;
+  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return NOSA_ERR_ARG;
+  if (kv->kind == NOSA_TABLE_PACKED_ROPE) {
+    if (!kv->q_pos || !(kv->rope_base > 1.f)) return NOSA_ERR_ARG;
+    if (dims->n_q_heads / dims->n_kv_heads > 8) return NOSA_ERR_UNSUPPORTED;
+  }
+  return from_hip(nosa::launch_decode(*dims, q, *kv, sel, sel_count, sel_cap, seq_lens, num_splits, sm_scale,
+                                      part_o, part_m, part_l, counters, o, m, l, stream));
 }
 
 nosa_status nosa_combine(const nosa_dims* dims, int32_t num_splits, const float* part_o, const float* part_m,

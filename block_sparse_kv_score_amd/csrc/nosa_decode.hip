@@ -65,6 +65,11 @@ struct DecodeArgs {
   float* part_o;
   float* part_m;
   float* part_l;
+  // fused combine (all null for the split-only call)
+  int32_t* counters;  // [B*Hkv], zero between calls
+  float* o;
+  float* m;
+  float* l;
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -108,6 +113,7 @@ struct DecodeShape {
 
 template <int D, int G, bool ROPE>
 struct DecodeSmem {
+  int32_t last;
   uint16_t p[kDecWaves][G][kTile];  // bf16 probabilities of the tile, per wave
   float qf[ROPE ? G : 1][ROPE ? D : 1];
   uint16_t qrot[ROPE ? kDecWaves : 1][ROPE ? 2 * G : 1][ROPE ? D : 8];  // rotated query, bf16 hi / lo rows
@@ -115,6 +121,83 @@ struct DecodeSmem {
   float lw[kDecWaves][G];
   float ow[kDecWaves][G][D];
 };
+
+// Split partials cross workgroups in the fused decode + combine.  They are
+// written with device-scope (agent) atomic stores, which the memory system
+// makes visible across all XCDs' L2 caches before the store completes, and
+// read back with device-scope atomic loads, which never hit a stale L2
+// line.  Ordering then needs only the per-wave wait for stores to complete
+// before the arrival counter is bumped -- no write-back or invalidation of
+// whole L2 caches.
+// s_waitcnt immediate (gfx9 family encoding) that waits for every vector
+// memory operation of the wave, stores included, and leaves the other
+// counters unconstrained: vmcnt = 0, expcnt = 7, lgkmcnt = 15.
+constexpr int kWaitVmcnt0 = (0xF << 8) | (0x7 << 4);
+__device__ __forceinline__ void store_shared_f32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <bool COHERENT>
+__device__ __forceinline__ float load_part(const float* p) {
+  if constexpr (COHERENT)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+
+// Merge of the P split partials of one output row at dim d [NOVITA, 2.
+// Attention modifications]: M = max of the non-empty splits' row maxima,
+// weights l_p * exp(m_p - M), O = sum_p w_p O_p / sum_p w_p.  The first
+// eight splits are loaded together (clamped, branch-free) so P <= 8 costs
+// one memory round trip.  Thread (row, d); the thread with d == 0 also
+// writes the row's m and l.  COHERENT: the partials come from other
+// workgroups of the same launch (device-scope loads).
+template <bool COHERENT>
+__device__ __forceinline__ void merge_splits(int P, int D, int64_t row, int d, const float* __restrict__ part_o,
+                                             const float* __restrict__ part_m, const float* __restrict__ part_l,
+                                             float* __restrict__ o, float* __restrict__ m, float* __restrict__ l) {
+  constexpr int PRE = 8;
+  const float* pm = part_m + row * P;
+  const float* pl = part_l + row * P;
+  const float* po = part_o + row * P * D + d;
+  float mv[PRE], lv[PRE], ov[PRE];
+#pragma unroll
+  for (int j = 0; j < PRE; ++j) {
+    const int k = min(j, P - 1);
+    mv[j] = load_part<COHERENT>(pm + k);
+    lv[j] = load_part<COHERENT>(pl + k);
+    ov[j] = load_part<COHERENT>(po + (int64_t)k * D);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < PRE; ++j)
+    if (j < P && lv[j] > 0.f) M = fmaxf(M, mv[j]);
+  for (int k = PRE; k < P; ++k) {
+    const float lk = load_part<COHERENT>(pl + k), mk = load_part<COHERENT>(pm + k);
+    if (lk > 0.f) M = fmaxf(M, mk);
+  }
+  float L = 0.f, O = 0.f;
+#pragma unroll
+  for (int j = 0; j < PRE; ++j) {
+    if (j < P && lv[j] > 0.f) {
+      const float wj = lv[j] * expf(mv[j] - M);
+      L += wj;
+      O += wj * ov[j];
+    }
+  }
+  for (int k = PRE; k < P; ++k) {
+    const float lk = load_part<COHERENT>(pl + k), mk = load_part<COHERENT>(pm + k);
+    if (lk > 0.f) {
+      const float wk = lk * expf(mk - M);
+      L += wk;
+      O += wk * load_part<COHERENT>(po + (int64_t)k * D);
+    }
+  }
+  o[row * D + d] = L > 0.f ? O / L : 0.f;
+  if (d == 0) {
+    m[row] = L > 0.f ? M : -INFINITY;
+    l[row] = L;
+  }
+}
 
 template <int D, int G, int KIND>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs a) {
@@ -404,59 +487,37 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
       }
     }
     const int64_t row = ((int64_t)b * a.Hq + (int64_t)h * G + g) * a.P + p;
-    a.part_o[row * D + d] = L > 0.f ? O / L : 0.f;
+    store_shared_f32(a.part_o + row * D + d, L > 0.f ? O / L : 0.f);
     if (d == 0) {
-      a.part_m[row] = L > 0.f ? M * kLn2 : -INFINITY;
-      a.part_l[row] = L;
+      store_shared_f32(a.part_m + row, L > 0.f ? M * kLn2 : -INFINITY);
+      store_shared_f32(a.part_l + row, L);
     }
   }
+
+  if (a.counters == nullptr) return;
+  // Fused combine: the last workgroup of this (b, h) to finish merges the P
+  // partials.  Every wave waits for its device-scope partial stores to
+  // complete, then one thread counts the workgroup's arrival; the last
+  // arrival reads the partials back with device-scope loads.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (threadIdx.x == 0) sh.last = atomicAdd(&a.counters[bh], 1) == a.P - 1;
+  __syncthreads();
+  if (!sh.last) return;
+  for (int k = threadIdx.x; k < G * D; k += kDecThreads) {
+    const int g = k / D, d = k % D;
+    const int64_t row = (int64_t)b * a.Hq + (int64_t)h * G + g;
+    merge_splits<true>(a.P, D, row, d, a.part_o, a.part_m, a.part_l, a.o, a.m, a.l);
+  }
+  if (threadIdx.x == 0) a.counters[bh] = 0;  // ready for the next call
 }
 
-// One workgroup per (b, query head); thread per dim.  Split weights are
-// formed once in LDS; partial outputs are loaded eight splits at a time.
+// One workgroup per (b, query head), thread per dim; the same merge as the
+// fused tail of decode_kernel.
 __global__ void combine_kernel(int P, int D, const float* __restrict__ part_o, const float* __restrict__ part_m,
                                const float* __restrict__ part_l, float* __restrict__ o, float* __restrict__ m,
                                float* __restrict__ l) {
-  __shared__ float wgt[256];
-  __shared__ float stat[2];
-  const int64_t row = blockIdx.x;
-  const float* pm = part_m + row * P;
-  const float* pl = part_l + row * P;
-  if (threadIdx.x < kWave) {
-    float M = -INFINITY;
-    for (int k = threadIdx.x; k < P; k += kWave)
-      if (pl[k] > 0.f) M = fmaxf(M, pm[k]);
-    M = wave_max(M);
-    float L = 0.f;
-    for (int k = threadIdx.x; k < P; k += kWave) {
-      const float wk = pl[k] > 0.f ? pl[k] * expf(pm[k] - M) : 0.f;
-      wgt[k] = wk;
-      L += wk;
-    }
-    L = wave_sum(L);
-    if (threadIdx.x == 0) {
-      stat[0] = M;
-      stat[1] = L;
-    }
-  }
-  __syncthreads();
-  const float M = stat[0], L = stat[1];
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float acc = 0.f;
-    for (int k0 = 0; k0 < P; k0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = k0 + j < P ? part_o[(row * P + k0 + j) * D + d] : 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (k0 + j < P) acc += wgt[k0 + j] * v[j];
-    }
-    o[row * D + d] = L > 0.f ? acc / L : 0.f;
-  }
-  if (threadIdx.x == 0) {
-    m[row] = L > 0.f ? M : -INFINITY;
-    l[row] = L;
-  }
+  merge_splits<false>(P, D, blockIdx.x, threadIdx.x, part_o, part_m, part_l, o, m, l);
 }
 
 template <int D, int G>
@@ -488,7 +549,8 @@ static void launch_decode_d(dim3 grid, const DecodeArgs& a, int G, int kind, hip
 hipError_t launch_decode(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv,
                          const int32_t* sel, const int32_t* sel_count, int32_t sel_cap,
                          const int32_t* seq_lens, int32_t num_splits, float sm_scale,
-                         float* part_o, float* part_m, float* part_l, hipStream_t stream) {
+                         float* part_o, float* part_m, float* part_l, int32_t* counters, float* o,
+                         float* m, float* l, hipStream_t stream) {
   DecodeArgs a;
   a.t = make_table(d, kv);
   a.Hq = d.n_q_heads;
@@ -507,6 +569,10 @@ hipError_t launch_decode(const nosa_dims& d, const uint16_t* q, const nosa_kv& k
   a.part_o = part_o;
   a.part_m = part_m;
   a.part_l = part_l;
+  a.counters = counters;
+  a.o = o;
+  a.m = m;
+  a.l = l;
   const dim3 grid(d.batch * d.n_kv_heads, num_splits);
   const int G = d.n_q_heads / d.n_kv_heads;
   if (d.head_dim == 128)

@@ -108,13 +108,14 @@ __device__ __forceinline__ void sum_key_quad(const uint16_t* kpage, int bs, int 
   for (int t0 = lo; t0 < hi; t0 += kSumBatch) {
     uint2 v[kSumBatch];
 #pragma unroll
-    for (int j = 0; j < kSumBatch; ++j) v[j] = t0 + j < hi ? base[(t0 + j) * 2] : make_uint2(0u, 0u);
+    for (int j = 0; j < kSumBatch; ++j) v[j] = base[min(t0 + j, hi - 1) * 2];  // clamped: no branch
 #pragma unroll
     for (int j = 0; j < kSumBatch; ++j) {
-      a0 += (double)bf16_lo(v[j].x);
-      a1 += (double)bf16_hi(v[j].x);
-      a2 += (double)bf16_lo(v[j].y);
-      a3 += (double)bf16_hi(v[j].y);
+      const bool in = t0 + j < hi;
+      a0 += in ? (double)bf16_lo(v[j].x) : 0.0;
+      a1 += in ? (double)bf16_hi(v[j].x) : 0.0;
+      a2 += in ? (double)bf16_lo(v[j].y) : 0.0;
+      a3 += in ? (double)bf16_hi(v[j].y) : 0.0;
     }
   }
 }
@@ -124,9 +125,9 @@ __device__ __forceinline__ double sum_logits(const float* ep, int lo, int hi) {
   for (int t0 = lo; t0 < hi; t0 += kSumBatch) {
     float v[kSumBatch];
 #pragma unroll
-    for (int j = 0; j < kSumBatch; ++j) v[j] = t0 + j < hi ? ep[t0 + j] : 0.f;
+    for (int j = 0; j < kSumBatch; ++j) v[j] = ep[min(t0 + j, hi - 1)];
 #pragma unroll
-    for (int j = 0; j < kSumBatch; ++j) a += (double)v[j];
+    for (int j = 0; j < kSumBatch; ++j) a += t0 + j < hi ? (double)v[j] : 0.0;
   }
   return a;
 }
@@ -179,7 +180,9 @@ __global__ __launch_bounds__(256) void summaries_kernel(Table t, int bs, int ss,
 // append: one workgroup per sequence, one wave per KV head.  Wave h writes
 // token T of (b, h) into its page and recomputes the summary of the
 // sub-block holding it (older tokens from the page, the new one from the
-// input, ascending order); the workgroup then advances seq_lens[b].
+// input, ascending order); the workgroup then advances seq_lens[b].  The new
+// token's loads go out before the position is known, so the kernel costs
+// three dependent memory round trips: position, page, older tokens.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void append_kernel(Table t, int bs, int ss, const uint16_t* __restrict__ k_new,
@@ -188,12 +191,21 @@ __global__ void append_kernel(Table t, int bs, int ss, const uint16_t* __restric
                               uint16_t* __restrict__ v_pages, float* __restrict__ e_pages,
                               float* __restrict__ k_summary, float* __restrict__ e_summary) {
   constexpr int NQ = D / 4;
+  constexpr int VL = D / kWave;  // value dims per lane
   const int b = blockIdx.x;
   const int h = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int bh = b * t.Hkv + h;
   const int nsub = bs / ss;
   const int CS = t.max_blocks * nsub;
+  const uint16_t* kn = k_new + (int64_t)bh * D;
+  const uint16_t* vn = v_new + (int64_t)bh * D;
+  const uint4 k_oct = reinterpret_cast<const uint4*>(kn)[lane % (D / 8)];
+  const uint2 k_quad = reinterpret_cast<const uint2*>(kn)[lane % NQ];
+  uint16_t v_dim[VL];
+#pragma unroll
+  for (int j = 0; j < VL; ++j) v_dim[j] = vn[lane + j * kWave];
+  const float e_tok = e_new[bh];
   const int pos = seq_lens[b];
   const bool in_range = pos >= 0 && pos < t.max_blocks * bs;
   if (in_range) {
@@ -203,15 +215,8 @@ __global__ void append_kernel(Table t, int bs, int ss, const uint16_t* __restric
     if (page < 0) {
       if (lane == 0) flag_error(t.err);
     } else {
-      const uint16_t* kn = k_new + (int64_t)bh * D;
-      const uint16_t* vn = v_new + (int64_t)bh * D;
       uint16_t* kpage = k_pages + page * (int64_t)bs * D;
       uint16_t* vpage = v_pages + page * (int64_t)bs * D;
-      if (lane < D / 8)
-        reinterpret_cast<uint4*>(kpage)[lane * bs + r] = reinterpret_cast<const uint4*>(kn)[lane];
-      for (int d = lane; d < D; d += kWave) vpage[((r / 8) * D + d) * 8 + r % 8] = vn[d];
-      if (lane == 0) e_pages[page * bs + r] = e_new[bh];
-
       const int j = r / ss;
       const int lo = j * ss;  // page-relative start of the sub-block
       const double inv_n = 1.0 / (double)(r - lo + 1);
@@ -219,11 +224,10 @@ __global__ void append_kernel(Table t, int bs, int ss, const uint16_t* __restric
       if (lane < NQ) {
         double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
         sum_key_quad<D>(kpage, bs, lane, lo, r, a0, a1, a2, a3);
-        const uint2 nv = reinterpret_cast<const uint2*>(kn)[lane];
-        a0 += (double)bf16_lo(nv.x);
-        a1 += (double)bf16_hi(nv.x);
-        a2 += (double)bf16_lo(nv.y);
-        a3 += (double)bf16_hi(nv.y);
+        a0 += (double)bf16_lo(k_quad.x);
+        a1 += (double)bf16_hi(k_quad.x);
+        a2 += (double)bf16_lo(k_quad.y);
+        a3 += (double)bf16_hi(k_quad.y);
         float4 o;
         o.x = (float)(a0 * inv_n);
         o.y = (float)(a1 * inv_n);
@@ -233,9 +237,14 @@ __global__ void append_kernel(Table t, int bs, int ss, const uint16_t* __restric
       }
       if (lane == NQ) {  // the logit mean runs beside the key quads
         double ae = sum_logits(e_pages + page * bs, lo, r);
-        ae += (double)e_new[bh];
+        ae += (double)e_tok;
         e_summary[(int64_t)bh * CS + s] = (float)(ae * inv_n);
       }
+      // the new token itself (after the reads of the older ones above)
+      if (lane < D / 8) reinterpret_cast<uint4*>(kpage)[lane * bs + r] = k_oct;
+#pragma unroll
+      for (int jj = 0; jj < VL; ++jj) vpage[((r / 8) * D + lane + jj * kWave) * 8 + r % 8] = v_dim[jj];
+      if (lane == 0) e_pages[page * bs + r] = e_tok;
     }
   } else if (threadIdx.x == 0) {
     flag_error(t.err);

@@ -36,6 +36,11 @@ struct SelShared {
   int32_t bc[2][4];
   uint32_t mm[2][kSelWaves][2];
   int32_t pos[32][kSelWaves];
+  // fused swap lists: membership bitmaps and per-wave counts
+  uint32_t pick_bm[kMaxBlocks / 32];
+  uint32_t prev_bm[kMaxBlocks / 32];
+  int32_t pos_load[32][kSelWaves];
+  int32_t pos_evict[32][kSelWaves];
 };
 
 // Workgroup sum of one int per wave (lane 0's value); one barrier.
@@ -170,7 +175,16 @@ __device__ void radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k, uint
   __syncthreads();  // sh.pos is reused by the caller
 }
 
-template <int R>
+struct SwapArgs {
+  const int32_t* prev;
+  const int32_t* prev_count;
+  int32_t* load;
+  int32_t* load_count;
+  int32_t* evict;
+  int32_t* evict_count;
+};
+
+template <int R, bool SWAP>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(int Hkv, int bs, int max_blocks,
                                                              const float* __restrict__ score_q,
                                                              const float* __restrict__ score_e,
@@ -178,7 +192,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int Hkv, int bs, in
                                                              int k_e, int k_q,
                                                              uint32_t* __restrict__ evicted,
                                                              int32_t* __restrict__ sel, int sel_cap,
-                                                             int32_t* __restrict__ sel_count) {
+                                                             int32_t* __restrict__ sel_count, const SwapArgs sw) {
   __shared__ SelShared sh;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int bh = blockIdx.x;
@@ -202,6 +216,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int Hkv, int bs, in
       kq[r] = order_key(sq[i]);
       ew[r] = ev[i >> 5];
     }
+  }
+  // fused swap lists: the previous selection (capacity sel_cap <= max_blocks,
+  // so R entries per thread cover it), loaded with everything else
+  int32_t pv[R];
+  int n_prev = 0;
+  if constexpr (SWAP) {
+    const int32_t* pl = sw.prev + (int64_t)bh * sel_cap;
+#pragma unroll
+    for (int r = 0; r < R; ++r) pv[r] = pl[min(r * kSelThreads + (int)threadIdx.x, sel_cap - 1)];
+    n_prev = min(max(sw.prev_count[bh], 0), sel_cap);
   }
   uint32_t valid = 0, evm = 0;
 #pragma unroll
@@ -269,10 +293,73 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int Hkv, int bs, in
     if (((pick >> r) & 1u) && pos < sel_cap) out[pos] = r * kSelThreads + threadIdx.x;
   }
   if (threadIdx.x == 0) sel_count[bh] = min(before, sel_cap);
+
+  if constexpr (SWAP) {
+    // load = selected now and not before (index order); evict = before and
+    // not now (order of the previous list) -- the set differences of
+    // nosa_swap_diff, from the selection still in registers
+    for (int wd = threadIdx.x; wd < (max_blocks + 31) / 32; wd += kSelThreads) sh.prev_bm[wd] = 0u;
+    if ((lane & 31) == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int i0 = r * kSelThreads + w * kWave + (lane & 32);
+        if (i0 < max_blocks) sh.pick_bm[i0 >> 5] = (uint32_t)(pm[r] >> (lane & 32));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int k = r * kSelThreads + threadIdx.x;
+      if (k < n_prev && pv[r] >= 0 && pv[r] < max_blocks) atomicOr(&sh.prev_bm[pv[r] >> 5], 1u << (pv[r] & 31));
+    }
+    __syncthreads();
+    uint64_t lm[R], em[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = r * kSelThreads + threadIdx.x;
+      const bool in_prev = i < max_blocks && ((sh.prev_bm[min(i, max_blocks - 1) >> 5] >> (i & 31)) & 1u);
+      lm[r] = __ballot(((pick >> r) & 1u) && !in_prev);
+      const int k = r * kSelThreads + threadIdx.x;
+      const int x = pv[r];
+      const bool live = k < n_prev && x >= 0 && x < max_blocks;
+      em[r] = __ballot(live && !((sh.pick_bm[live ? x >> 5 : 0] >> (x & 31)) & 1u));
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        sh.pos_load[r][w] = __popcll(lm[r]);
+        sh.pos_evict[r][w] = __popcll(em[r]);
+      }
+    }
+    __syncthreads();
+    int32_t* lo = sw.load + (int64_t)bh * sel_cap;
+    int32_t* eo = sw.evict + (int64_t)bh * sel_cap;
+    int bl = 0, be = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int pl_ = bl + lanes_below(lm[r]), pe = be + lanes_below(em[r]);
+#pragma unroll
+      for (int ww = 0; ww < kSelWaves; ++ww) {
+        const int cl = sh.pos_load[r][ww], ce = sh.pos_evict[r][ww];
+        pl_ += ww < w ? cl : 0;
+        pe += ww < w ? ce : 0;
+        bl += cl;
+        be += ce;
+      }
+      if (((lm[r] >> lane) & 1u) && pl_ < sel_cap) lo[pl_] = r * kSelThreads + threadIdx.x;
+      if (((em[r] >> lane) & 1u) && pe < sel_cap) eo[pe] = pv[r];
+    }
+    if (threadIdx.x == 0) {
+      sw.load_count[bh] = min(bl, sel_cap);
+      sw.evict_count[bh] = min(be, sel_cap);
+    }
+  }
 }
 
 // One wave per (b, h); membership through an LDS bitmap, order-preserving
-// compaction through ballots.
+// compaction through ballots.  The first 64 entries of both lists are
+// loaded with the counts (clamped, branch-free), so short lists cost one
+// memory round trip.
 __global__ __launch_bounds__(kWave) void swap_diff_kernel(int max_blocks, int cap,
                                                           const int32_t* __restrict__ prev,
                                                           const int32_t* __restrict__ prev_count,
@@ -282,51 +369,61 @@ __global__ __launch_bounds__(kWave) void swap_diff_kernel(int max_blocks, int ca
                                                           int32_t* __restrict__ load_count,
                                                           int32_t* __restrict__ evict,
                                                           int32_t* __restrict__ evict_count) {
-  __shared__ uint32_t bm[kMaxBlocks / 32];
+  __shared__ uint32_t bm[2][kMaxBlocks / 32];  // [0]: prev, [1]: cur
   const int bh = blockIdx.x;
   const int lane = threadIdx.x;
-  const int np = min(max(prev_count[bh], 0), cap);
-  const int nc = min(max(cur_count[bh], 0), cap);
-  const int32_t* p = prev + (int64_t)bh * cap;
-  const int32_t* c = cur + (int64_t)bh * cap;
-
-  // pass 0: load = cur \ prev;  pass 1: evict = prev \ cur
-  for (int pass = 0; pass < 2; ++pass) {
-    const int32_t* mark_list = pass == 0 ? p : c;
-    const int n_mark = pass == 0 ? np : nc;
-    const int32_t* test_list = pass == 0 ? c : p;
-    const int n_test = pass == 0 ? nc : np;
-    int32_t* out = (pass == 0 ? load : evict) + (int64_t)bh * cap;
-    for (int w = lane; w < kMaxBlocks / 32; w += kWave) bm[w] = 0;
-    wave_lds_sync();
-    for (int k = lane; k < n_mark; k += kWave) {
-      const int x = mark_list[k];
-      if (x >= 0 && x < max_blocks) atomicOr(&bm[x >> 5], 1u << (x & 31));
-    }
-    wave_lds_sync();
-    int n_out = 0;
-    for (int base = 0; base < n_test; base += kWave) {
+  const int32_t* lst[2] = {prev + (int64_t)bh * cap, cur + (int64_t)bh * cap};
+  const int first = min(lane, cap - 1);
+  const int x0[2] = {lst[0][first], lst[1][first]};
+  const int n[2] = {min(max(prev_count[bh], 0), cap), min(max(cur_count[bh], 0), cap)};
+  for (int w = lane; w < kMaxBlocks / 32; w += kWave) bm[0][w] = bm[1][w] = 0u;
+  wave_lds_sync();
+  // mark both lists
+#pragma unroll
+  for (int li = 0; li < 2; ++li) {
+    for (int base = 0; base < n[li]; base += kWave) {
       const int k = base + lane;
-      const int x = k < n_test ? test_list[k] : -1;
-      const bool keep = x >= 0 && x < max_blocks && !((bm[x >> 5] >> (x & 31)) & 1u);
-      const uint64_t m = __ballot(keep);
-      if (keep) out[n_out + lanes_below(m)] = x;
-      n_out += __popcll(m);
+      const int x = base == 0 ? x0[li] : (k < n[li] ? lst[li][k] : -1);
+      if (k < n[li] && x >= 0 && x < max_blocks) atomicOr(&bm[li][x >> 5], 1u << (x & 31));
     }
-    if (lane == 0) (pass == 0 ? load_count : evict_count)[bh] = n_out;
-    wave_lds_sync();
+  }
+  wave_lds_sync();
+  // load = cur \ prev (li = 1 tested against 0), evict = prev \ cur
+#pragma unroll
+  for (int li = 0; li < 2; ++li) {
+    const int tl = 1 - li;  // list under test: cur first, then prev
+    int32_t* out = (li == 0 ? load : evict) + (int64_t)bh * cap;
+    int n_out = 0;
+    for (int base = 0; base < n[tl]; base += kWave) {
+      const int k = base + lane;
+      const int x = base == 0 ? x0[tl] : (k < n[tl] ? lst[tl][k] : -1);
+      const bool keep = k < n[tl] && x >= 0 && x < max_blocks && !((bm[li][x >> 5] >> (x & 31)) & 1u);
+      const uint64_t mk = __ballot(keep);
+      if (keep) out[n_out + lanes_below(mk)] = x;
+      n_out += __popcll(mk);
+    }
+    if (lane == 0) (li == 0 ? load_count : evict_count)[bh] = n_out;
   }
 }
 
-hipError_t launch_select(const nosa_dims& d, const float* score_q, const float* score_e,
-                         const int32_t* seq_lens, int32_t k_e, int32_t k_q, uint32_t* evicted,
-                         int32_t* sel, int32_t sel_cap, int32_t* sel_count, hipStream_t stream) {
+static hipError_t launch_select_any(const nosa_dims& d, const float* score_q, const float* score_e,
+                                    const int32_t* seq_lens, int32_t k_e, int32_t k_q, uint32_t* evicted,
+                                    int32_t* sel, int32_t sel_cap, int32_t* sel_count, const SwapArgs* sw,
+                                    hipStream_t stream) {
   const int R = (d.max_blocks + kSelThreads - 1) / kSelThreads;  // elements per thread
   const dim3 grid(d.batch * d.n_kv_heads);
-#define NOSA_SELECT(RR)                                                                              \
-  select_kernel<RR><<<grid, kSelThreads, 0, stream>>>(d.n_kv_heads, d.block_size, d.max_blocks, score_q, \
-                                                      score_e, seq_lens, k_e, k_q, evicted, sel, sel_cap, \
-                                                      sel_count)
+  const SwapArgs none = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+#define NOSA_SELECT(RR)                                                                                         \
+  do {                                                                                                          \
+    if (sw)                                                                                                     \
+      select_kernel<RR, true><<<grid, kSelThreads, 0, stream>>>(d.n_kv_heads, d.block_size, d.max_blocks,       \
+                                                                score_q, score_e, seq_lens, k_e, k_q, evicted,  \
+                                                                sel, sel_cap, sel_count, *sw);                  \
+    else                                                                                                        \
+      select_kernel<RR, false><<<grid, kSelThreads, 0, stream>>>(d.n_kv_heads, d.block_size, d.max_blocks,      \
+                                                                 score_q, score_e, seq_lens, k_e, k_q, evicted, \
+                                                                 sel, sel_cap, sel_count, none);                \
+  } while (0)
   if (R <= 2) NOSA_SELECT(2);
   else if (R <= 4) NOSA_SELECT(4);
   else if (R <= 8) NOSA_SELECT(8);
@@ -334,6 +431,23 @@ hipError_t launch_select(const nosa_dims& d, const float* score_q, const float* 
   else NOSA_SELECT(32);
 #undef NOSA_SELECT
   return hipGetLastError();
+}
+
+hipError_t launch_select(const nosa_dims& d, const float* score_q, const float* score_e,
+                         const int32_t* seq_lens, int32_t k_e, int32_t k_q, uint32_t* evicted,
+                         int32_t* sel, int32_t sel_cap, int32_t* sel_count, hipStream_t stream) {
+  return launch_select_any(d, score_q, score_e, seq_lens, k_e, k_q, evicted, sel, sel_cap, sel_count, nullptr,
+                           stream);
+}
+
+hipError_t launch_select_swap(const nosa_dims& d, const float* score_q, const float* score_e,
+                              const int32_t* seq_lens, int32_t k_e, int32_t k_q, uint32_t* evicted,
+                              int32_t* sel, int32_t sel_cap, int32_t* sel_count, const int32_t* prev,
+                              const int32_t* prev_count, int32_t* load, int32_t* load_count, int32_t* evict,
+                              int32_t* evict_count, hipStream_t stream) {
+  const SwapArgs sw = {prev, prev_count, load, load_count, evict, evict_count};
+  return launch_select_any(d, score_q, score_e, seq_lens, k_e, k_q, evicted, sel, sel_cap, sel_count, &sw,
+                           stream);
 }
 
 hipError_t launch_swap_diff(const nosa_dims& d, int32_t cap, const int32_t* prev,

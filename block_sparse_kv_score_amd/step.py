@@ -10,6 +10,9 @@ Call sequence of decode step t (1-based):
   nosa_swap_diff         against the previous step's selection
   nosa_sparse_decode     split-K over the selected pages
   nosa_combine           -> O, rowmax m, l
+With `fused` (the default) select + swap_diff run as nosa_select_swap and
+decode + combine as nosa_sparse_decode_combine: the same results in four
+launches instead of six.
 """
 
 from __future__ import annotations
@@ -36,8 +39,9 @@ class DecodeSession:
     selection state and step outputs."""
 
     def __init__(self, w: Workload, inp: Inputs, splits: int | None = None, device: str = "cuda",
-                 poison: bool = True, stream: torch.cuda.Stream | None = None):
+                 poison: bool = True, stream: torch.cuda.Stream | None = None, fused: bool = True):
         self.w, self.inp = w, inp
+        self.fused = fused
         self.P = int(splits or w.splits)
         self.dev = torch.device(device)
         self.stream = stream
@@ -90,6 +94,7 @@ class DecodeSession:
         self.o = torch.full((B, Hq, D), fill, dtype=torch.float32, device=dev)
         self.m = torch.full((B, Hq), fill, dtype=torch.float32, device=dev)
         self.l = torch.full_like(self.m, fill)
+        self.counters = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)  # fused combine arrivals
 
         # per-step queries and appended tokens, resident before timing
         n_steps = w.n_append if w.append else 1
@@ -147,6 +152,16 @@ class DecodeSession:
         nosa.nosa_sparse_decode(self.dims, self.q(t), self.kv, self.sel, self.sel_count, self.seq_lens,
                                 self.P, self.w.sm_scale, self.part_o, self.part_m, self.part_l, self.stream)
 
+    def select_swap(self):
+        nosa.nosa_select_swap(self.dims, self.score_q, self.score_e, self.seq_lens, self.w.k_e, self.w.k_q,
+                              self.evicted, self.sel, self.sel_count, self.prev, self.prev_count,
+                              self.load, self.load_count, self.evict, self.evict_count, self.stream)
+
+    def decode_combine(self, t: int):
+        nosa.nosa_sparse_decode_combine(self.dims, self.q(t), self.kv, self.sel, self.sel_count, self.seq_lens,
+                                        self.P, self.w.sm_scale, self.part_o, self.part_m, self.part_l,
+                                        self.counters, self.o, self.m, self.l, self.stream)
+
     def combine(self):
         nosa.nosa_combine(self.dims, self.P, self.part_o, self.part_m, self.part_l, self.o, self.m, self.l,
                           self.stream)
@@ -172,9 +187,16 @@ class DecodeSession:
             self.append(t)
         if not w.select_all:
             self.score(t)
-            self.select()
-        self.swap_diff()
-        self.decode(t)
-        self.combine()
+            if self.fused:
+                self.select_swap()
+            else:
+                self.select()
+        if w.select_all or not self.fused:
+            self.swap_diff()
+        if self.fused:
+            self.decode_combine(t)
+        else:
+            self.decode(t)
+            self.combine()
         self.step_index = t
         return t

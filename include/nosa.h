@@ -194,6 +194,19 @@ nosa_status nosa_select(const nosa_dims* dims, const float* score_q, const float
                         const int32_t* seq_lens, int32_t k_e, int32_t k_q, uint32_t* evicted,
                         int32_t* sel, int32_t sel_cap, int32_t* sel_count, hipStream_t stream);
 
+/* nosa_select and nosa_swap_diff in one launch: the selection is made as
+ * by nosa_select, then load / evict are formed against prev exactly as
+ * nosa_swap_diff(prev, sel) would, from the selection still in registers
+ * (saves a launch and a round trip on the decode step).  prev, load and
+ * evict are int32 [B][Hkv][sel_cap] with counts [B][Hkv]; here
+ * sel_cap <= max_blocks, and sel, prev, load, evict must be distinct.    */
+nosa_status nosa_select_swap(const nosa_dims* dims, const float* score_q, const float* score_e,
+                             const int32_t* seq_lens, int32_t k_e, int32_t k_q, uint32_t* evicted,
+                             int32_t* sel, int32_t sel_cap, int32_t* sel_count,
+                             const int32_t* prev, const int32_t* prev_count,
+                             int32_t* load, int32_t* load_count, int32_t* evict, int32_t* evict_count,
+                             hipStream_t stream);
+
 /* Block-swap set differences [NOSA, NOSI set-difference kernel]:
  *   load  = cur  minus prev (in cur's order),
  *   evict = prev minus cur  (in prev's order),
@@ -221,6 +234,18 @@ nosa_status nosa_sparse_decode(const nosa_dims* dims, const uint16_t* q, const n
                                const int32_t* sel, const int32_t* sel_count, int32_t sel_cap,
                                const int32_t* seq_lens, int32_t num_splits, float sm_scale,
                                float* part_o, float* part_m, float* part_l, hipStream_t stream);
+
+/* nosa_sparse_decode and nosa_combine in one launch: the decode writes its
+ * split partials as above, and the last workgroup of each (b, h) to finish
+ * (counted with a device-scope atomic in counters[b*Hkv + h]) merges them
+ * into o, m, l exactly as nosa_combine defines.
+ *   counters: int32 [B][Hkv], all zero before the first call; every call
+ *   leaves them zero.  Calls that overlap on the same counters race.      */
+nosa_status nosa_sparse_decode_combine(const nosa_dims* dims, const uint16_t* q, const nosa_kv* kv,
+                                       const int32_t* sel, const int32_t* sel_count, int32_t sel_cap,
+                                       const int32_t* seq_lens, int32_t num_splits, float sm_scale,
+                                       float* part_o, float* part_m, float* part_l, int32_t* counters,
+                                       float* o, float* m, float* l, hipStream_t stream);
 
 /* Attention, combine [NOVITA: return rowmax and l with O]:
  *   m = max_p part_m (over p with part_l > 0), l = sum_p part_l e^(part_m - m),

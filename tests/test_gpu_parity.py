@@ -75,11 +75,11 @@ def gpu_invariants(w, t, g: Gpu, prev: Gpu | None):
             assert gamma >= (w.k_e - len(new & ge)) / w.k - 1e-12, ("locality", gamma)
 
 
-def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=True):
+def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=True, fused=True):
     announce(f"trajectory {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T0={w.T0} steps={steps or w.steps} "
-             f"P={splits or w.splits} pairs={'all' if pairs is None else pairs} seed={seed}")
+             f"P={splits or w.splits} pairs={'all' if pairs is None else pairs} seed={seed} fused={fused}")
     inp = synth.generate(w, seed)
-    sess = session(w, inp, splits=splits)
+    sess = session(w, inp, splits=splits, fused=fused)
     pairs = pairs or [(b, h) for b in range(w.B) for h in range(w.Hkv)]
     lgs = {p: logical_pair(inp, *p) for p in pairs}
     states = {p: PairState() for p in pairs}
@@ -90,6 +90,7 @@ def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=
         torch.cuda.synchronize()
         g = Gpu(sess)
         assert g.err == 0, "device contract flag raised"
+        assert not sess.counters.any().item(), "fused combine left a nonzero arrival counter"
         if not w.select_all:
             gpu_invariants(w, t, g, prev_g)
         forced = False
@@ -124,6 +125,63 @@ def test_8b_shape_small_ragged():
 def test_70b_shape_small_two_level():
     w = WORKLOADS["llama31_70b_256k"].scaled(B=2, Hq=16, Hkv=2, T0=16384 + 100, dir_entries=64)
     run_trajectory(w, seed=2)
+
+
+def test_tiny_nosa_separate_calls():
+    # the unfused sequence: nosa_select, nosa_swap_diff, nosa_sparse_decode,
+    # nosa_combine as six launches
+    run_trajectory(WORKLOADS["tiny_nosa"], seed=10, steps=8, fused=False)
+
+
+def test_8b_shape_small_separate_calls():
+    w = WORKLOADS["llama3_8b_32k"].scaled(B=2, Hq=8, Hkv=2, T0=4096 + 61)
+    run_trajectory(w, seed=1, splits=3, steps=6, fused=False)
+
+
+FUSED_CASES = [
+    ("tiny_nosa", {}, 2),
+    ("llama3_8b_32k", dict(B=2, Hq=8, Hkv=2, T0=4096 + 61), 3),
+    ("dense_8b_8k", dict(B=2, Hq=8, Hkv=2, T0=1000), 37),
+    ("llama31_70b_256k", dict(B=2, Hq=16, Hkv=2, T0=16384 + 100, dir_entries=64), 16),
+    ("lazy_rope_32k", dict(B=2, Hq=8, Hkv=2, T0=8 * 512, doc_len=512), 9),
+]
+
+
+@pytest.mark.parametrize("name,scale,splits", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_equals_separate(name, scale, splits):
+    """nosa_select_swap and nosa_sparse_decode_combine give bit-identical
+    results to the separate calls they fuse, step after step."""
+    w = WORKLOADS[name].scaled(**scale) if scale else WORKLOADS[name]
+    announce(f"fused vs separate {name} {scale} P={splits}")
+    inp = synth.generate(w, 11)
+    a = session(w, inp, splits=splits, fused=True)
+    s = session(w, inp, splits=splits, fused=False)
+    names = ["sel", "sel_count", "evicted", "load", "load_count", "evict", "evict_count",
+             "part_o", "part_m", "part_l", "o", "m", "l", "seq_lens"]
+    for t in range(1, min(w.steps, 6) + 1):
+        a.step(t)
+        s.step(t)
+        torch.cuda.synchronize()
+        for n in names:
+            x, y = getattr(a, n), getattr(s, n)
+            if n in ("load", "evict"):  # compare the listed prefix only
+                cnt = getattr(a, n + "_count")
+                assert torch.equal(cnt, getattr(s, n + "_count"))
+                for b in range(w.B):
+                    for h in range(w.Hkv):
+                        k = int(cnt[b, h])
+                        assert torch.equal(x[b, h, :k], y[b, h, :k]), (n, t, b, h)
+                continue
+            if n == "sel":
+                cnt = a.sel_count
+                for b in range(w.B):
+                    for h in range(w.Hkv):
+                        k = int(cnt[b, h])
+                        assert torch.equal(x[b, h, :k], y[b, h, :k]), (n, t, b, h)
+                continue
+            assert torch.equal(x.view(torch.int32) if x.dtype == torch.float32 else x,
+                               y.view(torch.int32) if y.dtype == torch.float32 else y), (n, t)
+        assert not a.counters.any().item()
 
 
 def test_dense_small_many_splits():
