@@ -5,8 +5,9 @@
 A step is the whole hot path over one batch: append -> score -> select ->
 swap_diff -> sparse_decode (split-K) -> combine, for every sequence of the
 batch, on synthetic inputs resident in HBM before timing starts.  By default
-select + swap_diff run as one launch (nosa_select_swap) and decode + combine
-as one (nosa_sparse_decode_combine); --unfused times the six separate calls.  The
+the step is three launches: append + score (nosa_append_score), select +
+swap_diff (nosa_select_swap) and decode + combine
+(nosa_sparse_decode_combine); --unfused times the six separate calls.  The
 default workload is the Llama-3-8B-shaped layer at 32K context.
 
 Timing (HIP events on the stream the kernels run on):
@@ -173,11 +174,13 @@ def main(argv=None) -> int:
 
     # pass 2: cold steps with an event between every launch
     fused = sess.fused
-    names = (["append"] if w.append else []) + ([] if w.select_all else ["score"])
     if fused:
-        names += (["swap_diff"] if w.select_all else ["select_swap"]) + ["decode_combine"]
+        names = ((["append"] if w.append else []) + ["swap_diff"]) if w.select_all else ["append_score",
+                                                                                          "select_swap"]
+        names += ["decode_combine"]
     else:
-        names += ([] if w.select_all else ["select"]) + ["swap_diff", "decode", "combine"]
+        names = (["append"] if w.append else []) + ([] if w.select_all else ["score", "select"])
+        names += ["swap_diff", "decode", "combine"]
     dec_name = "decode_combine" if fused else "decode"
     per = {n: [] for n in names}
     for k in range(K):
@@ -195,6 +198,8 @@ def main(argv=None) -> int:
                 sess.select()
             elif n == "select_swap":
                 sess.select_swap()
+            elif n == "append_score":
+                sess.append_score(t)
             elif n == "decode_combine":
                 sess.decode_combine(t)
             elif n == "swap_diff":

@@ -36,7 +36,8 @@ COMMON = [
     "-Wno-unused-command-line-argument",
 ]
 
-SOURCES = ["nosa_api.cpp", "nosa_index.hip", "nosa_score.hip", "nosa_select.hip", "nosa_decode.hip"]
+SOURCES = ["nosa_api.cpp", "nosa_index.hip", "nosa_score.hip", "nosa_select.hip", "nosa_fused.hip",
+           "nosa_decode.hip"]
 
 
 def _compile(src: str) -> str:

@@ -143,6 +143,26 @@ nosa_status nosa_select_swap(const nosa_dims* dims, const float* score_q, const 
                                            stream));
 }
 
+nosa_status nosa_append_score(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* k_new,
+                              const uint16_t* v_new, const float* e_new, const int32_t* seq_lens_in,
+                              int32_t* seq_lens_out, float* k_summary, float* e_summary, const uint16_t* q,
+                              float* score_q, float* score_e, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  const bool append = k_new != nullptr;
+  if ((st = check_kv(dims, kv, append)) != NOSA_OK) return st;
+  if (append) {
+    if (!v_new || !e_new || !seq_lens_out || !aligned16(k_new)) return NOSA_ERR_ARG;
+    if (seq_lens_out == seq_lens_in) return NOSA_ERR_ARG;
+  } else if (v_new || e_new) {
+    return NOSA_ERR_ARG;
+  }
+  if (!seq_lens_in || !k_summary || !e_summary || !q || !score_q || !score_e) return NOSA_ERR_ARG;
+  if (!aligned16(k_summary)) return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_append_score(*dims, *kv, k_new, v_new, e_new, seq_lens_in, seq_lens_out, k_summary,
+                                            e_summary, q, score_q, score_e, stream));
+}
+
 nosa_status nosa_swap_diff(const nosa_dims* dims, int32_t cap, const int32_t* prev, const int32_t* prev_count,
                            const int32_t* cur, const int32_t* cur_count, int32_t* load, int32_t* load_count,
                            int32_t* evict, int32_t* evict_count, hipStream_t stream) {

@@ -122,27 +122,9 @@ struct DecodeSmem {
   float ow[kDecWaves][G][D];
 };
 
-// Split partials cross workgroups in the fused decode + combine.  They are
-// written with device-scope (agent) atomic stores, which the memory system
-// makes visible across all XCDs' L2 caches before the store completes, and
-// read back with device-scope atomic loads, which never hit a stale L2
-// line.  Ordering then needs only the per-wave wait for stores to complete
-// before the arrival counter is bumped -- no write-back or invalidation of
-// whole L2 caches.
-// s_waitcnt immediate (gfx9 family encoding) that waits for every vector
-// memory operation of the wave, stores included, and leaves the other
-// counters unconstrained: vmcnt = 0, expcnt = 7, lgkmcnt = 15.
-constexpr int kWaitVmcnt0 = (0xF << 8) | (0x7 << 4);
-__device__ __forceinline__ void store_shared_f32(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <bool COHERENT>
-__device__ __forceinline__ float load_part(const float* p) {
-  if constexpr (COHERENT)
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    return *p;
-}
+// Split partials cross workgroups in the fused decode + combine: written
+// with store_coherent, read back with load_f32<true>, and ordered by the
+// wait-then-count arrival at the end of decode_kernel.
 
 // Merge of the P split partials of one output row at dim d [NOVITA, 2.
 // Attention modifications]: M = max of the non-empty splits' row maxima,
@@ -163,16 +145,16 @@ __device__ __forceinline__ void merge_splits(int P, int D, int64_t row, int d, c
 #pragma unroll
   for (int j = 0; j < PRE; ++j) {
     const int k = min(j, P - 1);
-    mv[j] = load_part<COHERENT>(pm + k);
-    lv[j] = load_part<COHERENT>(pl + k);
-    ov[j] = load_part<COHERENT>(po + (int64_t)k * D);
+    mv[j] = load_f32<COHERENT>(pm + k);
+    lv[j] = load_f32<COHERENT>(pl + k);
+    ov[j] = load_f32<COHERENT>(po + (int64_t)k * D);
   }
   float M = -INFINITY;
 #pragma unroll
   for (int j = 0; j < PRE; ++j)
     if (j < P && lv[j] > 0.f) M = fmaxf(M, mv[j]);
   for (int k = PRE; k < P; ++k) {
-    const float lk = load_part<COHERENT>(pl + k), mk = load_part<COHERENT>(pm + k);
+    const float lk = load_f32<COHERENT>(pl + k), mk = load_f32<COHERENT>(pm + k);
     if (lk > 0.f) M = fmaxf(M, mk);
   }
   float L = 0.f, O = 0.f;
@@ -185,12 +167,31 @@ __device__ __forceinline__ void merge_splits(int P, int D, int64_t row, int d, c
     }
   }
   for (int k = PRE; k < P; ++k) {
-    const float lk = load_part<COHERENT>(pl + k), mk = load_part<COHERENT>(pm + k);
+    const float lk = load_f32<COHERENT>(pl + k), mk = load_f32<COHERENT>(pm + k);
     if (lk > 0.f) {
       const float wk = lk * expf(mk - M);
       L += wk;
-      O += wk * load_part<COHERENT>(po + (int64_t)k * D);
+      O += wk * load_f32<COHERENT>(po + (int64_t)k * D);
     }
+  }
+  o[row * D + d] = L > 0.f ? O / L : 0.f;
+  if (d == 0) {
+    m[row] = L > 0.f ? M : -INFINITY;
+    l[row] = L;
+  }
+}
+
+// merge_splits for P == 1 with the split's values already in registers:
+// the same operations in the same order, so the result is bit-identical.
+__device__ __forceinline__ void merge_one(float pm, float pl, float po, int64_t row, int d, int D,
+                                          float* __restrict__ o, float* __restrict__ m, float* __restrict__ l) {
+  float M = -INFINITY;
+  if (pl > 0.f) M = fmaxf(M, pm);
+  float L = 0.f, O = 0.f;
+  if (pl > 0.f) {
+    const float w = pl * expf(pm - M);
+    L += w;
+    O += w * po;
   }
   o[row * D + d] = L > 0.f ? O / L : 0.f;
   if (d == 0) {
@@ -487,14 +488,19 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
       }
     }
     const int64_t row = ((int64_t)b * a.Hq + (int64_t)h * G + g) * a.P + p;
-    store_shared_f32(a.part_o + row * D + d, L > 0.f ? O / L : 0.f);
+    const float po = L > 0.f ? O / L : 0.f, pm = L > 0.f ? M * kLn2 : -INFINITY;
+    store_coherent(a.part_o + row * D + d, po);
     if (d == 0) {
-      store_shared_f32(a.part_m + row, L > 0.f ? M * kLn2 : -INFINITY);
-      store_shared_f32(a.part_l + row, L);
+      store_coherent(a.part_m + row, pm);
+      store_coherent(a.part_l + row, L);
+    }
+    if (a.counters != nullptr && a.P == 1) {  // fused combine of a single split, in registers
+      const int64_t orow = (int64_t)b * a.Hq + (int64_t)h * G + g;
+      merge_one(pm, L, po, orow, d, D, a.o, a.m, a.l);
     }
   }
 
-  if (a.counters == nullptr) return;
+  if (a.counters == nullptr || a.P == 1) return;
   // Fused combine: the last workgroup of this (b, h) to finish merges the P
   // partials.  Every wave waits for its device-scope partial stores to
   // complete, then one thread counts the workgroup's arrival; the last

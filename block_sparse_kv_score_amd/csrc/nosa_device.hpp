@@ -93,6 +93,31 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Data that other workgroups of the same launch read back.  Device-scope
+// (agent) atomic stores are made visible across every XCD's L2 before they
+// complete, and device-scope atomic loads never hit a stale L2 line, so a
+// producer needs only to wait for its stores to complete (s_waitcnt
+// vmcnt(0)) before it signals, and no L2 write-back or invalidate is
+// needed on either side.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Plain load, or a device-scope atomic load of data written by other
+// workgroups of the same launch with store_coherent.
+template <bool COHERENT>
+__device__ __forceinline__ float load_f32(const float* p) {
+  if constexpr (COHERENT)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+
+// s_waitcnt immediate (gfx9 family encoding) that waits for every vector
+// memory operation of the wave, stores included, and leaves the other
+// counters unconstrained: vmcnt = 0, expcnt = 7, lgkmcnt = 15.
+constexpr int kWaitVmcnt0 = (0xF << 8) | (0x7 << 4);
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll

@@ -1,0 +1,303 @@
+// Append and block scoring in one launch (nosa_append_score).
+//
+// The two stages are those of nosa_append and nosa_score_blocks, with the
+// same arithmetic, so the results are bit-identical to the two separate
+// calls:
+//   * append [NOSA summary (gist.science 2510.13602), Methodology 2: NOSI
+//     fuses pooling into the index-side kernel]: the new token goes into its
+//     page and the summary of its sub-block is recomputed (float64 sums in
+//     ascending token order, one rounding to fp32);
+//   * scoring [Methodology 1, block-wise implementation]: sub-block mean
+//     summaries dotted with the group's mean query, max over each block,
+//     and the eviction logits pooled the same way.
+//
+// Layout of the launch.  Grid (chunks of SPG sub-blocks, B * Hkv), 256
+// threads, as the score kernel, with the chunks of a pair taken last to
+// first: the chunk holding the new token is the last non-empty one, so its
+// "lead" workgroup is the first of the pair to be dispatched and the
+// append's dependent loads (position, page, older tokens) overlap the
+// streaming of the pair's other chunks.  (Starting every pair's append at
+// once, at the head of the launch, measured slower: the appends then
+// compete with each other.)  The lead workgroup scores its own chunk with
+// the new summary from LDS; no other workgroup reads what the append
+// writes.
+//
+// The new length is written to a second buffer (seq_lens_out), never to
+// the one every workgroup reads (seq_lens_in), so no reader can see it
+// early.
+
+#include "nosa_launch.hpp"
+#include "nosa_summary.hpp"
+
+namespace nosa {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kFusedThreads = 256;
+constexpr int kStageTok = 32;  // older tokens staged through LDS per pass
+
+struct FusedArgs {
+  Table t;
+  int Hq, bs, ss;
+  // append (k_new == nullptr: no append)
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const float* e_new;
+  uint16_t* k_pages;
+  uint16_t* v_pages;
+  float* e_pages;
+  const int32_t* seq_in;
+  int32_t* seq_out;
+  float* k_summary;
+  float* e_summary;
+  // scoring
+  const uint16_t* q;
+  float* score_q;
+  float* score_e;
+};
+
+template <int D>
+struct FusedSmem {
+  double qbar[D];
+  f4 knew[D / 4];  // the new token's sub-block summary (append workgroup)
+  uint4 kold[kStageTok][D / 8];  // staged older keys of that sub-block
+  float eold[kStageTok];
+  float enew;
+  int have_new;
+};
+
+// The append of pair bh, by the whole append workgroup (uniform call):
+// token position pos (in range).  The older tokens of the new token's
+// sub-block are staged through LDS kStageTok at a time by all threads (one
+// memory round trip per pass instead of one per batch of a single lane);
+// wave 0 then sums them in ascending token order exactly as sum_key_quad /
+// sum_logits do, adds the new token, and writes the summary (global memory
+// and sh.knew / sh.enew) and the token itself.  Mirrors append_kernel.
+template <int D>
+__device__ void append_token(const FusedArgs& a, FusedSmem<D>& sh, int bh, int pos) {
+  constexpr int NQ = D / 4;
+  constexpr int NO = D / 8;  // 16-byte octets per key row
+  constexpr int VL = D / kWave;
+  constexpr int IPT = (NO * kStageTok + kFusedThreads - 1) / kFusedThreads;  // staged items per thread
+  const Table& t = a.t;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int bs = a.bs, ss = a.ss, nsub = bs / ss, CS = t.max_blocks * nsub;
+  const int i = pos / bs, r = pos % bs;
+  const int j = r / ss;
+  const int lo = j * ss;  // page-relative start of the sub-block
+  uint32_t doc;
+  const int64_t page = page_of_any(t, bh, i, doc);  // same address in every lane
+  if (page < 0) {
+    if (threadIdx.x == 0) flag_error(t.err);
+    return;
+  }
+  uint16_t* kpage = a.k_pages + page * (int64_t)bs * D;
+  uint16_t* vpage = a.v_pages + page * (int64_t)bs * D;
+  float* epage = a.e_pages + page * bs;
+  double a0 = 0, a1 = 0, a2 = 0, a3 = 0, ae = 0;
+  for (int t0 = lo; t0 < r; t0 += kStageTok) {  // uniform trip count
+    const int n = min(kStageTok, r - t0);
+    uint4 kv[IPT];
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int it = min((int)threadIdx.x + u * kFusedThreads, NO * n - 1);  // clamped: no branch
+      const int o = it / n, tt = it % n;
+      kv[u] = reinterpret_cast<const uint4*>(kpage)[o * bs + t0 + tt];
+    }
+    const float ev = epage[t0 + min((int)threadIdx.x, n - 1)];
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int it = (int)threadIdx.x + u * kFusedThreads;
+      if (it < NO * n) sh.kold[it % n][it / n] = kv[u];
+    }
+    if ((int)threadIdx.x < n) sh.eold[threadIdx.x] = ev;
+    __syncthreads();
+    if (w == 0) {
+      if (lane < NQ) {
+        for (int tt = 0; tt < n; ++tt) {
+          const uint4 o8 = sh.kold[tt][lane >> 1];
+          const uint32_t x = (lane & 1) ? o8.z : o8.x, y = (lane & 1) ? o8.w : o8.y;
+          a0 += (double)bf16_lo(x);
+          a1 += (double)bf16_hi(x);
+          a2 += (double)bf16_lo(y);
+          a3 += (double)bf16_hi(y);
+        }
+      } else if (lane == NQ) {
+        for (int tt = 0; tt < n; ++tt) ae += (double)sh.eold[tt];
+      }
+    }
+    __syncthreads();  // the staging buffers are reused by the next pass
+  }
+  if (w != 0) return;
+  const uint16_t* kn = a.k_new + (int64_t)bh * D;
+  const uint16_t* vn = a.v_new + (int64_t)bh * D;
+  const double inv_n = 1.0 / (double)(r - lo + 1);
+  const int s = i * nsub + j;
+  if (lane < NQ) {
+    const uint2 k_quad = reinterpret_cast<const uint2*>(kn)[lane];
+    a0 += (double)bf16_lo(k_quad.x);
+    a1 += (double)bf16_hi(k_quad.x);
+    a2 += (double)bf16_lo(k_quad.y);
+    a3 += (double)bf16_hi(k_quad.y);
+    f4 o;
+    o.x = (float)(a0 * inv_n);
+    o.y = (float)(a1 * inv_n);
+    o.z = (float)(a2 * inv_n);
+    o.w = (float)(a3 * inv_n);
+    reinterpret_cast<f4*>(a.k_summary)[((int64_t)bh * NQ + lane) * CS + s] = o;
+    sh.knew[lane] = o;
+  } else if (lane == NQ) {
+    ae += (double)a.e_new[bh];
+    const float em = (float)(ae * inv_n);
+    a.e_summary[(int64_t)bh * CS + s] = em;
+    sh.enew = em;
+    sh.have_new = 1;
+  }
+  // the new token itself (the older ones were read above)
+  if (lane < NO) reinterpret_cast<uint4*>(kpage)[lane * bs + r] = reinterpret_cast<const uint4*>(kn)[lane];
+#pragma unroll
+  for (int jj = 0; jj < VL; ++jj) vpage[((r / 8) * D + lane + jj * kWave) * 8 + r % 8] = vn[lane + jj * kWave];
+  if (lane == 0) epage[r] = a.e_new[bh];
+}
+
+// L lanes per sub-block (see score_kernel).
+template <int D, int L>
+__global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const FusedArgs a) {
+  constexpr int NQ = D / 4;
+  constexpr int QL = NQ / L;
+  constexpr int SPW = kWave / L;
+  constexpr int SPG = SPW * (kFusedThreads / kWave);
+  __shared__ FusedSmem<D> sh;
+  const Table& t = a.t;
+  const int bh = blockIdx.y;
+  const int Hkv = t.Hkv;
+  const int b = bh / Hkv, h = bh % Hkv;
+  const int G = a.Hq / Hkv;
+  const int bs = a.bs, ss = a.ss, nsub = bs / ss;
+  const int MB = t.max_blocks, CS = MB * nsub, cap = MB * bs;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+
+  const int raw = a.seq_in[b];
+  const bool want_append = a.k_new != nullptr;
+  const bool append = want_append && raw >= 0 && raw < cap;
+  const int T = min(max(append ? raw + 1 : raw, 0), cap);
+  const int nb = (T + bs - 1) / bs;
+  // chunks last to first; sT: the new token's sub-block
+  const int sT = append ? (raw / bs) * nsub + (raw % bs) / ss : -1;
+  const int c = (int)gridDim.x - 1 - (int)blockIdx.x;
+  const int s0 = c * SPG;
+  const bool work = s0 < nb * nsub;
+  const bool lead = append && s0 <= sT && sT < s0 + SPG;
+  if (threadIdx.x == 0) {
+    sh.have_new = 0;
+    if (blockIdx.x == 0 && h == 0 && want_append) {
+      if (!append) flag_error(t.err);
+      a.seq_out[b] = append ? raw + 1 : raw;
+    }
+  }
+
+  __syncthreads();  // have_new cleared before the append sets it
+  if (lead) append_token<D>(a, sh, bh, raw);
+
+  // the group's query (clamped, branch-free loads)
+  const int dq = threadIdx.x < D ? threadIdx.x : 0;
+  const uint16_t* qh = a.q + ((int64_t)b * a.Hq + (int64_t)h * G) * D + dq;
+  uint16_t qraw[16];
+#pragma unroll
+  for (int g = 0; g < 16; ++g) qraw[g] = qh[(int64_t)min(g, G - 1) * D];
+
+  // this lane's slice of its sub-block's summary row
+  const int s = s0 + w * SPW + lane % SPW;
+  const int part = lane / SPW;
+  f4 v[QL];
+  float ev = 0.f;
+  if (work) {
+    const f4* p = reinterpret_cast<const f4*>(a.k_summary) + (int64_t)bh * NQ * CS + min(s, CS - 1) +
+                  (int64_t)(part * QL) * CS;
+#pragma unroll
+    for (int u = 0; u < QL; ++u) v[u] = __builtin_nontemporal_load(p + (int64_t)u * CS);
+    ev = a.e_summary[(int64_t)bh * CS + min(s, CS - 1)];
+  }
+  if (threadIdx.x < D) {
+    double acc = 0;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) acc += g < G ? (double)bf16_to_f32(qraw[g]) : 0.0;
+    sh.qbar[threadIdx.x] = acc / (double)G;
+  }
+  __syncthreads();  // qbar, and the append's summary
+
+  if (work) {
+    if (lead && s == sT && sh.have_new) {  // this step's summary of the new token's sub-block
+#pragma unroll
+      for (int u = 0; u < QL; ++u) v[u] = sh.knew[part * QL + u];
+      ev = sh.enew;
+    }
+    const int i = s / nsub, j = s % nsub;
+    const bool valid = i < nb && i * bs + j * ss < T;
+    double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+#pragma unroll
+    for (int u = 0; u < QL; ++u) {
+      const int d = 4 * (part * QL + u);
+      a0 = fma((double)v[u].x, sh.qbar[d + 0], a0);
+      a1 = fma((double)v[u].y, sh.qbar[d + 1], a1);
+      a2 = fma((double)v[u].z, sh.qbar[d + 2], a2);
+      a3 = fma((double)v[u].w, sh.qbar[d + 3], a3);
+    }
+    double dot = (a0 + a1) + (a2 + a3);
+#pragma unroll
+    for (int off = SPW; off < kWave; off <<= 1) dot += __shfl_xor(dot, off, kWave);
+    if (!valid) dot = -INFINITY;
+    float ek = valid ? ev : -INFINITY;
+    for (int off = 1; off < nsub; off <<= 1) {
+      dot = fmax(dot, __shfl_xor(dot, off, kWave));
+      ek = fmaxf(ek, __shfl_xor(ek, off, kWave));
+    }
+    if (valid && part == 0 && j == 0) {
+      a.score_q[(int64_t)bh * MB + i] = (float)(dot / sqrt((double)D));
+      a.score_e[(int64_t)bh * MB + i] = ek;
+    }
+  }
+}
+
+hipError_t launch_append_score(const nosa_dims& d, const nosa_kv& kv, const uint16_t* k_new,
+                               const uint16_t* v_new, const float* e_new, const int32_t* seq_lens_in,
+                               int32_t* seq_lens_out, float* k_summary, float* e_summary, const uint16_t* q,
+                               float* score_q, float* score_e, hipStream_t stream) {
+  FusedArgs a;
+  a.t = make_table(d, kv);
+  a.Hq = d.n_q_heads;
+  a.bs = d.block_size;
+  a.ss = d.sub_block;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.e_new = e_new;
+  a.k_pages = kv.k_pages;
+  a.v_pages = kv.v_pages;
+  a.e_pages = kv.e_pages;
+  a.seq_in = seq_lens_in;
+  a.seq_out = seq_lens_out;
+  a.k_summary = k_summary;
+  a.e_summary = e_summary;
+  a.q = q;
+  a.score_q = score_q;
+  a.score_e = score_e;
+  const int nsub = d.block_size / d.sub_block;
+  const int CS = d.max_blocks * nsub;
+  const int L = nsub <= 16 ? 4 : (nsub <= 32 ? 2 : 1);  // as score_kernel
+  const int spg = (kWave / L) * (kFusedThreads / kWave);
+  const dim3 grid((CS + spg - 1) / spg, d.batch * d.n_kv_heads);
+#define NOSA_APPEND_SCORE(DD, LL) append_score_kernel<DD, LL><<<grid, kFusedThreads, 0, stream>>>(a)
+  if (d.head_dim == 128) {
+    if (L == 4) NOSA_APPEND_SCORE(128, 4);
+    else if (L == 2) NOSA_APPEND_SCORE(128, 2);
+    else NOSA_APPEND_SCORE(128, 1);
+  } else {
+    if (L == 4) NOSA_APPEND_SCORE(64, 4);
+    else if (L == 2) NOSA_APPEND_SCORE(64, 2);
+    else NOSA_APPEND_SCORE(64, 1);
+  }
+#undef NOSA_APPEND_SCORE
+  return hipGetLastError();
+}
+
+}  // namespace nosa

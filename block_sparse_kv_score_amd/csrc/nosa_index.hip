@@ -14,6 +14,7 @@
 // nosa_append produce bit-identical entries for the same tokens.
 
 #include "nosa_launch.hpp"
+#include "nosa_summary.hpp"
 
 namespace nosa {
 
@@ -90,46 +91,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(Table t, int bs, const uin
     vp[to * D + d] = make_uint4(w[0], w[1], w[2], w[3]);
   }
   for (int tok = threadIdx.x; tok < ntok; tok += blockDim.x) e_pages[page * bs + tok] = es[tok];
-}
-
-// ---------------------------------------------------------------------------
-// Sums over a sub-block's present tokens [lo, hi) (page-relative), float64,
-// ascending token order.  Loads go out in batches of 16 (padding slots add
-// +0.0, which leaves a float64 sum unchanged), so build_summaries and append
-// produce identical sums for identical tokens.
-// ---------------------------------------------------------------------------
-constexpr int kSumBatch = 16;
-
-template <int D>
-__device__ __forceinline__ void sum_key_quad(const uint16_t* kpage, int bs, int u, int lo, int hi,
-                                             double& a0, double& a1, double& a2, double& a3) {
-  // quad u = dims 4u..4u+3 = half (u & 1) of octet u >> 1
-  const uint2* base = reinterpret_cast<const uint2*>(kpage) + ((u >> 1) * bs) * 2 + (u & 1);
-  for (int t0 = lo; t0 < hi; t0 += kSumBatch) {
-    uint2 v[kSumBatch];
-#pragma unroll
-    for (int j = 0; j < kSumBatch; ++j) v[j] = base[min(t0 + j, hi - 1) * 2];  // clamped: no branch
-#pragma unroll
-    for (int j = 0; j < kSumBatch; ++j) {
-      const bool in = t0 + j < hi;
-      a0 += in ? (double)bf16_lo(v[j].x) : 0.0;
-      a1 += in ? (double)bf16_hi(v[j].x) : 0.0;
-      a2 += in ? (double)bf16_lo(v[j].y) : 0.0;
-      a3 += in ? (double)bf16_hi(v[j].y) : 0.0;
-    }
-  }
-}
-
-__device__ __forceinline__ double sum_logits(const float* ep, int lo, int hi) {
-  double a = 0;
-  for (int t0 = lo; t0 < hi; t0 += kSumBatch) {
-    float v[kSumBatch];
-#pragma unroll
-    for (int j = 0; j < kSumBatch; ++j) v[j] = ep[min(t0 + j, hi - 1)];
-#pragma unroll
-    for (int j = 0; j < kSumBatch; ++j) a += t0 + j < hi ? (double)v[j] : 0.0;
-  }
-  return a;
 }
 
 // build_summaries: one thread per (sub-block, d-quad); threads with u == 0

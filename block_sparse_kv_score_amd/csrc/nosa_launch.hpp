@@ -38,6 +38,11 @@ hipError_t launch_select_swap(const nosa_dims& d, const float* score_q, const fl
                               const int32_t* prev_count, int32_t* load, int32_t* load_count, int32_t* evict,
                               int32_t* evict_count, hipStream_t stream);
 
+hipError_t launch_append_score(const nosa_dims& d, const nosa_kv& kv, const uint16_t* k_new,
+                               const uint16_t* v_new, const float* e_new, const int32_t* seq_lens_in,
+                               int32_t* seq_lens_out, float* k_summary, float* e_summary, const uint16_t* q,
+                               float* score_q, float* score_e, hipStream_t stream);
+
 hipError_t launch_swap_diff(const nosa_dims& d, int32_t cap, const int32_t* prev,
                             const int32_t* prev_count, const int32_t* cur, const int32_t* cur_count,
                             int32_t* load, int32_t* load_count, int32_t* evict,

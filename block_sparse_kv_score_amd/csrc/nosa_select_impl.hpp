@@ -1,0 +1,360 @@
+// Dual selection and the swap lists for one (b, h) pair, as a workgroup
+// device function, shared by the selection kernels and the fused
+// score + select kernel.
+//
+// NOSA summary (gist.science 2510.13602), Methodology 1: selection is split
+// into a query-aware part (recall, possibly far-away blocks) and a
+// query-agnostic eviction part that follows a strict policy -- whatever it
+// leaves out once it never takes back; with a fixed budget k_e for that part
+// most blocks chosen at step t were chosen at t-1 (locality at least
+// k_e / k).  Methodology 2 (NOSI): set differences between consecutive block
+// sets drive block swapping.
+//
+// Readings: the two parts are disjoint (the query part picks among blocks
+// the eviction part did not take), the never-return rule binds the eviction
+// part only, ties go to the lower block index, and a newly created block
+// starts as an eviction candidate.
+//
+// One workgroup of 256 threads per (b, h); each thread keeps its blocks'
+// keys in registers (block i = r * 256 + thread).  Top-k is a
+// most-significant-digit radix select over order-preserving 32-bit keys of
+// the fp32 scores (see radix_top_k); exact key ties go to the lowest index.
+// Outputs are compacted in index order with wave ballots, so they come out
+// ascending without a sort, and the eviction bitmap words are rebuilt from
+// ballots.
+#pragma once
+
+#include "nosa_device.hpp"
+
+namespace nosa {
+
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kMaxBlocks = 8192;
+
+// Per-workgroup scratch in LDS; small slots are double-buffered by phase so
+// one barrier per exchange suffices.
+struct SelShared {
+  uint32_t hist[kSelWaves][256];  // per-wave digit histograms
+  int32_t tot[2][kSelWaves];
+  int32_t bc[2][4];
+  uint32_t mm[2][kSelWaves][2];
+  int32_t pos[32][kSelWaves];
+  // fused swap lists: membership bitmaps and per-wave counts
+  uint32_t pick_bm[kMaxBlocks / 32];
+  uint32_t prev_bm[kMaxBlocks / 32];
+  int32_t pos_load[32][kSelWaves];
+  int32_t pos_evict[32][kSelWaves];
+};
+
+// Workgroup sum of one int per wave (lane 0's value); one barrier.
+__device__ __forceinline__ int block_sum(int v, int& phase, SelShared& sh) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int ph = phase++ & 1;
+  if (lane == 0) sh.tot[ph][w] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int k = 0; k < kSelWaves; ++k) t += sh.tot[ph][k];
+  return t;
+}
+
+// Element r of this thread is block i = r * kSelThreads + threadIdx.x; the
+// thread's R elements live in registers (keys) and bit masks (bit r).
+// Marks in `out` the k best of the elements in `cand` under (key desc,
+// index asc).  Requires 0 < k < number of candidates.
+//
+// Radix select over 8-bit digits.  The first digit starts at the highest
+// bit where the candidates' smallest and largest keys differ (the bits above
+// are common to all of them), so no pass is spent on a shared exponent.
+// Digits are counted in per-wave LDS histograms; a workgroup scan over the
+// 256 bins finds the bin holding the k-th key; the select stops as soon as
+// that bin is taken whole.
+template <int R>
+__device__ void radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k, uint32_t& out, int& phase,
+                            SelShared& sh) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  // range of the candidate keys
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if ((cand >> r) & 1u) {
+      kmin = min(kmin, key[r]);
+      kmax = max(kmax, key[r]);
+    }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
+  }
+  {
+    const int ph = phase++ & 1;
+    if (lane == 0) {
+      sh.mm[ph][w][0] = kmin;
+      sh.mm[ph][w][1] = kmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ww = 0; ww < kSelWaves; ++ww) {
+      kmin = min(kmin, sh.mm[ph][ww][0]);
+      kmax = max(kmax, sh.mm[ph][ww][1]);
+    }
+  }
+  int hi = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);  // bits [hi, 32) are shared
+  uint32_t prefix = hi >= 32 ? 0u : kmin & ~((1u << hi) - 1u);
+  uint32_t pmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
+  int rem = k, n_eq = 0;
+  bool done = false;
+  while (hi > 0 && !done) {
+    const int lo = hi > 8 ? hi - 8 : 0;
+    const uint32_t dmask = (1u << (hi - lo)) - 1u;
+    // per-wave histogram of this digit among the keys matching the prefix
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sh.hist[w][lane + 64 * j] = 0u;
+    wave_lds_sync();
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (((cand >> r) & 1u) && (key[r] & pmask) == prefix) atomicAdd(&sh.hist[w][(key[r] >> lo) & dmask], 1u);
+    __syncthreads();
+    // thread t owns digit 255 - t: inclusive scan gives the count of keys
+    // with a digit >= 255 - t
+    const int dg = 255 - (int)threadIdx.x;
+    int c = 0;
+#pragma unroll
+    for (int ww = 0; ww < kSelWaves; ++ww) c += (int)sh.hist[ww][dg];
+    int cum = c;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int t = __shfl_up(cum, off, kWave);
+      if (lane >= off) cum += t;
+    }
+    const int ph = phase++ & 1;
+    if (lane == kWave - 1) sh.tot[ph][w] = cum;
+    __syncthreads();
+#pragma unroll
+    for (int ww = 0; ww < kSelWaves; ++ww) cum += ww < w ? sh.tot[ph][ww] : 0;
+    if (c > 0 && cum >= rem && cum - c < rem) {
+      sh.bc[ph][0] = dg;
+      sh.bc[ph][1] = cum - c;
+      sh.bc[ph][2] = c;
+    }
+    __syncthreads();
+    const uint32_t digit = (uint32_t)sh.bc[ph][0];
+    rem -= sh.bc[ph][1];
+    n_eq = sh.bc[ph][2];
+    prefix |= digit << lo;
+    pmask |= dmask << lo;
+    hi = lo;
+    done = rem == n_eq;  // the whole bin is taken: prefix is the threshold
+  }
+  if (rem == n_eq) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (((cand >> r) & 1u) && (key[r] & pmask) >= prefix) out |= 1u << r;
+    return;
+  }
+  // exact key ties at the threshold: the rem lowest block indices win
+  uint64_t eqm[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) eqm[r] = __ballot(((cand >> r) & 1u) && key[r] == prefix);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) sh.pos[r][w] = __popcll(eqm[r]);
+  }
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int rank = before + lanes_below(eqm[r]);
+#pragma unroll
+    for (int ww = 0; ww < kSelWaves; ++ww) {
+      const int c = sh.pos[r][ww];
+      rank += ww < w ? c : 0;
+      before += c;
+    }
+    if ((cand >> r) & 1u) {
+      if (key[r] > prefix || (key[r] == prefix && rank < rem)) out |= 1u << r;
+    }
+  }
+  __syncthreads();  // sh.pos is reused by the caller
+}
+
+struct SwapArgs {
+  const int32_t* prev;
+  const int32_t* prev_count;
+  int32_t* load;
+  int32_t* load_count;
+  int32_t* evict;
+  int32_t* evict_count;
+};
+
+// Selection of pair bh over its first T tokens (nb = ceil(T / bs) blocks),
+// called by all kSelThreads threads of a workgroup.  R elements per thread
+// cover max_blocks.  SWAP: also form the load / evict lists against the
+// previous selection.  COHERENT: the scores come from other workgroups of
+// the same launch.
+template <int R, bool SWAP, bool COHERENT>
+__device__ void select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks,
+                            const float* __restrict__ score_q, const float* __restrict__ score_e, int k_e,
+                            int k_q, uint32_t* __restrict__ evicted, int32_t* __restrict__ sel, int sel_cap,
+                            int32_t* __restrict__ sel_count, const SwapArgs& sw) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int nb = (T + bs - 1) / bs;
+  const int words = (max_blocks + 31) / 32;
+  uint32_t* ev = evicted + (int64_t)bh * words;
+  const float* se = score_e + (int64_t)bh * max_blocks;
+  const float* sq = score_q + (int64_t)bh * max_blocks;
+
+  // every load up front, over the whole capacity so they need not wait for
+  // seq_lens; blocks >= nb are masked out afterwards
+  uint32_t ke[R], kq[R], ew[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = r * kSelThreads + threadIdx.x;
+    ke[r] = kq[r] = ew[r] = 0u;
+    if (i < max_blocks) {
+      ke[r] = order_key(load_f32<COHERENT>(se + i));
+      kq[r] = order_key(load_f32<COHERENT>(sq + i));
+      ew[r] = ev[i >> 5];
+    }
+  }
+  // fused swap lists: the previous selection (capacity sel_cap <= max_blocks,
+  // so R entries per thread cover it), loaded with everything else
+  int32_t pv[R];
+  int n_prev = 0;
+  if constexpr (SWAP) {
+    const int32_t* pl = sw.prev + (int64_t)bh * sel_cap;
+#pragma unroll
+    for (int r = 0; r < R; ++r) pv[r] = pl[min(r * kSelThreads + (int)threadIdx.x, sel_cap - 1)];
+    n_prev = min(max(sw.prev_count[bh], 0), sel_cap);
+  }
+  uint32_t valid = 0, evm = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = r * kSelThreads + threadIdx.x;
+    if (i < nb) {
+      valid |= 1u << r;
+      evm |= ((ew[r] >> (i & 31)) & 1u) << r;
+    }
+  }
+  int phase = 0;
+
+  // --- eviction part: candidates are the never-evicted blocks ------------
+  const uint32_t cand_e = valid & ~evm;
+  int wave_cand = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) wave_cand += __popcll(__ballot((cand_e >> r) & 1u));
+  const int n_cand = block_sum(wave_cand, phase, sh);
+  const int n_e = min(k_e, n_cand);
+  uint32_t in_e = 0;
+  if (n_e == n_cand) in_e = cand_e;
+  else if (n_e > 0) radix_top_k<R>(ke, cand_e, n_e, in_e, phase, sh);
+  evm |= cand_e & ~in_e;  // every candidate left out is evicted for good
+
+  // --- query part: best of the blocks the eviction part did not take ----
+  const uint32_t cand_q = valid & ~in_e;
+  const int rest = nb - n_e;
+  const int n_q = min(k_q, rest);
+  uint32_t in_q = 0;
+  if (n_q == rest) in_q = cand_q;
+  else if (n_q > 0) radix_top_k<R>(kq, cand_q, n_q, in_q, phase, sh);
+
+  // --- outputs: ascending union via ballots, eviction bitmap words ------
+  const uint32_t pick = in_e | in_q;
+  uint64_t pm[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    pm[r] = __ballot((pick >> r) & 1u);
+    const uint64_t em = __ballot((evm >> r) & 1u);
+    const uint64_t vm = __ballot((valid >> r) & 1u);
+    // lanes 0 and 32 own the two 32-bit words this wave covers at element r
+    const int i0 = r * kSelThreads + w * kWave + (lane & 32);
+    if ((lane & 31) == 0 && i0 < nb) {  // this lane loaded that word at the start
+      const uint32_t e32 = (uint32_t)(em >> (lane & 32));
+      const uint32_t v32 = (uint32_t)(vm >> (lane & 32));
+      ev[i0 >> 5] = (ew[r] & ~v32) | e32;
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) sh.pos[r][w] = __popcll(pm[r]);
+  }
+  __syncthreads();
+  int32_t* out = sel + (int64_t)bh * sel_cap;
+  int before = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int pos = before + lanes_below(pm[r]);
+#pragma unroll
+    for (int ww = 0; ww < kSelWaves; ++ww) {
+      const int c = sh.pos[r][ww];
+      pos += ww < w ? c : 0;
+      before += c;
+    }
+    if (((pick >> r) & 1u) && pos < sel_cap) out[pos] = r * kSelThreads + threadIdx.x;
+  }
+  if (threadIdx.x == 0) sel_count[bh] = min(before, sel_cap);
+
+  if constexpr (SWAP) {
+    // load = selected now and not before (index order); evict = before and
+    // not now (order of the previous list) -- the set differences of
+    // nosa_swap_diff, from the selection still in registers
+    for (int wd = threadIdx.x; wd < (max_blocks + 31) / 32; wd += kSelThreads) sh.prev_bm[wd] = 0u;
+    if ((lane & 31) == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int i0 = r * kSelThreads + w * kWave + (lane & 32);
+        if (i0 < max_blocks) sh.pick_bm[i0 >> 5] = (uint32_t)(pm[r] >> (lane & 32));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int k = r * kSelThreads + threadIdx.x;
+      if (k < n_prev && pv[r] >= 0 && pv[r] < max_blocks) atomicOr(&sh.prev_bm[pv[r] >> 5], 1u << (pv[r] & 31));
+    }
+    __syncthreads();
+    uint64_t lm[R], em[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = r * kSelThreads + threadIdx.x;
+      const bool in_prev = i < max_blocks && ((sh.prev_bm[min(i, max_blocks - 1) >> 5] >> (i & 31)) & 1u);
+      lm[r] = __ballot(((pick >> r) & 1u) && !in_prev);
+      const int k = r * kSelThreads + threadIdx.x;
+      const int x = pv[r];
+      const bool live = k < n_prev && x >= 0 && x < max_blocks;
+      em[r] = __ballot(live && !((sh.pick_bm[live ? x >> 5 : 0] >> (x & 31)) & 1u));
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        sh.pos_load[r][w] = __popcll(lm[r]);
+        sh.pos_evict[r][w] = __popcll(em[r]);
+      }
+    }
+    __syncthreads();
+    int32_t* lo = sw.load + (int64_t)bh * sel_cap;
+    int32_t* eo = sw.evict + (int64_t)bh * sel_cap;
+    int bl = 0, be = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int pl_ = bl + lanes_below(lm[r]), pe = be + lanes_below(em[r]);
+#pragma unroll
+      for (int ww = 0; ww < kSelWaves; ++ww) {
+        const int cl = sh.pos_load[r][ww], ce = sh.pos_evict[r][ww];
+        pl_ += ww < w ? cl : 0;
+        pe += ww < w ? ce : 0;
+        bl += cl;
+        be += ce;
+      }
+      if (((lm[r] >> lane) & 1u) && pl_ < sel_cap) lo[pl_] = r * kSelThreads + threadIdx.x;
+      if (((em[r] >> lane) & 1u) && pe < sel_cap) eo[pe] = pv[r];
+    }
+    if (threadIdx.x == 0) {
+      sw.load_count[bh] = min(bl, sel_cap);
+      sw.evict_count[bh] = min(be, sel_cap);
+    }
+  }
+}
+
+}  // namespace nosa

@@ -32,6 +32,7 @@ ENTRY_POINTS = [
     "nosa_score_blocks",
     "nosa_select",
     "nosa_select_swap",
+    "nosa_append_score",
     "nosa_swap_diff",
     "nosa_sparse_decode",
     "nosa_sparse_decode_combine",
@@ -93,6 +94,7 @@ _SIGNATURES = {
     "nosa_score_blocks": [_DIMS, _P, _P, _P, _P, _P, _P, _P],
     "nosa_select": [_DIMS, _P, _P, _P, _I32, _I32, _P, _P, _I32, _P, _P],
     "nosa_select_swap": [_DIMS, _P, _P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P],
+    "nosa_append_score": [_DIMS, _KV, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "nosa_swap_diff": [_DIMS, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "nosa_sparse_decode": [_DIMS, _P, _KV, _P, _P, _I32, _P, _I32, _F32, _P, _P, _P, _P],
     "nosa_sparse_decode_combine": [_DIMS, _P, _KV, _P, _P, _I32, _P, _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P],
@@ -238,6 +240,20 @@ def nosa_select_swap(dims, score_q, score_e, seq_lens, k_e, k_q, evicted, sel, s
           _dev(load, "load", (torch.int32,)), _dev(load_count, "load_count", (torch.int32,)),
           _dev(evict, "evict", (torch.int32,)), _dev(evict_count, "evict_count", (torch.int32,)),
           _stream(stream))
+
+
+def nosa_append_score(dims, kv, k_new, v_new, e_new, seq_lens_in, seq_lens_out, k_summary, e_summary, q,
+                      score_q, score_e, stream=None):
+    """k_new / v_new / e_new / seq_lens_out may all be None (no append)."""
+    opt = k_new is None
+    _call("nosa_append_score", ctypes.byref(dims), ctypes.byref(kv),
+          _dev(k_new, "k_new", _BF16_LIKE, optional=opt), _dev(v_new, "v_new", _BF16_LIKE, optional=opt),
+          _dev(e_new, "e_new", (torch.float32,), optional=opt),
+          _dev(seq_lens_in, "seq_lens_in", (torch.int32,)),
+          _dev(seq_lens_out, "seq_lens_out", (torch.int32,), optional=opt),
+          _dev(k_summary, "k_summary", (torch.float32,)), _dev(e_summary, "e_summary", (torch.float32,)),
+          _dev(q, "q", _BF16_LIKE), _dev(score_q, "score_q", (torch.float32,)),
+          _dev(score_e, "score_e", (torch.float32,)), _stream(stream))
 
 
 def nosa_swap_diff(dims, prev, prev_count, cur, cur_count, load, load_count, evict, evict_count,

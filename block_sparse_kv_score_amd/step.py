@@ -10,9 +10,13 @@ Call sequence of decode step t (1-based):
   nosa_swap_diff         against the previous step's selection
   nosa_sparse_decode     split-K over the selected pages
   nosa_combine           -> O, rowmax m, l
-With `fused` (the default) select + swap_diff run as nosa_select_swap and
-decode + combine as nosa_sparse_decode_combine: the same results in four
-launches instead of six.
+With `fused` (the default) the step is three launches with the same results:
+  nosa_append_score          append + score
+  nosa_select_swap           select + swap_diff
+  nosa_sparse_decode_combine decode + combine
+(with every block selected: nosa_swap_diff, then the fused decode).  The
+fused index launch writes the new lengths to the other of two seq_lens
+buffers, so `seq_lens` names the current one.
 """
 
 from __future__ import annotations
@@ -72,7 +76,8 @@ class DecodeSession:
                                seg_log2=w.seg_log2, blocks_log2=w.blocks_log2, packed=self.packed,
                                q_pos=self.q_pos, rope_base=w.rope_base, err_flags=self.err)
 
-        self.seq_lens = torch.full((B,), w.T0, dtype=torch.int32, device=dev)
+        self.seq_bufs = [torch.full((B,), w.T0, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.seq_lens = self.seq_bufs[0]
         self.k_summary = torch.full((B, Hkv, D // 4, CS, 4), fill, dtype=torch.float32, device=dev)
         self.e_summary = torch.full((B, Hkv, CS), fill, dtype=torch.float32, device=dev)
         self.score_q = torch.full((B, Hkv, MB), fill, dtype=torch.float32, device=dev)
@@ -152,6 +157,19 @@ class DecodeSession:
         nosa.nosa_sparse_decode(self.dims, self.q(t), self.kv, self.sel, self.sel_count, self.seq_lens,
                                 self.P, self.w.sm_scale, self.part_o, self.part_m, self.part_l, self.stream)
 
+    def append_score(self, t: int):
+        """Fused append + score; afterwards seq_lens is the other buffer."""
+        w = self.w
+        out = self.seq_bufs[1] if self.seq_lens is self.seq_bufs[0] else self.seq_bufs[0]
+        if w.append:
+            k_new, v_new, e_new, seq_out = self.k_new[t - 1], self.v_new[t - 1], self.e_new[t - 1], out
+        else:
+            k_new = v_new = e_new = seq_out = None
+        nosa.nosa_append_score(self.dims, self.kv, k_new, v_new, e_new, self.seq_lens, seq_out, self.k_summary,
+                               self.e_summary, self.q(t), self.score_q, self.score_e, self.stream)
+        if w.append:
+            self.seq_lens = out
+
     def select_swap(self):
         nosa.nosa_select_swap(self.dims, self.score_q, self.score_e, self.seq_lens, self.w.k_e, self.w.k_q,
                               self.evicted, self.sel, self.sel_count, self.prev, self.prev_count,
@@ -183,19 +201,22 @@ class DecodeSession:
         t = self.step_index + 1 if t is None else t
         w = self.w
         self.use_buffers(t)
-        if w.append:
-            self.append(t)
-        if not w.select_all:
-            self.score(t)
-            if self.fused:
-                self.select_swap()
-            else:
-                self.select()
-        if w.select_all or not self.fused:
-            self.swap_diff()
         if self.fused:
+            if w.select_all:
+                if w.append:
+                    self.append(t)
+                self.swap_diff()
+            else:
+                self.append_score(t)
+                self.select_swap()
             self.decode_combine(t)
         else:
+            if w.append:
+                self.append(t)
+            if not w.select_all:
+                self.score(t)
+                self.select()
+            self.swap_diff()
             self.decode(t)
             self.combine()
         self.step_index = t

@@ -98,7 +98,7 @@ WORKLOADS = {
                  bs=64, ss=16, k_e=4, k_q=4, splits=2),
         # 2: Llama-3-8B-shaped layer at 32K context (the headline workload)
         Workload(2, "llama3_8b_32k", B=32, Hq=32, Hkv=8, D=128, T0=32768, steps=8,
-                 bs=64, ss=16, k_e=32, k_q=32, splits=2,
+                 bs=64, ss=16, k_e=32, k_q=32, splits=1,
                  heavy_frac=0.01, heavy_scale=20.0, e_sigma=math.sqrt(2.0)),
         # 3: dense equivalence at the 8B shape, 8K context, every block
         Workload(3, "dense_8b_8k", B=32, Hq=32, Hkv=8, D=128, T0=8192, steps=1,

@@ -207,6 +207,24 @@ nosa_status nosa_select_swap(const nosa_dims* dims, const float* score_q, const 
                              int32_t* load, int32_t* load_count, int32_t* evict, int32_t* evict_count,
                              hipStream_t stream);
 
+/* nosa_append and nosa_score_blocks in one launch [NOSA, NOSI: pooling
+ * fused into the index-side kernel].  Results are bit-identical to the two
+ * calls in sequence, except for where the new lengths go:
+ *   k_new, v_new, e_new: as nosa_append, or all NULL for no append;
+ *   seq_lens_in int32 [B]: lengths before the append (read only);
+ *   seq_lens_out int32 [B]: written with the lengths after the append
+ *     (seq_lens_in[b] + 1, or unchanged where the append is out of range,
+ *     which also sets the error flag); required with an append and must
+ *     differ from seq_lens_in; ignored (may be NULL) without one;
+ *   k_summary, e_summary, q, score_q, score_e: as nosa_append /
+ *     nosa_score_blocks.
+ * Scoring uses the lengths after the append.                              */
+nosa_status nosa_append_score(const nosa_dims* dims, const nosa_kv* kv,
+                              const uint16_t* k_new, const uint16_t* v_new, const float* e_new,
+                              const int32_t* seq_lens_in, int32_t* seq_lens_out,
+                              float* k_summary, float* e_summary, const uint16_t* q,
+                              float* score_q, float* score_e, hipStream_t stream);
+
 /* Block-swap set differences [NOSA, NOSI set-difference kernel]:
  *   load  = cur  minus prev (in cur's order),
  *   evict = prev minus cur  (in prev's order),

@@ -117,6 +117,28 @@ def test_host_checks_reject_bad_arguments():
     # misaligned 16-byte operands
     assert L.nosa_score_blocks(D(d), fake, ctypes.c_void_p(4100), fake, fake, fake, fake,
                                None) == nosa.NOSA_ERR_ARG
+    # fused selection + swap lists: distinct list buffers, swap lists required
+    sel_a, sel_b = P(1024), P(2048)
+    assert L.nosa_select_swap(D(d), fake, fake, fake, 4, 4, fake, sel_a, 8, fake, sel_a, fake, fake, fake,
+                              sel_b, fake, None) == nosa.NOSA_ERR_ARG  # prev aliases sel
+    assert L.nosa_select_swap(D(d), fake, fake, fake, 4, 4, fake, sel_a, 8, fake, None, fake, fake, fake,
+                              sel_b, fake, None) == nosa.NOSA_ERR_ARG  # prev missing
+    # fused decode + combine: the arrival counters are required
+    kv.kind = nosa.NOSA_TABLE_FLAT
+    kv.table = ctypes.c_void_p(4096)
+    assert L.nosa_sparse_decode_combine(D(d), fake, D(kv), fake, fake, 8, fake, 4, 0.1, fake, fake, fake,
+                                        None, fake, fake, fake, None) == nosa.NOSA_ERR_ARG
+    # fused append + score
+    def ascore(k_new, seq_in, seq_out, v_new=None):
+        v = v_new if v_new is not None else (fake if k_new else None)
+        return L.nosa_append_score(D(d), D(kv), k_new, v, fake if k_new else None, seq_in, seq_out, fake, fake,
+                                   fake, fake, fake, None)
+    seq_a, seq_b = P(512), P(768)
+    assert ascore(fake, seq_a, seq_a) == nosa.NOSA_ERR_ARG      # lengths in place
+    assert ascore(fake, seq_a, None) == nosa.NOSA_ERR_ARG       # append without an output length
+    assert ascore(P(4100), seq_a, seq_b) == nosa.NOSA_ERR_ARG   # misaligned k_new
+    assert ascore(None, seq_a, None, v_new=fake) == nosa.NOSA_ERR_ARG  # v_new without k_new
+    assert ascore(None, None, None) == nosa.NOSA_ERR_ARG        # no lengths
 
 
 def test_binding_refuses_cpu_tensors():

@@ -140,24 +140,30 @@ def test_8b_shape_small_separate_calls():
 
 FUSED_CASES = [
     ("tiny_nosa", {}, 2),
+    ("tiny_nosa", {}, 1),
     ("llama3_8b_32k", dict(B=2, Hq=8, Hkv=2, T0=4096 + 61), 3),
+    ("llama3_8b_32k", dict(B=2, Hq=8, Hkv=2, T0=4096 + 61), 1),
     ("dense_8b_8k", dict(B=2, Hq=8, Hkv=2, T0=1000), 37),
     ("llama31_70b_256k", dict(B=2, Hq=16, Hkv=2, T0=16384 + 100, dir_entries=64), 16),
     ("lazy_rope_32k", dict(B=2, Hq=8, Hkv=2, T0=8 * 512, doc_len=512), 9),
 ]
 
 
-@pytest.mark.parametrize("name,scale,splits", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+@pytest.mark.parametrize("name,scale,splits", FUSED_CASES, ids=[f"{c[0]}-P{c[2]}" for c in FUSED_CASES])
 def test_fused_equals_separate(name, scale, splits):
-    """nosa_select_swap and nosa_sparse_decode_combine give bit-identical
-    results to the separate calls they fuse, step after step."""
+    """nosa_append_score, nosa_select_swap and nosa_sparse_decode_combine
+    give bit-identical results to the separate calls they fuse, step after
+    step:
+    selections, swap lists, partials, outputs, lengths, summaries, block
+    scores and pages."""
     w = WORKLOADS[name].scaled(**scale) if scale else WORKLOADS[name]
     announce(f"fused vs separate {name} {scale} P={splits}")
     inp = synth.generate(w, 11)
     a = session(w, inp, splits=splits, fused=True)
     s = session(w, inp, splits=splits, fused=False)
     names = ["sel", "sel_count", "evicted", "load", "load_count", "evict", "evict_count",
-             "part_o", "part_m", "part_l", "o", "m", "l", "seq_lens"]
+             "part_o", "part_m", "part_l", "o", "m", "l", "seq_lens", "k_summary", "e_summary",
+             "score_q", "score_e", "k_pages", "v_pages", "e_pages"]
     for t in range(1, min(w.steps, 6) + 1):
         a.step(t)
         s.step(t)
