@@ -5,9 +5,9 @@
 A step is the whole hot path over one batch: append -> score -> select ->
 swap_diff -> sparse_decode (split-K) -> combine, for every sequence of the
 batch, on synthetic inputs resident in HBM before timing starts.  By default
-the step is three launches: append + score (nosa_append_score), select +
-swap_diff (nosa_select_swap) and decode + combine
-(nosa_sparse_decode_combine); --unfused times the six separate calls.  The
+the step is two launches: append + score (nosa_append_score) and select +
+swap_diff + decode + combine (nosa_select_decode); --unfused times the six
+separate calls.  The
 default workload is the Llama-3-8B-shaped layer at 32K context.
 
 Timing (HIP events on the stream the kernels run on):
@@ -175,13 +175,16 @@ def main(argv=None) -> int:
     # pass 2: cold steps with an event between every launch
     fused = sess.fused
     if fused:
-        names = ((["append"] if w.append else []) + ["swap_diff"]) if w.select_all else ["append_score",
-                                                                                          "select_swap"]
-        names += ["decode_combine"]
+        if w.select_all:
+            names = (["append"] if w.append else []) + ["swap_diff", "decode_combine"]
+        elif sess.select_decode_ok:
+            names = ["append_score", "select_decode"]
+        else:
+            names = ["append_score", "select_swap", "decode_combine"]
     else:
         names = (["append"] if w.append else []) + ([] if w.select_all else ["score", "select"])
         names += ["swap_diff", "decode", "combine"]
-    dec_name = "decode_combine" if fused else "decode"
+    dec_name = "select_decode" if "select_decode" in names else ("decode_combine" if fused else "decode")
     per = {n: [] for n in names}
     for k in range(K):
         flush()
@@ -202,6 +205,8 @@ def main(argv=None) -> int:
                 sess.append_score(t)
             elif n == "decode_combine":
                 sess.decode_combine(t)
+            elif n == "select_decode":
+                sess.select_decode(t)
             elif n == "swap_diff":
                 sess.swap_diff()
             elif n == "decode":
@@ -239,7 +244,8 @@ def main(argv=None) -> int:
             traffic = tr.get("bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                "kernel": ("nosa_sparse_decode_combine" if fused else "nosa_sparse_decode") + " (decode_kernel)",
+                "kernel": {"select_decode": "nosa_select_decode", "decode_combine": "nosa_sparse_decode_combine",
+                           "decode": "nosa_sparse_decode"}[dec_name] + " (decode_kernel)",
                 "algorithmic_bytes_per_launch": int(kvb), "avg_launch_us": round(kernels_us[dec_name], 2)}
 
     if args.copy_calibration:

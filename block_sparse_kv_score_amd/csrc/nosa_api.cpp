@@ -214,6 +214,36 @@ nosa_status nosa_sparse_decode_combine(const nosa_dims* dims, const uint16_t* q,
                                       part_o, part_m, part_l, counters, o, m, l, stream));
 }
 
+nosa_status nosa_select_decode(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* q, const float* score_q,
+                               const float* score_e, const int32_t* seq_lens, int32_t k_e, int32_t k_q,
+                               const uint32_t* evicted_in, uint32_t* evicted_out, int32_t* sel, int32_t sel_cap,
+                               int32_t* sel_count, const int32_t* prev, const int32_t* prev_count, int32_t* load,
+                               int32_t* load_count, int32_t* evict, int32_t* evict_count, int32_t num_splits,
+                               float sm_scale, float* part_o, float* part_m, float* part_l, int32_t* counters,
+                               float* o, float* m, float* l, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if ((st = check_kv(dims, kv, true)) != NOSA_OK) return st;
+  if (kv->kind == NOSA_TABLE_PACKED_ROPE) return NOSA_ERR_UNSUPPORTED;
+  if (dims->max_blocks > NOSA_SELECT_DECODE_MAX_BLOCKS) return NOSA_ERR_UNSUPPORTED;
+  if (!q || !score_q || !score_e || !seq_lens || !evicted_in || !evicted_out || !sel || !sel_count)
+    return NOSA_ERR_ARG;
+  if (!prev || !prev_count || !load || !load_count || !evict || !evict_count) return NOSA_ERR_ARG;
+  if (!part_o || !part_m || !part_l || !counters || !o || !m || !l) return NOSA_ERR_ARG;
+  if (!aligned16(q)) return NOSA_ERR_ARG;
+  if (k_e < 0 || k_q < 0 || sel_cap < 1 || sel_cap > dims->max_blocks) return NOSA_ERR_ARG;
+  const int64_t k = (int64_t)k_e + k_q;
+  if ((int64_t)sel_cap < (k < dims->max_blocks ? k : (int64_t)dims->max_blocks)) return NOSA_ERR_ARG;
+  if (prev == sel || load == sel || evict == sel || load == evict) return NOSA_ERR_ARG;
+  if (num_splits < 1 || num_splits > 256) return NOSA_ERR_ARG;
+  if (num_splits > 1 && evicted_in == evicted_out) return NOSA_ERR_ARG;
+  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_select_decode(*dims, q, *kv, score_q, score_e, seq_lens, k_e, k_q, evicted_in,
+                                             evicted_out, sel, sel_cap, sel_count, prev, prev_count, load, load_count,
+                                             evict, evict_count, num_splits, sm_scale, part_o, part_m, part_l,
+                                             counters, o, m, l, stream));
+}
+
 nosa_status nosa_combine(const nosa_dims* dims, int32_t num_splits, const float* part_o, const float* part_m,
                          const float* part_l, float* o, float* m, float* l, hipStream_t stream) {
   nosa_status st = check_dims(dims);

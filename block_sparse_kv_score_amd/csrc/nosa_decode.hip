@@ -41,6 +41,7 @@
 // MFMA (|error| ~ 2^-16 relative).
 
 #include "nosa_launch.hpp"
+#include "nosa_select_impl.hpp"
 
 namespace nosa {
 
@@ -70,7 +71,30 @@ struct DecodeArgs {
   float* o;
   float* m;
   float* l;
+  // fused selection (select variants only): every workgroup of a pair makes
+  // the pair's selection; split 0 writes it, the new bitmap and the swap
+  // lists out
+  const float* score_q;
+  const float* score_e;
+  int k_e, k_q;
+  const uint32_t* ev_in;
+  uint32_t* ev_out;
+  int32_t* sel_w;
+  int32_t* sel_count_w;
+  SwapArgs sw;
 };
+
+constexpr int kDecSelCap = 4 * kSelThreads;  // capacity of the select variants (SR = 4)
+
+// LDS of the fused selection (SR > 0: elements per select thread).
+template <int SR>
+struct DecodeSelSmem {
+  SelShared sel;
+  int32_t list[kDecSelCap];
+  int32_t n;
+};
+template <>
+struct DecodeSelSmem<0> {};
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -200,12 +224,16 @@ __device__ __forceinline__ void merge_one(float pm, float pl, float po, int64_t 
   }
 }
 
-template <int D, int G, int KIND>
+// SR > 0: the select variant (SR elements per thread of the selection,
+// covering max_blocks <= SR * kSelThreads).
+template <int D, int G, int KIND, int SR>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs a) {
   constexpr bool ROPE = KIND == NOSA_TABLE_PACKED_ROPE;
   using S = DecodeShape<D, G, ROPE>;
   constexpr int GE = S::GE, LPS = S::LPS, TPM = S::TPM, TH = S::TH, NDS = S::NDS, NDT = S::NDT;
   __shared__ DecodeSmem<D, G, ROPE> sh;
+  __shared__ DecodeSelSmem<SR> ssh;
+  static_assert(SR == 0 || kDecThreads == kSelThreads, "the selection runs on the whole workgroup");
 
   const int bh = blockIdx.x, p = blockIdx.y;
   const int Hkv = a.t.Hkv;
@@ -219,7 +247,30 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
 
   const int T = min(max(a.seq_lens[b], 0), a.t.max_blocks * a.bs);
   const int nb = (T + a.bs - 1) / a.bs;
-  const int n = min(max(a.sel_count[bh], 0), a.sel_cap);
+  int n;
+  const int32_t* selp = a.sel + (int64_t)bh * a.sel_cap;  // global list (SR == 0)
+  if constexpr (SR > 0) {
+    // the pair's selection, into LDS; split 0 also writes the outputs
+    const bool lead = p == 0;
+    {
+      const int words = (a.t.max_blocks + 31) / 32;
+      SwapArgs sw = a.sw;  // a copy (see select_pair)
+      if (!lead) sw.load = nullptr;
+      const int ns = select_pair<SR, true>(ssh.sel, bh, T, a.bs, a.t.max_blocks, a.score_q, a.score_e, a.k_e, a.k_q,
+                                           a.ev_in + (int64_t)bh * words,
+                                           lead ? a.ev_out + (int64_t)bh * words : nullptr, ssh.list, a.sel_cap,
+                                           nullptr, sw);
+      if (threadIdx.x == 0) ssh.n = ns;
+    }
+    __syncthreads();  // the list and its size
+    n = ssh.n;
+    if (lead) {
+      for (int k = threadIdx.x; k < n; k += kDecThreads) a.sel_w[(int64_t)bh * a.sel_cap + k] = ssh.list[k];
+      if (threadIdx.x == 0) a.sel_count_w[bh] = n;
+    }
+  } else {
+    n = min(max(a.sel_count[bh], 0), a.sel_cap);
+  }
   const int c = (n + a.P - 1) / a.P;
   const int j0 = min(p * c, n), j1 = min(j0 + c, n);
   const int tpb = a.bs / kTile;
@@ -251,13 +302,18 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* selp = a.sel + (int64_t)bh * a.sel_cap;
   // Tile k of this split: block sel[j0 + k / tpb], 64-token slice k % tpb.
   // Returns the next tile >= k with data, skipping (and flagging) entries the
   // table cannot resolve; ntiles when there is none.
   auto next_tile = [&](int k, int64_t& page, int& ntok, uint32_t& docb, int& sub) -> int {
     for (; k < ntiles; k += kDecWaves) {
-      const int i = selp[j0 + k / tpb];
+      // the LDS list is read by name (LDS instructions): through a generic
+      // pointer every read would also wait for the in-flight tile loads
+      int i;
+      if constexpr (SR > 0)
+        i = ssh.list[j0 + k / tpb];
+      else
+        i = selp[j0 + k / tpb];
       sub = k % tpb;
       if (i < 0 || i >= nb) {
         if (lane == 0) flag_error(a.t.err);
@@ -363,7 +419,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x = acc[e];
-        if constexpr (ROPE) x += __shfl_xor(x, G, kWave);  // hi + lo parts
+        if constexpr (ROPE) x += lane_xor<G>(x);  // hi + lo parts
         const int tok = th * TPM + 16 * cset + 4 * lq + e;
         sv[th][e] = tok < ntok ? x * a.scale_log2 : -INFINITY;
       }
@@ -383,8 +439,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
     for (int th = 0; th < TH; ++th)
 #pragma unroll
       for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sv[th][e]);
-#pragma unroll
-    for (int off = GE; off < kWave; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+    mx = xor_reduce<GE, kWave>(mx, [](float x, float y) { return fmaxf(x, y); });
     const float mn = fmaxf(m_run, mx);
     const float alpha = exp2f(m_run - mn);
     m_run = mn;
@@ -455,11 +510,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int off = GE; off < 16; off <<= 1) oacc[dt][e] += __shfl_xor(oacc[dt][e], off, kWave);
+      oacc[dt][e] = xor_reduce<GE, 16>(oacc[dt][e], [](float x, float y) { return x + y; });
   float lsum = l_run;
-#pragma unroll
-  for (int off = GE; off < kWave; off <<= 1) lsum += __shfl_xor(lsum, off, kWave);
+  lsum = xor_reduce<GE, kWave>(lsum, [](float x, float y) { return x + y; });
   if (real && cset == 0) {
     if (lq == 0) {
       sh.mw[w][cg] = m_run;
@@ -527,37 +580,43 @@ __global__ void combine_kernel(int P, int D, const float* __restrict__ part_o, c
 }
 
 template <int D, int G>
-static void launch_decode_dg(dim3 grid, const DecodeArgs& a, int kind, hipStream_t stream) {
+static void launch_decode_dg(dim3 grid, const DecodeArgs& a, int kind, bool select, hipStream_t stream) {
+  if (select) {  // flat and two-level tables, max_blocks <= kDecSelCap
+    if (kind == NOSA_TABLE_FLAT)
+      decode_kernel<D, G, NOSA_TABLE_FLAT, 4><<<grid, kDecThreads, 0, stream>>>(a);
+    else
+      decode_kernel<D, G, NOSA_TABLE_TWO_LEVEL, 4><<<grid, kDecThreads, 0, stream>>>(a);
+    return;
+  }
   switch (kind) {
     case NOSA_TABLE_FLAT:
-      decode_kernel<D, G, NOSA_TABLE_FLAT><<<grid, kDecThreads, 0, stream>>>(a);
+      decode_kernel<D, G, NOSA_TABLE_FLAT, 0><<<grid, kDecThreads, 0, stream>>>(a);
       break;
     case NOSA_TABLE_TWO_LEVEL:
-      decode_kernel<D, G, NOSA_TABLE_TWO_LEVEL><<<grid, kDecThreads, 0, stream>>>(a);
+      decode_kernel<D, G, NOSA_TABLE_TWO_LEVEL, 0><<<grid, kDecThreads, 0, stream>>>(a);
       break;
     default:
-      if constexpr (G <= 8) decode_kernel<D, G, NOSA_TABLE_PACKED_ROPE><<<grid, kDecThreads, 0, stream>>>(a);
+      if constexpr (G <= 8) decode_kernel<D, G, NOSA_TABLE_PACKED_ROPE, 0><<<grid, kDecThreads, 0, stream>>>(a);
       break;
   }
 }
 
 template <int D>
-static void launch_decode_d(dim3 grid, const DecodeArgs& a, int G, int kind, hipStream_t stream) {
+static void launch_decode_d(dim3 grid, const DecodeArgs& a, int G, int kind, bool select, hipStream_t stream) {
   switch (G) {
-    case 1: launch_decode_dg<D, 1>(grid, a, kind, stream); break;
-    case 2: launch_decode_dg<D, 2>(grid, a, kind, stream); break;
-    case 4: launch_decode_dg<D, 4>(grid, a, kind, stream); break;
-    case 8: launch_decode_dg<D, 8>(grid, a, kind, stream); break;
-    default: launch_decode_dg<D, 16>(grid, a, kind, stream); break;
+    case 1: launch_decode_dg<D, 1>(grid, a, kind, select, stream); break;
+    case 2: launch_decode_dg<D, 2>(grid, a, kind, select, stream); break;
+    case 4: launch_decode_dg<D, 4>(grid, a, kind, select, stream); break;
+    case 8: launch_decode_dg<D, 8>(grid, a, kind, select, stream); break;
+    default: launch_decode_dg<D, 16>(grid, a, kind, select, stream); break;
   }
 }
 
-hipError_t launch_decode(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv,
-                         const int32_t* sel, const int32_t* sel_count, int32_t sel_cap,
-                         const int32_t* seq_lens, int32_t num_splits, float sm_scale,
-                         float* part_o, float* part_m, float* part_l, int32_t* counters, float* o,
-                         float* m, float* l, hipStream_t stream) {
-  DecodeArgs a;
+static DecodeArgs decode_args(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv, const int32_t* sel,
+                              const int32_t* sel_count, int32_t sel_cap, const int32_t* seq_lens, int32_t num_splits,
+                              float sm_scale, float* part_o, float* part_m, float* part_l, int32_t* counters,
+                              float* o, float* m, float* l) {
+  DecodeArgs a = {};
   a.t = make_table(d, kv);
   a.Hq = d.n_q_heads;
   a.bs = d.block_size;
@@ -579,13 +638,49 @@ hipError_t launch_decode(const nosa_dims& d, const uint16_t* q, const nosa_kv& k
   a.o = o;
   a.m = m;
   a.l = l;
-  const dim3 grid(d.batch * d.n_kv_heads, num_splits);
+  return a;
+}
+
+static hipError_t launch_decode_args(const nosa_dims& d, const DecodeArgs& a, int kind, bool select,
+                                     hipStream_t stream) {
+  const dim3 grid(d.batch * d.n_kv_heads, a.P);
   const int G = d.n_q_heads / d.n_kv_heads;
   if (d.head_dim == 128)
-    launch_decode_d<128>(grid, a, G, kv.kind, stream);
+    launch_decode_d<128>(grid, a, G, kind, select, stream);
   else
-    launch_decode_d<64>(grid, a, G, kv.kind, stream);
+    launch_decode_d<64>(grid, a, G, kind, select, stream);
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv,
+                         const int32_t* sel, const int32_t* sel_count, int32_t sel_cap,
+                         const int32_t* seq_lens, int32_t num_splits, float sm_scale,
+                         float* part_o, float* part_m, float* part_l, int32_t* counters, float* o,
+                         float* m, float* l, hipStream_t stream) {
+  const DecodeArgs a = decode_args(d, q, kv, sel, sel_count, sel_cap, seq_lens, num_splits, sm_scale, part_o,
+                                   part_m, part_l, counters, o, m, l);
+  return launch_decode_args(d, a, kv.kind, false, stream);
+}
+
+hipError_t launch_select_decode(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv, const float* score_q,
+                                const float* score_e, const int32_t* seq_lens, int32_t k_e, int32_t k_q,
+                                const uint32_t* evicted_in, uint32_t* evicted_out, int32_t* sel, int32_t sel_cap,
+                                int32_t* sel_count, const int32_t* prev, const int32_t* prev_count, int32_t* load,
+                                int32_t* load_count, int32_t* evict, int32_t* evict_count, int32_t num_splits,
+                                float sm_scale, float* part_o, float* part_m, float* part_l, int32_t* counters,
+                                float* o, float* m, float* l, hipStream_t stream) {
+  DecodeArgs a = decode_args(d, q, kv, nullptr, nullptr, sel_cap, seq_lens, num_splits, sm_scale, part_o, part_m,
+                             part_l, counters, o, m, l);
+  a.score_q = score_q;
+  a.score_e = score_e;
+  a.k_e = k_e;
+  a.k_q = k_q;
+  a.ev_in = evicted_in;
+  a.ev_out = evicted_out;
+  a.sel_w = sel;
+  a.sel_count_w = sel_count;
+  a.sw = SwapArgs{prev, prev_count, load, load_count, evict, evict_count};
+  return launch_decode_args(d, a, kv.kind, true, stream);
 }
 
 hipError_t launch_combine(const nosa_dims& d, int32_t num_splits, const float* part_o,

@@ -118,18 +118,91 @@ __device__ __forceinline__ float load_f32(const float* p) {
 // counters unconstrained: vmcnt = 0, expcnt = 7, lgkmcnt = 15.
 constexpr int kWaitVmcnt0 = (0xF << 8) | (0x7 << 4);
 
-template <typename T>
-__device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, kWave));
+// ---------------------------------------------------------------------------
+// Cross-lane exchanges in registers.  HIP's __shfl family goes through the
+// LDS crossbar (ds_bpermute), one dependent LDS round trip per step; these
+// use DPP row operations and the gfx950 permlane swaps instead (lane
+// layouts as documented for CDNA: quad_perm, row_shl/shr/ror within rows of
+// 16 lanes, row_bcast:15/31 across rows, v_permlane16/32_swap exchanging
+// rows / halves between two registers).
+// ---------------------------------------------------------------------------
+
+// The value of lane (this lane ^ M), M a power of two below 64.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v) {
+  const int x = (int)v;
+  if constexpr (M == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    const int up = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xf, 0xf, false);  // row_shl:4: lane i <- i + 4
+    const int dn = __builtin_amdgcn_update_dpp(x, x, 0x114, 0xf, 0xf, false);  // row_shr:4: lane i <- i - 4
+    return (uint32_t)((threadIdx.x & 4) ? dn : up);
+  } else if constexpr (M == 8) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x128, 0xf, 0xf, false);  // row_ror:8
+  } else if constexpr (M == 16) {
+    // with both operands x: [0] = rows (0,0,2,2), [1] = rows (1,1,3,3)
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (uint32_t)((threadIdx.x & 16) ? p[0] : p[1]);
+  } else {
+    static_assert(M == 32, "lane_xor: M in {1, 2, 4, 8, 16, 32}");
+    // with both operands x: [0] = halves (0,0), [1] = halves (1,1)
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (uint32_t)((threadIdx.x & 32) ? p[0] : p[1]);
+  }
+}
+
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  return __uint_as_float(lane_xor_u32<M>(__float_as_uint(v)));
+}
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  return lane_xor_u32<M>(v);
+}
+template <int M>
+__device__ __forceinline__ double lane_xor(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint64_t lo = lane_xor_u32<M>((uint32_t)u), hi = lane_xor_u32<M>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(lo | (hi << 32)));
+}
+
+// v = op(v, v of lane ^ M) for M = FROM, 2 FROM, .. < TO: the reduction over
+// the lanes that agree with this one outside bits [log2 FROM, log2 TO), in
+// the same order as the classic butterfly.
+template <int FROM, int TO, typename T, typename Op>
+__device__ __forceinline__ T xor_reduce(T v, Op op) {
+  if constexpr (FROM < TO) {
+    v = op(v, lane_xor<FROM>(v));
+    return xor_reduce<FROM * 2, TO>(v, op);
+  } else {
+    return v;
+  }
+}
+
+// As xor_reduce<1, 64>, but only over bits below log2 n (n a power of two,
+// 1 <= n <= 64, uniform at run time).
+template <typename T, typename Op>
+__device__ __forceinline__ T xor_reduce_below(T v, int n, Op op) {
+  if (n > 1) v = op(v, lane_xor<1>(v));
+  if (n > 2) v = op(v, lane_xor<2>(v));
+  if (n > 4) v = op(v, lane_xor<4>(v));
+  if (n > 8) v = op(v, lane_xor<8>(v));
+  if (n > 16) v = op(v, lane_xor<16>(v));
+  if (n > 32) v = op(v, lane_xor<32>(v));
   return v;
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+// Inclusive prefix sum over the 64 lanes of the wave.
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1 (row start reads 0)
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2 and 3
+  return x;
 }
 
 }  // namespace nosa

@@ -54,6 +54,14 @@ hipError_t launch_decode(const nosa_dims& d, const uint16_t* q, const nosa_kv& k
                          float* part_o, float* part_m, float* part_l, int32_t* counters, float* o,
                          float* m, float* l, hipStream_t stream);
 
+hipError_t launch_select_decode(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv, const float* score_q,
+                                const float* score_e, const int32_t* seq_lens, int32_t k_e, int32_t k_q,
+                                const uint32_t* evicted_in, uint32_t* evicted_out, int32_t* sel, int32_t sel_cap,
+                                int32_t* sel_count, const int32_t* prev, const int32_t* prev_count, int32_t* load,
+                                int32_t* load_count, int32_t* evict, int32_t* evict_count, int32_t num_splits,
+                                float sm_scale, float* part_o, float* part_m, float* part_l, int32_t* counters,
+                                float* o, float* m, float* l, hipStream_t stream);
+
 hipError_t launch_combine(const nosa_dims& d, int32_t num_splits, const float* part_o,
                           const float* part_m, const float* part_l, float* o, float* m, float* l,
                           hipStream_t stream);

@@ -96,15 +96,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(int Hq, int Hkv, i
     a3 = fma((double)v[u].w, qbar[d + 3], a3);
   }
   double dot = (a0 + a1) + (a2 + a3);
-#pragma unroll
-  for (int off = SPW; off < kWave; off <<= 1) dot += __shfl_xor(dot, off, kWave);  // the L slices
+  dot = xor_reduce<SPW, kWave>(dot, [](double x, double y) { return x + y; });  // the L slices
   if (!valid) dot = -INFINITY;
   float ek = valid ? ev : -INFINITY;
   // max over the nsub sub-blocks of each block: nsub <= SPW consecutive lanes
-  for (int off = 1; off < nsub; off <<= 1) {
-    dot = fmax(dot, __shfl_xor(dot, off, kWave));
-    ek = fmaxf(ek, __shfl_xor(ek, off, kWave));
-  }
+  dot = xor_reduce_below(dot, nsub, [](double x, double y) { return fmax(x, y); });
+  ek = xor_reduce_below(ek, nsub, [](float x, float y) { return fmaxf(x, y); });
   if (valid && part == 0 && j == 0) {
     score_q[(int64_t)bh * max_blocks + i] = (float)(dot / sqrt((double)D));
     score_e[(int64_t)bh * max_blocks + i] = ek;

@@ -9,20 +9,21 @@
 
 namespace nosa {
 
+// One workgroup per (b, h).
 template <int R, bool SWAP>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(int Hkv, int bs, int max_blocks,
-                                                             const float* __restrict__ score_q,
-                                                             const float* __restrict__ score_e,
-                                                             const int32_t* __restrict__ seq_lens,
-                                                             int k_e, int k_q,
-                                                             uint32_t* __restrict__ evicted,
-                                                             int32_t* __restrict__ sel, int sel_cap,
-                                                             int32_t* __restrict__ sel_count, const SwapArgs sw) {
+                                                            const float* __restrict__ score_q,
+                                                            const float* __restrict__ score_e,
+                                                            const int32_t* __restrict__ seq_lens, int k_e, int k_q,
+                                                            uint32_t* __restrict__ evicted,
+                                                            int32_t* __restrict__ sel, int sel_cap,
+                                                            int32_t* __restrict__ sel_count, const SwapArgs sw) {
   __shared__ SelShared sh;
   const int bh = blockIdx.x;
   const int T = min(max(seq_lens[bh / Hkv], 0), max_blocks * bs);
-  select_pair<R, SWAP, false>(sh, bh, T, bs, max_blocks, score_q, score_e, k_e, k_q, evicted, sel, sel_cap,
-                              sel_count, sw);
+  uint32_t* ev = evicted + (int64_t)bh * ((max_blocks + 31) / 32);
+  select_pair<R, SWAP>(sh, bh, T, bs, max_blocks, score_q, score_e, k_e, k_q, ev, ev,
+                           sel + (int64_t)bh * sel_cap, sel_cap, sel_count + bh, sw);
 }
 
 // One wave per (b, h); membership through an LDS bitmap, order-preserving
@@ -79,20 +80,21 @@ static hipError_t launch_select_any(const nosa_dims& d, const float* score_q, co
                                     const int32_t* seq_lens, int32_t k_e, int32_t k_q, uint32_t* evicted,
                                     int32_t* sel, int32_t sel_cap, int32_t* sel_count, const SwapArgs* sw,
                                     hipStream_t stream) {
-  const int R = (d.max_blocks + kSelThreads - 1) / kSelThreads;  // elements per thread
   const dim3 grid(d.batch * d.n_kv_heads);
   const SwapArgs none = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-#define NOSA_SELECT(RR)                                                                                         \
-  do {                                                                                                          \
-    if (sw)                                                                                                     \
-      select_kernel<RR, true><<<grid, kSelThreads, 0, stream>>>(d.n_kv_heads, d.block_size, d.max_blocks,       \
-                                                                score_q, score_e, seq_lens, k_e, k_q, evicted,  \
-                                                                sel, sel_cap, sel_count, *sw);                  \
-    else                                                                                                        \
-      select_kernel<RR, false><<<grid, kSelThreads, 0, stream>>>(d.n_kv_heads, d.block_size, d.max_blocks,      \
-                                                                 score_q, score_e, seq_lens, k_e, k_q, evicted, \
-                                                                 sel, sel_cap, sel_count, none);                \
+  const SwapArgs args = sw ? *sw : none;
+#define NOSA_SELECT(RR)                                                                                        \
+  do {                                                                                                         \
+    if (sw)                                                                                                    \
+      select_kernel<RR, true><<<grid, kSelThreads, 0, stream>>>(d.n_kv_heads, d.block_size, d.max_blocks,     \
+                                                                score_q, score_e, seq_lens, k_e, k_q, evicted, \
+                                                                sel, sel_cap, sel_count, args);                \
+    else                                                                                                       \
+      select_kernel<RR, false><<<grid, kSelThreads, 0, stream>>>(d.n_kv_heads, d.block_size, d.max_blocks,    \
+                                                                 score_q, score_e, seq_lens, k_e, k_q,         \
+                                                                 evicted, sel, sel_cap, sel_count, args);      \
   } while (0)
+  const int R = (d.max_blocks + kSelThreads - 1) / kSelThreads;  // elements per thread
   if (R <= 2) NOSA_SELECT(2);
   else if (R <= 4) NOSA_SELECT(4);
   else if (R <= 8) NOSA_SELECT(8);

@@ -1,6 +1,6 @@
 // Dual selection and the swap lists for one (b, h) pair, as a workgroup
-// device function, shared by the selection kernels and the fused
-// score + select kernel.
+// device function, shared by the selection kernel and the decode kernel's
+// select variant.
 //
 // NOSA summary (gist.science 2510.13602), Methodology 1: selection is split
 // into a query-aware part (recall, possibly far-away blocks) and a
@@ -15,20 +15,21 @@
 // part only, ties go to the lower block index, and a newly created block
 // starts as an eviction candidate.
 //
-// One workgroup of 256 threads per (b, h); each thread keeps its blocks'
-// keys in registers (block i = r * 256 + thread).  Top-k is a
-// most-significant-digit radix select over order-preserving 32-bit keys of
-// the fp32 scores (see radix_top_k); exact key ties go to the lowest index.
-// Outputs are compacted in index order with wave ballots, so they come out
-// ascending without a sort, and the eviction bitmap words are rebuilt from
-// ballots.
+// NT = 256 threads per (b, h); each keeps its blocks' keys in registers
+// (block i = r * NT + thread).  Top-k is a most-significant-digit radix
+// select over order-preserving 32-bit keys of the fp32 scores (see
+// radix_top_k); exact key ties go to the lowest index.  Outputs are
+// compacted in index order with wave ballots, so they come out ascending
+// without a sort, and the eviction bitmap words are rebuilt from ballots.
+// (A one-wave form with 16 elements per lane, free of workgroup barriers,
+// measured slower for 516 blocks.)
 #pragma once
 
 #include "nosa_device.hpp"
 
 namespace nosa {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 256;                // the four-wave form
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kMaxBlocks = 8192;
 
@@ -47,7 +48,8 @@ struct SelShared {
   int32_t pos_evict[32][kSelWaves];
 };
 
-// Workgroup sum of one int per wave (lane 0's value); one barrier.
+// Workgroup sum of one int per wave (the same value in every lane); one
+// barrier.
 __device__ __forceinline__ int block_sum(int v, int& phase, SelShared& sh) {
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int ph = phase++ & 1;
@@ -82,11 +84,8 @@ __device__ void radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k, uint
       kmin = min(kmin, key[r]);
       kmax = max(kmax, key[r]);
     }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
-  }
+  kmin = xor_reduce<1, kWave>(kmin, [](uint32_t a, uint32_t b) { return min(a, b); });
+  kmax = xor_reduce<1, kWave>(kmax, [](uint32_t a, uint32_t b) { return max(a, b); });
   {
     const int ph = phase++ & 1;
     if (lane == 0) {
@@ -116,19 +115,14 @@ __device__ void radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k, uint
     for (int r = 0; r < R; ++r)
       if (((cand >> r) & 1u) && (key[r] & pmask) == prefix) atomicAdd(&sh.hist[w][(key[r] >> lo) & dmask], 1u);
     __syncthreads();
+    const int ph = phase++ & 1;
     // thread t owns digit 255 - t: inclusive scan gives the count of keys
     // with a digit >= 255 - t
     const int dg = 255 - (int)threadIdx.x;
     int c = 0;
 #pragma unroll
     for (int ww = 0; ww < kSelWaves; ++ww) c += (int)sh.hist[ww][dg];
-    int cum = c;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int t = __shfl_up(cum, off, kWave);
-      if (lane >= off) cum += t;
-    }
-    const int ph = phase++ & 1;
+    int cum = wave_scan_incl(c);
     if (lane == kWave - 1) sh.tot[ph][w] = cum;
     __syncthreads();
 #pragma unroll
@@ -189,49 +183,57 @@ struct SwapArgs {
 };
 
 // Selection of pair bh over its first T tokens (nb = ceil(T / bs) blocks),
-// called by all kSelThreads threads of a workgroup.  R elements per thread
-// cover max_blocks.  SWAP: also form the load / evict lists against the
-// previous selection.  COHERENT: the scores come from other workgroups of
-// the same launch.
-template <int R, bool SWAP, bool COHERENT>
-__device__ void select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks,
-                            const float* __restrict__ score_q, const float* __restrict__ score_e, int k_e,
-                            int k_q, uint32_t* __restrict__ evicted, int32_t* __restrict__ sel, int sel_cap,
-                            int32_t* __restrict__ sel_count, const SwapArgs& sw) {
+// called by all NT threads of a workgroup; returns the selection size (the
+// same value in every thread).  R elements per thread cover max_blocks
+// (R * NT >= max_blocks).
+//   ev_in / ev_out: the pair's eviction bitmap words before / after (may be
+//     the same; ev_out == nullptr: the new bitmap is not written);
+//   sel_row: the pair's list, sel_cap entries (global memory or LDS);
+//   sel_count_slot: where the size goes (nullptr: not written);
+//   SWAP with sw.load != nullptr: also form the load / evict lists against
+//     the previous selection (global memory).  sw is taken by value: a
+//     reference into a kernel's by-value argument would force a stack copy
+//     of the whole argument and turn every global access into a flat one.
+template <int R, bool SWAP>
+__device__ int select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks,
+                           const float* __restrict__ score_q, const float* __restrict__ score_e, int k_e,
+                           int k_q, const uint32_t* ev_in, uint32_t* ev_out, int32_t* sel_row, int sel_cap,
+                           int32_t* sel_count_slot, const SwapArgs sw) {
+  constexpr int NT = kSelThreads;
+  static_assert(R <= 32, "selection shape");
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int nb = (T + bs - 1) / bs;
-  const int words = (max_blocks + 31) / 32;
-  uint32_t* ev = evicted + (int64_t)bh * words;
   const float* se = score_e + (int64_t)bh * max_blocks;
   const float* sq = score_q + (int64_t)bh * max_blocks;
+  const bool swap_lists = SWAP && sw.load != nullptr;
 
   // every load up front, over the whole capacity so they need not wait for
   // seq_lens; blocks >= nb are masked out afterwards
   uint32_t ke[R], kq[R], ew[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int i = r * kSelThreads + threadIdx.x;
+    const int i = r * NT + threadIdx.x;
     ke[r] = kq[r] = ew[r] = 0u;
     if (i < max_blocks) {
-      ke[r] = order_key(load_f32<COHERENT>(se + i));
-      kq[r] = order_key(load_f32<COHERENT>(sq + i));
-      ew[r] = ev[i >> 5];
+      ke[r] = order_key(se[i]);
+      kq[r] = order_key(sq[i]);
+      ew[r] = ev_in[i >> 5];
     }
   }
   // fused swap lists: the previous selection (capacity sel_cap <= max_blocks,
   // so R entries per thread cover it), loaded with everything else
   int32_t pv[R];
   int n_prev = 0;
-  if constexpr (SWAP) {
+  if (swap_lists) {
     const int32_t* pl = sw.prev + (int64_t)bh * sel_cap;
 #pragma unroll
-    for (int r = 0; r < R; ++r) pv[r] = pl[min(r * kSelThreads + (int)threadIdx.x, sel_cap - 1)];
+    for (int r = 0; r < R; ++r) pv[r] = pl[min(r * NT + (int)threadIdx.x, sel_cap - 1)];
     n_prev = min(max(sw.prev_count[bh], 0), sel_cap);
   }
   uint32_t valid = 0, evm = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int i = r * kSelThreads + threadIdx.x;
+    const int i = r * NT + threadIdx.x;
     if (i < nb) {
       valid |= 1u << r;
       evm |= ((ew[r] >> (i & 31)) & 1u) << r;
@@ -261,26 +263,31 @@ __device__ void select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks
 
   // --- outputs: ascending union via ballots, eviction bitmap words ------
   const uint32_t pick = in_e | in_q;
+  int32_t* out = sel_row;
+  int n_all;  // size of the union
+  // the 32-bit words element r of this wave covers: lanes 0 and 32 own them
+  auto write_words = [&](int r, uint64_t pmr) {
+    const uint64_t em = __ballot((evm >> r) & 1u);
+    const uint64_t vm = __ballot((valid >> r) & 1u);
+    const int i0 = r * NT + w * kWave + (lane & 32);
+    if (ev_out != nullptr && (lane & 31) == 0 && i0 < nb) {  // this lane loaded that word at the start
+      const uint32_t e32 = (uint32_t)(em >> (lane & 32));
+      const uint32_t v32 = (uint32_t)(vm >> (lane & 32));
+      ev_out[i0 >> 5] = (ew[r] & ~v32) | e32;
+    }
+    if (swap_lists && (lane & 31) == 0 && i0 < max_blocks) sh.pick_bm[i0 >> 5] = (uint32_t)(pmr >> (lane & 32));
+  };
   uint64_t pm[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     pm[r] = __ballot((pick >> r) & 1u);
-    const uint64_t em = __ballot((evm >> r) & 1u);
-    const uint64_t vm = __ballot((valid >> r) & 1u);
-    // lanes 0 and 32 own the two 32-bit words this wave covers at element r
-    const int i0 = r * kSelThreads + w * kWave + (lane & 32);
-    if ((lane & 31) == 0 && i0 < nb) {  // this lane loaded that word at the start
-      const uint32_t e32 = (uint32_t)(em >> (lane & 32));
-      const uint32_t v32 = (uint32_t)(vm >> (lane & 32));
-      ev[i0 >> 5] = (ew[r] & ~v32) | e32;
-    }
+    write_words(r, pm[r]);
   }
   if (lane == 0) {
 #pragma unroll
     for (int r = 0; r < R; ++r) sh.pos[r][w] = __popcll(pm[r]);
   }
   __syncthreads();
-  int32_t* out = sel + (int64_t)bh * sel_cap;
   int before = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -291,40 +298,42 @@ __device__ void select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks
       pos += ww < w ? c : 0;
       before += c;
     }
-    if (((pick >> r) & 1u) && pos < sel_cap) out[pos] = r * kSelThreads + threadIdx.x;
+    if (((pick >> r) & 1u) && pos < sel_cap) out[pos] = r * NT + threadIdx.x;
   }
-  if (threadIdx.x == 0) sel_count[bh] = min(before, sel_cap);
+  n_all = before;
 
-  if constexpr (SWAP) {
+  const int n_sel = min(n_all, sel_cap);
+  if (threadIdx.x == 0 && sel_count_slot != nullptr) *sel_count_slot = n_sel;
+
+  if (swap_lists) {
     // load = selected now and not before (index order); evict = before and
     // not now (order of the previous list) -- the set differences of
-    // nosa_swap_diff, from the selection still in registers
-    for (int wd = threadIdx.x; wd < (max_blocks + 31) / 32; wd += kSelThreads) sh.prev_bm[wd] = 0u;
-    if ((lane & 31) == 0) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int i0 = r * kSelThreads + w * kWave + (lane & 32);
-        if (i0 < max_blocks) sh.pick_bm[i0 >> 5] = (uint32_t)(pm[r] >> (lane & 32));
-      }
-    }
+    // nosa_swap_diff, from the selection still in registers.  pick_bm was
+    // filled with the outputs above.
+    for (int wd = threadIdx.x; wd < (max_blocks + 31) / 32; wd += NT) sh.prev_bm[wd] = 0u;
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int k = r * kSelThreads + threadIdx.x;
+      const int k = r * NT + threadIdx.x;
       if (k < n_prev && pv[r] >= 0 && pv[r] < max_blocks) atomicOr(&sh.prev_bm[pv[r] >> 5], 1u << (pv[r] & 31));
     }
     __syncthreads();
+    int32_t* lo = sw.load + (int64_t)bh * sel_cap;
+    int32_t* eo = sw.evict + (int64_t)bh * sel_cap;
+    // element r: load if picked and not in prev; evict if entry r of prev is
+    // live and not picked
+    auto masks = [&](int r, uint64_t& lm, uint64_t& em) {
+      const int i = r * NT + threadIdx.x;
+      const bool in_prev = i < max_blocks && ((sh.prev_bm[min(i, max_blocks - 1) >> 5] >> (i & 31)) & 1u);
+      lm = __ballot(((pick >> r) & 1u) && !in_prev);
+      const int x = pv[r];
+      const bool live = i < n_prev && x >= 0 && x < max_blocks;
+      em = __ballot(live && !((sh.pick_bm[live ? x >> 5 : 0] >> (x & 31)) & 1u));
+    };
+    int bl = 0, be = 0;
     uint64_t lm[R], em[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int i = r * kSelThreads + threadIdx.x;
-      const bool in_prev = i < max_blocks && ((sh.prev_bm[min(i, max_blocks - 1) >> 5] >> (i & 31)) & 1u);
-      lm[r] = __ballot(((pick >> r) & 1u) && !in_prev);
-      const int k = r * kSelThreads + threadIdx.x;
-      const int x = pv[r];
-      const bool live = k < n_prev && x >= 0 && x < max_blocks;
-      em[r] = __ballot(live && !((sh.pick_bm[live ? x >> 5 : 0] >> (x & 31)) & 1u));
-    }
+    for (int r = 0; r < R; ++r) masks(r, lm[r], em[r]);
     if (lane == 0) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -333,9 +342,6 @@ __device__ void select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks
       }
     }
     __syncthreads();
-    int32_t* lo = sw.load + (int64_t)bh * sel_cap;
-    int32_t* eo = sw.evict + (int64_t)bh * sel_cap;
-    int bl = 0, be = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       int pl_ = bl + lanes_below(lm[r]), pe = be + lanes_below(em[r]);
@@ -347,7 +353,7 @@ __device__ void select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks
         bl += cl;
         be += ce;
       }
-      if (((lm[r] >> lane) & 1u) && pl_ < sel_cap) lo[pl_] = r * kSelThreads + threadIdx.x;
+      if (((lm[r] >> lane) & 1u) && pl_ < sel_cap) lo[pl_] = r * NT + threadIdx.x;
       if (((em[r] >> lane) & 1u) && pe < sel_cap) eo[pe] = pv[r];
     }
     if (threadIdx.x == 0) {
@@ -355,6 +361,7 @@ __device__ void select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks
       sw.evict_count[bh] = min(be, sel_cap);
     }
   }
+  return n_sel;
 }
 
 }  // namespace nosa

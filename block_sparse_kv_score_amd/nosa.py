@@ -36,6 +36,7 @@ ENTRY_POINTS = [
     "nosa_swap_diff",
     "nosa_sparse_decode",
     "nosa_sparse_decode_combine",
+    "nosa_select_decode",
     "nosa_combine",
     "nosa_status_string",
 ]
@@ -98,6 +99,8 @@ _SIGNATURES = {
     "nosa_swap_diff": [_DIMS, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "nosa_sparse_decode": [_DIMS, _P, _KV, _P, _P, _I32, _P, _I32, _F32, _P, _P, _P, _P],
     "nosa_sparse_decode_combine": [_DIMS, _P, _KV, _P, _P, _I32, _P, _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P],
+    "nosa_select_decode": [_DIMS, _KV, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P,
+                           _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P],
     "nosa_combine": [_DIMS, _I32, _P, _P, _P, _P, _P, _P, _P],
 }
 
@@ -286,6 +289,31 @@ def nosa_sparse_decode_combine(dims, q, kv, sel, sel_count, seq_lens, num_splits
           _dev(sel, "sel", (torch.int32,)), _dev(sel_count, "sel_count", (torch.int32,)),
           int(sel.shape[-1]), _dev(seq_lens, "seq_lens", (torch.int32,)), int(num_splits),
           float(sm_scale), _dev(part_o, "part_o", (torch.float32,)),
+          _dev(part_m, "part_m", (torch.float32,)), _dev(part_l, "part_l", (torch.float32,)),
+          _dev(counters, "counters", (torch.int32,)), _dev(o, "o", (torch.float32,)),
+          _dev(m, "m", (torch.float32,)), _dev(l, "l", (torch.float32,)), _stream(stream))
+
+
+SELECT_DECODE_MAX_BLOCKS = 1024
+
+
+def nosa_select_decode(dims, kv, q, score_q, score_e, seq_lens, k_e, k_q, evicted_in, evicted_out, sel, sel_count,
+                       prev, prev_count, load, load_count, evict, evict_count, num_splits, sm_scale,
+                       part_o, part_m, part_l, counters, o, m, l, stream=None):
+    cap = int(sel.shape[-1])
+    for t, n in ((prev, "prev"), (load, "load"), (evict, "evict")):
+        if int(t.shape[-1]) != cap:
+            raise ValueError(f"{n} must have the same last dimension as sel ({cap})")
+    ev = (torch.int32, torch.uint32)
+    _call("nosa_select_decode", ctypes.byref(dims), ctypes.byref(kv), _dev(q, "q", _BF16_LIKE),
+          _dev(score_q, "score_q", (torch.float32,)), _dev(score_e, "score_e", (torch.float32,)),
+          _dev(seq_lens, "seq_lens", (torch.int32,)), int(k_e), int(k_q),
+          _dev(evicted_in, "evicted_in", ev), _dev(evicted_out, "evicted_out", ev),
+          _dev(sel, "sel", (torch.int32,)), cap, _dev(sel_count, "sel_count", (torch.int32,)),
+          _dev(prev, "prev", (torch.int32,)), _dev(prev_count, "prev_count", (torch.int32,)),
+          _dev(load, "load", (torch.int32,)), _dev(load_count, "load_count", (torch.int32,)),
+          _dev(evict, "evict", (torch.int32,)), _dev(evict_count, "evict_count", (torch.int32,)),
+          int(num_splits), float(sm_scale), _dev(part_o, "part_o", (torch.float32,)),
           _dev(part_m, "part_m", (torch.float32,)), _dev(part_l, "part_l", (torch.float32,)),
           _dev(counters, "counters", (torch.int32,)), _dev(o, "o", (torch.float32,)),
           _dev(m, "m", (torch.float32,)), _dev(l, "l", (torch.float32,)), _stream(stream))

@@ -10,13 +10,14 @@ Call sequence of decode step t (1-based):
   nosa_swap_diff         against the previous step's selection
   nosa_sparse_decode     split-K over the selected pages
   nosa_combine           -> O, rowmax m, l
-With `fused` (the default) the step is three launches with the same results:
+With `fused` (the default) the step is two launches with the same results:
   nosa_append_score          append + score
-  nosa_select_swap           select + swap_diff
-  nosa_sparse_decode_combine decode + combine
-(with every block selected: nosa_swap_diff, then the fused decode).  The
-fused index launch writes the new lengths to the other of two seq_lens
-buffers, so `seq_lens` names the current one.
+  nosa_select_decode         select + swap_diff + decode + combine
+(where nosa_select_decode is not supported -- more than 1024 blocks of
+capacity -- nosa_select_swap then nosa_sparse_decode_combine; with every
+block selected: nosa_swap_diff, then the fused decode).  The fused launches
+write the new lengths and the new eviction bitmap to the other of two
+buffers, so `seq_lens` and `evicted` name the current ones.
 """
 
 from __future__ import annotations
@@ -82,7 +83,9 @@ class DecodeSession:
         self.e_summary = torch.full((B, Hkv, CS), fill, dtype=torch.float32, device=dev)
         self.score_q = torch.full((B, Hkv, MB), fill, dtype=torch.float32, device=dev)
         self.score_e = torch.full_like(self.score_q, fill)
-        self.evicted = torch.zeros((B, Hkv, (MB + 31) // 32), dtype=torch.int32, device=dev)
+        self.ev_bufs = [torch.zeros((B, Hkv, (MB + 31) // 32), dtype=torch.int32, device=dev) for _ in range(2)]
+        self.evicted = self.ev_bufs[0]
+        self.select_decode_ok = MB <= nosa.SELECT_DECODE_MAX_BLOCKS and w.table != TABLE_PACKED_ROPE
         # selections ping-pong between two buffers: step t writes buffer t % 2
         # and diffs against buffer (t - 1) % 2 (both start empty)
         self.sel_bufs = [torch.full((B, Hkv, self.cap), -1, dtype=torch.int32, device=dev) for _ in range(2)]
@@ -180,6 +183,18 @@ class DecodeSession:
                                         self.P, self.w.sm_scale, self.part_o, self.part_m, self.part_l,
                                         self.counters, self.o, self.m, self.l, self.stream)
 
+    def select_decode(self, t: int):
+        """Fused select + swap lists + decode + combine; afterwards evicted is
+        the other buffer."""
+        w = self.w
+        out = self.ev_bufs[1] if self.evicted is self.ev_bufs[0] else self.ev_bufs[0]
+        nosa.nosa_select_decode(self.dims, self.kv, self.q(t), self.score_q, self.score_e, self.seq_lens, w.k_e,
+                                w.k_q, self.evicted, out, self.sel, self.sel_count, self.prev, self.prev_count,
+                                self.load, self.load_count, self.evict, self.evict_count, self.P, w.sm_scale,
+                                self.part_o, self.part_m, self.part_l, self.counters, self.o, self.m, self.l,
+                                self.stream)
+        self.evicted = out
+
     def combine(self):
         nosa.nosa_combine(self.dims, self.P, self.part_o, self.part_m, self.part_l, self.o, self.m, self.l,
                           self.stream)
@@ -206,10 +221,14 @@ class DecodeSession:
                 if w.append:
                     self.append(t)
                 self.swap_diff()
+                self.decode_combine(t)
+            elif self.select_decode_ok:
+                self.append_score(t)
+                self.select_decode(t)
             else:
                 self.append_score(t)
                 self.select_swap()
-            self.decode_combine(t)
+                self.decode_combine(t)
         else:
             if w.append:
                 self.append(t)

@@ -265,6 +265,33 @@ nosa_status nosa_sparse_decode_combine(const nosa_dims* dims, const uint16_t* q,
                                        float* part_o, float* part_m, float* part_l, int32_t* counters,
                                        float* o, float* m, float* l, hipStream_t stream);
 
+/* nosa_select_swap and nosa_sparse_decode_combine in one launch [SPIN 2.A:
+ * Select and Attention kept as stages of one launch].  Every workgroup of
+ * a (b, h) pair makes the pair's selection from score_q / score_e into
+ * on-chip memory, exactly as nosa_select_swap, and decodes its split of it;
+ * the workgroup of split 0 also writes the selection, the new eviction
+ * bitmap and the swap lists.  Results are bit-identical to
+ * nosa_select_swap followed by nosa_sparse_decode_combine, except that the
+ * bitmap is read from evicted_in and written to evicted_out:
+ *   evicted_in, evicted_out: uint32 [B][Hkv][ceil(max_blocks / 32)]; the
+ *     same buffer is allowed only with num_splits == 1;
+ *   score_q, score_e, seq_lens, k_e, k_q, sel .. evict_count: as
+ *     nosa_select_swap (sel_cap <= max_blocks);
+ *   q, num_splits, sm_scale, part_* , counters, o, m, l: as
+ *     nosa_sparse_decode_combine.
+ * Supported for the flat and two-level tables with
+ * max_blocks <= NOSA_SELECT_DECODE_MAX_BLOCKS (NOSA_ERR_UNSUPPORTED
+ * otherwise: make the two calls).                                         */
+#define NOSA_SELECT_DECODE_MAX_BLOCKS 1024
+nosa_status nosa_select_decode(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* q,
+                               const float* score_q, const float* score_e, const int32_t* seq_lens,
+                               int32_t k_e, int32_t k_q, const uint32_t* evicted_in, uint32_t* evicted_out,
+                               int32_t* sel, int32_t sel_cap, int32_t* sel_count,
+                               const int32_t* prev, const int32_t* prev_count,
+                               int32_t* load, int32_t* load_count, int32_t* evict, int32_t* evict_count,
+                               int32_t num_splits, float sm_scale, float* part_o, float* part_m, float* part_l,
+                               int32_t* counters, float* o, float* m, float* l, hipStream_t stream);
+
 /* Attention, combine [NOVITA: return rowmax and l with O]:
  *   m = max_p part_m (over p with part_l > 0), l = sum_p part_l e^(part_m - m),
  *   O = sum_p part_l e^(part_m - m) part_o / l;  all empty: O = 0, m = -inf, l = 0.

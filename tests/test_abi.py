@@ -128,6 +128,19 @@ def test_host_checks_reject_bad_arguments():
     kv.table = ctypes.c_void_p(4096)
     assert L.nosa_sparse_decode_combine(D(d), fake, D(kv), fake, fake, 8, fake, 4, 0.1, fake, fake, fake,
                                         None, fake, fake, fake, None) == nosa.NOSA_ERR_ARG
+    # fused select + decode
+    def sdec(kvd, dims=d, ev_in=P(256), ev_out=P(512), splits=1, counters=fake):
+        return L.nosa_select_decode(D(dims), D(kvd), fake, fake, fake, fake, 4, 4, ev_in, ev_out, sel_a, 8, fake,
+                                    P(3072), fake, P(4096), fake, P(8192), fake, splits, 0.1, fake, fake, fake,
+                                    counters, fake, fake, fake, None)
+    assert sdec(kv, ev_in=P(256), ev_out=P(256), splits=2) == nosa.NOSA_ERR_ARG  # shared bitmap, 2 splits
+    assert sdec(kv, counters=None) == nosa.NOSA_ERR_ARG
+    big = nosa.make_dims(2, 8, 2, 128, 64, 16, 1025)
+    assert sdec(kv, dims=big) == nosa.NOSA_ERR_UNSUPPORTED  # capacity above the fused selection's
+    rope = nosa.nosa_kv()
+    rope.k_pages = rope.v_pages = rope.e_pages = ctypes.c_void_p(4096)
+    rope.num_pages, rope.kind, rope.packed = 10, nosa.NOSA_TABLE_PACKED_ROPE, ctypes.c_void_p(4096)
+    assert sdec(rope) == nosa.NOSA_ERR_UNSUPPORTED
     # fused append + score
     def ascore(k_new, seq_in, seq_out, v_new=None):
         v = v_new if v_new is not None else (fake if k_new else None)
