@@ -38,7 +38,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBPS = 8000.0
 METRIC = "sparse decode attn tokens/s + achieved HBM GB/s (% peak), 8B shape @32K"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_llama3_8b_32k.json")
-DECODE_SRC = os.path.join(ROOT, "block_sparse_kv_score_amd", "csrc", "nosa_decode.hip")
+CSRC = os.path.join(ROOT, "block_sparse_kv_score_amd", "csrc")
+# the sources the decode kernel (and its select variant) is built from
+DECODE_SRCS = [os.path.join(CSRC, f) for f in ("nosa_decode.hip", "nosa_select_impl.hpp", "nosa_device.hpp")]
 
 
 def parse(argv=None):
@@ -57,8 +59,11 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
-def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic_bytes(w, sel, sel_count, T):
@@ -239,8 +244,8 @@ def main(argv=None) -> int:
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("decode_source_sha256_16") == source_hash(DECODE_SRC) and tr.get("workload") == w.name \
-                and tr.get("splits") == sess.P:
+        if tr.get("decode_sources_sha256_16") == source_hash(DECODE_SRCS) and tr.get("workload") == w.name \
+                and tr.get("splits") == sess.P and tr.get("entry_point") == dec_name:
             traffic = tr.get("bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,

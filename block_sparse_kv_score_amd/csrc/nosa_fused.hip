@@ -67,14 +67,14 @@ struct FusedSmem {
 };
 
 // The append of pair bh, by the whole append workgroup (uniform call):
-// token position pos (in range).  The older tokens of the new token's
+// token position pos (in range), page the page of its block (-1: none).  The older tokens of the new token's
 // sub-block are staged through LDS kStageTok at a time by all threads (one
 // memory round trip per pass instead of one per batch of a single lane);
 // wave 0 then sums them in ascending token order exactly as sum_key_quad /
 // sum_logits do, adds the new token, and writes the summary (global memory
 // and sh.knew / sh.enew) and the token itself.  Mirrors append_kernel.
 template <int D>
-__device__ void append_token(const FusedArgs& a, FusedSmem<D>& sh, int bh, int pos) {
+__device__ void append_token(const FusedArgs& a, FusedSmem<D>& sh, int bh, int pos, int64_t page) {
   constexpr int NQ = D / 4;
   constexpr int NO = D / 8;  // 16-byte octets per key row
   constexpr int VL = D / kWave;
@@ -85,8 +85,6 @@ __device__ void append_token(const FusedArgs& a, FusedSmem<D>& sh, int bh, int p
   const int i = pos / bs, r = pos % bs;
   const int j = r / ss;
   const int lo = j * ss;  // page-relative start of the sub-block
-  uint32_t doc;
-  const int64_t page = page_of_any(t, bh, i, doc);  // same address in every lane
   if (page < 0) {
     if (threadIdx.x == 0) flag_error(t.err);
     return;
@@ -177,15 +175,29 @@ __global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const Fused
   const int MB = t.max_blocks, CS = MB * nsub, cap = MB * bs;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
 
-  const int raw = a.seq_in[b];
   const bool want_append = a.k_new != nullptr;
+  const int c = (int)gridDim.x - 1 - (int)blockIdx.x;  // chunks last to first
+  const int s0 = c * SPG;
+  // Issued together, before any of them is needed: the length, the pages of
+  // this chunk's blocks (with an append: one lane per block in every wave,
+  // so the append needs no dependent table lookup), the group's query.
+  const int raw = a.seq_in[b];
+  const int bpc = SPG / nsub;  // blocks per chunk (<= 64)
+  int64_t spec_page = -1;
+  if (want_append && lane < bpc && c * bpc + lane < MB) {
+    uint32_t doc;
+    spec_page = page_of_any(t, bh, c * bpc + lane, doc);
+  }
+  const int dq = threadIdx.x < D ? threadIdx.x : 0;
+  const uint16_t* qh = a.q + ((int64_t)b * a.Hq + (int64_t)h * G) * D + dq;
+  uint16_t qraw[16];
+#pragma unroll
+  for (int g = 0; g < 16; ++g) qraw[g] = qh[(int64_t)min(g, G - 1) * D];
+
   const bool append = want_append && raw >= 0 && raw < cap;
   const int T = min(max(append ? raw + 1 : raw, 0), cap);
   const int nb = (T + bs - 1) / bs;
-  // chunks last to first; sT: the new token's sub-block
-  const int sT = append ? (raw / bs) * nsub + (raw % bs) / ss : -1;
-  const int c = (int)gridDim.x - 1 - (int)blockIdx.x;
-  const int s0 = c * SPG;
+  const int sT = append ? (raw / bs) * nsub + (raw % bs) / ss : -1;  // the new token's sub-block
   const bool work = s0 < nb * nsub;
   const bool lead = append && s0 <= sT && sT < s0 + SPG;
   if (threadIdx.x == 0) {
@@ -196,33 +208,34 @@ __global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const Fused
     }
   }
 
-  __syncthreads();  // have_new cleared before the append sets it
-  if (lead) append_token<D>(a, sh, bh, raw);
-
-  // the group's query (clamped, branch-free loads)
-  const int dq = threadIdx.x < D ? threadIdx.x : 0;
-  const uint16_t* qh = a.q + ((int64_t)b * a.Hq + (int64_t)h * G) * D + dq;
-  uint16_t qraw[16];
-#pragma unroll
-  for (int g = 0; g < 16; ++g) qraw[g] = qh[(int64_t)min(g, G - 1) * D];
-
   // this lane's slice of its sub-block's summary row
   const int s = s0 + w * SPW + lane % SPW;
   const int part = lane / SPW;
   f4 v[QL];
   float ev = 0.f;
-  if (work) {
+  auto load_summary = [&]() {
     const f4* p = reinterpret_cast<const f4*>(a.k_summary) + (int64_t)bh * NQ * CS + min(s, CS - 1) +
                   (int64_t)(part * QL) * CS;
 #pragma unroll
     for (int u = 0; u < QL; ++u) v[u] = __builtin_nontemporal_load(p + (int64_t)u * CS);
     ev = a.e_summary[(int64_t)bh * CS + min(s, CS - 1)];
-  }
+  };
+  // the lead loads its summaries after the append (its registers are then
+  // free), every other workgroup right away
+  if (work && !lead) load_summary();
   if (threadIdx.x < D) {
     double acc = 0;
 #pragma unroll
     for (int g = 0; g < 16; ++g) acc += g < G ? (double)bf16_to_f32(qraw[g]) : 0.0;
     sh.qbar[threadIdx.x] = acc / (double)G;
+  }
+  __syncthreads();  // have_new cleared before the append sets it
+  if (lead) {  // the page of the new token's block, from this wave's lookups
+    const int idx = raw / bs - c * bpc;
+    const int64_t page = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(spec_page >> 32), idx) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane((int)spec_page, idx));
+    append_token<D>(a, sh, bh, raw, page);
+    load_summary();
   }
   __syncthreads();  // qbar, and the append's summary
 

@@ -16,11 +16,11 @@
 // d-quad-major ([D/4][CS][4] fp32), so for each d-quad consecutive lanes read
 // consecutive 16-byte entries of consecutive sub-blocks.  L lanes (4, 2 or
 // 1, by block size) split one sub-block's quads and add their partial dots
-// with two shuffles: more, shorter non-temporal load streams per CU keep HBM
-// busier than one long stream per lane.  Products and sums
+// with in-register lane exchanges: more, shorter non-temporal load streams
+// per CU keep HBM busier than one long stream per lane.  Products and sums
 // are in float64 (qbar is exact in float64), so the only rounding of
 // consequence is the one-time fp32 rounding of the summary entries.  The
-// block max is a DPP/shuffle max over the nsub lanes of a block.  The kernel
+// block max is a DPP max over the nsub lanes of a block.  The kernel
 // is bound by HBM bandwidth: 4 * D bytes per sub-block plus 4 bytes of logit.
 
 #include "nosa_launch.hpp"
