@@ -75,10 +75,11 @@ def gpu_invariants(w, t, g: Gpu, prev: Gpu | None):
             assert gamma >= (w.k_e - len(new & ge)) / w.k - 1e-12, ("locality", gamma)
 
 
-def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=True, fused=True):
-    announce(f"trajectory {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T0={w.T0} steps={steps or w.steps} "
-             f"P={splits or w.splits} pairs={'all' if pairs is None else pairs} seed={seed} fused={fused}")
-    inp = synth.generate(w, seed)
+def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=True, fused=True, inp=None):
+    announce(f"trajectory {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T0={w.T0} k={w.k_e}/{w.k_q} "
+             f"steps={steps or w.steps} P={splits or w.splits} pairs={'all' if pairs is None else pairs} "
+             f"seed={seed} fused={fused}")
+    inp = inp if inp is not None else synth.generate(w, seed)
     sess = session(w, inp, splits=splits, fused=fused)
     pairs = pairs or [(b, h) for b in range(w.B) for h in range(w.Hkv)]
     lgs = {p: logical_pair(inp, *p) for p in pairs}
@@ -224,6 +225,83 @@ def test_fewer_blocks_than_budget():
     # nb < k_e: every block kept, no eviction
     w = WORKLOADS["tiny_nosa"].scaled(B=1, T0=100, k_e=4, k_q=4)
     run_trajectory(w, seed=9, steps=4)
+
+
+# ---------------------------------------------------------------------------
+# edge cases: exact ties, empty context, zero budgets, maximum capacity,
+# out-of-range appends
+# ---------------------------------------------------------------------------
+
+def tie_inputs(w, seed, n_distinct):
+    """Every whole block's tokens share one of n_distinct key vectors and
+    logits (by block index), so those blocks' scores tie exactly in float32
+    and in float64.  Blocks from the first partial one on (T0 // bs: the
+    tail while tokens are appended) get their own vector and logit: the
+    oracle averages per-token float64 scores, which rounds differently for a
+    partial sub-block than for a whole one, so a tail block would only
+    near-tie."""
+    inp = synth.generate(w, seed)
+    rng = np.random.default_rng(1000 + n_distinct)
+    n_blk = -(-inp.K.shape[2] // w.bs)
+    first_tail = w.T0 // w.bs
+    keys = synth.f32_to_bf16_bits(rng.standard_normal((n_distinct + n_blk, w.D)).astype(np.float32))
+    logits = rng.standard_normal(n_distinct + n_blk).astype(np.float32)
+    blk = np.arange(inp.K.shape[2]) // w.bs
+    vec = np.where(blk < first_tail, blk % n_distinct, n_distinct + blk)
+    inp.K[...] = keys[vec][None, None]
+    inp.e[...] = logits[vec][None, None]
+    return inp
+
+
+@pytest.mark.parametrize("n_distinct", [1, 3])
+def test_exact_ties_lowest_index_wins(n_distinct):
+    # ties must resolve exactly as the oracle's (score desc, index asc): no
+    # near-tie allowance is used
+    w = WORKLOADS["tiny_nosa"].scaled(B=2, Hq=8, Hkv=2, T0=1500, k_e=3, k_q=5)
+    log = run_trajectory(w, seed=20, steps=6, inp=tie_inputs(w, 20, n_distinct))
+    assert not log, log
+    w = WORKLOADS["llama3_8b_32k"].scaled(B=1, Hq=8, Hkv=2, T0=4096 + 7)
+    log = run_trajectory(w, seed=21, steps=3, inp=tie_inputs(w, 21, n_distinct))
+    assert not log, log
+
+
+def test_empty_context():
+    # no prefill: the first step appends token 0 and attends to it alone
+    run_trajectory(WORKLOADS["tiny_nosa"].scaled(B=2, Hq=4, Hkv=2, T0=0), seed=22, steps=8)
+
+
+@pytest.mark.parametrize("k_e,k_q", [(0, 6), (6, 0)])
+def test_zero_budgets(k_e, k_q):
+    w = WORKLOADS["tiny_nosa"].scaled(B=2, Hq=8, Hkv=2, T0=1500, k_e=k_e, k_q=k_q)
+    run_trajectory(w, seed=23, steps=5)
+
+
+def test_maximum_capacity():
+    # 8192 blocks of capacity (the widest selection form; the fused select +
+    # decode falls back to the two calls above 1024 blocks)
+    w = WORKLOADS["tiny_nosa"].scaled(B=1, Hq=4, Hkv=1, T0=8192 * 64 - 256 - 10, k_e=6, k_q=10)
+    assert w.max_blocks == 8192
+    run_trajectory(w, seed=24, steps=3, splits=3)
+
+
+def test_append_past_capacity_flags_and_keeps_length():
+    from block_sparse_kv_score_amd import nosa
+    w = WORKLOADS["tiny_nosa"].scaled(B=2, Hq=4, Hkv=2, T0=100)
+    announce("append past capacity: error flag, lengths unchanged")
+    inp = synth.generate(w, 25)
+    sess = session(w, inp)
+    cap = w.max_blocks * w.bs
+    full = torch.full((w.B,), cap, dtype=torch.int32, device="cuda")
+    nosa.nosa_append(sess.dims, sess.kv, sess.k_new[0], sess.v_new[0], sess.e_new[0], full, sess.k_summary,
+                     sess.e_summary)
+    torch.cuda.synchronize()
+    assert int(sess.err.item()) == 1 and full.tolist() == [cap] * w.B
+    sess.err.zero_()
+    out = torch.zeros_like(full)
+    nosa.nosa_append_score(sess.dims, sess.kv, sess.k_new[0], sess.v_new[0], sess.e_new[0], full, out,
+                           sess.k_summary, sess.e_summary, sess.q(1), sess.score_q, sess.score_e)
+    torch.cuda.synchronize()
+    assert int(sess.err.item()) == 1 and out.tolist() == [cap] * w.B
 
 
 # ---------------------------------------------------------------------------
