@@ -101,6 +101,8 @@ def cpu_baseline(w, inp, budget_s: float):
     T = w.seq_len(t)
     q = inp.q(t)
     done, elapsed = 0, 0.0
+    stage = {"score": 0.0, "select": 0.0, "swap": 0.0, "attend": 0.0}
+    scale = 1.0 / math.sqrt(w.D)
     for (b, h) in pairs:
         t0 = time.perf_counter()
         K = oracle.bf16_to_f64(inp.K[b, h, :T])
@@ -110,17 +112,38 @@ def cpu_baseline(w, inp, budget_s: float):
         rope = None
         if w.select_all and w.rope_base:
             rope = dict(q_pos=int(inp.q_pos[b]), block_start=synth.block_doc_start(w) * w.bs, base=w.rope_base)
-        oracle.decode_step_bh(qg, K, V, e, T, w.bs, w.ss, w.k_e, w.k_q, set(), [], w.splits,
-                              1.0 / math.sqrt(w.D), select_all=w.select_all, rope=rope)
+        oracle.decode_step_bh(qg, K, V, e, T, w.bs, w.ss, w.k_e, w.k_q, set(), [], w.splits, scale,
+                              select_all=w.select_all, rope=rope)
         elapsed += time.perf_counter() - t0
+        if not w.select_all:
+            # the same pair again, stage by stage through the oracle's own stage functions
+            t1 = time.perf_counter()
+            S_q = oracle.pool_block_scores(oracle.query_token_scores(qg, K), T, w.bs, w.ss)
+            E = oracle.pool_block_scores(oracle.eviction_token_scores(e), T, w.bs, w.ss)
+            t2 = time.perf_counter()
+            gamma = oracle.select_blocks(S_q, E, oracle.num_blocks(T, w.bs), w.k_e, w.k_q, set())[2]
+            t3 = time.perf_counter()
+            oracle.swap_lists([], gamma)
+            t4 = time.perf_counter()
+            for chunk in oracle.split_chunks(gamma, w.splits):
+                toks = oracle.tokens_of_blocks(chunk, T, w.bs)
+                oracle.attend(qg, K[toks], V[toks], scale)
+            toks = oracle.tokens_of_blocks(gamma, T, w.bs)
+            oracle.attend(qg, K[toks], V[toks], scale)
+            t5 = time.perf_counter()
+            for k_, dt in zip(stage, (t2 - t1, t3 - t2, t4 - t3, t5 - t4)):
+                stage[k_] += dt
         done += 1
         if elapsed >= budget_s:
             break
     step_s = elapsed / done * len(pairs)
-    return {"value": w.B / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {len(pairs)} (b,h) pairs of decode step 1 ({elapsed:.1f} s), "
-                      f"scaled to the batch; float64 NumPy, BLAS threads = {threads}",
-            "sec_per_step": step_s}
+    out = {"value": w.B / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{done} of {len(pairs)} (b,h) pairs of decode step 1 ({elapsed:.1f} s), "
+                     f"scaled to the batch; float64 NumPy, BLAS threads = {threads}",
+           "sec_per_step": step_s}
+    if not w.select_all:
+        out["stage_sec_per_step"] = {k_: round(v / done * len(pairs), 4) for k_, v in stage.items()}
+    return out
 
 
 def main(argv=None) -> int:
