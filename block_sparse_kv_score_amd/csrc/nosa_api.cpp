@@ -244,6 +244,41 @@ nosa_status nosa_select_decode(const nosa_dims* dims, const nosa_kv* kv, const u
                                              counters, o, m, l, stream));
 }
 
+nosa_status nosa_host_device_pointer(const void* host_ptr, void** device_ptr) {
+  if (!host_ptr || !device_ptr) return NOSA_ERR_ARG;
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, const_cast<void*>(host_ptr), 0) != hipSuccess || !d) {
+    (void)hipGetLastError();  // not pinned and mapped: leave no sticky error behind
+    return NOSA_ERR_ARG;
+  }
+  *device_ptr = d;
+  return NOSA_OK;
+}
+
+nosa_status nosa_retrieve(const nosa_dims* dims, const nosa_kv* host_kv, uint16_t* dev_k_pages,
+                          uint16_t* dev_v_pages, float* dev_e_pages, int32_t slots, int32_t* resident,
+                          int32_t* slot_owner, const int32_t* load, const int32_t* load_count, const int32_t* evict,
+                          const int32_t* evict_count, int32_t cap, const int32_t* seq_lens, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if ((st = check_kv(dims, host_kv, true)) != NOSA_OK) return st;
+  if (!dev_k_pages || !dev_v_pages || !dev_e_pages || !resident || !slot_owner || !seq_lens) return NOSA_ERR_ARG;
+  if (!load || !load_count || !evict || !evict_count) return NOSA_ERR_ARG;
+  if (!aligned16(dev_k_pages) || !aligned16(dev_v_pages) || !aligned16(dev_e_pages)) return NOSA_ERR_ARG;
+  if (slots < 1 || slots > nosa::kMaxRetrieveSlots || cap < 1) return NOSA_ERR_ARG;
+  if ((int64_t)dims->batch * dims->n_kv_heads * slots > ((int64_t)1 << 31) - 1) return NOSA_ERR_UNSUPPORTED;
+  // the host pools are read through their device mapping; memory that is
+  // not pinned and mapped is refused here, never dereferenced
+  void *hk = nullptr, *hv = nullptr, *he = nullptr;
+  if (nosa_host_device_pointer(host_kv->k_pages, &hk) != NOSA_OK) return NOSA_ERR_ARG;
+  if (nosa_host_device_pointer(host_kv->v_pages, &hv) != NOSA_OK) return NOSA_ERR_ARG;
+  if (nosa_host_device_pointer(host_kv->e_pages, &he) != NOSA_OK) return NOSA_ERR_ARG;
+  if (!aligned16(hk) || !aligned16(hv) || !aligned16(he)) return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_retrieve(*dims, *host_kv, hk, hv, he, dev_k_pages, dev_v_pages, dev_e_pages, slots,
+                                        resident, slot_owner, load, load_count, evict, evict_count, cap, seq_lens,
+                                        stream));
+}
+
 nosa_status nosa_combine(const nosa_dims* dims, int32_t num_splits, const float* part_o, const float* part_m,
                          const float* part_l, float* o, float* m, float* l, hipStream_t stream) {
   nosa_status st = check_dims(dims);

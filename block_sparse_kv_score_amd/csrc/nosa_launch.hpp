@@ -11,6 +11,8 @@
 
 namespace nosa {
 
+constexpr int kMaxRetrieveSlots = 1024;  // resident slots per (b, h) in the host-tier retrieve
+
 Table make_table(const nosa_dims& d, const nosa_kv& kv);
 
 hipError_t launch_prefill(const nosa_dims& d, const nosa_kv& kv, const uint16_t* k_src,
@@ -61,6 +63,12 @@ hipError_t launch_select_decode(const nosa_dims& d, const uint16_t* q, const nos
                                 int32_t* load_count, int32_t* evict, int32_t* evict_count, int32_t num_splits,
                                 float sm_scale, float* part_o, float* part_m, float* part_l, int32_t* counters,
                                 float* o, float* m, float* l, hipStream_t stream);
+
+hipError_t launch_retrieve(const nosa_dims& d, const nosa_kv& host_kv, const void* host_k, const void* host_v,
+                           const void* host_e, uint16_t* dev_k, uint16_t* dev_v, float* dev_e, int32_t slots,
+                           int32_t* resident, int32_t* slot_owner, const int32_t* load, const int32_t* load_count,
+                           const int32_t* evict, const int32_t* evict_count, int32_t cap, const int32_t* seq_lens,
+                           hipStream_t stream);
 
 hipError_t launch_combine(const nosa_dims& d, int32_t num_splits, const float* part_o,
                           const float* part_m, const float* part_l, float* o, float* m, float* l,

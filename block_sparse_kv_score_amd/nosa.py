@@ -38,6 +38,8 @@ ENTRY_POINTS = [
     "nosa_sparse_decode_combine",
     "nosa_select_decode",
     "nosa_combine",
+    "nosa_retrieve",
+    "nosa_host_device_pointer",
     "nosa_status_string",
 ]
 
@@ -102,6 +104,8 @@ _SIGNATURES = {
     "nosa_select_decode": [_DIMS, _KV, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P,
                            _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P],
     "nosa_combine": [_DIMS, _I32, _P, _P, _P, _P, _P, _P, _P],
+    "nosa_retrieve": [_DIMS, _KV, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P],
+    "nosa_host_device_pointer": [_P, ctypes.POINTER(ctypes.c_void_p)],
 }
 
 
@@ -165,13 +169,21 @@ def make_dims(B, Hq, Hkv, D, bs, ss, max_blocks) -> nosa_dims:
 
 def make_kv(k_pages, v_pages, e_pages, kind, *, table=None, directory=None, segments=None,
             seg_log2=0, blocks_log2=0, packed=None, q_pos=None, rope_base=0.0,
-            err_flags=None) -> nosa_kv:
+            err_flags=None, page_ptrs=None) -> nosa_kv:
     """Build the nosa_kv descriptor.  The tensors must outlive every call
-    that receives the descriptor."""
+    that receives the descriptor.  page_ptrs: (k, v, e) raw addresses used
+    instead of the page tensors' device addresses (host pools: their host
+    addresses, or their device mapping from nosa_host_device_pointer)."""
     kv = nosa_kv()
-    kv.k_pages = _dev(k_pages, "k_pages", _BF16_LIKE)
-    kv.v_pages = _dev(v_pages, "v_pages", _BF16_LIKE)
-    kv.e_pages = _dev(e_pages, "e_pages", (torch.float32,))
+    if page_ptrs is None:
+        kv.k_pages = _dev(k_pages, "k_pages", _BF16_LIKE)
+        kv.v_pages = _dev(v_pages, "v_pages", _BF16_LIKE)
+        kv.e_pages = _dev(e_pages, "e_pages", (torch.float32,))
+    else:
+        for t, n in ((k_pages, "k_pages"), (v_pages, "v_pages"), (e_pages, "e_pages")):
+            if t.is_cuda or not t.is_pinned() or not t.is_contiguous():
+                raise ValueError(f"{n}: a host pool must be a contiguous pinned CPU tensor")
+        kv.k_pages, kv.v_pages, kv.e_pages = (ctypes.c_void_p(int(x)) for x in page_ptrs)
     kv.num_pages = int(k_pages.shape[0])
     kv.kind = int(kind)
     kv.table = _dev(table, "table", (torch.int32,), optional=True)
@@ -317,6 +329,30 @@ def nosa_select_decode(dims, kv, q, score_q, score_e, seq_lens, k_e, k_q, evicte
           _dev(part_m, "part_m", (torch.float32,)), _dev(part_l, "part_l", (torch.float32,)),
           _dev(counters, "counters", (torch.int32,)), _dev(o, "o", (torch.float32,)),
           _dev(m, "m", (torch.float32,)), _dev(l, "l", (torch.float32,)), _stream(stream))
+
+
+def nosa_host_device_pointer(t: torch.Tensor) -> int:
+    """Device address of a pinned host tensor."""
+    if t.is_cuda or not t.is_pinned():
+        raise ValueError("a pinned CPU tensor is required")
+    out = ctypes.c_void_p()
+    _call("nosa_host_device_pointer", ctypes.c_void_p(t.data_ptr()), ctypes.byref(out))
+    return int(out.value)
+
+
+def nosa_retrieve(dims, host_kv, dev_k, dev_v, dev_e, slots, resident, slot_owner, load, load_count, evict,
+                  evict_count, seq_lens, stream=None):
+    """host_kv: descriptor whose page pointers are the host pools' HOST
+    addresses (make_kv(..., page_ptrs=(t.data_ptr() ...)))."""
+    cap = int(load.shape[-1])
+    if int(evict.shape[-1]) != cap:
+        raise ValueError("load and evict must have the same last dimension")
+    _call("nosa_retrieve", ctypes.byref(dims), ctypes.byref(host_kv), _dev(dev_k, "dev_k", _BF16_LIKE),
+          _dev(dev_v, "dev_v", _BF16_LIKE), _dev(dev_e, "dev_e", (torch.float32,)), int(slots),
+          _dev(resident, "resident", (torch.int32,)), _dev(slot_owner, "slot_owner", (torch.int32,)),
+          _dev(load, "load", (torch.int32,)), _dev(load_count, "load_count", (torch.int32,)),
+          _dev(evict, "evict", (torch.int32,)), _dev(evict_count, "evict_count", (torch.int32,)), cap,
+          _dev(seq_lens, "seq_lens", (torch.int32,)), _stream(stream))
 
 
 def nosa_combine(dims, num_splits, part_o, part_m, part_l, o, m, l, stream=None):

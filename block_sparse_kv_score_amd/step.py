@@ -18,6 +18,12 @@ capacity -- nosa_select_swap then nosa_sparse_decode_combine; with every
 block selected: nosa_swap_diff, then the fused decode).  The fused launches
 write the new lengths and the new eviction bitmap to the other of two
 buffers, so `seq_lens` and `evicted` name the current ones.
+
+With `offload` the whole paged cache lives in pinned host memory and HBM
+keeps `cap` resident pages per (b, h) (the host tier): the step is
+nosa_append_score (into the host pages), nosa_select_swap, nosa_retrieve
+(the swap lists move pages into the resident slots) and
+nosa_sparse_decode_combine over the resident pages.
 """
 
 from __future__ import annotations
@@ -44,9 +50,13 @@ class DecodeSession:
     selection state and step outputs."""
 
     def __init__(self, w: Workload, inp: Inputs, splits: int | None = None, device: str = "cuda",
-                 poison: bool = True, stream: torch.cuda.Stream | None = None, fused: bool = True):
+                 poison: bool = True, stream: torch.cuda.Stream | None = None, fused: bool = True,
+                 offload: bool = False):
         self.w, self.inp = w, inp
         self.fused = fused
+        self.offload = offload
+        if offload and (w.select_all or w.table == TABLE_PACKED_ROPE):
+            raise ValueError("the host tier is built for selecting workloads with flat or two-level tables")
         self.P = int(splits or w.splits)
         self.dev = torch.device(device)
         self.stream = stream
@@ -72,10 +82,7 @@ class DecodeSession:
         else:
             self.packed = _i32(inp.packed).to(dev)
             self.q_pos = torch.from_numpy(inp.q_pos).to(dev)
-        self.kv = nosa.make_kv(self.k_pages, self.v_pages, self.e_pages, _KIND[w.table],
-                               table=self.table, directory=self.directory, segments=self.segments,
-                               seg_log2=w.seg_log2, blocks_log2=w.blocks_log2, packed=self.packed,
-                               q_pos=self.q_pos, rope_base=w.rope_base, err_flags=self.err)
+        self.kv = nosa.make_kv(self.k_pages, self.v_pages, self.e_pages, _KIND[w.table], **self._table_kw())
 
         self.seq_bufs = [torch.full((B,), w.T0, dtype=torch.int32, device=dev) for _ in range(2)]
         self.seq_lens = self.seq_bufs[0]
@@ -122,6 +129,44 @@ class DecodeSession:
             self.all_sel = torch.from_numpy(sel).to(dev)
             self.all_count = torch.full((B, Hkv), nb, dtype=torch.int32, device=dev)
         self.prefill()
+        if offload:
+            self._init_offload(poison)
+
+    def _table_kw(self) -> dict:
+        w = self.w
+        return dict(table=self.table, directory=self.directory, segments=self.segments, seg_log2=w.seg_log2,
+                    blocks_log2=w.blocks_log2, packed=self.packed, q_pos=self.q_pos, rope_base=w.rope_base,
+                    err_flags=self.err)
+
+    def _init_offload(self, poison: bool):
+        """Move the paged cache to pinned host memory; keep `cap` resident
+        pages per (b, h) in HBM."""
+        w = self.w
+        self.host_k = torch.empty(self.k_pages.shape, dtype=torch.int16, pin_memory=True)
+        self.host_v = torch.empty(self.v_pages.shape, dtype=torch.int16, pin_memory=True)
+        self.host_e = torch.empty(self.e_pages.shape, dtype=torch.float32, pin_memory=True)
+        self.host_k.copy_(self.k_pages)
+        self.host_v.copy_(self.v_pages)
+        self.host_e.copy_(self.e_pages)
+        torch.cuda.synchronize()
+        del self.k_pages, self.v_pages, self.e_pages
+        hosts = (self.host_k, self.host_v, self.host_e)
+        kw = self._table_kw()
+        # the retrieve reads the host pools by their host addresses; the
+        # append writes them (and reads older tokens) through their device mapping
+        self.host_kv = nosa.make_kv(*hosts, _KIND[w.table], page_ptrs=[t.data_ptr() for t in hosts], **kw)
+        self.kv = nosa.make_kv(*hosts, _KIND[w.table], page_ptrs=[nosa.nosa_host_device_pointer(t) for t in hosts],
+                               **kw)
+        self.slots = self.cap
+        n = w.B * w.Hkv * self.slots
+        fill = float("nan") if poison else 0.0
+        self.k_pages = torch.full((n, w.bs * w.D), BF16_NAN if poison else 0, dtype=torch.int16, device=self.dev)
+        self.v_pages = torch.full_like(self.k_pages, BF16_NAN if poison else 0)
+        self.e_pages = torch.full((n, w.bs), fill, dtype=torch.float32, device=self.dev)
+        self.resident = torch.full((w.B, w.Hkv, w.max_blocks), -1, dtype=torch.int32, device=self.dev)
+        self.slot_owner = torch.full((w.B, w.Hkv, self.slots), -1, dtype=torch.int32, device=self.dev)
+        self.dev_kv = nosa.make_kv(self.k_pages, self.v_pages, self.e_pages, nosa.NOSA_TABLE_FLAT,
+                                   table=self.resident, err_flags=self.err)
 
     # ------------------------------------------------------------------
     def prefill(self):
@@ -178,8 +223,14 @@ class DecodeSession:
                               self.evicted, self.sel, self.sel_count, self.prev, self.prev_count,
                               self.load, self.load_count, self.evict, self.evict_count, self.stream)
 
+    def retrieve(self):
+        nosa.nosa_retrieve(self.dims, self.host_kv, self.k_pages, self.v_pages, self.e_pages, self.slots,
+                           self.resident, self.slot_owner, self.load, self.load_count, self.evict,
+                           self.evict_count, self.seq_lens, self.stream)
+
     def decode_combine(self, t: int):
-        nosa.nosa_sparse_decode_combine(self.dims, self.q(t), self.kv, self.sel, self.sel_count, self.seq_lens,
+        kv = self.dev_kv if self.offload else self.kv
+        nosa.nosa_sparse_decode_combine(self.dims, self.q(t), kv, self.sel, self.sel_count, self.seq_lens,
                                         self.P, self.w.sm_scale, self.part_o, self.part_m, self.part_l,
                                         self.counters, self.o, self.m, self.l, self.stream)
 
@@ -216,7 +267,12 @@ class DecodeSession:
         t = self.step_index + 1 if t is None else t
         w = self.w
         self.use_buffers(t)
-        if self.fused:
+        if self.offload:
+            self.append_score(t)
+            self.select_swap()
+            self.retrieve()
+            self.decode_combine(t)
+        elif self.fused:
             if w.select_all:
                 if w.append:
                     self.append(t)

@@ -292,6 +292,43 @@ nosa_status nosa_select_decode(const nosa_dims* dims, const nosa_kv* kv, const u
                                int32_t num_splits, float sm_scale, float* part_o, float* part_m, float* part_l,
                                int32_t* counters, float* o, float* m, float* l, hipStream_t stream);
 
+/* Retrieve: the host tier [NOSA, Methodology 2 (NOSI): block-sized KV
+ * units, set differences drive block swapping, a host-to-device transfer
+ * kernel over unified virtual addressing; SPIN 2.A: Offload / Retrieve as
+ * system-managed operations; 2.B: per-head pages].
+ *   host_kv: the whole paged cache in pinned host memory: k_pages, v_pages,
+ *     e_pages are HOST pointers (allocated pinned and mapped, e.g. by
+ *     hipHostMalloc); its table / directory / segments / packed words map
+ *     logical blocks to host pages as in nosa_kv (device pointers).
+ *   dev_k_pages, dev_v_pages, dev_e_pages: the resident pools in HBM,
+ *     B * Hkv * slots pages, same page layouts; device page bh * slots + s
+ *     is slot s of pair bh (bh = b * Hkv + h).
+ *   resident int32 [B][Hkv][max_blocks]: device page of each resident
+ *     logical block, -1 elsewhere (the flat table a decode over the
+ *     resident pools takes); slot_owner int32 [B][Hkv][slots]: logical
+ *     block in each slot, -1 for a free slot.  Both all -1 before the first
+ *     call; the library keeps them consistent.
+ *   load / evict (+ counts), cap: the swap lists of this step (as produced
+ *     by nosa_swap_diff or nosa_select_swap).
+ *   seq_lens int32 [B]: lengths after this step's append.
+ * Per pair: every evicted block frees its slot; the j-th loaded block takes
+ * the j-th free slot in ascending slot order and its K, V and E pages are
+ * copied from host memory into it (zero-copy reads by the kernel); the
+ * resident block holding the last token is copied again (an append writes
+ * into the host pool).  More loads than free slots set the error flag and
+ * the excess blocks stay out.  1 <= slots <= 1024.                        */
+nosa_status nosa_retrieve(const nosa_dims* dims, const nosa_kv* host_kv,
+                          uint16_t* dev_k_pages, uint16_t* dev_v_pages, float* dev_e_pages, int32_t slots,
+                          int32_t* resident, int32_t* slot_owner,
+                          const int32_t* load, const int32_t* load_count,
+                          const int32_t* evict, const int32_t* evict_count, int32_t cap,
+                          const int32_t* seq_lens, hipStream_t stream);
+
+/* The device address of pinned, mapped host memory (to pass host pools to
+ * the calls that read or write pages through a kernel, e.g. an append into
+ * the host tier).  NOSA_ERR_ARG for memory that is not pinned and mapped. */
+nosa_status nosa_host_device_pointer(const void* host_ptr, void** device_ptr);
+
 /* Attention, combine [NOVITA: return rowmax and l with O]:
  *   m = max_p part_m (over p with part_l > 0), l = sum_p part_l e^(part_m - m),
  *   O = sum_p part_l e^(part_m - m) part_o / l;  all empty: O = 0, m = -inf, l = 0.

@@ -141,6 +141,14 @@ def test_host_checks_reject_bad_arguments():
     rope.k_pages = rope.v_pages = rope.e_pages = ctypes.c_void_p(4096)
     rope.num_pages, rope.kind, rope.packed = 10, nosa.NOSA_TABLE_PACKED_ROPE, ctypes.c_void_p(4096)
     assert sdec(rope) == nosa.NOSA_ERR_UNSUPPORTED
+    # host-tier retrieve: slot count bounds, required lists
+    def retr(slots, load=fake):
+        return L.nosa_retrieve(D(d), D(kv), P(4096), P(8192), P(12288), slots, fake, fake, load, fake, fake, fake,
+                               8, fake, None)
+    assert retr(0) == nosa.NOSA_ERR_ARG
+    assert retr(1025) == nosa.NOSA_ERR_ARG
+    assert retr(8, load=None) == nosa.NOSA_ERR_ARG
+    assert L.nosa_host_device_pointer(None, ctypes.byref(ctypes.c_void_p())) == nosa.NOSA_ERR_ARG
     # fused append + score
     def ascore(k_new, seq_in, seq_out, v_new=None):
         v = v_new if v_new is not None else (fake if k_new else None)

@@ -305,6 +305,87 @@ def test_append_past_capacity_flags_and_keeps_length():
 
 
 # ---------------------------------------------------------------------------
+# host tier: pages in pinned host memory, resident slots in HBM
+# ---------------------------------------------------------------------------
+
+def host_page(w, inp, b, h, i):
+    """Page of logical block i of pair (b, h) in the session's page pools."""
+    if inp.directory is None:
+        return int(inp.pages[b, h, i])
+    key = ((b * w.Hkv + h) << w.blocks_log2) | i
+    seg = int(inp.directory[key >> w.seg_log2])
+    return int(inp.segments.reshape(-1)[(seg << w.seg_log2) | (key & ((1 << w.seg_log2) - 1))])
+
+
+OFFLOAD_CASES = [
+    ("tiny_nosa", {}, 2),
+    ("llama3_8b_32k", dict(B=2, Hq=8, Hkv=2, T0=4096 + 61), 3),
+    ("llama31_70b_256k", dict(B=2, Hq=16, Hkv=2, T0=16384 + 100, dir_entries=64), 4),
+]
+
+
+@pytest.mark.parametrize("name,scale,splits", OFFLOAD_CASES, ids=[c[0] for c in OFFLOAD_CASES])
+def test_offload_equals_resident(name, scale, splits):
+    """The host-tier step gives the same bits as the all-in-HBM step, the
+    resident set is exactly the selection, and every resident slot holds
+    its block's pages."""
+    w = WORKLOADS[name].scaled(**scale) if scale else WORKLOADS[name]
+    announce(f"host tier vs resident {name} {scale} P={splits}")
+    inp = synth.generate(w, 30)
+    a = session(w, inp, splits=splits, offload=True)
+    s = session(w, inp, splits=splits)
+    for t in range(1, min(w.steps, 6) + 1):
+        a.step(t)
+        s.step(t)
+        torch.cuda.synchronize()
+        assert int(a.err.item()) == 0 and int(s.err.item()) == 0
+        for n in ["sel_count", "evicted", "load_count", "evict_count", "part_o", "part_m", "part_l", "o", "m", "l",
+                  "seq_lens", "k_summary", "e_summary", "score_q", "score_e"]:
+            x, y = getattr(a, n), getattr(s, n)
+            if x.dtype == torch.float32:
+                x, y = x.view(torch.int32), y.view(torch.int32)
+            assert torch.equal(x, y), (n, t)
+        res = a.resident.cpu().numpy()
+        own = a.slot_owner.cpu().numpy()
+        sel = a.sel.cpu().numpy()
+        cnt = a.sel_count.cpu().numpy()
+        dk, dv = a.k_pages.cpu(), a.v_pages.cpu()
+        sk, sv = s.k_pages.cpu(), s.v_pages.cpu()
+        assert torch.equal(a.host_k, sk) and torch.equal(a.host_v, sv)  # the host pools took every append
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                bh = b * w.Hkv + h
+                chosen = sel[b, h, :cnt[b, h]].tolist()
+                assert set(np.nonzero(res[b, h] >= 0)[0].tolist()) == set(chosen), (t, b, h)
+                for x in chosen:
+                    dp = int(res[b, h, x])
+                    assert bh * a.slots <= dp < (bh + 1) * a.slots and own[b, h, dp - bh * a.slots] == x
+                    hp = host_page(w, inp, b, h, x)
+                    assert torch.equal(dk[dp], sk[hp]) and torch.equal(dv[dp], sv[hp]), (t, b, h, x)
+                assert int((own[b, h] >= 0).sum()) == len(chosen)
+
+
+def test_offload_more_loads_than_slots_flags():
+    from block_sparse_kv_score_amd import nosa
+    w = WORKLOADS["tiny_nosa"].scaled(B=1, Hq=4, Hkv=1, T0=1500)
+    announce("host tier: more loads than free slots sets the error flag")
+    inp = synth.generate(w, 31)
+    a = session(w, inp, offload=True)
+    t = 1
+    a.use_buffers(t)
+    a.append_score(t)
+    a.select_swap()
+    torch.cuda.synchronize()
+    n_load = int(a.load_count.item())
+    small = torch.full((1, 1, max(n_load - 2, 1)), -1, dtype=torch.int32, device="cuda")
+    nosa.nosa_retrieve(a.dims, a.host_kv, a.k_pages, a.v_pages, a.e_pages, max(n_load - 2, 1), a.resident,
+                       small, a.load, a.load_count, a.evict, a.evict_count, a.seq_lens)
+    torch.cuda.synchronize()
+    assert n_load > 2 and int(a.err.item()) == 1
+    assert int((a.resident >= 0).sum().item()) == max(n_load - 2, 1)
+
+
+# ---------------------------------------------------------------------------
 # full sizes, launch configuration of the benchmark
 # ---------------------------------------------------------------------------
 
