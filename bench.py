@@ -36,6 +36,7 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBPS = 8000.0
+PEAK_HOST_LINK_GBPS = 64.0  # PCIe 5.0 x16, one direction
 METRIC = "sparse decode attn tokens/s + achieved HBM GB/s (% peak), 8B shape @32K"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_llama3_8b_32k.json")
 CSRC = os.path.join(ROOT, "block_sparse_kv_score_amd", "csrc")
@@ -54,6 +55,8 @@ def parse(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="time the six separate entry points")
+    ap.add_argument("--offload", action="store_true",
+                    help="host tier: pages in pinned host memory, resident slots in HBM, nosa_retrieve per step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with one plain 1 GiB device copy, a known-size kernel for counter calibration")
     return ap.parse_args(argv)
@@ -166,7 +169,8 @@ def main(argv=None) -> int:
         raise SystemExit(f"at most {w.n_append} appended tokens: lower --steps/--warmup")
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = synth.generate(w, args.seed)
-    sess = DecodeSession(w, inp, splits=args.splits, poison=False, fused=not args.unfused)
+    sess = DecodeSession(w, inp, splits=args.splits, poison=False, fused=not args.unfused or args.offload,
+                         offload=args.offload)
     stream = torch.cuda.current_stream()
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
 
@@ -202,7 +206,9 @@ def main(argv=None) -> int:
 
     # pass 2: cold steps with an event between every launch
     fused = sess.fused
-    if fused:
+    if sess.offload:
+        names = ["append_score", "select_swap", "retrieve", "decode_combine"]
+    elif fused:
         if w.select_all:
             names = (["append"] if w.append else []) + ["swap_diff", "decode_combine"]
         elif sess.select_decode_ok:
@@ -214,6 +220,8 @@ def main(argv=None) -> int:
         names += ["swap_diff", "decode", "combine"]
     dec_name = "select_decode" if "select_decode" in names else ("decode_combine" if fused else "decode")
     per = {n: [] for n in names}
+    page_bytes = 2 * w.bs * w.D * 2 + w.bs * 4  # K + V + E of one page
+    retrieved = []  # bytes the retrieve copied, per step
     for k in range(K):
         flush()
         t = next_t()
@@ -235,6 +243,8 @@ def main(argv=None) -> int:
                 sess.decode_combine(t)
             elif n == "select_decode":
                 sess.select_decode(t)
+            elif n == "retrieve":
+                sess.retrieve()
             elif n == "swap_diff":
                 sess.swap_diff()
             elif n == "decode":
@@ -246,6 +256,10 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         for j, n in enumerate(names):
             per[n].append(evs[j].elapsed_time(evs[j + 1]))
+        if sess.offload:  # loaded pages + the resident tail pages copied again
+            T = w.seq_len(t)
+            tail = sess.resident[:, :, (T - 1) // w.bs]
+            retrieved.append(page_bytes * (int(sess.load_count.sum().item()) + int((tail >= 0).sum().item())))
     kernels_us = {n: float(np.mean(v) * 1e3) for n, v in per.items()}
 
     # pass 3: warm, back to back
@@ -275,6 +289,20 @@ def main(argv=None) -> int:
                 "kernel": {"select_decode": "nosa_select_decode", "decode_combine": "nosa_sparse_decode_combine",
                            "decode": "nosa_sparse_decode"}[dec_name] + " (decode_kernel)",
                 "algorithmic_bytes_per_launch": int(kvb), "avg_launch_us": round(kernels_us[dec_name], 2)}
+    offload = None
+    if sess.offload:
+        # the dominant launch is the retrieve, bound by the host link
+        rb = float(np.mean(retrieved))
+        r_gbps = rb / (kernels_us["retrieve"] / 1e6) / 1e9
+        roofline = {"bound": "host_link", "achieved": round(r_gbps, 2), "peak": PEAK_HOST_LINK_GBPS, "unit": "GB/s",
+                    "frac": round(r_gbps / PEAK_HOST_LINK_GBPS, 4), "traffic": None,
+                    "kernel": "nosa_retrieve (retrieve_kernel)", "algorithmic_bytes_per_launch": int(rb),
+                    "avg_launch_us": round(kernels_us["retrieve"], 2)}
+        offload = {"host_pool_bytes": int(sess.host_k.numel() * 2 * 2 + sess.host_e.numel() * 4),
+                   "resident_pool_bytes": int(sess.k_pages.numel() * 2 * 2 + sess.e_pages.numel() * 4),
+                   "resident_slots_per_pair": sess.slots, "retrieve_bytes_per_step": int(rb),
+                   "pages_per_pair_per_step": round(rb / page_bytes / (w.B * w.Hkv), 2),
+                   "host_link_gbps": round(r_gbps, 2)}
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -290,7 +318,8 @@ def main(argv=None) -> int:
         cpu = cpu_baseline(w, inp, args.cpu_seconds)
 
     out = {
-        "metric": METRIC if w.name == "llama3_8b_32k" else f"sparse decode attn tokens/s ({w.name})",
+        "metric": (METRIC if w.name == "llama3_8b_32k" else f"sparse decode attn tokens/s ({w.name})")
+        + (" [host tier: pages in pinned host memory]" if sess.offload else ""),
         "value": round(w.B / t_step, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -304,7 +333,8 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
                    "context": w.T0, "block": w.bs, "sub_block": w.ss, "k_e": w.k_e, "k_q": w.k_q,
-                   "splits": sess.P, "table": w.table, "fused": fused, "parallelism": "single GPU"},
+                   "splits": sess.P, "table": w.table, "fused": fused, "offload": sess.offload,
+                   "parallelism": "single GPU"},
         "hbm_gbps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": int(total_bytes),
@@ -314,6 +344,7 @@ def main(argv=None) -> int:
         "wall_ms_per_step_incl_flush": round(wall_cold / K * 1e3, 4),
         "kernels_us": {k: round(v, 2) for k, v in kernels_us.items()},
         "roofline": roofline,
+        "offload": offload,
         "cpu_baseline": cpu,
         "seed": args.seed,
     }

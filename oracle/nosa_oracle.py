@@ -23,7 +23,8 @@ Sources (web pages; cited by title and section):
         swapping).
 [SPIN]  "Unifying Sparse Attention with Hierarchical Memory for Scalable
         Long-Context LLM Serving" summary (gist.science, 2604.26837),
-        section 2.A (five-operation pipeline), 2.B (per-head physical pages),
+        section 2.A (five-operation pipeline, including Offload and
+        Retrieve), 2.B (per-head physical pages),
         2.C (two-level index).
 [LAZY]  "LazyAttention" technical summary (gist.science, 2606.04302),
         "Technical implementation -- 2. Decoding" and "Mathematical
@@ -40,7 +41,8 @@ Pinning status: every function here is pinned by the CPU tests in
 invariants) except the selection *semantics* choices marked READING, whose
 agreement with the GPU is agreement on the reading: parity unpinned beyond
 the reading for those choices (disjoint budgets, initial state, new-block
-candidacy, no forced local window, tie order).
+candidacy, no forced local window, tie order, slot placement of the host
+tier).
 """
 
 from __future__ import annotations
@@ -61,6 +63,7 @@ __all__ = [
     "top_by_score",
     "select_blocks",
     "swap_lists",
+    "place_blocks",
     "tokens_of_blocks",
     "split_chunks",
     "attend",
@@ -200,6 +203,32 @@ def swap_lists(prev: Iterable[int], cur: Iterable[int]):
     both ascending."""
     p, c = set(int(x) for x in prev), set(int(x) for x in cur)
     return sorted(c - p), sorted(p - c)
+
+
+def place_blocks(owner: list[int], drop: Iterable[int], load: Iterable[int]):
+    """Resident slots of one (b, h) pair after a block swap, for the host
+    tier where HBM holds a fixed number of page slots per pair [NOSA, NOSI
+    memory layout: set differences drive block swapping; SPIN 2.A: Offload
+    and Retrieve move pages between host memory and the GPU].
+
+    owner: owner[s] is the block held by slot s, or -1 for a free slot.
+    Every slot holding a dropped block is freed; then the blocks to load
+    take free slots.
+
+    READING: the pages fix which blocks move, not where they land.  Here
+    the j-th block of the load list takes the j-th free slot in ascending
+    slot order (counted after the drops), so placement is deterministic.
+
+    Returns (new_owner, placed): loads past the last free slot are not
+    placed (placed < len(load) is a capacity error for the caller).
+    """
+    dropped = set(int(x) for x in drop)
+    new = [-1 if int(x) in dropped else int(x) for x in owner]
+    free = [s for s, x in enumerate(new) if x < 0]
+    load = [int(x) for x in load]
+    for s, x in zip(free, load):
+        new[s] = x
+    return new, min(len(free), len(load))
 
 
 # ---------------------------------------------------------------------------

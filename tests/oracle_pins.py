@@ -244,6 +244,60 @@ def check_swap_lists(O, seed=7):
         assert load == sorted(load) and drop == sorted(drop)
 
 
+def check_place_blocks(O, seed=8):
+    """Host-tier slot placement: a worked example by hand, brute-force
+    checks of the placement rule on random slot states, and a selection
+    trajectory in which the resident set always equals the selection."""
+    # slots [5, -, 2, 7]; drop 2; load 1 then 9 -> free slots 1, 2
+    assert O.place_blocks([5, -1, 2, 7], [2], [1, 9]) == ([5, 1, 9, 7], 2)
+    # dropping a block that is not resident changes nothing
+    assert O.place_blocks([4, -1], [6], [3]) == ([4, 3], 1)
+    # more loads than free slots: the extra ones are not placed
+    assert O.place_blocks([0, -1, -1], [], [3, 4, 5]) == ([0, 3, 4], 2)
+    rng = np.random.default_rng(seed)
+    for _ in range(300):
+        RS = int(rng.integers(1, 12))
+        pool = rng.permutation(40)
+        n_res = int(rng.integers(0, RS + 1))
+        owner = [-1] * RS
+        for s, x in zip(rng.permutation(RS)[:n_res], pool[:n_res]):
+            owner[int(s)] = int(x)
+        resident = [x for x in owner if x >= 0]
+        drop = [x for x in resident if rng.random() < 0.4] + [int(x) for x in pool[30:32]]
+        load = [int(x) for x in pool[n_res:n_res + int(rng.integers(0, RS + 2))]]
+        new, placed = O.place_blocks(owner, drop, load)
+        kept = set(resident) - set(drop)
+        free_after_drop = sorted(s for s in range(RS) if owner[s] < 0 or owner[s] in set(drop))
+        assert placed == min(len(load), len(free_after_drop))
+        for s in range(RS):  # kept blocks never move
+            if owner[s] in kept:
+                assert new[s] == owner[s]
+        assert set(x for x in new if x >= 0) == kept | set(load[:placed])
+        assert len([x for x in new if x >= 0]) == len(kept) + placed
+        # brute force over the slots: every free slot below a loaded one is
+        # taken by an earlier load, and loads land in list order
+        slot_of = {x: s for s, x in enumerate(new) if x >= 0}
+        used = [slot_of[x] for x in load[:placed]]
+        assert used == sorted(used)
+        for s in free_after_drop:
+            if used and s < used[-1]:
+                assert s in used
+    # along a dual-selection trajectory with as many slots as the budget,
+    # the swap lists keep the resident set equal to the selection
+    nb, k_e, k_q = 40, 6, 4
+    owner, evicted, prev = [-1] * (k_e + k_q), set(), []
+    for t in range(25):
+        nbt = nb + t // 3
+        S_q = rng.standard_normal(nbt)
+        E = rng.standard_normal(nbt)
+        _, _, g, evicted = O.select_blocks(S_q, E, nbt, k_e, k_q, evicted)
+        load, drop = O.swap_lists(prev, g)
+        owner, placed = O.place_blocks(owner, drop, load)
+        assert placed == len(load)
+        assert sorted(x for x in owner if x >= 0) == g
+        prev = g
+
+
 # ---------------------------------------------------------------------------
 # rotary embedding and the deferred (lazy) rotation
 # ---------------------------------------------------------------------------
@@ -357,7 +411,7 @@ ALL_CHECKS = [
     check_attend_vs_sdpa, check_merge_vs_sdpa, check_split_chunks,
     check_pool_closed_form, check_pool_linearity, check_eviction_pre_exp,
     check_select_bruteforce, check_select_sizes, check_trajectory_invariants,
-    check_swap_lists, check_rope_complex, check_rope_identities,
+    check_swap_lists, check_place_blocks, check_rope_complex, check_rope_identities,
     check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
     check_bf16_decode,
 ]

@@ -75,15 +75,35 @@ def gpu_invariants(w, t, g: Gpu, prev: Gpu | None):
             assert gamma >= (w.k_e - len(new & ge)) / w.k - 1e-12, ("locality", gamma)
 
 
-def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=True, fused=True, inp=None):
+def force_slots(sess, b: int, h: int, owner: list):
+    """Host tier: after a forced selection, give the pair the oracle's slot
+    state (owners, resident table and the pages in the slots)."""
+    w, inp = sess.w, sess.inp
+    bh = b * w.Hkv + h
+    res = torch.full((w.max_blocks,), -1, dtype=torch.int32)
+    for s, x in enumerate(owner):
+        if x >= 0:
+            dp, hp = bh * sess.slots + s, host_page(w, inp, b, h, x)
+            res[x] = dp
+            sess.k_pages[dp] = sess.host_k[hp].to(sess.dev)
+            sess.v_pages[dp] = sess.host_v[hp].to(sess.dev)
+            sess.e_pages[dp] = sess.host_e[hp].to(sess.dev)
+    sess.resident[b, h] = res.to(sess.dev)
+    sess.slot_owner[b, h] = torch.tensor(owner, dtype=torch.int32, device=sess.dev)
+    torch.cuda.synchronize()
+
+
+def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=True, fused=True, inp=None,
+                   offload=False):
     announce(f"trajectory {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T0={w.T0} k={w.k_e}/{w.k_q} "
              f"steps={steps or w.steps} P={splits or w.splits} pairs={'all' if pairs is None else pairs} "
-             f"seed={seed} fused={fused}")
+             f"seed={seed} fused={fused} offload={offload}")
     inp = inp if inp is not None else synth.generate(w, seed)
-    sess = session(w, inp, splits=splits, fused=fused)
+    sess = session(w, inp, splits=splits, fused=fused, offload=offload)
     pairs = pairs or [(b, h) for b in range(w.B) for h in range(w.Hkv)]
     lgs = {p: logical_pair(inp, *p) for p in pairs}
     states = {p: PairState() for p in pairs}
+    owners = {p: [-1] * sess.slots for p in pairs} if offload else None
     log: list[str] = []
     prev_g = None
     for t in range(1, (steps or w.steps) + 1):
@@ -95,11 +115,22 @@ def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=
         if not w.select_all:
             gpu_invariants(w, t, g, prev_g)
         forced = False
+        slot_owner = sess.slot_owner.cpu().numpy() if offload else None
         for (b, h) in pairs:
             r = compare_pair(w, inp, lgs[(b, h)], g, b, h, t, states[(b, h)], sess.P, log, check_scores)
             n = int(g.sel_count[b, h])
-            if g.sel[b, h, :n].tolist() != r["sel"] or bitmap_set(g.evicted[b, h], r["nb"]) != r["evicted"]:
+            same = g.sel[b, h, :n].tolist() == r["sel"]
+            if offload:
+                # the oracle's swap lists placed into the oracle's slot state
+                want, placed = oracle.place_blocks(owners[(b, h)], r["evict"], r["load"])
+                assert placed == len(r["load"]), (t, b, h, "slots overflow")
+                if same:
+                    assert slot_owner[b, h].tolist() == want, (w.name, t, b, h, "slot owners")
+                owners[(b, h)] = want
+            if not same or bitmap_set(g.evicted[b, h], r["nb"]) != r["evicted"]:
                 force_pair(sess, b, h, r)
+                if offload:
+                    force_slots(sess, b, h, owners[(b, h)])
                 forced = True
             states[(b, h)] = PairState(set(r["evicted"]), list(r["sel"]))
         prev_g = Gpu(sess) if forced else g
@@ -363,6 +394,15 @@ def test_offload_equals_resident(name, scale, splits):
                     hp = host_page(w, inp, b, h, x)
                     assert torch.equal(dk[dp], sk[hp]) and torch.equal(dv[dp], sv[hp]), (t, b, h, x)
                 assert int((own[b, h] >= 0).sum()) == len(chosen)
+
+
+@pytest.mark.parametrize("name,scale,splits", OFFLOAD_CASES, ids=[c[0] for c in OFFLOAD_CASES])
+def test_offload_trajectory_vs_oracle(name, scale, splits):
+    """Host tier against the oracle: selections, swap lists and attention
+    as in the resident trajectories, plus the slot of every resident block
+    (the oracle's placement of its own swap lists), bit-exact."""
+    w = WORKLOADS[name].scaled(**scale) if scale else WORKLOADS[name]
+    run_trajectory(w, seed=32, splits=splits, steps=min(w.steps, 6), offload=True)
 
 
 def test_offload_more_loads_than_slots_flags():

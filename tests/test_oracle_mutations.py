@@ -24,6 +24,7 @@ _select = O.select_blocks
 _rotate = O.rope_rotate
 _top = O.top_by_score
 _swap = O.swap_lists
+_place = O.place_blocks
 _qscore = O.query_token_scores
 _freq = O.rope_inv_freq
 
@@ -99,6 +100,19 @@ def _swap_reversed(prev, cur):
     return b, a
 
 
+def _place_no_drop(owner, drop, load):
+    return _place(owner, [], load)
+
+
+def _place_from_top(owner, drop, load):
+    new, placed = _place(list(reversed(owner)), drop, load)
+    return list(reversed(new)), placed
+
+
+def _place_reversed_loads(owner, drop, load):
+    return _place(owner, drop, list(reversed(list(load))))
+
+
 def _rotate_sign(x, pos, base):
     return _rotate(x, -np.asarray(pos), base)
 
@@ -134,6 +148,9 @@ MUTANTS = [
     ("select_blocks", _select_overlapping, P.check_select_sizes),
     ("select_blocks", _select_swapped_scores, P.check_select_bruteforce),
     ("swap_lists", _swap_reversed, P.check_swap_lists),
+    ("place_blocks", _place_no_drop, P.check_place_blocks),
+    ("place_blocks", _place_from_top, P.check_place_blocks),
+    ("place_blocks", _place_reversed_loads, P.check_place_blocks),
     ("rope_rotate", _rotate_sign, P.check_rope_complex),
     ("rope_rotate", _rotate_pairs_adjacent, P.check_rope_complex),
     ("rope_inv_freq", _freq_wrong_exponent, P.check_rope_complex),
