@@ -42,7 +42,7 @@ invariants) except the selection *semantics* choices marked READING, whose
 agreement with the GPU is agreement on the reading: parity unpinned beyond
 the reading for those choices (disjoint budgets, initial state, new-block
 candidacy, no forced local window, tie order, slot placement of the host
-tier).
+tier, the recency bucket and the in-bucket order of the buffer).
 """
 
 from __future__ import annotations
@@ -64,6 +64,8 @@ __all__ = [
     "select_blocks",
     "swap_lists",
     "place_blocks",
+    "recency_bucket",
+    "buffer_retrieve",
     "tokens_of_blocks",
     "split_chunks",
     "attend",
@@ -229,6 +231,60 @@ def place_blocks(owner: list[int], drop: Iterable[int], load: Iterable[int]):
     for s, x in zip(free, load):
         new[s] = x
     return new, min(len(free), len(load))
+
+
+RECENCY_BUCKETS = 64
+
+
+def recency_bucket(age: int, width: int) -> int:
+    """Recency bucket of a buffered page last selected `age` >= 1 steps ago:
+    buckets of `width` steps, the last one open-ended [SPIN 2.B, bucketed
+    LRU over recency timestamps, e.g. 64 buckets].  READING: the timestamp
+    is the step at which the page was last selected; bucket 0 holds the
+    most recent pages."""
+    return min((max(int(age), 1) - 1) // int(width), RECENCY_BUCKETS - 1)
+
+
+def buffer_retrieve(owner: list[int], last_use: list[int], sel: Iterable[int], t: int, width: int):
+    """One step of the host tier with a locality-aware buffer [SPIN 2.B:
+    the per-request GPU buffer holds the pages this step needs and buffered
+    pages kept for temporal locality; buffered pages are evicted by a
+    bucketed LRU instead of a global LRU].
+
+    owner[s]: block in slot s or -1; last_use[s]: step at which that block
+    was last selected.  sel: this step's selection (ascending).  Steps:
+      1. a selected block already in a slot is a hit: its slot's timestamp
+         becomes t;
+      2. the selected blocks not in any slot are the misses (in selection
+         order);
+      3. if the free slots are too few, buffered pages (resident, not
+         selected) are dropped oldest bucket first; READING: inside the
+         bucket where dropping stops, lowest slot first;
+      4. the misses take the free slots as in place_blocks (the j-th miss
+         the j-th free slot in ascending order), timestamp t.
+
+    Returns (owner, last_use, misses, dropped, placed): new lists, the
+    missed blocks, the blocks dropped from the buffer, and how many misses
+    found a slot.
+    """
+    owner = [int(x) for x in owner]
+    last_use = [int(x) for x in last_use]
+    sel = [int(x) for x in sel]
+    slot_of = {x: s for s, x in enumerate(owner) if x >= 0}
+    for x in sel:
+        if x in slot_of:
+            last_use[slot_of[x]] = int(t)
+    misses = [x for x in sel if x not in slot_of]
+    n_free = sum(1 for x in owner if x < 0)
+    chosen = set(sel)
+    buffered = [s for s, x in enumerate(owner) if x >= 0 and x not in chosen]
+    order = sorted(buffered, key=lambda s: (-recency_bucket(t - last_use[s], width), s))
+    dropped = [owner[s] for s in order[:max(0, len(misses) - n_free)]]
+    owner, placed = place_blocks(owner, dropped, misses)
+    for s, x in enumerate(owner):
+        if x in set(misses[:placed]):
+            last_use[s] = int(t)
+    return owner, last_use, misses, dropped, placed
 
 
 # ---------------------------------------------------------------------------

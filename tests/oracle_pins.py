@@ -298,6 +298,90 @@ def check_place_blocks(O, seed=8):
         prev = g
 
 
+def check_buffer_retrieve(O, seed=9):
+    """Host tier with a buffer: a worked example by hand, the bucket's
+    closed form, agreement with the plain swap placement when the buffer
+    holds exactly the selection, agreement with an exact LRU while every
+    page is younger than the last bucket, and the eviction-order invariants
+    on random states."""
+    # slots [5, -, 2, 7], stamps [3, 0, 1, 2]; step 4 selects {1, 5, 9}:
+    # 5 is a hit; misses 1, 9; one free slot, so the oldest buffered page
+    # (block 2, last used at step 1) goes; 1 -> slot 1, 9 -> slot 2
+    assert O.buffer_retrieve([5, -1, 2, 7], [3, 0, 1, 2], [1, 5, 9], 4, 1) == \
+        ([5, 1, 9, 7], [4, 4, 4, 2], [1, 9], [2], 2)
+    assert [O.recency_bucket(a, 1) for a in (1, 2, 64, 65, 10 ** 6)] == [0, 1, 63, 63, 63]
+    assert [O.recency_bucket(a, 4) for a in (1, 4, 5, 8, 9, 256, 257)] == [0, 0, 1, 1, 2, 63, 63]
+    rng = np.random.default_rng(seed)
+    # (1) a buffer of exactly k slots with k-block selections is the plain
+    # swap placement, step by step
+    nb, k_e, k_q = 48, 5, 3
+    k = k_e + k_q
+    plain, buf, stamps, evicted, prev = [-1] * k, [-1] * k, [0] * k, set(), []
+    for t in range(1, 30):
+        _, _, g, evicted = O.select_blocks(rng.standard_normal(nb + t), rng.standard_normal(nb + t), nb + t,
+                                           k_e, k_q, evicted)
+        load, drop = O.swap_lists(prev, g)
+        plain, _ = O.place_blocks(plain, drop, load)
+        buf, stamps, misses, dropped, placed = O.buffer_retrieve(buf, stamps, g, t, 3)
+        assert buf == plain and misses == load and sorted(dropped) == drop and placed == len(load)
+        prev = g
+    # (2) with one-step buckets and fewer than 64 steps, the bucketed LRU
+    # is the exact LRU
+    for trial in range(20):
+        RS = int(rng.integers(4, 12))
+        owner, lu, ref_owner, ref_lu = [-1] * RS, [0] * RS, [-1] * RS, [0] * RS
+        for t in range(1, 50):
+            n = int(rng.integers(1, RS + 1))
+            sel = sorted(rng.choice(20, n, replace=False).tolist())
+            owner, lu, misses, dropped, placed = O.buffer_retrieve(owner, lu, sel, t, 1)
+            assert placed == len(misses)
+            # reference: exact LRU victims, then the same slot rule
+            where = {x: s for s, x in enumerate(ref_owner) if x >= 0}
+            for x in sel:
+                if x in where:
+                    ref_lu[where[x]] = t
+            ref_miss = [x for x in sel if x not in where]
+            free = [s for s in range(RS) if ref_owner[s] < 0]
+            victims = sorted((s for s in range(RS) if ref_owner[s] >= 0 and ref_owner[s] not in sel),
+                             key=lambda s: (ref_lu[s], s))[:max(0, len(ref_miss) - len(free))]
+            assert sorted(ref_owner[s] for s in victims) == sorted(dropped), (trial, t)
+            for s in victims:
+                ref_owner[s] = -1
+            for s, x in zip([s for s in range(RS) if ref_owner[s] < 0], ref_miss):
+                ref_owner[s], ref_lu[s] = x, t
+            assert ref_owner == owner and ref_lu == lu, (trial, t)
+    # (3) invariants on random states and wider buckets
+    for _ in range(300):
+        RS = int(rng.integers(2, 16))
+        width = int(rng.integers(1, 5))
+        t = int(rng.integers(2, 400))
+        blocks = rng.permutation(60)
+        owner = [int(blocks[s]) if rng.random() < 0.8 else -1 for s in range(RS)]
+        lu = [int(rng.integers(max(0, t - 300), t)) for _ in range(RS)]
+        n = int(rng.integers(0, RS + 1))
+        pool = [x for x in owner if x >= 0][:n // 2] + [int(x) for x in blocks[RS:RS + n - n // 2]]
+        sel = sorted(set(pool))
+        new, nlu, misses, dropped, placed = O.buffer_retrieve(owner, lu, sel, t, width)
+        was = {x: s for s, x in enumerate(owner) if x >= 0}
+        assert misses == [x for x in sel if x not in was]
+        assert placed == len(misses) and set(sel) <= set(new)
+        n_free = owner.count(-1)
+        assert len(dropped) == max(0, len(misses) - n_free)
+        assert not set(dropped) & set(sel)
+        for x in sel:
+            if x in was:  # hits keep their slot and take the new timestamp
+                assert new[was[x]] == x and nlu[was[x]] == t
+        kept = [s for s, x in enumerate(owner) if x >= 0 and x not in sel and x not in dropped]
+        for d in dropped:
+            sd = was[d]
+            bd = O.recency_bucket(t - lu[sd], width)
+            for sk in kept:
+                bk = O.recency_bucket(t - lu[sk], width)
+                assert bd > bk or (bd == bk and sd < sk), (bd, bk, sd, sk)
+        for s in kept:
+            assert new[s] == owner[s] and nlu[s] == lu[s]
+
+
 # ---------------------------------------------------------------------------
 # rotary embedding and the deferred (lazy) rotation
 # ---------------------------------------------------------------------------
@@ -411,7 +495,7 @@ ALL_CHECKS = [
     check_attend_vs_sdpa, check_merge_vs_sdpa, check_split_chunks,
     check_pool_closed_form, check_pool_linearity, check_eviction_pre_exp,
     check_select_bruteforce, check_select_sizes, check_trajectory_invariants,
-    check_swap_lists, check_place_blocks, check_rope_complex, check_rope_identities,
+    check_swap_lists, check_place_blocks, check_buffer_retrieve, check_rope_complex, check_rope_identities,
     check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
     check_bf16_decode,
 ]

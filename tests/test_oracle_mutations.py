@@ -25,6 +25,8 @@ _rotate = O.rope_rotate
 _top = O.top_by_score
 _swap = O.swap_lists
 _place = O.place_blocks
+_bucket = O.recency_bucket
+_buffer = O.buffer_retrieve
 _qscore = O.query_token_scores
 _freq = O.rope_inv_freq
 
@@ -113,6 +115,27 @@ def _place_reversed_loads(owner, drop, load):
     return _place(owner, drop, list(reversed(list(load))))
 
 
+def _bucket_reversed(age, width):
+    return O.RECENCY_BUCKETS - 1 - _bucket(age, width)
+
+
+def _bucket_off_by_one(age, width):
+    return min(int(age) // int(width), O.RECENCY_BUCKETS - 1)
+
+
+def _buffer_no_hit_refresh(owner, last_use, sel, t, width):
+    new, lu, misses, dropped, placed = _buffer(owner, last_use, sel, t, width)
+    for s, x in enumerate(owner):
+        if x >= 0 and x in set(sel):
+            lu[s] = last_use[s]
+    return new, lu, misses, dropped, placed
+
+
+def _buffer_high_slot_first(owner, last_use, sel, t, width):
+    new, lu, misses, dropped, placed = _buffer(owner[::-1], last_use[::-1], sel, t, width)
+    return new[::-1], lu[::-1], misses, dropped, placed
+
+
 def _rotate_sign(x, pos, base):
     return _rotate(x, -np.asarray(pos), base)
 
@@ -151,6 +174,10 @@ MUTANTS = [
     ("place_blocks", _place_no_drop, P.check_place_blocks),
     ("place_blocks", _place_from_top, P.check_place_blocks),
     ("place_blocks", _place_reversed_loads, P.check_place_blocks),
+    ("recency_bucket", _bucket_reversed, P.check_buffer_retrieve),
+    ("recency_bucket", _bucket_off_by_one, P.check_buffer_retrieve),
+    ("buffer_retrieve", _buffer_no_hit_refresh, P.check_buffer_retrieve),
+    ("buffer_retrieve", _buffer_high_slot_first, P.check_buffer_retrieve),
     ("rope_rotate", _rotate_sign, P.check_rope_complex),
     ("rope_rotate", _rotate_pairs_adjacent, P.check_rope_complex),
     ("rope_inv_freq", _freq_wrong_exponent, P.check_rope_complex),
