@@ -48,7 +48,8 @@ def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default 5; 60 with --buffer-slots, so the buffer has filled)")
     ap.add_argument("--workload", default="llama3_8b_32k")
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--seed", type=int, default=0)
@@ -57,6 +58,10 @@ def parse(argv=None):
     ap.add_argument("--unfused", action="store_true", help="time the six separate entry points")
     ap.add_argument("--offload", action="store_true",
                     help="host tier: pages in pinned host memory, resident slots in HBM, nosa_retrieve per step")
+    ap.add_argument("--buffer-slots", type=int, default=None,
+                    help="host tier with this many HBM slots per (b, h) (>= the selection budget): pages stay "
+                         "buffered after leaving the selection, bucketed-LRU eviction (nosa_retrieve_buffered)")
+    ap.add_argument("--bucket-width", type=int, default=1, help="steps per recency bucket of the buffer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with one plain 1 GiB device copy, a known-size kernel for counter calibration")
     return ap.parse_args(argv)
@@ -163,14 +168,18 @@ def main(argv=None) -> int:
     from block_sparse_kv_score_amd.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
+    if args.warmup is None:
+        args.warmup = 60 if args.buffer_slots is not None else 5
     K, W = args.steps, args.warmup
     passes = 3
     if w.append and W + passes * K > w.n_append:
         raise SystemExit(f"at most {w.n_append} appended tokens: lower --steps/--warmup")
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = synth.generate(w, args.seed)
+    if args.buffer_slots is not None:
+        args.offload = True
     sess = DecodeSession(w, inp, splits=args.splits, poison=False, fused=not args.unfused or args.offload,
-                         offload=args.offload)
+                         offload=args.offload, buffer_slots=args.buffer_slots, bucket_width=args.bucket_width)
     stream = torch.cuda.current_stream()
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
 
@@ -222,9 +231,12 @@ def main(argv=None) -> int:
     per = {n: [] for n in names}
     page_bytes = 2 * w.bs * w.D * 2 + w.bs * 4  # K + V + E of one page
     retrieved = []  # bytes the retrieve copied, per step
+    misses, selected = 0, 0
     for k in range(K):
         flush()
         t = next_t()
+        if sess.offload:  # residency of the tail blocks before this step's retrieve
+            tail_before = sess.resident[:, :, (w.seq_len(t) - 1) // w.bs].clone()
         sess.use_buffers(t)
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
         evs[0].record(stream)
@@ -256,10 +268,16 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         for j, n in enumerate(names):
             per[n].append(evs[j].elapsed_time(evs[j + 1]))
-        if sess.offload:  # loaded pages + the resident tail pages copied again
-            T = w.seq_len(t)
-            tail = sess.resident[:, :, (T - 1) // w.bs]
-            retrieved.append(page_bytes * (int(sess.load_count.sum().item()) + int((tail >= 0).sum().item())))
+        if sess.offload:  # loaded pages + the appended tokens of tail pages resident before and after
+            tail = sess.resident[:, :, (w.seq_len(t) - 1) // w.bs]
+            refreshed = int(((tail_before >= 0) & (tail >= 0)).sum().item())
+            loaded = int((sess.miss_count if sess.buffered else sess.load_count).sum().item())
+            # a refresh copies the appended token's units: D/8 of K, the
+            # 8-token row of V (D units), the 4-token unit of E
+            refresh_bytes = 16 * (w.D // 8 + w.D + 1) if w.append else page_bytes
+            retrieved.append(page_bytes * loaded + refresh_bytes * refreshed)
+            misses += loaded
+            selected += int(sess.sel_count.sum().item())
     kernels_us = {n: float(np.mean(v) * 1e3) for n, v in per.items()}
 
     # pass 3: warm, back to back
@@ -294,15 +312,21 @@ def main(argv=None) -> int:
         # the dominant launch is the retrieve, bound by the host link
         rb = float(np.mean(retrieved))
         r_gbps = rb / (kernels_us["retrieve"] / 1e6) / 1e9
+        kname = ("nosa_retrieve_buffered (retrieve_buffered_kernel)" if sess.buffered
+                 else "nosa_retrieve (retrieve_kernel)")
         roofline = {"bound": "host_link", "achieved": round(r_gbps, 2), "peak": PEAK_HOST_LINK_GBPS, "unit": "GB/s",
                     "frac": round(r_gbps / PEAK_HOST_LINK_GBPS, 4), "traffic": None,
-                    "kernel": "nosa_retrieve (retrieve_kernel)", "algorithmic_bytes_per_launch": int(rb),
+                    "kernel": kname, "algorithmic_bytes_per_launch": int(rb),
                     "avg_launch_us": round(kernels_us["retrieve"], 2)}
         offload = {"host_pool_bytes": int(sess.host_k.numel() * 2 * 2 + sess.host_e.numel() * 4),
                    "resident_pool_bytes": int(sess.k_pages.numel() * 2 * 2 + sess.e_pages.numel() * 4),
                    "resident_slots_per_pair": sess.slots, "retrieve_bytes_per_step": int(rb),
                    "pages_per_pair_per_step": round(rb / page_bytes / (w.B * w.Hkv), 2),
-                   "host_link_gbps": round(r_gbps, 2)}
+                   "host_link_gbps": round(r_gbps, 2),
+                   "buffer_slots": sess.buffer_slots, "bucket_width": sess.bucket_width if sess.buffered else None,
+                   "selected_pages_resident_before_retrieve": round(1.0 - misses / max(selected, 1), 4),
+                   "retrieve_bytes_per_step_p10_p90": [int(np.percentile(retrieved, 10)),
+                                                       int(np.percentile(retrieved, 90))]}
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -319,7 +343,9 @@ def main(argv=None) -> int:
 
     out = {
         "metric": (METRIC if w.name == "llama3_8b_32k" else f"sparse decode attn tokens/s ({w.name})")
-        + (" [host tier: pages in pinned host memory]" if sess.offload else ""),
+        + (" [host tier: pages in pinned host memory]" if sess.offload and not sess.buffered else "")
+        + (f" [host tier: pages in pinned host memory, {sess.slots}-slot HBM buffer per (b, h)]"
+           if sess.buffered else ""),
         "value": round(w.B / t_step, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -334,6 +360,7 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
                    "context": w.T0, "block": w.bs, "sub_block": w.ss, "k_e": w.k_e, "k_q": w.k_q,
                    "splits": sess.P, "table": w.table, "fused": fused, "offload": sess.offload,
+                   "buffer_slots": sess.buffer_slots,
                    "parallelism": "single GPU"},
         "hbm_gbps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),

@@ -258,7 +258,8 @@ nosa_status nosa_host_device_pointer(const void* host_ptr, void** device_ptr) {
 nosa_status nosa_retrieve(const nosa_dims* dims, const nosa_kv* host_kv, uint16_t* dev_k_pages,
                           uint16_t* dev_v_pages, float* dev_e_pages, int32_t slots, int32_t* resident,
                           int32_t* slot_owner, const int32_t* load, const int32_t* load_count, const int32_t* evict,
-                          const int32_t* evict_count, int32_t cap, const int32_t* seq_lens, hipStream_t stream) {
+                          const int32_t* evict_count, int32_t cap, const int32_t* seq_lens,
+                          const int32_t* seq_lens_prev, hipStream_t stream) {
   nosa_status st = check_dims(dims);
   if (st != NOSA_OK) return st;
   if ((st = check_kv(dims, host_kv, true)) != NOSA_OK) return st;
@@ -276,7 +277,34 @@ nosa_status nosa_retrieve(const nosa_dims* dims, const nosa_kv* host_kv, uint16_
   if (!aligned16(hk) || !aligned16(hv) || !aligned16(he)) return NOSA_ERR_ARG;
   return from_hip(nosa::launch_retrieve(*dims, *host_kv, hk, hv, he, dev_k_pages, dev_v_pages, dev_e_pages, slots,
                                         resident, slot_owner, load, load_count, evict, evict_count, cap, seq_lens,
-                                        stream));
+                                        seq_lens_prev, stream));
+}
+
+nosa_status nosa_retrieve_buffered(const nosa_dims* dims, const nosa_kv* host_kv, uint16_t* dev_k_pages,
+                                   uint16_t* dev_v_pages, float* dev_e_pages, int32_t slots, int32_t* resident,
+                                   int32_t* slot_owner, int32_t* last_use, const int32_t* sel,
+                                   const int32_t* sel_count, int32_t cap, int32_t step, int32_t bucket_width,
+                                   const int32_t* seq_lens, const int32_t* seq_lens_prev, int32_t* miss_count,
+                                   hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if ((st = check_kv(dims, host_kv, true)) != NOSA_OK) return st;
+  if (!dev_k_pages || !dev_v_pages || !dev_e_pages || !resident || !slot_owner || !last_use || !seq_lens)
+    return NOSA_ERR_ARG;
+  if (!sel || !sel_count) return NOSA_ERR_ARG;
+  if (!aligned16(dev_k_pages) || !aligned16(dev_v_pages) || !aligned16(dev_e_pages)) return NOSA_ERR_ARG;
+  if (slots < 1 || slots > nosa::kMaxRetrieveSlots || cap < 1 || cap > slots) return NOSA_ERR_ARG;
+  if (step < 1 || bucket_width < 1) return NOSA_ERR_ARG;
+  if ((int64_t)dims->batch * dims->n_kv_heads * slots > ((int64_t)1 << 31) - 1) return NOSA_ERR_UNSUPPORTED;
+  void *hk = nullptr, *hv = nullptr, *he = nullptr;
+  if (nosa_host_device_pointer(host_kv->k_pages, &hk) != NOSA_OK) return NOSA_ERR_ARG;
+  if (nosa_host_device_pointer(host_kv->v_pages, &hv) != NOSA_OK) return NOSA_ERR_ARG;
+  if (nosa_host_device_pointer(host_kv->e_pages, &he) != NOSA_OK) return NOSA_ERR_ARG;
+  if (!aligned16(hk) || !aligned16(hv) || !aligned16(he)) return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_retrieve_buffered(*dims, *host_kv, hk, hv, he, dev_k_pages, dev_v_pages,
+                                                 dev_e_pages, slots, resident, slot_owner, last_use, sel, sel_count,
+                                                 cap, step, bucket_width, seq_lens, seq_lens_prev, miss_count,
+                                                 stream));
 }
 
 nosa_status nosa_combine(const nosa_dims* dims, int32_t num_splits, const float* part_o, const float* part_m,

@@ -68,7 +68,14 @@ hipError_t launch_retrieve(const nosa_dims& d, const nosa_kv& host_kv, const voi
                            const void* host_e, uint16_t* dev_k, uint16_t* dev_v, float* dev_e, int32_t slots,
                            int32_t* resident, int32_t* slot_owner, const int32_t* load, const int32_t* load_count,
                            const int32_t* evict, const int32_t* evict_count, int32_t cap, const int32_t* seq_lens,
-                           hipStream_t stream);
+                           const int32_t* seq_prev, hipStream_t stream);
+
+hipError_t launch_retrieve_buffered(const nosa_dims& d, const nosa_kv& host_kv, const void* host_k,
+                                    const void* host_v, const void* host_e, uint16_t* dev_k, uint16_t* dev_v,
+                                    float* dev_e, int32_t slots, int32_t* resident, int32_t* slot_owner,
+                                    int32_t* last_use, const int32_t* sel, const int32_t* sel_count, int32_t cap,
+                                    int32_t step, int32_t bucket_width, const int32_t* seq_lens,
+                                    const int32_t* seq_prev, int32_t* miss_count, hipStream_t stream);
 
 hipError_t launch_combine(const nosa_dims& d, int32_t num_splits, const float* part_o,
                           const float* part_m, const float* part_l, float* o, float* m, float* l,

@@ -39,6 +39,7 @@ ENTRY_POINTS = [
     "nosa_select_decode",
     "nosa_combine",
     "nosa_retrieve",
+    "nosa_retrieve_buffered",
     "nosa_host_device_pointer",
     "nosa_status_string",
 ]
@@ -104,7 +105,8 @@ _SIGNATURES = {
     "nosa_select_decode": [_DIMS, _KV, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P,
                            _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P],
     "nosa_combine": [_DIMS, _I32, _P, _P, _P, _P, _P, _P, _P],
-    "nosa_retrieve": [_DIMS, _KV, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P],
+    "nosa_retrieve": [_DIMS, _KV, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P],
+    "nosa_retrieve_buffered": [_DIMS, _KV, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P],
     "nosa_host_device_pointer": [_P, ctypes.POINTER(ctypes.c_void_p)],
 }
 
@@ -341,7 +343,7 @@ def nosa_host_device_pointer(t: torch.Tensor) -> int:
 
 
 def nosa_retrieve(dims, host_kv, dev_k, dev_v, dev_e, slots, resident, slot_owner, load, load_count, evict,
-                  evict_count, seq_lens, stream=None):
+                  evict_count, seq_lens, seq_lens_prev=None, stream=None):
     """host_kv: descriptor whose page pointers are the host pools' HOST
     addresses (make_kv(..., page_ptrs=(t.data_ptr() ...)))."""
     cap = int(load.shape[-1])
@@ -352,7 +354,22 @@ def nosa_retrieve(dims, host_kv, dev_k, dev_v, dev_e, slots, resident, slot_owne
           _dev(resident, "resident", (torch.int32,)), _dev(slot_owner, "slot_owner", (torch.int32,)),
           _dev(load, "load", (torch.int32,)), _dev(load_count, "load_count", (torch.int32,)),
           _dev(evict, "evict", (torch.int32,)), _dev(evict_count, "evict_count", (torch.int32,)), cap,
-          _dev(seq_lens, "seq_lens", (torch.int32,)), _stream(stream))
+          _dev(seq_lens, "seq_lens", (torch.int32,)), _dev(seq_lens_prev, "seq_lens_prev", (torch.int32,), True),
+          _stream(stream))
+
+
+def nosa_retrieve_buffered(dims, host_kv, dev_k, dev_v, dev_e, slots, resident, slot_owner, last_use, sel,
+                           sel_count, step, bucket_width, seq_lens, seq_lens_prev=None, miss_count=None,
+                           stream=None):
+    """As nosa_retrieve, driven by the selection itself, with the slots
+    beyond the selection's capacity kept as a buffer (bucketed LRU)."""
+    _call("nosa_retrieve_buffered", ctypes.byref(dims), ctypes.byref(host_kv), _dev(dev_k, "dev_k", _BF16_LIKE),
+          _dev(dev_v, "dev_v", _BF16_LIKE), _dev(dev_e, "dev_e", (torch.float32,)), int(slots),
+          _dev(resident, "resident", (torch.int32,)), _dev(slot_owner, "slot_owner", (torch.int32,)),
+          _dev(last_use, "last_use", (torch.int32,)), _dev(sel, "sel", (torch.int32,)),
+          _dev(sel_count, "sel_count", (torch.int32,)), int(sel.shape[-1]), int(step), int(bucket_width),
+          _dev(seq_lens, "seq_lens", (torch.int32,)), _dev(seq_lens_prev, "seq_lens_prev", (torch.int32,), True),
+          _dev(miss_count, "miss_count", (torch.int32,), optional=True), _stream(stream))
 
 
 def nosa_combine(dims, num_splits, part_o, part_m, part_l, o, m, l, stream=None):

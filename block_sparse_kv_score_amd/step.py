@@ -23,7 +23,10 @@ With `offload` the whole paged cache lives in pinned host memory and HBM
 keeps `cap` resident pages per (b, h) (the host tier): the step is
 nosa_append_score (into the host pages), nosa_select_swap, nosa_retrieve
 (the swap lists move pages into the resident slots) and
-nosa_sparse_decode_combine over the resident pages.
+nosa_sparse_decode_combine over the resident pages.  With `buffer_slots`
+(>= the selection's capacity) HBM keeps that many slots per (b, h) and
+nosa_retrieve_buffered replaces nosa_retrieve: pages stay resident after
+they leave the selection and a bucketed LRU frees slots for misses.
 """
 
 from __future__ import annotations
@@ -51,8 +54,13 @@ class DecodeSession:
 
     def __init__(self, w: Workload, inp: Inputs, splits: int | None = None, device: str = "cuda",
                  poison: bool = True, stream: torch.cuda.Stream | None = None, fused: bool = True,
-                 offload: bool = False):
+                 offload: bool = False, buffer_slots: int | None = None, bucket_width: int = 1):
         self.w, self.inp = w, inp
+        self.buffered = buffer_slots is not None
+        self.buffer_slots, self.bucket_width = buffer_slots, int(bucket_width)
+        self.buffer_clock = 0  # the buffer's timestamps: one tick per retrieve
+        if self.buffered and not offload:
+            raise ValueError("buffer_slots needs the host tier (offload=True)")
         self.fused = fused
         self.offload = offload
         if offload and (w.select_all or w.table == TABLE_PACKED_ROPE):
@@ -158,6 +166,12 @@ class DecodeSession:
         self.kv = nosa.make_kv(*hosts, _KIND[w.table], page_ptrs=[nosa.nosa_host_device_pointer(t) for t in hosts],
                                **kw)
         self.slots = self.cap
+        if self.buffered:
+            if self.buffer_slots < self.cap:
+                raise ValueError(f"buffer_slots must be at least the selection capacity {self.cap}")
+            self.slots = int(self.buffer_slots)
+            self.last_use = torch.zeros((w.B, w.Hkv, self.slots), dtype=torch.int32, device=self.dev)
+            self.miss_count = torch.zeros((w.B, w.Hkv), dtype=torch.int32, device=self.dev)
         n = w.B * w.Hkv * self.slots
         fill = float("nan") if poison else 0.0
         self.k_pages = torch.full((n, w.bs * w.D), BF16_NAN if poison else 0, dtype=torch.int16, device=self.dev)
@@ -224,9 +238,22 @@ class DecodeSession:
                               self.load, self.load_count, self.evict, self.evict_count, self.stream)
 
     def retrieve(self):
-        nosa.nosa_retrieve(self.dims, self.host_kv, self.k_pages, self.v_pages, self.e_pages, self.slots,
-                           self.resident, self.slot_owner, self.load, self.load_count, self.evict,
-                           self.evict_count, self.seq_lens, self.stream)
+        """Host tier: bring the selection into the resident slots.  The
+        lengths before this step's append are the other length buffer, so
+        only the appended token is copied into a resident tail page."""
+        prev = self.seq_bufs[1] if self.seq_lens is self.seq_bufs[0] else self.seq_bufs[0]
+        if not self.w.append:
+            prev = self.seq_lens
+        if self.buffered:
+            self.buffer_clock += 1
+            nosa.nosa_retrieve_buffered(self.dims, self.host_kv, self.k_pages, self.v_pages, self.e_pages,
+                                        self.slots, self.resident, self.slot_owner, self.last_use, self.sel,
+                                        self.sel_count, self.buffer_clock, self.bucket_width, self.seq_lens,
+                                        prev, self.miss_count, self.stream)
+        else:
+            nosa.nosa_retrieve(self.dims, self.host_kv, self.k_pages, self.v_pages, self.e_pages, self.slots,
+                               self.resident, self.slot_owner, self.load, self.load_count, self.evict,
+                               self.evict_count, self.seq_lens, prev, self.stream)
 
     def decode_combine(self, t: int):
         kv = self.dev_kv if self.offload else self.kv

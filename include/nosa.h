@@ -311,18 +311,53 @@ nosa_status nosa_select_decode(const nosa_dims* dims, const nosa_kv* kv, const u
  *   load / evict (+ counts), cap: the swap lists of this step (as produced
  *     by nosa_swap_diff or nosa_select_swap).
  *   seq_lens int32 [B]: lengths after this step's append.
+ *   seq_lens_prev int32 [B] or null: the lengths at the previous call; the
+ *     tokens [seq_lens_prev[b], seq_lens[b]) were appended into the host
+ *     pools since then.
  * Per pair: every evicted block frees its slot; the j-th loaded block takes
  * the j-th free slot in ascending slot order and its K, V and E pages are
- * copied from host memory into it (zero-copy reads by the kernel); the
- * resident block holding the last token is copied again (an append writes
- * into the host pool).  More loads than free slots set the error flag and
- * the excess blocks stay out.  1 <= slots <= 1024.                        */
+ * copied from host memory into it (zero-copy reads by the kernel).  Every
+ * other resident block holding appended tokens gets those tokens copied
+ * (K: their D/8 16-byte units; V: the 8-token rows that hold them; E: the
+ * 4-token units that hold them); with seq_lens_prev null the resident
+ * block holding the last token is copied whole instead.  More loads than
+ * free slots set the error flag and the excess blocks stay out.
+ * 1 <= slots <= 1024.                                                     */
 nosa_status nosa_retrieve(const nosa_dims* dims, const nosa_kv* host_kv,
                           uint16_t* dev_k_pages, uint16_t* dev_v_pages, float* dev_e_pages, int32_t slots,
                           int32_t* resident, int32_t* slot_owner,
                           const int32_t* load, const int32_t* load_count,
                           const int32_t* evict, const int32_t* evict_count, int32_t cap,
-                          const int32_t* seq_lens, hipStream_t stream);
+                          const int32_t* seq_lens, const int32_t* seq_lens_prev, hipStream_t stream);
+
+/* Retrieve with a locality-aware buffer [SPIN 2.B: the GPU buffer of a
+ * request holds the pages the current step needs plus buffered pages kept
+ * for temporal locality; buffered pages are evicted by a bucketed LRU over
+ * recency timestamps (e.g. 64 buckets), decided in parallel on the GPU
+ * without a global sort].
+ *   host_kv, dev_*_pages, resident, slot_owner: as nosa_retrieve, with
+ *     cap <= slots <= 1024 (slots beyond cap are the buffer).
+ *   last_use int32 [B][Hkv][slots]: the step at which each slot's block was
+ *     last selected (ignored for free slots); kept by the library.
+ *   sel, sel_count, cap: this step's selection (ascending block ids).
+ *   step: this step's number, >= 1, larger than every earlier step.
+ *   bucket_width: steps per recency bucket (>= 1).
+ *   miss_count int32 [B][Hkv] or null: pages loaded per pair.
+ * Per pair: selected blocks already resident are hits (timestamp := step);
+ * the others are misses.  When the free slots are fewer than the misses,
+ * buffered pages (resident, not selected) are dropped, oldest first by
+ * bucket = min((step - last_use - 1) / bucket_width, 63), lowest slot first
+ * inside the bucket where dropping stops.  The j-th miss (selection order)
+ * takes the j-th free slot in ascending order (timestamp := step) and its
+ * K, V and E pages are copied from host memory; appended tokens reach the
+ * resident pages as in nosa_retrieve (seq_lens_prev as there).  The swap
+ * lists are not needed.                                                   */
+nosa_status nosa_retrieve_buffered(const nosa_dims* dims, const nosa_kv* host_kv,
+                                   uint16_t* dev_k_pages, uint16_t* dev_v_pages, float* dev_e_pages,
+                                   int32_t slots, int32_t* resident, int32_t* slot_owner, int32_t* last_use,
+                                   const int32_t* sel, const int32_t* sel_count, int32_t cap, int32_t step,
+                                   int32_t bucket_width, const int32_t* seq_lens,
+                                   const int32_t* seq_lens_prev, int32_t* miss_count, hipStream_t stream);
 
 /* The device address of pinned, mapped host memory (to pass host pools to
  * the calls that read or write pages through a kernel, e.g. an append into

@@ -144,11 +144,20 @@ def test_host_checks_reject_bad_arguments():
     # host-tier retrieve: slot count bounds, required lists
     def retr(slots, load=fake):
         return L.nosa_retrieve(D(d), D(kv), P(4096), P(8192), P(12288), slots, fake, fake, load, fake, fake, fake,
-                               8, fake, None)
+                               8, fake, None, None)
     assert retr(0) == nosa.NOSA_ERR_ARG
     assert retr(1025) == nosa.NOSA_ERR_ARG
     assert retr(8, load=None) == nosa.NOSA_ERR_ARG
     assert L.nosa_host_device_pointer(None, ctypes.byref(ctypes.c_void_p())) == nosa.NOSA_ERR_ARG
+    # buffered retrieve: cap <= slots <= 1024, step >= 1, bucket width >= 1
+    def buf(slots, cap=8, step=1, width=1, last_use=fake):
+        return L.nosa_retrieve_buffered(D(d), D(kv), P(4096), P(8192), P(12288), slots, fake, fake, last_use, fake,
+                                        fake, cap, step, width, fake, None, None, None)
+    assert buf(7) == nosa.NOSA_ERR_ARG                 # fewer slots than the selection can hold
+    assert buf(1025) == nosa.NOSA_ERR_ARG
+    assert buf(16, step=0) == nosa.NOSA_ERR_ARG
+    assert buf(16, width=0) == nosa.NOSA_ERR_ARG
+    assert buf(16, last_use=None) == nosa.NOSA_ERR_ARG
     # fused append + score
     def ascore(k_new, seq_in, seq_out, v_new=None):
         v = v_new if v_new is not None else (fake if k_new else None)

@@ -75,9 +75,9 @@ def gpu_invariants(w, t, g: Gpu, prev: Gpu | None):
             assert gamma >= (w.k_e - len(new & ge)) / w.k - 1e-12, ("locality", gamma)
 
 
-def force_slots(sess, b: int, h: int, owner: list):
+def force_slots(sess, b: int, h: int, owner: list, last_use: list | None = None):
     """Host tier: after a forced selection, give the pair the oracle's slot
-    state (owners, resident table and the pages in the slots)."""
+    state (owners, timestamps, resident table and the pages in the slots)."""
     w, inp = sess.w, sess.inp
     bh = b * w.Hkv + h
     res = torch.full((w.max_blocks,), -1, dtype=torch.int32)
@@ -90,20 +90,25 @@ def force_slots(sess, b: int, h: int, owner: list):
             sess.e_pages[dp] = sess.host_e[hp].to(sess.dev)
     sess.resident[b, h] = res.to(sess.dev)
     sess.slot_owner[b, h] = torch.tensor(owner, dtype=torch.int32, device=sess.dev)
+    if last_use is not None:
+        sess.last_use[b, h] = torch.tensor(last_use, dtype=torch.int32, device=sess.dev)
     torch.cuda.synchronize()
 
 
 def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=True, fused=True, inp=None,
-                   offload=False):
+                   offload=False, buffer_slots=None, bucket_width=1):
     announce(f"trajectory {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T0={w.T0} k={w.k_e}/{w.k_q} "
              f"steps={steps or w.steps} P={splits or w.splits} pairs={'all' if pairs is None else pairs} "
-             f"seed={seed} fused={fused} offload={offload}")
+             f"seed={seed} fused={fused} offload={offload} buffer={buffer_slots}/{bucket_width}")
     inp = inp if inp is not None else synth.generate(w, seed)
-    sess = session(w, inp, splits=splits, fused=fused, offload=offload)
+    sess = session(w, inp, splits=splits, fused=fused, offload=offload, buffer_slots=buffer_slots,
+                   bucket_width=bucket_width)
     pairs = pairs or [(b, h) for b in range(w.B) for h in range(w.Hkv)]
     lgs = {p: logical_pair(inp, *p) for p in pairs}
     states = {p: PairState() for p in pairs}
     owners = {p: [-1] * sess.slots for p in pairs} if offload else None
+    stamps = {p: [0] * sess.slots for p in pairs} if offload else None
+    total_misses = 0
     log: list[str] = []
     prev_g = None
     for t in range(1, (steps or w.steps) + 1):
@@ -116,11 +121,26 @@ def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=
             gpu_invariants(w, t, g, prev_g)
         forced = False
         slot_owner = sess.slot_owner.cpu().numpy() if offload else None
+        if offload and sess.buffered:
+            last_use = sess.last_use.cpu().numpy()
+            miss_count = sess.miss_count.cpu().numpy()
         for (b, h) in pairs:
             r = compare_pair(w, inp, lgs[(b, h)], g, b, h, t, states[(b, h)], sess.P, log, check_scores)
             n = int(g.sel_count[b, h])
             same = g.sel[b, h, :n].tolist() == r["sel"]
-            if offload:
+            if offload and sess.buffered:
+                # the oracle's selection through the oracle's buffer
+                want, lu, misses, _, placed = oracle.buffer_retrieve(owners[(b, h)], stamps[(b, h)], r["sel"],
+                                                                     sess.buffer_clock, bucket_width)
+                assert placed == len(misses), (t, b, h, "slots overflow")
+                if same:
+                    assert slot_owner[b, h].tolist() == want, (w.name, t, b, h, "slot owners")
+                    live = [s for s in range(sess.slots) if want[s] >= 0]
+                    assert [int(last_use[b, h, s]) for s in live] == [lu[s] for s in live], (t, b, h, "stamps")
+                    assert int(miss_count[b, h]) == len(misses), (t, b, h, "misses")
+                owners[(b, h)], stamps[(b, h)] = want, lu
+                total_misses += len(misses)
+            elif offload:
                 # the oracle's swap lists placed into the oracle's slot state
                 want, placed = oracle.place_blocks(owners[(b, h)], r["evict"], r["load"])
                 assert placed == len(r["load"]), (t, b, h, "slots overflow")
@@ -130,12 +150,14 @@ def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=
             if not same or bitmap_set(g.evicted[b, h], r["nb"]) != r["evicted"]:
                 force_pair(sess, b, h, r)
                 if offload:
-                    force_slots(sess, b, h, owners[(b, h)])
+                    force_slots(sess, b, h, owners[(b, h)], stamps[(b, h)] if sess.buffered else None)
                 forced = True
             states[(b, h)] = PairState(set(r["evicted"]), list(r["sel"]))
         prev_g = Gpu(sess) if forced else g
     for line in log:
         print("near-tie:", line)
+    if offload and sess.buffered:
+        print(f"buffer misses over the trajectory: {total_misses}")
     return log
 
 
@@ -403,6 +425,63 @@ def test_offload_trajectory_vs_oracle(name, scale, splits):
     (the oracle's placement of its own swap lists), bit-exact."""
     w = WORKLOADS[name].scaled(**scale) if scale else WORKLOADS[name]
     run_trajectory(w, seed=32, splits=splits, steps=min(w.steps, 6), offload=True)
+
+
+BUFFER_CASES = [
+    # (workload, scaling, splits, buffer slots, bucket width): few spare
+    # slots and fresh query picks, so the LRU evicts most steps
+    ("tiny_nosa", dict(steps=24, T0=2048 + 50, k_e=2, k_q=6), 2, 11, 1),
+    ("tiny_nosa", dict(steps=24, T0=2048 + 50, k_e=2, k_q=6), 1, 10, 3),
+    ("llama3_8b_32k", dict(B=2, Hq=8, Hkv=2, T0=8192 + 61, steps=8), 3, 80, 1),
+    ("llama31_70b_256k", dict(B=2, Hq=16, Hkv=2, T0=16384 + 100, dir_entries=64, steps=6), 4, 150, 2),
+]
+
+
+@pytest.mark.parametrize("name,scale,splits,slots,width", BUFFER_CASES,
+                         ids=[f"{c[0]}-{c[3]}x{c[4]}" for c in BUFFER_CASES])
+def test_buffered_trajectory_vs_oracle(name, scale, splits, slots, width):
+    """Host tier with a buffer against the oracle: selections, swap lists
+    and attention, plus every slot's block and timestamp and the misses
+    per pair (the oracle's bucketed LRU over its own selections)."""
+    w = WORKLOADS[name].scaled(**scale)
+    run_trajectory(w, seed=33, splits=splits, offload=True, buffer_slots=slots, bucket_width=width)
+
+
+@pytest.mark.parametrize("name,scale,splits,slots,width", BUFFER_CASES[::2],
+                         ids=[f"{c[0]}-{c[3]}x{c[4]}" for c in BUFFER_CASES[::2]])
+def test_buffered_equals_resident(name, scale, splits, slots, width):
+    """The buffered host-tier step gives the resident step's bits, and
+    every resident slot (selected or buffered) holds its block's pages as
+    they are in host memory."""
+    w = WORKLOADS[name].scaled(**scale)
+    announce(f"buffered host tier vs resident {name} {scale} P={splits} slots={slots} width={width}")
+    inp = synth.generate(w, 34)
+    a = session(w, inp, splits=splits, offload=True, buffer_slots=slots, bucket_width=width)
+    s = session(w, inp, splits=splits)
+    for t in range(1, w.steps + 1):
+        a.step(t)
+        s.step(t)
+        torch.cuda.synchronize()
+        assert int(a.err.item()) == 0 and int(s.err.item()) == 0
+        for n in ["sel_count", "evicted", "o", "m", "l", "part_o", "part_m", "part_l", "seq_lens", "score_q"]:
+            x, y = getattr(a, n), getattr(s, n)
+            if x.dtype == torch.float32:
+                x, y = x.view(torch.int32), y.view(torch.int32)
+            assert torch.equal(x, y), (n, t)
+        res, own = a.resident.cpu().numpy(), a.slot_owner.cpu().numpy()
+        sel, cnt = a.sel.cpu().numpy(), a.sel_count.cpu().numpy()
+        dk, dv, de = a.k_pages.cpu(), a.v_pages.cpu(), a.e_pages.cpu()
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                bh = b * w.Hkv + h
+                assert set(sel[b, h, :cnt[b, h]].tolist()) <= set(np.nonzero(res[b, h] >= 0)[0].tolist())
+                for x in np.nonzero(res[b, h] >= 0)[0].tolist():
+                    dp = int(res[b, h, x])
+                    assert bh * a.slots <= dp < (bh + 1) * a.slots and own[b, h, dp - bh * a.slots] == x
+                    hp = host_page(w, inp, b, h, x)
+                    assert torch.equal(dk[dp], a.host_k[hp]) and torch.equal(dv[dp], a.host_v[hp]), (t, b, h, x)
+                    assert torch.equal(de[dp].view(torch.int32), a.host_e[hp].view(torch.int32)), (t, b, h, x)
+                assert int((own[b, h] >= 0).sum()) == int((res[b, h] >= 0).sum())
 
 
 def test_offload_more_loads_than_slots_flags():
