@@ -70,6 +70,7 @@ __all__ = [
     "split_chunks",
     "attend",
     "merge_partials",
+    "softmax_block_mass",
     "rope_inv_freq",
     "rope_rotate",
     "decode_step_bh",
@@ -347,6 +348,36 @@ def merge_partials(o_parts: np.ndarray, m_parts: np.ndarray, l_parts: np.ndarray
     return O, float(m), float(l)
 
 
+def softmax_block_mass(q: np.ndarray, K: np.ndarray, blocks: list[int], T: int, bs: int, scale: float):
+    """The online-softmax score step [NOVITA, 2. Attention modifications:
+    with the returned row max and l, p = exp(q.k - rowmax) / l is each key's
+    softmax score, and a row-wise sum turns it into a sparsification score].
+
+    Softmax over the tokens of the given blocks, computed by its definition
+    (max, exponentials, sum, divide); then, for every query row and block,
+    the sum of that row's probabilities over the block's tokens.  READING:
+    in a decode step the rows are the group's query heads, the sum runs over
+    each selected block's present tokens, and the result stays per head.
+
+    q: (G, D); K: (>=T, D) keys in logical order.  Returns (G, len(blocks)).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    G = q.shape[0]
+    out = np.zeros((G, len(blocks)))
+    toks = tokens_of_blocks(blocks, T, bs)
+    if len(toks) == 0:
+        return out
+    s = (q @ np.asarray(K, dtype=np.float64)[toks].T) * scale      # (G, n)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    start = 0
+    for j, i in enumerate(blocks):
+        n = len(block_token_range(int(i), T, bs))
+        out[:, j] = p[:, start:start + n].sum(axis=1)
+        start += n
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Rotary position embedding  [LAZY, decoding + mathematical equivalence]
 # ---------------------------------------------------------------------------
@@ -389,7 +420,8 @@ def decode_step_bh(q_group, K, V, e, T, bs, ss, k_e, k_q, evicted, prev_sel,
     select_all: skip scoring and take every block (deferred-RoPE workload).
 
     Returns a dict with block scores, the selection, swap lists, per-split
-    partials and the merged (O, m, l).
+    partials, the merged (O, m, l) and each selected block's softmax mass
+    per query head.
     """
     nb = num_blocks(T, bs)
     out: dict = {"nb": nb}
@@ -428,4 +460,5 @@ def decode_step_bh(q_group, K, V, e, T, bs, ss, k_e, k_q, evicted, prev_sel,
     toks = tokens_of_blocks(gamma, T, bs)
     O, m, l = attend(qt, Kt[toks], V[toks], scale)
     out.update(part_o=part_o, part_m=part_m, part_l=part_l, O=O, m=m, l=l)
+    out["mass"] = softmax_block_mass(qt, Kt, gamma, T, bs, scale)
     return out

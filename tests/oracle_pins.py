@@ -382,6 +382,51 @@ def check_buffer_retrieve(O, seed=9):
             assert new[s] == owner[s] and nlu[s] == lu[s]
 
 
+def check_softmax_block_mass(O, seed=10):
+    """The softmax score step: a hand-worked example, torch's softmax summed
+    per block, the uniform closed form (mass = share of tokens), and the
+    route through attend's returned row max and l, p = exp(s - m) / l."""
+    # one dim, q = 1, keys 0, ln 2, ln 3: p = 1/6, 2/6, 3/6; blocks of 2
+    K = np.array([[0.0], [math.log(2.0)], [math.log(3.0)]])
+    got = O.softmax_block_mass(np.array([[1.0]]), K, [0, 1], 3, 2, 1.0)
+    assert np.allclose(got, [[0.5, 0.5]], rtol=0, atol=1e-15), got
+    got = O.softmax_block_mass(np.array([[1.0]]), K, [1], 3, 2, 1.0)
+    assert np.allclose(got, [[1.0]], rtol=0, atol=1e-15)
+    assert O.softmax_block_mass(np.ones((2, 1)), K, [], 3, 2, 1.0).shape == (2, 0)
+    rng = np.random.default_rng(seed)
+    for _ in range(20):
+        G, D, bs = int(rng.integers(1, 5)), 8, int(rng.choice([2, 4, 8]))
+        T = int(rng.integers(1, 60))
+        nb = -(-T // bs)
+        blocks = sorted(rng.choice(nb, int(rng.integers(1, nb + 1)), replace=False).tolist())
+        q = rng.standard_normal((G, D))
+        K = rng.standard_normal((T, D)) * 2
+        scale = 1 / math.sqrt(D)
+        got = O.softmax_block_mass(q, K, blocks, T, bs, scale)
+        toks = O.tokens_of_blocks(blocks, T, bs)
+        p = torch.softmax(torch.from_numpy(q @ K[toks].T * scale), dim=1).numpy()
+        ref = np.zeros_like(got)
+        pos = 0
+        for j, i in enumerate(blocks):
+            n = min(T, (i + 1) * bs) - i * bs
+            ref[:, j] = p[:, pos:pos + n].sum(axis=1)
+            pos += n
+        assert np.abs(got - ref).max() <= 1e-12
+        assert np.abs(got.sum(axis=1) - 1).max() <= 1e-12
+        # the returned (m, l) route
+        _, m, l = O.attend(q, K[toks], K[toks], scale)
+        pos = 0
+        for j, i in enumerate(blocks):
+            n = min(T, (i + 1) * bs) - i * bs
+            s = q @ K[toks[pos:pos + n]].T * scale
+            assert np.abs(np.exp(s - m[:, None]).sum(axis=1) / l - got[:, j]).max() <= 1e-12
+            pos += n
+        # identical keys: mass is the share of present tokens
+        flat = O.softmax_block_mass(q, np.ones((T, D)), blocks, T, bs, scale)
+        counts = np.array([min(T, (i + 1) * bs) - i * bs for i in blocks], dtype=np.float64)
+        assert np.abs(flat - counts / counts.sum()).max() <= 1e-12
+
+
 # ---------------------------------------------------------------------------
 # rotary embedding and the deferred (lazy) rotation
 # ---------------------------------------------------------------------------
@@ -496,6 +541,6 @@ ALL_CHECKS = [
     check_pool_closed_form, check_pool_linearity, check_eviction_pre_exp,
     check_select_bruteforce, check_select_sizes, check_trajectory_invariants,
     check_swap_lists, check_place_blocks, check_buffer_retrieve, check_rope_complex, check_rope_identities,
-    check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
+    check_softmax_block_mass, check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
     check_bf16_decode,
 ]

@@ -27,6 +27,7 @@ _swap = O.swap_lists
 _place = O.place_blocks
 _bucket = O.recency_bucket
 _buffer = O.buffer_retrieve
+_mass = O.softmax_block_mass
 _qscore = O.query_token_scores
 _freq = O.rope_inv_freq
 
@@ -136,6 +137,23 @@ def _buffer_high_slot_first(owner, last_use, sel, t, width):
     return new[::-1], lu[::-1], misses, dropped, placed
 
 
+def _mass_unnormalised(q, K, blocks, T, bs, scale):
+    toks = O.tokens_of_blocks(blocks, T, bs)
+    out = _mass(q, K, blocks, T, bs, scale)
+    if len(toks):
+        s = (np.asarray(q) @ np.asarray(K)[toks].T) * scale
+        out = out * np.exp(s - s.max(axis=1, keepdims=True)).sum(axis=1, keepdims=True)
+    return out
+
+
+def _mass_blocks_reversed(q, K, blocks, T, bs, scale):
+    return _mass(q, K, blocks, T, bs, scale)[:, ::-1]
+
+
+def _mass_no_scale(q, K, blocks, T, bs, scale):
+    return _mass(q, K, blocks, T, bs, 1.0)
+
+
 def _rotate_sign(x, pos, base):
     return _rotate(x, -np.asarray(pos), base)
 
@@ -178,6 +196,9 @@ MUTANTS = [
     ("recency_bucket", _bucket_off_by_one, P.check_buffer_retrieve),
     ("buffer_retrieve", _buffer_no_hit_refresh, P.check_buffer_retrieve),
     ("buffer_retrieve", _buffer_high_slot_first, P.check_buffer_retrieve),
+    ("softmax_block_mass", _mass_unnormalised, P.check_softmax_block_mass),
+    ("softmax_block_mass", _mass_blocks_reversed, P.check_softmax_block_mass),
+    ("softmax_block_mass", _mass_no_scale, P.check_softmax_block_mass),
     ("rope_rotate", _rotate_sign, P.check_rope_complex),
     ("rope_rotate", _rotate_pairs_adjacent, P.check_rope_complex),
     ("rope_inv_freq", _freq_wrong_exponent, P.check_rope_complex),
