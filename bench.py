@@ -62,6 +62,8 @@ def parse(argv=None):
                     help="host tier with this many HBM slots per (b, h) (>= the selection budget): pages stay "
                          "buffered after leaving the selection, bucketed-LRU eviction (nosa_retrieve_buffered)")
     ap.add_argument("--bucket-width", type=int, default=1, help="steps per recency bucket of the buffer")
+    ap.add_argument("--mass", action="store_true",
+                    help="decode with the softmax score step (nosa_sparse_decode_mass): block masses per head")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with one plain 1 GiB device copy, a known-size kernel for counter calibration")
     return ap.parse_args(argv)
@@ -179,7 +181,8 @@ def main(argv=None) -> int:
     if args.buffer_slots is not None:
         args.offload = True
     sess = DecodeSession(w, inp, splits=args.splits, poison=False, fused=not args.unfused or args.offload,
-                         offload=args.offload, buffer_slots=args.buffer_slots, bucket_width=args.bucket_width)
+                         offload=args.offload, buffer_slots=args.buffer_slots, bucket_width=args.bucket_width,
+                         mass=args.mass)
     stream = torch.cuda.current_stream()
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
 
@@ -220,7 +223,7 @@ def main(argv=None) -> int:
     elif fused:
         if w.select_all:
             names = (["append"] if w.append else []) + ["swap_diff", "decode_combine"]
-        elif sess.select_decode_ok:
+        elif sess.select_decode_ok and not sess.mass_on:
             names = ["append_score", "select_decode"]
         else:
             names = ["append_score", "select_swap", "decode_combine"]
@@ -300,11 +303,13 @@ def main(argv=None) -> int:
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
         if tr.get("decode_sources_sha256_16") == source_hash(DECODE_SRCS) and tr.get("workload") == w.name \
-                and tr.get("splits") == sess.P and tr.get("entry_point") == dec_name:
+                and tr.get("splits") == sess.P and tr.get("entry_point") == dec_name and not sess.mass_on:
             traffic = tr.get("bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                "kernel": {"select_decode": "nosa_select_decode", "decode_combine": "nosa_sparse_decode_combine",
+                "kernel": {"select_decode": "nosa_select_decode",
+                           "decode_combine": ("nosa_sparse_decode_mass" if sess.mass_on
+                                              else "nosa_sparse_decode_combine"),
                            "decode": "nosa_sparse_decode"}[dec_name] + " (decode_kernel)",
                 "algorithmic_bytes_per_launch": int(kvb), "avg_launch_us": round(kernels_us[dec_name], 2)}
     offload = None
@@ -323,7 +328,7 @@ def main(argv=None) -> int:
                    "resident_slots_per_pair": sess.slots, "retrieve_bytes_per_step": int(rb),
                    "pages_per_pair_per_step": round(rb / page_bytes / (w.B * w.Hkv), 2),
                    "host_link_gbps": round(r_gbps, 2),
-                   "buffer_slots": sess.buffer_slots, "bucket_width": sess.bucket_width if sess.buffered else None,
+                   "buffer_slots": sess.buffer_slots, "softmax_mass": sess.mass_on, "bucket_width": sess.bucket_width if sess.buffered else None,
                    "selected_pages_resident_before_retrieve": round(1.0 - misses / max(selected, 1), 4),
                    "retrieve_bytes_per_step_p10_p90": [int(np.percentile(retrieved, 10)),
                                                        int(np.percentile(retrieved, 90))]}
@@ -345,7 +350,8 @@ def main(argv=None) -> int:
         "metric": (METRIC if w.name == "llama3_8b_32k" else f"sparse decode attn tokens/s ({w.name})")
         + (" [host tier: pages in pinned host memory]" if sess.offload and not sess.buffered else "")
         + (f" [host tier: pages in pinned host memory, {sess.slots}-slot HBM buffer per (b, h)]"
-           if sess.buffered else ""),
+           if sess.buffered else "")
+        + (" [with the softmax score step]" if sess.mass_on else ""),
         "value": round(w.B / t_step, 1),
         "unit": "tokens/s",
         "n_gpus": 1,

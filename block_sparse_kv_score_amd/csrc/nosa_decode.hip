@@ -39,6 +39,15 @@
 // bf16 while l sums the fp32 values.  With deferred RoPE the rotated query
 // is split into bf16 hi + lo parts that fill spare head columns of the same
 // MFMA (|error| ~ 2^-16 relative).
+//
+// Softmax score step (Novita page, 2. Attention modifications: with the
+// returned row max and l, p = exp(q.k - rowmax) / l is each key's softmax
+// score, summed row-wise into a sparsification score).  With MASS the wave
+// also stores, per tile and head, the sum of the tile's fp32 probabilities
+// and the running max they are relative to; the workgroup that completes the
+// combine turns them into each selected block's softmax mass per query
+// head, mass = sum over the block's tiles of l_t 2^(m_t - M) / L, with the
+// final M and L.  K is not read again.
 
 #include "nosa_launch.hpp"
 #include "nosa_select_impl.hpp"
@@ -82,6 +91,9 @@ struct DecodeArgs {
   int32_t* sel_w;
   int32_t* sel_count_w;
   SwapArgs sw;
+  // softmax score step (MASS variants only)
+  float* tile_stats;  // [B*Hkv][sel_cap * bs/64][G][2]: tile sum of p, running max (log2 units)
+  float* mass;        // [B][Hq][sel_cap]
 };
 
 constexpr int kDecSelCap = 4 * kSelThreads;  // capacity of the select variants (SR = 4)
@@ -224,9 +236,41 @@ __device__ __forceinline__ void merge_one(float pm, float pl, float po, int64_t 
   }
 }
 
+// Softmax mass of every selected block of pair bh for query head g of the
+// group, given the final row max M2 (log2 units) and sum L of that head:
+// the sum over the block's tiles that hold tokens of l_t 2^(m_t - M2) / L.
+// Entries n .. sel_cap-1 receive 0.  Threads of the workgroup split the
+// (head, block) pairs; the tile statistics are read with device-scope
+// loads (they may come from other workgroups of the launch).
+template <int G, int KIND>
+__device__ __forceinline__ void finish_mass(const Table& t, int bh, int b, int h, int Hq, int bs, int sel_cap, int n,
+                                            int T, const int32_t* list, const float* tile_stats, const float* M2,
+                                            const float* L, float* mass) {
+  const int tpb = bs / kTile;
+  const int nb = (T + bs - 1) / bs;
+  for (int x = threadIdx.x; x < G * sel_cap; x += kDecThreads) {
+    const int g = x / sel_cap, j = x % sel_cap;
+    float acc = 0.f;
+    if (j < n && L[g] > 0.f) {
+      const int i = list[j];
+      uint32_t docb;
+      if (i >= 0 && i < nb && page_of<KIND>(t, bh, i, docb) >= 0) {
+        for (int sub = 0; sub < tpb; ++sub) {
+          if (T - (i * bs + sub * kTile) <= 0) break;  // no tokens from here on
+          const float* st = tile_stats + (((int64_t)bh * sel_cap * tpb + (int64_t)j * tpb + sub) * G + g) * 2;
+          acc += load_f32<true>(st) * exp2f(load_f32<true>(st + 1) - M2[g]);
+        }
+        acc /= L[g];
+      }
+    }
+    mass[((int64_t)b * Hq + (int64_t)h * G + g) * sel_cap + j] = acc;
+  }
+}
+
 // SR > 0: the select variant (SR elements per thread of the selection,
-// covering max_blocks <= SR * kSelThreads).
-template <int D, int G, int KIND, int SR>
+// covering max_blocks <= SR * kSelThreads).  MASS: the softmax score step
+// (SR == 0 with the fused combine only).
+template <int D, int G, int KIND, int SR, bool MASS = false>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs a) {
   constexpr bool ROPE = KIND == NOSA_TABLE_PACKED_ROPE;
   using S = DecodeShape<D, G, ROPE>;
@@ -459,6 +503,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+    if constexpr (MASS) {  // the tile's probability sum per head slot
+      const float tsum = xor_reduce<GE, kWave>(psum, [](float x, float y) { return x + y; });
+      if (real && cset == 0 && lq == 0) {
+        float* st = a.tile_stats + (((int64_t)bh * a.sel_cap * tpb + (int64_t)j0 * tpb + k) * G + cg) * 2;
+        store_coherent(st, tsum);
+        store_coherent(st + 1, mn);
+      }
+    }
 
     // tokens past the end hold stale page data: zero their V entries
     if (ntok < kTile) {
@@ -553,6 +605,29 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
     }
   }
 
+  if constexpr (MASS) {
+    if (a.P == 1) {  // the final M and L are this workgroup's own merge
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();  // every wave's tile statistics
+      __shared__ float fm[G], fl[G];
+      if (threadIdx.x < G) {
+        const int g = threadIdx.x;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < kDecWaves; ++ww)
+          if (sh.lw[ww][g] > 0.f) M = fmaxf(M, sh.mw[ww][g]);
+        float L = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kDecWaves; ++ww)
+          if (sh.lw[ww][g] > 0.f) L += sh.lw[ww][g] * exp2f(sh.mw[ww][g] - M);
+        fm[g] = M;
+        fl[g] = L;
+      }
+      __syncthreads();
+      finish_mass<G, KIND>(a.t, bh, b, h, a.Hq, a.bs, a.sel_cap, n, T, selp, a.tile_stats, fm, fl, a.mass);
+      return;
+    }
+  }
   if (a.counters == nullptr || a.P == 1) return;
   // Fused combine: the last workgroup of this (b, h) to finish merges the P
   // partials.  Every wave waits for its device-scope partial stores to
@@ -568,6 +643,24 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
     const int64_t row = (int64_t)b * a.Hq + (int64_t)h * G + g;
     merge_splits<true>(a.P, D, row, d, a.part_o, a.part_m, a.part_l, a.o, a.m, a.l);
   }
+  if constexpr (MASS) {  // final M (log2 units) and L of each head from the partials
+    __shared__ float fm[G], fl[G];
+    if (threadIdx.x < G) {
+      const int64_t row = ((int64_t)b * a.Hq + (int64_t)h * G + threadIdx.x) * a.P;
+      float M = -INFINITY;
+      for (int q = 0; q < a.P; ++q)
+        if (load_f32<true>(a.part_l + row + q) > 0.f) M = fmaxf(M, load_f32<true>(a.part_m + row + q) * kLog2e);
+      float L = 0.f;
+      for (int q = 0; q < a.P; ++q) {
+        const float lq = load_f32<true>(a.part_l + row + q);
+        if (lq > 0.f) L += lq * exp2f(load_f32<true>(a.part_m + row + q) * kLog2e - M);
+      }
+      fm[threadIdx.x] = M;
+      fl[threadIdx.x] = L;
+    }
+    __syncthreads();
+    finish_mass<G, KIND>(a.t, bh, b, h, a.Hq, a.bs, a.sel_cap, n, T, selp, a.tile_stats, fm, fl, a.mass);
+  }
   if (threadIdx.x == 0) a.counters[bh] = 0;  // ready for the next call
 }
 
@@ -581,6 +674,13 @@ __global__ void combine_kernel(int P, int D, const float* __restrict__ part_o, c
 
 template <int D, int G>
 static void launch_decode_dg(dim3 grid, const DecodeArgs& a, int kind, bool select, hipStream_t stream) {
+  if (a.mass != nullptr) {  // the softmax score step: flat and two-level tables
+    if (kind == NOSA_TABLE_FLAT)
+      decode_kernel<D, G, NOSA_TABLE_FLAT, 0, true><<<grid, kDecThreads, 0, stream>>>(a);
+    else
+      decode_kernel<D, G, NOSA_TABLE_TWO_LEVEL, 0, true><<<grid, kDecThreads, 0, stream>>>(a);
+    return;
+  }
   if (select) {  // flat and two-level tables, max_blocks <= kDecSelCap
     if (kind == NOSA_TABLE_FLAT)
       decode_kernel<D, G, NOSA_TABLE_FLAT, 4><<<grid, kDecThreads, 0, stream>>>(a);
@@ -681,6 +781,17 @@ hipError_t launch_select_decode(const nosa_dims& d, const uint16_t* q, const nos
   a.sel_count_w = sel_count;
   a.sw = SwapArgs{prev, prev_count, load, load_count, evict, evict_count};
   return launch_decode_args(d, a, kv.kind, true, stream);
+}
+
+hipError_t launch_decode_mass(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv, const int32_t* sel,
+                              const int32_t* sel_count, int32_t sel_cap, const int32_t* seq_lens, int32_t num_splits,
+                              float sm_scale, float* part_o, float* part_m, float* part_l, int32_t* counters, float* o,
+                              float* m, float* l, float* tile_stats, float* mass, hipStream_t stream) {
+  DecodeArgs a = decode_args(d, q, kv, sel, sel_count, sel_cap, seq_lens, num_splits, sm_scale, part_o, part_m,
+                             part_l, counters, o, m, l);
+  a.tile_stats = tile_stats;
+  a.mass = mass;
+  return launch_decode_args(d, a, kv.kind, false, stream);
 }
 
 hipError_t launch_combine(const nosa_dims& d, int32_t num_splits, const float* part_o,

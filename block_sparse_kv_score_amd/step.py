@@ -27,6 +27,10 @@ nosa_sparse_decode_combine over the resident pages.  With `buffer_slots`
 (>= the selection's capacity) HBM keeps that many slots per (b, h) and
 nosa_retrieve_buffered replaces nosa_retrieve: pages stay resident after
 they leave the selection and a bucketed LRU frees slots for misses.
+
+With `mass` the decode is nosa_sparse_decode_mass (after nosa_select_swap):
+the softmax score step adds each selected block's softmax mass per query
+head (`mass`) to O, m, l.
 """
 
 from __future__ import annotations
@@ -54,11 +58,15 @@ class DecodeSession:
 
     def __init__(self, w: Workload, inp: Inputs, splits: int | None = None, device: str = "cuda",
                  poison: bool = True, stream: torch.cuda.Stream | None = None, fused: bool = True,
-                 offload: bool = False, buffer_slots: int | None = None, bucket_width: int = 1):
+                 offload: bool = False, buffer_slots: int | None = None, bucket_width: int = 1,
+                 mass: bool = False):
         self.w, self.inp = w, inp
         self.buffered = buffer_slots is not None
         self.buffer_slots, self.bucket_width = buffer_slots, int(bucket_width)
         self.buffer_clock = 0  # the buffer's timestamps: one tick per retrieve
+        self.mass_on = mass
+        if mass and (w.table == TABLE_PACKED_ROPE or not fused):
+            raise ValueError("the softmax score step runs in the fused decode over flat or two-level tables")
         if self.buffered and not offload:
             raise ValueError("buffer_slots needs the host tier (offload=True)")
         self.fused = fused
@@ -118,6 +126,9 @@ class DecodeSession:
         self.m = torch.full((B, Hq), fill, dtype=torch.float32, device=dev)
         self.l = torch.full_like(self.m, fill)
         self.counters = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)  # fused combine arrivals
+        if mass:  # softmax score step: per-tile workspace and the block masses
+            self.tile_stats = torch.zeros(B * Hkv * self.cap * (bs // 64) * w.G * 2, dtype=torch.float32, device=dev)
+            self.mass = torch.full((B, Hq, self.cap), fill, dtype=torch.float32, device=dev)
 
         # per-step queries and appended tokens, resident before timing
         n_steps = w.n_append if w.append else 1
@@ -257,6 +268,11 @@ class DecodeSession:
 
     def decode_combine(self, t: int):
         kv = self.dev_kv if self.offload else self.kv
+        if self.mass_on:
+            nosa.nosa_sparse_decode_mass(self.dims, self.q(t), kv, self.sel, self.sel_count, self.seq_lens, self.P,
+                                         self.w.sm_scale, self.part_o, self.part_m, self.part_l, self.counters,
+                                         self.o, self.m, self.l, self.tile_stats, self.mass, self.stream)
+            return
         nosa.nosa_sparse_decode_combine(self.dims, self.q(t), kv, self.sel, self.sel_count, self.seq_lens,
                                         self.P, self.w.sm_scale, self.part_o, self.part_m, self.part_l,
                                         self.counters, self.o, self.m, self.l, self.stream)
@@ -305,7 +321,7 @@ class DecodeSession:
                     self.append(t)
                 self.swap_diff()
                 self.decode_combine(t)
-            elif self.select_decode_ok:
+            elif self.select_decode_ok and not self.mass_on:
                 self.append_score(t)
                 self.select_decode(t)
             else:

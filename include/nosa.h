@@ -265,6 +265,29 @@ nosa_status nosa_sparse_decode_combine(const nosa_dims* dims, const uint16_t* q,
                                        float* part_o, float* part_m, float* part_l, int32_t* counters,
                                        float* o, float* m, float* l, hipStream_t stream);
 
+/* nosa_sparse_decode_combine with the softmax score step [NOVITA, 2.
+ * Attention modifications: with the returned row max and l, p =
+ * exp(q.k - rowmax) / l is each key's softmax score, summed row-wise into a
+ * sparsification score].  Besides o, m, l (bit-identical to
+ * nosa_sparse_decode_combine):
+ *   mass fp32 [B][Hq][sel_cap]: mass[b][j][s] = the sum of query head j's
+ *     probabilities exp(s_t - m) / l over the present tokens of block
+ *     sel[b][h][s] (h = j / G), so each head's row sums to 1 over the
+ *     selection; entries at or past sel_count and blocks the table cannot
+ *     resolve receive 0;
+ *   tile_stats fp32 [B][Hkv][sel_cap * block_size / 64][G][2]: workspace
+ *     (per 64-token tile and head: the sum of its probabilities and the
+ *     running max they are relative to), written and read by the call.
+ * The keys are read once: the mass comes from statistics of the decode's
+ * own tiles.  Flat and two-level tables (NOSA_ERR_UNSUPPORTED for the
+ * packed RoPE kind).                                                      */
+nosa_status nosa_sparse_decode_mass(const nosa_dims* dims, const uint16_t* q, const nosa_kv* kv,
+                                    const int32_t* sel, const int32_t* sel_count, int32_t sel_cap,
+                                    const int32_t* seq_lens, int32_t num_splits, float sm_scale,
+                                    float* part_o, float* part_m, float* part_l, int32_t* counters,
+                                    float* o, float* m, float* l, float* tile_stats, float* mass,
+                                    hipStream_t stream);
+
 /* nosa_select_swap and nosa_sparse_decode_combine in one launch [SPIN 2.A:
  * Select and Attention kept as stages of one launch].  Every workgroup of
  * a (b, h) pair makes the pair's selection from score_q / score_e into

@@ -11,7 +11,10 @@ Acceptance (per pair and step):
   same for every non-empty split partial; empty splits are exactly
   (m, l, O) = (-inf, 0, 0);
 * block scores within a bound derived from the arithmetic (one fp32
-  rounding of each summary element and of the result).
+  rounding of each summary element and of the result);
+* softmax block masses (when the session computes them) within 2e-3
+  relative + 1e-6 absolute of the oracle's, and exactly 0 past the
+  selection.
 """
 
 from __future__ import annotations
@@ -28,6 +31,11 @@ from block_sparse_kv_score_amd.workloads import TABLE_PACKED_ROPE, Workload
 O_TOL = 1e-2
 LSE_TOL = 1e-3
 TIE_REL = 1e-6
+# softmax block mass: p = exp(s - LSE), so an LSE error within LSE_TOL moves
+# every probability by that relative amount, and a block's mass (a sum of
+# them) by no more; twice that, plus an absolute floor for fp32 rounding
+MASS_REL = 2e-3
+MASS_ABS = 1e-6
 
 
 @dataclass
@@ -140,6 +148,7 @@ class Gpu:
         self.part_m = s.part_m.cpu().numpy()
         self.part_l = s.part_l.cpu().numpy()
         self.err = int(s.err.cpu().numpy()[0])
+        self.mass = s.mass.cpu().numpy() if getattr(s, "mass_on", False) else None
 
 
 def compare_pair(w: Workload, inp, lg: Logical, g: Gpu, b: int, h: int, t: int, st: PairState,
@@ -187,4 +196,10 @@ def compare_pair(w: Workload, inp, lg: Logical, g: Gpu, b: int, h: int, t: int, 
         hs = slice(h * G, (h + 1) * G)
         check_attention(r, g.o[b, hs], g.m[b, hs], g.l[b, hs], g.part_o[b, hs], g.part_m[b, hs],
                         g.part_l[b, hs], where)
+        if g.mass is not None:
+            got = g.mass[b, hs, :len(sel)]
+            want = r["mass"]
+            err = np.abs(got - want)
+            assert np.all(err <= MASS_REL * want + MASS_ABS), (where, "mass", float(err.max()))
+            assert np.all(g.mass[b, hs, len(sel):] == 0), (where, "mass past the selection")
     return r

@@ -141,6 +141,14 @@ def test_host_checks_reject_bad_arguments():
     rope.k_pages = rope.v_pages = rope.e_pages = ctypes.c_void_p(4096)
     rope.num_pages, rope.kind, rope.packed = 10, nosa.NOSA_TABLE_PACKED_ROPE, ctypes.c_void_p(4096)
     assert sdec(rope) == nosa.NOSA_ERR_UNSUPPORTED
+    # softmax score step: workspace and output required, no packed RoPE kind
+    def mdec(kvd, stats=fake, mass=fake):
+        return L.nosa_sparse_decode_mass(D(d), fake, D(kvd), fake, fake, 8, fake, 1, 0.1, fake, fake, fake, fake,
+                                         fake, fake, fake, stats, mass, None)
+    assert mdec(kv, stats=None) == nosa.NOSA_ERR_ARG
+    assert mdec(kv, mass=None) == nosa.NOSA_ERR_ARG
+    rope.q_pos, rope.rope_base = ctypes.c_void_p(4096), 10000.0
+    assert mdec(rope) == nosa.NOSA_ERR_UNSUPPORTED
     # host-tier retrieve: slot count bounds, required lists
     def retr(slots, load=fake):
         return L.nosa_retrieve(D(d), D(kv), P(4096), P(8192), P(12288), slots, fake, fake, load, fake, fake, fake,

@@ -96,13 +96,13 @@ def force_slots(sess, b: int, h: int, owner: list, last_use: list | None = None)
 
 
 def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=True, fused=True, inp=None,
-                   offload=False, buffer_slots=None, bucket_width=1):
+                   offload=False, buffer_slots=None, bucket_width=1, mass=False):
     announce(f"trajectory {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T0={w.T0} k={w.k_e}/{w.k_q} "
              f"steps={steps or w.steps} P={splits or w.splits} pairs={'all' if pairs is None else pairs} "
-             f"seed={seed} fused={fused} offload={offload} buffer={buffer_slots}/{bucket_width}")
+             f"seed={seed} fused={fused} offload={offload} buffer={buffer_slots}/{bucket_width} mass={mass}")
     inp = inp if inp is not None else synth.generate(w, seed)
     sess = session(w, inp, splits=splits, fused=fused, offload=offload, buffer_slots=buffer_slots,
-                   bucket_width=bucket_width)
+                   bucket_width=bucket_width, mass=mass)
     pairs = pairs or [(b, h) for b in range(w.B) for h in range(w.Hkv)]
     lgs = {p: logical_pair(inp, *p) for p in pairs}
     states = {p: PairState() for p in pairs}
@@ -482,6 +482,46 @@ def test_buffered_equals_resident(name, scale, splits, slots, width):
                     assert torch.equal(dk[dp], a.host_k[hp]) and torch.equal(dv[dp], a.host_v[hp]), (t, b, h, x)
                     assert torch.equal(de[dp].view(torch.int32), a.host_e[hp].view(torch.int32)), (t, b, h, x)
                 assert int((own[b, h] >= 0).sum()) == int((res[b, h] >= 0).sum())
+
+
+MASS_CASES = [
+    ("tiny_nosa", {}, 2),
+    ("llama3_8b_32k", dict(B=2, Hq=8, Hkv=2, T0=4096 + 61), 1),
+    ("llama3_8b_32k", dict(B=2, Hq=8, Hkv=2, T0=4096 + 61), 3),
+    ("llama31_70b_256k", dict(B=2, Hq=16, Hkv=2, T0=16384 + 100, dir_entries=64), 4),
+    ("dense_8b_8k", dict(B=2, Hq=8, Hkv=2, T0=2048 + 40), 5),
+]
+
+
+@pytest.mark.parametrize("name,scale,splits", MASS_CASES, ids=[f"{c[0]}-P{c[2]}" for c in MASS_CASES])
+def test_softmax_mass_trajectory(name, scale, splits):
+    """The softmax score step against the oracle along a trajectory (every
+    pair, every step), with selections, swap lists and attention checked as
+    in the other trajectories."""
+    w = WORKLOADS[name].scaled(**scale) if scale else WORKLOADS[name]
+    run_trajectory(w, seed=35, splits=splits, steps=min(w.steps, 6), mass=True)
+
+
+@pytest.mark.parametrize("name,scale,splits", MASS_CASES[1:3], ids=[f"{c[0]}-P{c[2]}" for c in MASS_CASES[1:3]])
+def test_softmax_mass_keeps_attention_bits(name, scale, splits):
+    """With the score step the attention outputs are the same bits as the
+    plain fused decode, and every head's masses sum to 1."""
+    w = WORKLOADS[name].scaled(**scale)
+    announce(f"mass vs plain decode bits {name} {scale} P={splits}")
+    inp = synth.generate(w, 36)
+    a = session(w, inp, splits=splits, mass=True)
+    s = session(w, inp, splits=splits)
+    for t in range(1, 5):
+        a.step(t)
+        s.step(t)
+        torch.cuda.synchronize()
+        for n in ["sel_count", "o", "m", "l", "part_o", "part_m", "part_l"]:
+            x, y = getattr(a, n), getattr(s, n)
+            if x.dtype == torch.float32:
+                x, y = x.view(torch.int32), y.view(torch.int32)
+            assert torch.equal(x, y), (n, t)
+        assert torch.allclose(a.mass.sum(dim=2), torch.ones_like(a.m), rtol=0, atol=1e-5)
+        assert not a.counters.any().item()
 
 
 def test_offload_more_loads_than_slots_flags():
