@@ -71,6 +71,8 @@ __all__ = [
     "attend",
     "merge_partials",
     "softmax_block_mass",
+    "alibi_slopes",
+    "alibi_bias",
     "rope_inv_freq",
     "rope_rotate",
     "decode_step_bh",
@@ -309,12 +311,13 @@ def split_chunks(sel: list[int], P: int) -> list[list[int]]:
     return [list(sel[p * c:(p + 1) * c]) if c else [] for p in range(P)]
 
 
-def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, bias: np.ndarray | None = None):
     """Softmax attention of each query row over the given keys/values.
 
-    s = scale * q . k; m = max s; l = sum exp(s - m); O = sum exp(s - m) v / l.
-    q: (G, D); K, V: (n, D).  Returns O (G, D), m (G,), l (G,).  With no
-    tokens: O = 0, m = -inf, l = 0.
+    s = scale * q . k (+ bias); m = max s; l = sum exp(s - m);
+    O = sum exp(s - m) v / l.  q: (G, D); K, V: (n, D); bias: (G, n) or
+    None.  Returns O (G, D), m (G,), l (G,).  With no tokens: O = 0,
+    m = -inf, l = 0.
     """
     q = np.asarray(q, dtype=np.float64)
     G, D = q.shape
@@ -322,6 +325,8 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
     if n == 0:
         return np.zeros((G, D)), np.full(G, -np.inf), np.zeros(G)
     s = (q @ np.asarray(K, dtype=np.float64).T) * scale
+    if bias is not None:
+        s = s + np.asarray(bias, dtype=np.float64)
     m = s.max(axis=1)
     p = np.exp(s - m[:, None])
     l = p.sum(axis=1)
@@ -379,6 +384,27 @@ def softmax_block_mass(q: np.ndarray, K: np.ndarray, blocks: list[int], T: int, 
 
 
 # ---------------------------------------------------------------------------
+# ALiBi  [LAZY, generalisation: the deferred treatment of positions carries
+# over to other relative schemes, ALiBi among them]
+# ---------------------------------------------------------------------------
+
+def alibi_slopes(H: int) -> np.ndarray:
+    """Per-head ALiBi slopes.  READING (the pages name ALiBi, not its
+    slopes): the usual geometric sequence, slope_j = 2^(-8 (j + 1) / H) for
+    H a power of two."""
+    return np.power(2.0, -8.0 * (np.arange(H, dtype=np.float64) + 1.0) / H)
+
+
+def alibi_bias(slopes: np.ndarray, n: int, positions: np.ndarray) -> np.ndarray:
+    """Additive attention bias of a query at position n over keys at the
+    given positions: -slope * (n - position), one row per head.  Nothing is
+    stored with the keys, so the bias is applied at attention time."""
+    slopes = np.asarray(slopes, dtype=np.float64)
+    d = float(n) - np.asarray(positions, dtype=np.float64)
+    return -slopes[:, None] * d[None, :]
+
+
+# ---------------------------------------------------------------------------
 # Rotary position embedding  [LAZY, decoding + mathematical equivalence]
 # ---------------------------------------------------------------------------
 
@@ -403,7 +429,7 @@ def rope_rotate(x: np.ndarray, pos, base: float) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def decode_step_bh(q_group, K, V, e, T, bs, ss, k_e, k_q, evicted, prev_sel,
-                   num_splits, scale, select_all=False, rope=None):
+                   num_splits, scale, select_all=False, rope=None, alibi=None):
     """The whole step for one (sequence, KV head), from already-appended
     inputs, in the order the pages give: score, select, set differences,
     attention.
@@ -418,6 +444,10 @@ def decode_step_bh(q_group, K, V, e, T, bs, ss, k_e, k_q, evicted, prev_sel,
              Rot(n) q (READING: stored keys carry their in-document
              rotation).
     select_all: skip scoring and take every block (deferred-RoPE workload).
+    alibi:   None, or the group's (G,) slopes: attention adds
+             alibi_bias(slopes, T - 1, token positions) (READING: the query
+             sits at the newest token's position T - 1, and selection scores
+             stay as without ALiBi).
 
     Returns a dict with block scores, the selection, swap lists, per-split
     partials, the merged (O, m, l) and each selected block's softmax mass
@@ -449,16 +479,20 @@ def decode_step_bh(q_group, K, V, e, T, bs, ss, k_e, k_q, evicted, prev_sel,
     else:
         Kt, qt = K[:T], q_group
 
+    def bias(toks):
+        return None if alibi is None else alibi_bias(alibi, T - 1, toks)
+
     parts = []
     for chunk in split_chunks(gamma, num_splits):
         toks = tokens_of_blocks(chunk, T, bs)
-        parts.append(attend(qt, Kt[toks], V[toks], scale))
+        parts.append(attend(qt, Kt[toks], V[toks], scale, bias(toks)))
     G, D = qt.shape
     part_o = np.stack([p[0] for p in parts], axis=1)   # (G, P, D)
     part_m = np.stack([p[1] for p in parts], axis=1)   # (G, P)
     part_l = np.stack([p[2] for p in parts], axis=1)
     toks = tokens_of_blocks(gamma, T, bs)
-    O, m, l = attend(qt, Kt[toks], V[toks], scale)
+    O, m, l = attend(qt, Kt[toks], V[toks], scale, bias(toks))
     out.update(part_o=part_o, part_m=part_m, part_l=part_l, O=O, m=m, l=l)
-    out["mass"] = softmax_block_mass(qt, Kt, gamma, T, bs, scale)
+    if alibi is None:
+        out["mass"] = softmax_block_mass(qt, Kt, gamma, T, bs, scale)
     return out

@@ -427,6 +427,53 @@ def check_softmax_block_mass(O, seed=10):
         assert np.abs(flat - counts / counts.sum()).max() <= 1e-12
 
 
+def check_alibi(O, seed=11):
+    """ALiBi: the slopes' values, a hand-worked softmax over bias alone,
+    attention with the bias against torch's float64 SDPA with the same
+    additive mask (and its log-sum-exp against torch.logsumexp), zero
+    slopes = plain attention, and a whole dense step against SDPA."""
+    assert O.alibi_slopes(8).tolist() == [2.0 ** -k for k in range(1, 9)]
+    assert np.allclose(O.alibi_slopes(4), [2.0 ** -2, 2.0 ** -4, 2.0 ** -6, 2.0 ** -8], rtol=0, atol=0)
+    # zero query: weights exp(-ln2 (2 - j)) = 1/4, 1/2, 1 over positions 0, 1, 2
+    b = O.alibi_bias(np.array([math.log(2.0)]), 2, np.arange(3))
+    Ob, mb, lb = O.attend(np.zeros((1, 1)), np.ones((3, 1)), np.arange(3, dtype=np.float64)[:, None], 1.0, b)
+    assert abs(Ob[0, 0] - 10.0 / 7.0) <= 1e-15 and mb[0] == 0.0 and abs(lb[0] - 7.0 / 4.0) <= 1e-15
+    rng = np.random.default_rng(seed)
+    for G, n, D in [(2, 5, 8), (4, 70, 32), (8, 130, 64)]:
+        q = rng.standard_normal((G, D))
+        K = rng.standard_normal((n, D))
+        V = rng.standard_normal((n, D))
+        pos = np.sort(rng.choice(4 * n, n, replace=False))
+        slopes = O.alibi_slopes(G)
+        qpos = int(pos[-1]) + int(rng.integers(0, 5))
+        bias = O.alibi_bias(slopes, qpos, pos)
+        scale = 1 / math.sqrt(D)
+        Ow, m, l = O.attend(q, K, V, scale, bias)
+        t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            t(q)[:, None], t(K)[None].expand(G, n, D), t(V)[None].expand(G, n, D), attn_mask=t(bias)[:, None],
+            scale=scale)[:, 0].numpy()
+        assert np.abs(Ow - ref).max() <= 1e-12
+        lse = torch.logsumexp(t(q) @ t(K).T * scale + t(bias), dim=1).numpy()
+        assert np.abs(m + np.log(l) - lse).max() <= 1e-12
+        O0 = O.attend(q, K, V, scale, O.alibi_bias(np.zeros(G), qpos, pos))
+        assert np.abs(O0[0] - _sdpa(q, K, V, scale)).max() <= 1e-12
+    # the whole step, every block selected, against SDPA over all tokens
+    G, D, T, bs = 4, 16, 150, 16
+    q = rng.standard_normal((G, D))
+    K = rng.standard_normal((T, D))
+    V = rng.standard_normal((T, D))
+    slopes = O.alibi_slopes(G)
+    r = O.decode_step_bh(q, K, V, np.zeros(T), T, bs, bs, 0, 64, set(), [], 3, 1 / math.sqrt(D),
+                         select_all=True, alibi=slopes)
+    bias = O.alibi_bias(slopes, T - 1, np.arange(T))
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        t(q)[:, None], t(K)[None].expand(G, T, D), t(V)[None].expand(G, T, D), attn_mask=t(bias)[:, None],
+        scale=1 / math.sqrt(D))[:, 0].numpy()
+    assert np.abs(r["O"] - ref).max() <= 1e-12
+
+
 # ---------------------------------------------------------------------------
 # rotary embedding and the deferred (lazy) rotation
 # ---------------------------------------------------------------------------
@@ -541,6 +588,6 @@ ALL_CHECKS = [
     check_pool_closed_form, check_pool_linearity, check_eviction_pre_exp,
     check_select_bruteforce, check_select_sizes, check_trajectory_invariants,
     check_swap_lists, check_place_blocks, check_buffer_retrieve, check_rope_complex, check_rope_identities,
-    check_softmax_block_mass, check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
+    check_softmax_block_mass, check_alibi, check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
     check_bf16_decode,
 ]

@@ -28,6 +28,8 @@ _place = O.place_blocks
 _bucket = O.recency_bucket
 _buffer = O.buffer_retrieve
 _mass = O.softmax_block_mass
+_abias = O.alibi_bias
+_aslopes = O.alibi_slopes
 _qscore = O.query_token_scores
 _freq = O.rope_inv_freq
 
@@ -154,6 +156,18 @@ def _mass_no_scale(q, K, blocks, T, bs, scale):
     return _mass(q, K, blocks, T, bs, 1.0)
 
 
+def _alibi_sign(slopes, n, positions):
+    return -_abias(slopes, n, positions)
+
+
+def _alibi_from_origin(slopes, n, positions):
+    return _abias(slopes, 0, positions)  # slope * position: the same softmax, another row max
+
+
+def _alibi_slopes_reversed(H):
+    return _aslopes(H)[::-1].copy()
+
+
 def _rotate_sign(x, pos, base):
     return _rotate(x, -np.asarray(pos), base)
 
@@ -199,6 +213,9 @@ MUTANTS = [
     ("softmax_block_mass", _mass_unnormalised, P.check_softmax_block_mass),
     ("softmax_block_mass", _mass_blocks_reversed, P.check_softmax_block_mass),
     ("softmax_block_mass", _mass_no_scale, P.check_softmax_block_mass),
+    ("alibi_bias", _alibi_sign, P.check_alibi),
+    ("alibi_bias", _alibi_from_origin, P.check_alibi),
+    ("alibi_slopes", _alibi_slopes_reversed, P.check_alibi),
     ("rope_rotate", _rotate_sign, P.check_rope_complex),
     ("rope_rotate", _rotate_pairs_adjacent, P.check_rope_complex),
     ("rope_inv_freq", _freq_wrong_exponent, P.check_rope_complex),
