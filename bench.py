@@ -64,6 +64,8 @@ def parse(argv=None):
     ap.add_argument("--bucket-width", type=int, default=1, help="steps per recency bucket of the buffer")
     ap.add_argument("--mass", action="store_true",
                     help="decode with the softmax score step (nosa_sparse_decode_mass): block masses per head")
+    ap.add_argument("--alibi", action="store_true",
+                    help="decode with ALiBi biases (nosa_sparse_decode_alibi), slopes 2^(-8(j+1)/Hq)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with one plain 1 GiB device copy, a known-size kernel for counter calibration")
     return ap.parse_args(argv)
@@ -182,7 +184,7 @@ def main(argv=None) -> int:
         args.offload = True
     sess = DecodeSession(w, inp, splits=args.splits, poison=False, fused=not args.unfused or args.offload,
                          offload=args.offload, buffer_slots=args.buffer_slots, bucket_width=args.bucket_width,
-                         mass=args.mass)
+                         mass=args.mass, alibi=args.alibi)
     stream = torch.cuda.current_stream()
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
 
@@ -223,7 +225,7 @@ def main(argv=None) -> int:
     elif fused:
         if w.select_all:
             names = (["append"] if w.append else []) + ["swap_diff", "decode_combine"]
-        elif sess.select_decode_ok and not sess.mass_on:
+        elif sess.select_decode_ok and not sess.mass_on and not sess.alibi_on:
             names = ["append_score", "select_decode"]
         else:
             names = ["append_score", "select_swap", "decode_combine"]
@@ -303,12 +305,14 @@ def main(argv=None) -> int:
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
         if tr.get("decode_sources_sha256_16") == source_hash(DECODE_SRCS) and tr.get("workload") == w.name \
-                and tr.get("splits") == sess.P and tr.get("entry_point") == dec_name and not sess.mass_on:
+                and tr.get("splits") == sess.P and tr.get("entry_point") == dec_name and not sess.mass_on \
+                and not sess.alibi_on:
             traffic = tr.get("bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
                 "kernel": {"select_decode": "nosa_select_decode",
                            "decode_combine": ("nosa_sparse_decode_mass" if sess.mass_on
+                                              else "nosa_sparse_decode_alibi" if sess.alibi_on
                                               else "nosa_sparse_decode_combine"),
                            "decode": "nosa_sparse_decode"}[dec_name] + " (decode_kernel)",
                 "algorithmic_bytes_per_launch": int(kvb), "avg_launch_us": round(kernels_us[dec_name], 2)}
@@ -328,7 +332,7 @@ def main(argv=None) -> int:
                    "resident_slots_per_pair": sess.slots, "retrieve_bytes_per_step": int(rb),
                    "pages_per_pair_per_step": round(rb / page_bytes / (w.B * w.Hkv), 2),
                    "host_link_gbps": round(r_gbps, 2),
-                   "buffer_slots": sess.buffer_slots, "softmax_mass": sess.mass_on, "bucket_width": sess.bucket_width if sess.buffered else None,
+                   "buffer_slots": sess.buffer_slots, "softmax_mass": sess.mass_on, "alibi": sess.alibi_on, "bucket_width": sess.bucket_width if sess.buffered else None,
                    "selected_pages_resident_before_retrieve": round(1.0 - misses / max(selected, 1), 4),
                    "retrieve_bytes_per_step_p10_p90": [int(np.percentile(retrieved, 10)),
                                                        int(np.percentile(retrieved, 90))]}
@@ -351,7 +355,8 @@ def main(argv=None) -> int:
         + (" [host tier: pages in pinned host memory]" if sess.offload and not sess.buffered else "")
         + (f" [host tier: pages in pinned host memory, {sess.slots}-slot HBM buffer per (b, h)]"
            if sess.buffered else "")
-        + (" [with the softmax score step]" if sess.mass_on else ""),
+        + (" [with the softmax score step]" if sess.mass_on else "")
+        + (" [ALiBi]" if sess.alibi_on else ""),
         "value": round(w.B / t_step, 1),
         "unit": "tokens/s",
         "n_gpus": 1,

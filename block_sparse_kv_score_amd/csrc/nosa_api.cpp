@@ -232,6 +232,24 @@ nosa_status nosa_sparse_decode_mass(const nosa_dims* dims, const uint16_t* q, co
                                            part_o, part_m, part_l, counters, o, m, l, tile_stats, mass, stream));
 }
 
+nosa_status nosa_sparse_decode_alibi(const nosa_dims* dims, const uint16_t* q, const nosa_kv* kv,
+                                     const int32_t* sel, const int32_t* sel_count, int32_t sel_cap,
+                                     const int32_t* seq_lens, int32_t num_splits, float sm_scale,
+                                     const float* alibi_slopes, float* part_o, float* part_m, float* part_l,
+                                     int32_t* counters, float* o, float* m, float* l, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if ((st = check_kv(dims, kv, true)) != NOSA_OK) return st;
+  if (!q || !sel || !sel_count || !seq_lens || !part_o || !part_m || !part_l || !alibi_slopes) return NOSA_ERR_ARG;
+  if (!counters || !o || !m || !l) return NOSA_ERR_ARG;
+  if (!aligned16(q)) return NOSA_ERR_ARG;
+  if (sel_cap < 1 || num_splits < 1 || num_splits > 256) return NOSA_ERR_ARG;
+  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return NOSA_ERR_ARG;
+  if (kv->kind == NOSA_TABLE_PACKED_ROPE) return NOSA_ERR_UNSUPPORTED;
+  return from_hip(nosa::launch_decode_alibi(*dims, q, *kv, sel, sel_count, sel_cap, seq_lens, num_splits, sm_scale,
+                                            alibi_slopes, part_o, part_m, part_l, counters, o, m, l, stream));
+}
+
 nosa_status nosa_select_decode(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* q, const float* score_q,
                                const float* score_e, const int32_t* seq_lens, int32_t k_e, int32_t k_q,
                                const uint32_t* evicted_in, uint32_t* evicted_out, int32_t* sel, int32_t sel_cap,

@@ -48,6 +48,11 @@
 // combine turns them into each selected block's softmax mass per query
 // head, mass = sum over the block's tiles of l_t 2^(m_t - M) / L, with the
 // final M and L.  K is not read again.
+//
+// ALiBi (LazyAttention summary, generalisation to other relative position
+// schemes): keys carry no position, and each score gets -slope_j (n - t)
+// for key position t and query position n = T - 1, added in the tile loop
+// from the tile's first position; nothing else changes.
 
 #include "nosa_launch.hpp"
 #include "nosa_select_impl.hpp"
@@ -94,6 +99,8 @@ struct DecodeArgs {
   // softmax score step (MASS variants only)
   float* tile_stats;  // [B*Hkv][sel_cap * bs/64][G][2]: tile sum of p, running max (log2 units)
   float* mass;        // [B][Hq][sel_cap]
+  // ALiBi (ALIBI variants only)
+  const float* alibi;  // [Hq] slopes
 };
 
 constexpr int kDecSelCap = 4 * kSelThreads;  // capacity of the select variants (SR = 4)
@@ -269,8 +276,8 @@ __device__ __forceinline__ void finish_mass(const Table& t, int bh, int b, int h
 
 // SR > 0: the select variant (SR elements per thread of the selection,
 // covering max_blocks <= SR * kSelThreads).  MASS: the softmax score step
-// (SR == 0 with the fused combine only).
-template <int D, int G, int KIND, int SR, bool MASS = false>
+// (SR == 0 with the fused combine only).  ALIBI: ALiBi biases (SR == 0).
+template <int D, int G, int KIND, int SR, bool MASS = false, bool ALIBI = false>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs a) {
   constexpr bool ROPE = KIND == NOSA_TABLE_PACKED_ROPE;
   using S = DecodeShape<D, G, ROPE>;
@@ -342,6 +349,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
   uint32_t cur_doc = 0xffffffffu;
 
   float m_run = -INFINITY, l_run = 0.f;  // for head slot cg, log2 units
+  // ALiBi slope of head slot cg in log2 units, and the query position
+  const float slope = ALIBI && real ? a.alibi[h * G + cg] * kLog2e : 0.f;
+  const int qn = T - 1;
   floatx4 oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -349,7 +359,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
   // Tile k of this split: block sel[j0 + k / tpb], 64-token slice k % tpb.
   // Returns the next tile >= k with data, skipping (and flagging) entries the
   // table cannot resolve; ntiles when there is none.
-  auto next_tile = [&](int k, int64_t& page, int& ntok, uint32_t& docb, int& sub) -> int {
+  auto next_tile = [&](int k, int64_t& page, int& ntok, uint32_t& docb, int& sub, int& pos0) -> int {
     for (; k < ntiles; k += kDecWaves) {
       // the LDS list is read by name (LDS instructions): through a generic
       // pointer every read would also wait for the in-flight tile loads
@@ -368,6 +378,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
         if (lane == 0) flag_error(a.t.err);
         continue;
       }
+      if constexpr (ALIBI) pos0 = i * a.bs + sub * kTile;
       ntok = min(kTile, T - (i * a.bs + sub * kTile));
       if (ntok > 0) return k;
     }
@@ -386,9 +397,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
   uint4 kr[TH][NDS];
   uint4 vr[2][NDT];
   int64_t page = 0;
-  int ntok = 0, sub = 0;
+  int ntok = 0, sub = 0, pos0 = 0;
   uint32_t docb = 0;
-  int k = next_tile(w, page, ntok, docb, sub);
+  int k = next_tile(w, page, ntok, docb, sub, pos0);
   if (k < ntiles) {
     const uint4* kpg = k_ptr(page, sub);
 #pragma unroll
@@ -408,9 +419,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
   // loads in flight while it computes.
   while (k < ntiles) {
     int64_t npage = 0;
-    int nntok = 0, nsub = 0;
+    int nntok = 0, nsub = 0, npos0 = 0;
     uint32_t ndocb = 0;
-    const int nk = next_tile(k + kDecWaves, npage, nntok, ndocb, nsub);
+    const int nk = next_tile(k + kDecWaves, npage, nntok, ndocb, nsub, npos0);
 
     // Slots past the end hold stale page data.  A row of the q.k MFMA mixes
     // tokens of every token set (the query is zero outside a set's slots),
@@ -465,7 +476,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
         float x = acc[e];
         if constexpr (ROPE) x += lane_xor<G>(x);  // hi + lo parts
         const int tok = th * TPM + 16 * cset + 4 * lq + e;
-        sv[th][e] = tok < ntok ? x * a.scale_log2 : -INFINITY;
+        if constexpr (ALIBI)
+          sv[th][e] = tok < ntok ? x * a.scale_log2 - slope * (float)(qn - (pos0 + tok)) : -INFINITY;
+        else
+          sv[th][e] = tok < ntok ? x * a.scale_log2 : -INFINITY;
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -555,6 +569,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
     ntok = nntok;
     sub = nsub;
     docb = ndocb;
+    if constexpr (ALIBI) pos0 = npos0;
   }
 
   // per-wave totals: sum the token sets of each head slot, then the lanes
@@ -674,6 +689,13 @@ __global__ void combine_kernel(int P, int D, const float* __restrict__ part_o, c
 
 template <int D, int G>
 static void launch_decode_dg(dim3 grid, const DecodeArgs& a, int kind, bool select, hipStream_t stream) {
+  if (a.alibi != nullptr) {  // ALiBi: flat and two-level tables
+    if (kind == NOSA_TABLE_FLAT)
+      decode_kernel<D, G, NOSA_TABLE_FLAT, 0, false, true><<<grid, kDecThreads, 0, stream>>>(a);
+    else
+      decode_kernel<D, G, NOSA_TABLE_TWO_LEVEL, 0, false, true><<<grid, kDecThreads, 0, stream>>>(a);
+    return;
+  }
   if (a.mass != nullptr) {  // the softmax score step: flat and two-level tables
     if (kind == NOSA_TABLE_FLAT)
       decode_kernel<D, G, NOSA_TABLE_FLAT, 0, true><<<grid, kDecThreads, 0, stream>>>(a);
@@ -791,6 +813,17 @@ hipError_t launch_decode_mass(const nosa_dims& d, const uint16_t* q, const nosa_
                              part_l, counters, o, m, l);
   a.tile_stats = tile_stats;
   a.mass = mass;
+  return launch_decode_args(d, a, kv.kind, false, stream);
+}
+
+hipError_t launch_decode_alibi(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv, const int32_t* sel,
+                               const int32_t* sel_count, int32_t sel_cap, const int32_t* seq_lens,
+                               int32_t num_splits, float sm_scale, const float* alibi_slopes, float* part_o,
+                               float* part_m, float* part_l, int32_t* counters, float* o, float* m, float* l,
+                               hipStream_t stream) {
+  DecodeArgs a = decode_args(d, q, kv, sel, sel_count, sel_cap, seq_lens, num_splits, sm_scale, part_o, part_m,
+                             part_l, counters, o, m, l);
+  a.alibi = alibi_slopes;
   return launch_decode_args(d, a, kv.kind, false, stream);
 }
 

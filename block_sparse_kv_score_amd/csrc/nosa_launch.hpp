@@ -82,6 +82,12 @@ hipError_t launch_decode_mass(const nosa_dims& d, const uint16_t* q, const nosa_
                               float sm_scale, float* part_o, float* part_m, float* part_l, int32_t* counters, float* o,
                               float* m, float* l, float* tile_stats, float* mass, hipStream_t stream);
 
+hipError_t launch_decode_alibi(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv, const int32_t* sel,
+                               const int32_t* sel_count, int32_t sel_cap, const int32_t* seq_lens,
+                               int32_t num_splits, float sm_scale, const float* alibi_slopes, float* part_o,
+                               float* part_m, float* part_l, int32_t* counters, float* o, float* m, float* l,
+                               hipStream_t stream);
+
 hipError_t launch_combine(const nosa_dims& d, int32_t num_splits, const float* part_o,
                           const float* part_m, const float* part_l, float* o, float* m, float* l,
                           hipStream_t stream);

@@ -38,6 +38,7 @@ ENTRY_POINTS = [
     "nosa_sparse_decode_combine",
     "nosa_select_decode",
     "nosa_sparse_decode_mass",
+    "nosa_sparse_decode_alibi",
     "nosa_combine",
     "nosa_retrieve",
     "nosa_retrieve_buffered",
@@ -107,6 +108,8 @@ _SIGNATURES = {
                            _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P],
     "nosa_sparse_decode_mass": [_DIMS, _P, _KV, _P, _P, _I32, _P, _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _P],
+    "nosa_sparse_decode_alibi": [_DIMS, _P, _KV, _P, _P, _I32, _P, _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _P],
     "nosa_combine": [_DIMS, _I32, _P, _P, _P, _P, _P, _P, _P],
     "nosa_retrieve": [_DIMS, _KV, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P],
     "nosa_retrieve_buffered": [_DIMS, _KV, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P],
@@ -324,6 +327,19 @@ def nosa_sparse_decode_mass(dims, q, kv, sel, sel_count, seq_lens, num_splits, s
           _dev(counters, "counters", (torch.int32,)), _dev(o, "o", (torch.float32,)),
           _dev(m, "m", (torch.float32,)), _dev(l, "l", (torch.float32,)),
           _dev(tile_stats, "tile_stats", (torch.float32,)), _dev(mass, "mass", (torch.float32,)), _stream(stream))
+
+
+def nosa_sparse_decode_alibi(dims, q, kv, sel, sel_count, seq_lens, num_splits, sm_scale, alibi_slopes, part_o,
+                             part_m, part_l, counters, o, m, l, stream=None):
+    """nosa_sparse_decode_combine with ALiBi biases (alibi_slopes: fp32 [Hq])."""
+    _call("nosa_sparse_decode_alibi", ctypes.byref(dims), _dev(q, "q", _BF16_LIKE), ctypes.byref(kv),
+          _dev(sel, "sel", (torch.int32,)), _dev(sel_count, "sel_count", (torch.int32,)),
+          int(sel.shape[-1]), _dev(seq_lens, "seq_lens", (torch.int32,)), int(num_splits),
+          float(sm_scale), _dev(alibi_slopes, "alibi_slopes", (torch.float32,)),
+          _dev(part_o, "part_o", (torch.float32,)),
+          _dev(part_m, "part_m", (torch.float32,)), _dev(part_l, "part_l", (torch.float32,)),
+          _dev(counters, "counters", (torch.int32,)), _dev(o, "o", (torch.float32,)),
+          _dev(m, "m", (torch.float32,)), _dev(l, "l", (torch.float32,)), _stream(stream))
 
 
 SELECT_DECODE_MAX_BLOCKS = 1024

@@ -30,7 +30,8 @@ they leave the selection and a bucketed LRU frees slots for misses.
 
 With `mass` the decode is nosa_sparse_decode_mass (after nosa_select_swap):
 the softmax score step adds each selected block's softmax mass per query
-head (`mass`) to O, m, l.
+head (`mass`) to O, m, l.  With `alibi` it is nosa_sparse_decode_alibi,
+with the slopes of the synthetic inputs.
 """
 
 from __future__ import annotations
@@ -38,7 +39,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import nosa
+from . import nosa, synth
 from .synth import Inputs
 from .workloads import TABLE_FLAT, TABLE_PACKED_ROPE, TABLE_TWO_LEVEL, Workload
 
@@ -59,7 +60,7 @@ class DecodeSession:
     def __init__(self, w: Workload, inp: Inputs, splits: int | None = None, device: str = "cuda",
                  poison: bool = True, stream: torch.cuda.Stream | None = None, fused: bool = True,
                  offload: bool = False, buffer_slots: int | None = None, bucket_width: int = 1,
-                 mass: bool = False):
+                 mass: bool = False, alibi: bool = False):
         self.w, self.inp = w, inp
         self.buffered = buffer_slots is not None
         self.buffer_slots, self.bucket_width = buffer_slots, int(bucket_width)
@@ -67,6 +68,9 @@ class DecodeSession:
         self.mass_on = mass
         if mass and (w.table == TABLE_PACKED_ROPE or not fused):
             raise ValueError("the softmax score step runs in the fused decode over flat or two-level tables")
+        self.alibi_on = alibi
+        if alibi and (w.table == TABLE_PACKED_ROPE or not fused or mass):
+            raise ValueError("ALiBi runs in the fused decode over flat or two-level tables, without the mass step")
         if self.buffered and not offload:
             raise ValueError("buffer_slots needs the host tier (offload=True)")
         self.fused = fused
@@ -126,6 +130,8 @@ class DecodeSession:
         self.m = torch.full((B, Hq), fill, dtype=torch.float32, device=dev)
         self.l = torch.full_like(self.m, fill)
         self.counters = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)  # fused combine arrivals
+        if alibi:  # per query head slopes
+            self.alibi_slopes = torch.from_numpy(synth.alibi_slopes(Hq)).to(dev)
         if mass:  # softmax score step: per-tile workspace and the block masses
             self.tile_stats = torch.zeros(B * Hkv * self.cap * (bs // 64) * w.G * 2, dtype=torch.float32, device=dev)
             self.mass = torch.full((B, Hq, self.cap), fill, dtype=torch.float32, device=dev)
@@ -268,6 +274,11 @@ class DecodeSession:
 
     def decode_combine(self, t: int):
         kv = self.dev_kv if self.offload else self.kv
+        if self.alibi_on:
+            nosa.nosa_sparse_decode_alibi(self.dims, self.q(t), kv, self.sel, self.sel_count, self.seq_lens, self.P,
+                                          self.w.sm_scale, self.alibi_slopes, self.part_o, self.part_m, self.part_l,
+                                          self.counters, self.o, self.m, self.l, self.stream)
+            return
         if self.mass_on:
             nosa.nosa_sparse_decode_mass(self.dims, self.q(t), kv, self.sel, self.sel_count, self.seq_lens, self.P,
                                          self.w.sm_scale, self.part_o, self.part_m, self.part_l, self.counters,
@@ -321,7 +332,7 @@ class DecodeSession:
                     self.append(t)
                 self.swap_diff()
                 self.decode_combine(t)
-            elif self.select_decode_ok and not self.mass_on:
+            elif self.select_decode_ok and not self.mass_on and not self.alibi_on:
                 self.append_score(t)
                 self.select_decode(t)
             else:

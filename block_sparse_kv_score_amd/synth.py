@@ -101,6 +101,12 @@ def queries(w: Workload, seed: int, step: int) -> np.ndarray:
 # page tables
 # ---------------------------------------------------------------------------
 
+def alibi_slopes(n_heads: int) -> np.ndarray:
+    """Per-head ALiBi slopes for the synthetic runs (an input of the
+    ALiBi decode, like the queries): 2^(-8 (j + 1) / n_heads), float32."""
+    return np.power(2.0, -8.0 * (np.arange(n_heads) + 1.0) / n_heads).astype(np.float32)
+
+
 def page_ids(w: Workload, seed: int) -> np.ndarray:
     """(B, Hkv, max_blocks) int32 physical page of each *storage* block: a
     random permutation of range(num_pages)."""

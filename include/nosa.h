@@ -288,6 +288,23 @@ nosa_status nosa_sparse_decode_mass(const nosa_dims* dims, const uint16_t* q, co
                                     float* o, float* m, float* l, float* tile_stats, float* mass,
                                     hipStream_t stream);
 
+/* nosa_sparse_decode_combine with ALiBi position biases [LAZY,
+ * generalisation: the deferred treatment of positions carries over to
+ * relative schemes such as ALiBi; keys are stored without positions and
+ * the bias is applied at attention time]:
+ *   s = sm_scale * q_j . k_t - alibi_slopes[j] * (n - t)
+ * for query head j, key position t (its logical token index) and query
+ * position n = seq_lens[b] - 1 (the newest token); everything else as
+ * nosa_sparse_decode_combine.
+ *   alibi_slopes fp32 [Hq] (device), e.g. 2^(-8 (j + 1) / Hq).
+ * Flat and two-level tables (NOSA_ERR_UNSUPPORTED for the packed RoPE
+ * kind).                                                                  */
+nosa_status nosa_sparse_decode_alibi(const nosa_dims* dims, const uint16_t* q, const nosa_kv* kv,
+                                     const int32_t* sel, const int32_t* sel_count, int32_t sel_cap,
+                                     const int32_t* seq_lens, int32_t num_splits, float sm_scale,
+                                     const float* alibi_slopes, float* part_o, float* part_m, float* part_l,
+                                     int32_t* counters, float* o, float* m, float* l, hipStream_t stream);
+
 /* nosa_select_swap and nosa_sparse_decode_combine in one launch [SPIN 2.A:
  * Select and Attention kept as stages of one launch].  Every workgroup of
  * a (b, h) pair makes the pair's selection from score_q / score_e into

@@ -58,14 +58,17 @@ def logical_pair(inp: synth.Inputs, b: int, h: int) -> Logical:
 
 
 def oracle_step(w: Workload, inp: synth.Inputs, lg: Logical, b: int, h: int, t: int,
-                st: PairState, P: int) -> dict:
+                st: PairState, P: int, alibi: bool = False) -> dict:
     T = w.seq_len(t)
     q = oracle.bf16_to_f64(inp.q(t)[b, h * w.G:(h + 1) * w.G])
     rope = None
     if w.table == TABLE_PACKED_ROPE:
         rope = dict(q_pos=int(inp.q_pos[b]), block_start=synth.block_doc_start(w) * w.bs, base=w.rope_base)
+    slopes = None
+    if alibi:  # the group's slopes, as the HIP path receives them (float32)
+        slopes = synth.alibi_slopes(w.Hq)[h * w.G:(h + 1) * w.G].astype(np.float64)
     return oracle.decode_step_bh(q, lg.K, lg.V, lg.e, T, w.bs, w.ss, w.k_e, w.k_q, st.evicted, st.prev,
-                                 P, 1.0 / math.sqrt(w.D), select_all=w.select_all, rope=rope)
+                                 P, 1.0 / math.sqrt(w.D), select_all=w.select_all, rope=rope, alibi=slopes)
 
 
 def bitmap_set(words: np.ndarray, nb: int) -> set:
@@ -152,12 +155,12 @@ class Gpu:
 
 
 def compare_pair(w: Workload, inp, lg: Logical, g: Gpu, b: int, h: int, t: int, st: PairState,
-                 P: int, log: list, check_scores: bool = True) -> dict:
+                 P: int, log: list, check_scores: bool = True, alibi: bool = False) -> dict:
     """Compare one pair at step t; returns the oracle result.  Selection
     mismatches must be near-ties (logged); attention is then not compared
     for this pair and step because the two sides attend over different
     blocks."""
-    r = oracle_step(w, inp, lg, b, h, t, st, P)
+    r = oracle_step(w, inp, lg, b, h, t, st, P, alibi)
     where = f"{w.name} t={t} b={b} h={h}"
     nb = r["nb"]
     G = w.G

@@ -149,6 +149,12 @@ def test_host_checks_reject_bad_arguments():
     assert mdec(kv, mass=None) == nosa.NOSA_ERR_ARG
     rope.q_pos, rope.rope_base = ctypes.c_void_p(4096), 10000.0
     assert mdec(rope) == nosa.NOSA_ERR_UNSUPPORTED
+    # ALiBi decode: slopes required, no packed RoPE kind
+    def adec(kvd, slopes=fake):
+        return L.nosa_sparse_decode_alibi(D(d), fake, D(kvd), fake, fake, 8, fake, 1, 0.1, slopes, fake, fake, fake,
+                                          fake, fake, fake, fake, None)
+    assert adec(kv, slopes=None) == nosa.NOSA_ERR_ARG
+    assert adec(rope) == nosa.NOSA_ERR_UNSUPPORTED
     # host-tier retrieve: slot count bounds, required lists
     def retr(slots, load=fake):
         return L.nosa_retrieve(D(d), D(kv), P(4096), P(8192), P(12288), slots, fake, fake, load, fake, fake, fake,

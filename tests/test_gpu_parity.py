@@ -96,13 +96,14 @@ def force_slots(sess, b: int, h: int, owner: list, last_use: list | None = None)
 
 
 def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=True, fused=True, inp=None,
-                   offload=False, buffer_slots=None, bucket_width=1, mass=False):
+                   offload=False, buffer_slots=None, bucket_width=1, mass=False, alibi=False):
     announce(f"trajectory {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T0={w.T0} k={w.k_e}/{w.k_q} "
              f"steps={steps or w.steps} P={splits or w.splits} pairs={'all' if pairs is None else pairs} "
-             f"seed={seed} fused={fused} offload={offload} buffer={buffer_slots}/{bucket_width} mass={mass}")
+             f"seed={seed} fused={fused} offload={offload} buffer={buffer_slots}/{bucket_width} mass={mass} "
+             f"alibi={alibi}")
     inp = inp if inp is not None else synth.generate(w, seed)
     sess = session(w, inp, splits=splits, fused=fused, offload=offload, buffer_slots=buffer_slots,
-                   bucket_width=bucket_width, mass=mass)
+                   bucket_width=bucket_width, mass=mass, alibi=alibi)
     pairs = pairs or [(b, h) for b in range(w.B) for h in range(w.Hkv)]
     lgs = {p: logical_pair(inp, *p) for p in pairs}
     states = {p: PairState() for p in pairs}
@@ -125,7 +126,7 @@ def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=
             last_use = sess.last_use.cpu().numpy()
             miss_count = sess.miss_count.cpu().numpy()
         for (b, h) in pairs:
-            r = compare_pair(w, inp, lgs[(b, h)], g, b, h, t, states[(b, h)], sess.P, log, check_scores)
+            r = compare_pair(w, inp, lgs[(b, h)], g, b, h, t, states[(b, h)], sess.P, log, check_scores, alibi)
             n = int(g.sel_count[b, h])
             same = g.sel[b, h, :n].tolist() == r["sel"]
             if offload and sess.buffered:
@@ -522,6 +523,29 @@ def test_softmax_mass_keeps_attention_bits(name, scale, splits):
             assert torch.equal(x, y), (n, t)
         assert torch.allclose(a.mass.sum(dim=2), torch.ones_like(a.m), rtol=0, atol=1e-5)
         assert not a.counters.any().item()
+
+
+ALIBI_CASES = [
+    ("tiny_nosa", {}, 2),
+    ("llama3_8b_32k", dict(B=2, Hq=8, Hkv=2, T0=4096 + 61), 1),
+    ("llama31_70b_256k", dict(B=2, Hq=16, Hkv=2, T0=16384 + 100, dir_entries=64), 4),
+    ("dense_8b_8k", dict(B=2, Hq=8, Hkv=2, T0=2048 + 40), 5),
+]
+
+
+@pytest.mark.parametrize("name,scale,splits", ALIBI_CASES, ids=[f"{c[0]}-P{c[2]}" for c in ALIBI_CASES])
+def test_alibi_trajectory(name, scale, splits):
+    """ALiBi decode against the oracle (bias -slope (n - t) at attention
+    time) along a trajectory, every pair and step."""
+    w = WORKLOADS[name].scaled(**scale) if scale else WORKLOADS[name]
+    run_trajectory(w, seed=37, splits=splits, steps=min(w.steps, 6), alibi=True)
+
+
+def test_alibi_full_size_sampled():
+    """ALiBi at the 8B shape @32K in the benchmark's launch configuration,
+    sampled pairs against the oracle."""
+    w = WORKLOADS["llama3_8b_32k"]
+    run_trajectory(w, seed=38, steps=2, alibi=True, pairs=[(0, 0), (9, 4), (31, 7)])
 
 
 def test_offload_more_loads_than_slots_flags():
