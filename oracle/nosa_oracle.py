@@ -442,7 +442,7 @@ def decode_step_bh(q_group, K, V, e, T, bs, ss, k_e, k_q, evicted, prev_sel,
              position of the document holding each block, base=...).  Keys
              are then materialised as Rot(doc start) k_stored and queries as
              Rot(n) q (READING: stored keys carry their in-document
-             rotation).
+             rotation), for the query-aware scores as for attention.
     select_all: skip scoring and take every block (deferred-RoPE workload).
     alibi:   None, or the group's (G,) slopes: attention adds
              alibi_bias(slopes, T - 1, token positions) (READING: the query
@@ -455,20 +455,6 @@ def decode_step_bh(q_group, K, V, e, T, bs, ss, k_e, k_q, evicted, prev_sel,
     """
     nb = num_blocks(T, bs)
     out: dict = {"nb": nb}
-    if select_all:
-        gamma_e, gamma_q, gamma = [], list(range(nb)), list(range(nb))
-        evicted_after = set(evicted)
-    else:
-        s_q = query_token_scores(q_group, K[:T])
-        s_e = eviction_token_scores(e[:T])
-        S_q = pool_block_scores(s_q, T, bs, ss)
-        E = pool_block_scores(s_e, T, bs, ss)
-        out["S_q"], out["E"] = S_q, E
-        gamma_e, gamma_q, gamma, evicted_after = select_blocks(S_q, E, nb, k_e, k_q, evicted)
-    load, drop = swap_lists(prev_sel, gamma)
-    out.update(gamma_e=gamma_e, gamma_q=gamma_q, sel=gamma, evicted=evicted_after,
-               load=load, evict=drop)
-
     if rope is not None:
         Kt = np.empty((T, K.shape[1]))
         starts = np.asarray(rope["block_start"], dtype=np.float64)
@@ -478,6 +464,19 @@ def decode_step_bh(q_group, K, V, e, T, bs, ss, k_e, k_q, evicted, prev_sel,
         qt = rope_rotate(q_group, rope["q_pos"], rope["base"])
     else:
         Kt, qt = K[:T], q_group
+    if select_all:
+        gamma_e, gamma_q, gamma = [], list(range(nb)), list(range(nb))
+        evicted_after = set(evicted)
+    else:
+        s_q = query_token_scores(qt, Kt)  # with RoPE: the rotated query and keys
+        s_e = eviction_token_scores(e[:T])
+        S_q = pool_block_scores(s_q, T, bs, ss)
+        E = pool_block_scores(s_e, T, bs, ss)
+        out["S_q"], out["E"] = S_q, E
+        gamma_e, gamma_q, gamma, evicted_after = select_blocks(S_q, E, nb, k_e, k_q, evicted)
+    load, drop = swap_lists(prev_sel, gamma)
+    out.update(gamma_e=gamma_e, gamma_q=gamma_q, sel=gamma, evicted=evicted_after,
+               load=load, evict=drop)
 
     def bias(toks):
         return None if alibi is None else alibi_bias(alibi, T - 1, toks)

@@ -474,6 +474,41 @@ def check_alibi(O, seed=11):
     assert np.abs(r["O"] - ref).max() <= 1e-12
 
 
+def check_rope_scores(O, seed=12):
+    """Query-aware block scores with deferred RoPE against the complex-number
+    form of the rotated dot product (q and k as D/2 complex numbers turned by
+    e^(i n theta) and e^(i start theta); the real part of q conj(k)), pooled
+    by explicit loops; and with every document starting at the query
+    position they reduce to the unrotated scores of the stored keys."""
+    rng = np.random.default_rng(seed)
+    G, D, bs, ss, base = 2, 16, 8, 4, 500.0
+    T = 45
+    nb = -(-T // bs)
+    q = rng.standard_normal((G, D))
+    K = rng.standard_normal((T, D))
+    V = rng.standard_normal((T, D))
+    starts = np.repeat([0.0, 16.0, 24.0, 40.0], 2)[:nb]  # documents of 2 blocks
+    n = 77
+    r = O.decode_step_bh(q, K, V, np.zeros(T), T, bs, ss, 2, 2, set(), [], 1, 1 / math.sqrt(D),
+                         rope=dict(q_pos=n, block_start=starts, base=base))
+    theta = base ** (-2.0 * np.arange(D // 2) / D)
+    qc = (q[:, :D // 2] + 1j * q[:, D // 2:]) * np.exp(1j * n * theta)
+    want = np.full(nb, -np.inf)
+    for i in range(nb):
+        for lo in range(i * bs, min(T, (i + 1) * bs), ss):
+            hi = min(lo + ss, T, (i + 1) * bs)
+            vals = []
+            for t in range(lo, hi):
+                kc = (K[t, :D // 2] + 1j * K[t, D // 2:]) * np.exp(1j * starts[i] * theta)
+                vals.append(np.mean(np.real(qc @ np.conj(kc))) / math.sqrt(D))
+            want[i] = max(want[i], float(np.mean(vals)))
+    assert np.abs(r["S_q"] - want).max() <= 1e-12, np.abs(r["S_q"] - want).max()
+    r0 = O.decode_step_bh(q, K, V, np.zeros(T), T, bs, ss, 2, 2, set(), [], 1, 1 / math.sqrt(D),
+                          rope=dict(q_pos=n, block_start=np.full(nb, float(n)), base=base))
+    plain = O.pool_block_scores(O.query_token_scores(q, K), T, bs, ss)
+    assert np.abs(r0["S_q"] - plain).max() <= 1e-12
+
+
 # ---------------------------------------------------------------------------
 # rotary embedding and the deferred (lazy) rotation
 # ---------------------------------------------------------------------------
@@ -588,6 +623,6 @@ ALL_CHECKS = [
     check_pool_closed_form, check_pool_linearity, check_eviction_pre_exp,
     check_select_bruteforce, check_select_sizes, check_trajectory_invariants,
     check_swap_lists, check_place_blocks, check_buffer_retrieve, check_rope_complex, check_rope_identities,
-    check_softmax_block_mass, check_alibi, check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
+    check_softmax_block_mass, check_alibi, check_rope_scores, check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
     check_bf16_decode,
 ]

@@ -168,6 +168,10 @@ def _alibi_slopes_reversed(H):
     return _aslopes(H)[::-1].copy()
 
 
+def _rotate_none(x, pos, base):
+    return np.asarray(x, dtype=np.float64)
+
+
 def _rotate_sign(x, pos, base):
     return _rotate(x, -np.asarray(pos), base)
 
@@ -216,6 +220,7 @@ MUTANTS = [
     ("alibi_bias", _alibi_sign, P.check_alibi),
     ("alibi_bias", _alibi_from_origin, P.check_alibi),
     ("alibi_slopes", _alibi_slopes_reversed, P.check_alibi),
+    ("rope_rotate", _rotate_none, P.check_rope_scores),
     ("rope_rotate", _rotate_sign, P.check_rope_complex),
     ("rope_rotate", _rotate_pairs_adjacent, P.check_rope_complex),
     ("rope_inv_freq", _freq_wrong_exponent, P.check_rope_complex),
