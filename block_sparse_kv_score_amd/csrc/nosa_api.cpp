@@ -159,6 +159,12 @@ nosa_status nosa_append_score(const nosa_dims* dims, const nosa_kv* kv, const ui
   }
   if (!seq_lens_in || !k_summary || !e_summary || !q || !score_q || !score_e) return NOSA_ERR_ARG;
   if (!aligned16(k_summary)) return NOSA_ERR_ARG;
+  if (kv->kind == NOSA_TABLE_PACKED_ROPE) {  // scoring with the rotated query; no append
+    if (append) return NOSA_ERR_UNSUPPORTED;
+    if (!kv->q_pos || !(kv->rope_base > 1.f)) return NOSA_ERR_ARG;
+    const int nsub = dims->block_size / dims->sub_block;
+    if (nsub < 4 || nsub > 16) return NOSA_ERR_UNSUPPORTED;
+  }
   return from_hip(nosa::launch_append_score(*dims, *kv, k_new, v_new, e_new, seq_lens_in, seq_lens_out, k_summary,
                                             e_summary, q, score_q, score_e, stream));
 }

@@ -25,6 +25,15 @@
 // The new length is written to a second buffer (seq_lens_out), never to
 // the one every workgroup reads (seq_lens_in), so no reader can see it
 // early.
+//
+// Deferred RoPE (packed table; scoring only).  Stored keys carry only their
+// in-document rotation (LazyAttention summary, 2. Decoding), so the
+// query-aware score of a block in the document starting at position st is
+// taken with the group's mean query turned by (n - st): by linearity of the
+// rotation and the mean, Rot(n - st) qbar . kbar_stored equals the mean of
+// Rot(n) q_g . Rot(st) k over the sub-block.  Each wave keeps the rotated
+// mean query of each of its blocks in LDS (float64), computing a rotation
+// (one sincos per lane) only where the document changes.
 
 #include "nosa_launch.hpp"
 #include "nosa_summary.hpp"
@@ -35,6 +44,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFusedThreads = 256;
 constexpr int kStageTok = 32;  // older tokens staged through LDS per pass
+constexpr int kRopeBlocksPerWave = 4;  // RoPE scoring: nsub >= 4 (SPW / nsub blocks per wave)
 
 struct FusedArgs {
   Table t;
@@ -54,7 +64,19 @@ struct FusedArgs {
   const uint16_t* q;
   float* score_q;
   float* score_e;
+  // deferred RoPE (packed table): query positions [B] and the base
+  const int32_t* q_pos;
+  double rope_base;
 };
+
+// The group's mean query turned by (n - start) for every block of this wave
+// (RoPE scoring): rq[w][bw][d] for block bw of wave w.
+template <int D, bool ROPE>
+struct RopeSmem {
+  double rq[kFusedThreads / kWave][kRopeBlocksPerWave][D];
+};
+template <int D>
+struct RopeSmem<D, false> {};
 
 template <int D>
 struct FusedSmem {
@@ -158,14 +180,16 @@ __device__ void append_token(const FusedArgs& a, FusedSmem<D>& sh, int bh, int p
   if (lane == 0) epage[r] = a.e_new[bh];
 }
 
-// L lanes per sub-block (see score_kernel).
-template <int D, int L>
+// L lanes per sub-block (see score_kernel).  ROPE: packed table, scoring
+// only, nsub >= 4.
+template <int D, int L, bool ROPE = false>
 __global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const FusedArgs a) {
   constexpr int NQ = D / 4;
   constexpr int QL = NQ / L;
   constexpr int SPW = kWave / L;
   constexpr int SPG = SPW * (kFusedThreads / kWave);
   __shared__ FusedSmem<D> sh;
+  __shared__ RopeSmem<D, ROPE> rsh;
   const Table& t = a.t;
   const int bh = blockIdx.y;
   const int Hkv = t.Hkv;
@@ -239,6 +263,39 @@ __global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const Fused
   }
   __syncthreads();  // qbar, and the append's summary
 
+  if constexpr (ROPE) {
+    // rotated mean query of each of this wave's blocks (document starts
+    // from the packed words; one rotation per document change)
+    if (work) {
+      const int nsb = SPW / nsub;  // blocks of this wave (<= kRopeBlocksPerWave)
+      const int blk0 = (s0 + w * SPW) / nsub;
+      uint32_t docw = 0;
+      if (lane < nsb && blk0 + lane < MB) {
+        (void)page_of<NOSA_TABLE_PACKED_ROPE>(t, bh, blk0 + lane, docw);
+      }
+      const double theta = lane < D / 2 ? pow(a.rope_base, -2.0 * (double)lane / (double)D) : 0.0;
+      const int64_t n = a.q_pos[b];
+      int64_t cur = -1;
+      for (int bw = 0; bw < nsb; ++bw) {
+        const int64_t st = (int64_t)__builtin_amdgcn_readlane((int)docw, bw) * bs;
+        if (lane < D / 2) {
+          if (st != cur) {
+            double sv, cv;
+            sincos((double)(n - st) * theta, &sv, &cv);
+            const double x1 = sh.qbar[lane], x2 = sh.qbar[lane + D / 2];
+            rsh.rq[w][bw][lane] = x1 * cv - x2 * sv;
+            rsh.rq[w][bw][lane + D / 2] = x2 * cv + x1 * sv;
+          } else {
+            rsh.rq[w][bw][lane] = rsh.rq[w][bw - 1][lane];
+            rsh.rq[w][bw][lane + D / 2] = rsh.rq[w][bw - 1][lane + D / 2];
+          }
+        }
+        cur = st;
+        wave_lds_sync();
+      }
+    }
+  }
+
   if (work) {
     if (lead && s == sT && sh.have_new) {  // this step's summary of the new token's sub-block
 #pragma unroll
@@ -248,13 +305,25 @@ __global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const Fused
     const int i = s / nsub, j = s % nsub;
     const bool valid = i < nb && i * bs + j * ss < T;
     double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+    if constexpr (ROPE) {
+      const double* rq = rsh.rq[w][(lane % SPW) / nsub];
 #pragma unroll
-    for (int u = 0; u < QL; ++u) {
-      const int d = 4 * (part * QL + u);
-      a0 = fma((double)v[u].x, sh.qbar[d + 0], a0);
-      a1 = fma((double)v[u].y, sh.qbar[d + 1], a1);
-      a2 = fma((double)v[u].z, sh.qbar[d + 2], a2);
-      a3 = fma((double)v[u].w, sh.qbar[d + 3], a3);
+      for (int u = 0; u < QL; ++u) {
+        const int d = 4 * (part * QL + u);
+        a0 = fma((double)v[u].x, rq[d + 0], a0);
+        a1 = fma((double)v[u].y, rq[d + 1], a1);
+        a2 = fma((double)v[u].z, rq[d + 2], a2);
+        a3 = fma((double)v[u].w, rq[d + 3], a3);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < QL; ++u) {
+        const int d = 4 * (part * QL + u);
+        a0 = fma((double)v[u].x, sh.qbar[d + 0], a0);
+        a1 = fma((double)v[u].y, sh.qbar[d + 1], a1);
+        a2 = fma((double)v[u].z, sh.qbar[d + 2], a2);
+        a3 = fma((double)v[u].w, sh.qbar[d + 3], a3);
+      }
     }
     double dot = (a0 + a1) + (a2 + a3);
     dot = xor_reduce<SPW, kWave>(dot, [](double x, double y) { return x + y; });  // the L slices
@@ -291,12 +360,21 @@ hipError_t launch_append_score(const nosa_dims& d, const nosa_kv& kv, const uint
   a.q = q;
   a.score_q = score_q;
   a.score_e = score_e;
+  a.q_pos = kv.q_pos;
+  a.rope_base = (double)kv.rope_base;
   const int nsub = d.block_size / d.sub_block;
   const int CS = d.max_blocks * nsub;
   const int L = nsub <= 16 ? 4 : (nsub <= 32 ? 2 : 1);  // as score_kernel
   const int spg = (kWave / L) * (kFusedThreads / kWave);
   const dim3 grid((CS + spg - 1) / spg, d.batch * d.n_kv_heads);
 #define NOSA_APPEND_SCORE(DD, LL) append_score_kernel<DD, LL><<<grid, kFusedThreads, 0, stream>>>(a)
+  if (kv.kind == NOSA_TABLE_PACKED_ROPE) {  // scoring only, nsub in [4, 16] (L == 4)
+    if (d.head_dim == 128)
+      append_score_kernel<128, 4, true><<<grid, kFusedThreads, 0, stream>>>(a);
+    else
+      append_score_kernel<64, 4, true><<<grid, kFusedThreads, 0, stream>>>(a);
+    return hipGetLastError();
+  }
   if (d.head_dim == 128) {
     if (L == 4) NOSA_APPEND_SCORE(128, 4);
     else if (L == 2) NOSA_APPEND_SCORE(128, 2);

@@ -137,7 +137,7 @@ class DecodeSession:
             self.mass = torch.full((B, Hq, self.cap), fill, dtype=torch.float32, device=dev)
 
         # per-step queries and appended tokens, resident before timing
-        n_steps = w.n_append if w.append else 1
+        n_steps = w.n_append if w.append else max(1, w.steps)
         self.q_all = torch.from_numpy(np.stack([inp.q(t).view(np.int16) for t in range(1, n_steps + 1)])).to(dev)
         if w.append:
             A = w.n_append
@@ -221,6 +221,12 @@ class DecodeSession:
                          self.seq_lens, self.k_summary, self.e_summary, self.stream)
 
     def score(self, t: int):
+        if self.w.table == TABLE_PACKED_ROPE:
+            # scores need the per-document query rotation: the descriptor-aware
+            # scoring of nosa_append_score (no append on this table kind)
+            nosa.nosa_append_score(self.dims, self.kv, None, None, None, self.seq_lens, None, self.k_summary,
+                                   self.e_summary, self.q(t), self.score_q, self.score_e, self.stream)
+            return
         nosa.nosa_score_blocks(self.dims, self.q(t), self.k_summary, self.e_summary, self.seq_lens,
                                self.score_q, self.score_e, self.stream)
 

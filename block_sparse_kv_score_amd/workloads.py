@@ -1,4 +1,4 @@
-"""The five decode-step workloads, as named presets.
+"""The decode-step workloads, as named presets.
 
 Shapes follow the model families the pages measure on (a Llama-3-8B-shaped
 layer and a Llama-3.1-70B-shaped layer) and their context lengths; the data
@@ -111,6 +111,11 @@ WORKLOADS = {
                  bs=64, ss=16, k_e=0, k_q=512, splits=8, table=TABLE_PACKED_ROPE,
                  append=False, select_all=True, rope_base=500000.0,
                  n_docs=8, doc_len=4096),
+        # 6: the same deferred-RoPE cache with NOSA selection (64 of 512
+        # blocks): query-aware scores with the per-document rotated query
+        Workload(6, "lazy_rope_sparse_32k", B=64, Hq=32, Hkv=8, D=128, T0=32768, steps=4,
+                 bs=64, ss=16, k_e=32, k_q=32, splits=1, table=TABLE_PACKED_ROPE,
+                 append=False, rope_base=500000.0, n_docs=8, doc_len=4096),
     ]
 }
 

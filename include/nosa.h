@@ -173,7 +173,9 @@ nosa_status nosa_append(const nosa_dims* dims, const nosa_kv* kv,
  *   score_e[b][h][i] = max over non-empty sub-blocks of the mean eviction
  *                      logit (raw logits, no exponent).
  *   q: bf16 [B][Hq][D].  score_q, score_e: fp32 [B][Hkv][max_blocks];
- * entries i >= nb are not written.                                         */
+ * entries i >= nb are not written.  The query is taken as stored keys are:
+ * for a cache with deferred RoPE (packed table) score through
+ * nosa_append_score, which takes the descriptor and rotates the query.    */
 nosa_status nosa_score_blocks(const nosa_dims* dims, const uint16_t* q,
                               const float* k_summary, const float* e_summary, const int32_t* seq_lens,
                               float* score_q, float* score_e, hipStream_t stream);
@@ -218,7 +220,15 @@ nosa_status nosa_select_swap(const nosa_dims* dims, const float* score_q, const 
  *     differ from seq_lens_in; ignored (may be NULL) without one;
  *   k_summary, e_summary, q, score_q, score_e: as nosa_append /
  *     nosa_score_blocks.
- * Scoring uses the lengths after the append.                              */
+ * Scoring uses the lengths after the append.
+ * With a NOSA_TABLE_PACKED_ROPE descriptor (scoring only: no append, and
+ * 4 <= block_size / sub_block <= 16, else NOSA_ERR_UNSUPPORTED; q_pos and
+ * rope_base required) the stored keys carry their in-document rotation
+ * [LAZY, 2. Decoding], and score_q of a block in the document starting at
+ * position st is taken with the group's mean query turned by q_pos[b] - st:
+ *   score_q[i] = max_j Rot(q_pos - st) qbar . kbar_ij / sqrt(D),
+ * which equals the sub-block mean of Rot(q_pos) q . Rot(st) k_stored over
+ * the group; score_e is as without RoPE.                                  */
 nosa_status nosa_append_score(const nosa_dims* dims, const nosa_kv* kv,
                               const uint16_t* k_new, const uint16_t* v_new, const float* e_new,
                               const int32_t* seq_lens_in, int32_t* seq_lens_out,

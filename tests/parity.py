@@ -122,10 +122,14 @@ def score_bound(w: Workload, lg: Logical, q: np.ndarray, T: int) -> np.ndarray:
     qbar = np.abs(q.mean(axis=0))
     nb = -(-T // w.bs)
     out = np.zeros(nb)
+    rope = w.table == TABLE_PACKED_ROPE
     for i in range(nb):
         for r in oracle.subblock_token_ranges(i, T, w.bs, w.ss):
             kbar = np.abs(lg.K[r.start:r.stop].mean(axis=0))
-            out[i] = max(out[i], float(kbar @ qbar) / math.sqrt(w.D))
+            # with deferred RoPE the query is rotated: bound its products by
+            # norms (the rotation keeps them), |rq|.|kbar| <= ||qbar|| ||kbar||
+            x = float(np.linalg.norm(qbar) * np.linalg.norm(kbar)) if rope else float(kbar @ qbar)
+            out[i] = max(out[i], x / math.sqrt(w.D))
     return out * 2.0 ** -22
 
 

@@ -201,6 +201,7 @@ FUSED_CASES = [
     ("dense_8b_8k", dict(B=2, Hq=8, Hkv=2, T0=1000), 37),
     ("llama31_70b_256k", dict(B=2, Hq=16, Hkv=2, T0=16384 + 100, dir_entries=64), 16),
     ("lazy_rope_32k", dict(B=2, Hq=8, Hkv=2, T0=8 * 512, doc_len=512), 9),
+    ("lazy_rope_sparse_32k", dict(B=2, Hq=8, Hkv=2, T0=8 * 512, doc_len=512), 2),
 ]
 
 
@@ -254,6 +255,19 @@ def test_dense_small_many_splits():
 def test_lazy_rope_small():
     w = WORKLOADS["lazy_rope_32k"].scaled(B=2, Hq=8, Hkv=2, T0=8 * 512, doc_len=512)
     run_trajectory(w, seed=4)
+
+
+def test_lazy_rope_sparse_small():
+    """NOSA selection over a deferred-RoPE cache: query-aware scores with the
+    per-document rotated query, then the rotated decode over the selection."""
+    w = WORKLOADS["lazy_rope_sparse_32k"].scaled(B=2, Hq=8, Hkv=2, T0=8 * 512, doc_len=512)
+    run_trajectory(w, seed=39)
+
+
+def test_lazy_rope_sparse_g8_split():
+    w = WORKLOADS["lazy_rope_sparse_32k"].scaled(B=1, Hq=16, Hkv=2, T0=4 * 1024, doc_len=1024, n_docs=4,
+                                                   k_e=8, k_q=24, splits=3)
+    run_trajectory(w, seed=40)
 
 
 def test_lazy_rope_g8_and_g1():
@@ -586,6 +600,11 @@ def test_8b_32k_full_sampled():
 def test_70b_256k_full_sampled():
     w = WORKLOADS["llama31_70b_256k"]
     run_trajectory(w, seed=0, pairs=[(0, 0), (3, 5), (7, 7)])
+
+
+def test_lazy_rope_sparse_32k_full_sampled():
+    w = WORKLOADS["lazy_rope_sparse_32k"]
+    run_trajectory(w, seed=0, steps=2, pairs=[(0, 0), (33, 5), (63, 7)])
 
 
 def test_lazy_rope_32k_full_sampled():
