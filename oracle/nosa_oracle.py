@@ -59,6 +59,8 @@ __all__ = [
     "subblock_token_ranges",
     "query_token_scores",
     "eviction_token_scores",
+    "split_qkv",
+    "eviction_head",
     "pool_block_scores",
     "top_by_score",
     "select_blocks",
@@ -92,6 +94,32 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     """
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Index-side inputs  [NOSA, NOSI kernel fusion: the eviction head, the QKV
+# split and pooling run in one kernel]
+# ---------------------------------------------------------------------------
+
+def split_qkv(row: np.ndarray, Hq: int, Hkv: int, D: int):
+    """One token's fused QKV projection row, [q heads | k heads | v heads]
+    (READING: the usual concatenated layout), into q (Hq, D), k (Hkv, D)
+    and v (Hkv, D)."""
+    row = np.asarray(row)
+    q = row[:Hq * D].reshape(Hq, D)
+    k = row[Hq * D:(Hq + Hkv) * D].reshape(Hkv, D)
+    v = row[(Hq + Hkv) * D:(Hq + 2 * Hkv) * D].reshape(Hkv, D)
+    return q, k, v
+
+
+def eviction_head(v: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Eviction logits of the query-agnostic selection [NOSA, dual selection:
+    a DMA-inspired eviction head scores tokens independently of the query;
+    ED-DMA: no exponent before selection].  READING: per KV head a learned
+    linear map of the token's value vector, e = w_h . v, evaluated in
+    float64 and stored as float32 (one logit per token and KV head).
+    v: (..., D) float64; w: (D,).  Returns float32 logits (...)."""
+    return (np.asarray(v, dtype=np.float64) @ np.asarray(w, dtype=np.float64)).astype(np.float32)
 
 
 # ---------------------------------------------------------------------------

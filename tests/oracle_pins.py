@@ -509,6 +509,31 @@ def check_rope_scores(O, seed=12):
     assert np.abs(r0["S_q"] - plain).max() <= 1e-12
 
 
+def check_index_inputs(O, seed=13):
+    """QKV split and eviction head: a hand-built row splits into the blocks
+    it was made of; a one-hot weight reads one value dim exactly; the head is
+    linear in the weights; and it matches an explicit float64 loop over dims,
+    rounded once to float32."""
+    Hq, Hkv, D = 4, 2, 3
+    row = np.arange((Hq + 2 * Hkv) * D)
+    q, k, v = O.split_qkv(row, Hq, Hkv, D)
+    assert q[1, 2] == 5 and k[0, 0] == 12 and k[1, 2] == 17 and v[0, 0] == 18 and v[1, 2] == 23
+    assert q.shape == (4, 3) and k.shape == (2, 3) and v.shape == (2, 3)
+    rng = np.random.default_rng(seed)
+    V = rng.standard_normal((50, 8))
+    onehot = np.zeros(8)
+    onehot[5] = 1.0
+    assert np.array_equal(O.eviction_head(V, onehot), V[:, 5].astype(np.float32))
+    w1, w2 = rng.standard_normal(8), rng.standard_normal(8)
+    e = O.eviction_head(V, w1 + w2).astype(np.float64)
+    assert np.abs(e - (O.eviction_head(V, w1).astype(np.float64) + O.eviction_head(V, w2))).max() <= 1e-5
+    for t in range(50):
+        acc = 0.0
+        for d in range(8):
+            acc += float(V[t, d]) * float(w1[d])
+        assert O.eviction_head(V[t], w1) == np.float32(acc)
+
+
 # ---------------------------------------------------------------------------
 # rotary embedding and the deferred (lazy) rotation
 # ---------------------------------------------------------------------------
@@ -623,6 +648,6 @@ ALL_CHECKS = [
     check_pool_closed_form, check_pool_linearity, check_eviction_pre_exp,
     check_select_bruteforce, check_select_sizes, check_trajectory_invariants,
     check_swap_lists, check_place_blocks, check_buffer_retrieve, check_rope_complex, check_rope_identities,
-    check_softmax_block_mass, check_alibi, check_rope_scores, check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
+    check_softmax_block_mass, check_alibi, check_rope_scores, check_index_inputs, check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
     check_bf16_decode,
 ]

@@ -30,6 +30,8 @@ _buffer = O.buffer_retrieve
 _mass = O.softmax_block_mass
 _abias = O.alibi_bias
 _aslopes = O.alibi_slopes
+_split = O.split_qkv
+_ehead = O.eviction_head
 _qscore = O.query_token_scores
 _freq = O.rope_inv_freq
 
@@ -172,6 +174,15 @@ def _rotate_none(x, pos, base):
     return np.asarray(x, dtype=np.float64)
 
 
+def _split_kv_swapped(row, Hq, Hkv, D):
+    q, k, v = _split(row, Hq, Hkv, D)
+    return q, v, k
+
+
+def _ehead_on_exp(v, w):
+    return _ehead(np.exp(np.asarray(v, dtype=np.float64)), w)
+
+
 def _rotate_sign(x, pos, base):
     return _rotate(x, -np.asarray(pos), base)
 
@@ -221,6 +232,8 @@ MUTANTS = [
     ("alibi_bias", _alibi_from_origin, P.check_alibi),
     ("alibi_slopes", _alibi_slopes_reversed, P.check_alibi),
     ("rope_rotate", _rotate_none, P.check_rope_scores),
+    ("split_qkv", _split_kv_swapped, P.check_index_inputs),
+    ("eviction_head", _ehead_on_exp, P.check_index_inputs),
     ("rope_rotate", _rotate_sign, P.check_rope_complex),
     ("rope_rotate", _rotate_pairs_adjacent, P.check_rope_complex),
     ("rope_inv_freq", _freq_wrong_exponent, P.check_rope_complex),
