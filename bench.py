@@ -66,6 +66,9 @@ def parse(argv=None):
                     help="decode with the softmax score step (nosa_sparse_decode_mass): block masses per head")
     ap.add_argument("--alibi", action="store_true",
                     help="decode with ALiBi biases (nosa_sparse_decode_alibi), slopes 2^(-8(j+1)/Hq)")
+    ap.add_argument("--qkv", action="store_true",
+                    help="the step's input is each sequence's fused projection row: nosa_append_score_qkv "
+                         "(QKV split + eviction head + pooling + scoring in one launch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with one plain 1 GiB device copy, a known-size kernel for counter calibration")
     return ap.parse_args(argv)
@@ -184,7 +187,7 @@ def main(argv=None) -> int:
         args.offload = True
     sess = DecodeSession(w, inp, splits=args.splits, poison=False, fused=not args.unfused or args.offload,
                          offload=args.offload, buffer_slots=args.buffer_slots, bucket_width=args.bucket_width,
-                         mass=args.mass, alibi=args.alibi)
+                         mass=args.mass, alibi=args.alibi, qkv=args.qkv)
     stream = torch.cuda.current_stream()
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
 
@@ -332,7 +335,7 @@ def main(argv=None) -> int:
                    "resident_slots_per_pair": sess.slots, "retrieve_bytes_per_step": int(rb),
                    "pages_per_pair_per_step": round(rb / page_bytes / (w.B * w.Hkv), 2),
                    "host_link_gbps": round(r_gbps, 2),
-                   "buffer_slots": sess.buffer_slots, "softmax_mass": sess.mass_on, "alibi": sess.alibi_on, "bucket_width": sess.bucket_width if sess.buffered else None,
+                   "buffer_slots": sess.buffer_slots, "softmax_mass": sess.mass_on, "alibi": sess.alibi_on, "qkv_rows": sess.qkv_on, "bucket_width": sess.bucket_width if sess.buffered else None,
                    "selected_pages_resident_before_retrieve": round(1.0 - misses / max(selected, 1), 4),
                    "retrieve_bytes_per_step_p10_p90": [int(np.percentile(retrieved, 10)),
                                                        int(np.percentile(retrieved, 90))]}
@@ -356,7 +359,8 @@ def main(argv=None) -> int:
         + (f" [host tier: pages in pinned host memory, {sess.slots}-slot HBM buffer per (b, h)]"
            if sess.buffered else "")
         + (" [with the softmax score step]" if sess.mass_on else "")
-        + (" [ALiBi]" if sess.alibi_on else ""),
+        + (" [ALiBi]" if sess.alibi_on else "")
+        + (" [input: fused QKV rows + eviction head]" if sess.qkv_on else ""),
         "value": round(w.B / t_step, 1),
         "unit": "tokens/s",
         "n_gpus": 1,

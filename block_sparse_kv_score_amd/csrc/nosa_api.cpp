@@ -169,6 +169,23 @@ nosa_status nosa_append_score(const nosa_dims* dims, const nosa_kv* kv, const ui
                                             e_summary, q, score_q, score_e, stream));
 }
 
+nosa_status nosa_append_score_qkv(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* qkv,
+                                  const float* w_evict, const int32_t* seq_lens_in, int32_t* seq_lens_out,
+                                  float* k_summary, float* e_summary, uint16_t* q_out, float* score_q,
+                                  float* score_e, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if ((st = check_kv(dims, kv, true)) != NOSA_OK) return st;
+  if (kv->kind == NOSA_TABLE_PACKED_ROPE) return NOSA_ERR_UNSUPPORTED;
+  if (!qkv || !w_evict || !seq_lens_in || !seq_lens_out || !k_summary || !e_summary || !q_out || !score_q ||
+      !score_e)
+    return NOSA_ERR_ARG;
+  if (seq_lens_out == seq_lens_in) return NOSA_ERR_ARG;
+  if (!aligned16(qkv) || !aligned16(q_out) || !aligned16(k_summary)) return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_append_score_qkv(*dims, *kv, qkv, w_evict, seq_lens_in, seq_lens_out, k_summary,
+                                                e_summary, q_out, score_q, score_e, stream));
+}
+
 nosa_status nosa_swap_diff(const nosa_dims* dims, int32_t cap, const int32_t* prev, const int32_t* prev_count,
                            const int32_t* cur, const int32_t* cur_count, int32_t* load, int32_t* load_count,
                            int32_t* evict, int32_t* evict_count, hipStream_t stream) {

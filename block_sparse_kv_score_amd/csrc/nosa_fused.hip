@@ -34,6 +34,13 @@
 // Rot(n) q_g . Rot(st) k over the sub-block.  Each wave keeps the rotated
 // mean query of each of its blocks in LDS (float64), computing a rotation
 // (one sincos per lane) only where the document changes.
+//
+// QKV input (nosa_append_score_qkv; NOSA summary, Methodology 2: NOSI fuses
+// the eviction head, the QKV split and pooling into one kernel).  The new
+// token arrives as each sequence's fused projection row [q | k | v]; k and v
+// are read from the row, the eviction logit is the head's w_h . v (float64,
+// one rounding to fp32), the group's query for scoring comes from the row,
+// and one workgroup per pair writes the split query out for the decode.
 
 #include "nosa_launch.hpp"
 #include "nosa_summary.hpp"
@@ -67,6 +74,10 @@ struct FusedArgs {
   // deferred RoPE (packed table): query positions [B] and the base
   const int32_t* q_pos;
   double rope_base;
+  // QKV input (QKV variants): fused projection rows, eviction head, split query
+  const uint16_t* qkv;   // [B][(Hq + 2 Hkv) D]
+  const float* w_evict;  // [Hkv][D]
+  uint16_t* q_out;       // [B][Hq][D]
 };
 
 // The group's mean query turned by (n - start) for every block of this wave
@@ -96,7 +107,8 @@ struct FusedSmem {
 // sum_logits do, adds the new token, and writes the summary (global memory
 // and sh.knew / sh.enew) and the token itself.  Mirrors append_kernel.
 template <int D>
-__device__ void append_token(const FusedArgs& a, FusedSmem<D>& sh, int bh, int pos, int64_t page) {
+__device__ void append_token(const FusedArgs& a, FusedSmem<D>& sh, int bh, int pos, int64_t page,
+                             const uint16_t* kn, const uint16_t* vn, float e_new) {
   constexpr int NQ = D / 4;
   constexpr int NO = D / 8;  // 16-byte octets per key row
   constexpr int VL = D / kWave;
@@ -149,8 +161,6 @@ __device__ void append_token(const FusedArgs& a, FusedSmem<D>& sh, int bh, int p
     __syncthreads();  // the staging buffers are reused by the next pass
   }
   if (w != 0) return;
-  const uint16_t* kn = a.k_new + (int64_t)bh * D;
-  const uint16_t* vn = a.v_new + (int64_t)bh * D;
   const double inv_n = 1.0 / (double)(r - lo + 1);
   const int s = i * nsub + j;
   if (lane < NQ) {
@@ -167,7 +177,7 @@ __device__ void append_token(const FusedArgs& a, FusedSmem<D>& sh, int bh, int p
     reinterpret_cast<f4*>(a.k_summary)[((int64_t)bh * NQ + lane) * CS + s] = o;
     sh.knew[lane] = o;
   } else if (lane == NQ) {
-    ae += (double)a.e_new[bh];
+    ae += (double)e_new;
     const float em = (float)(ae * inv_n);
     a.e_summary[(int64_t)bh * CS + s] = em;
     sh.enew = em;
@@ -177,12 +187,13 @@ __device__ void append_token(const FusedArgs& a, FusedSmem<D>& sh, int bh, int p
   if (lane < NO) reinterpret_cast<uint4*>(kpage)[lane * bs + r] = reinterpret_cast<const uint4*>(kn)[lane];
 #pragma unroll
   for (int jj = 0; jj < VL; ++jj) vpage[((r / 8) * D + lane + jj * kWave) * 8 + r % 8] = vn[lane + jj * kWave];
-  if (lane == 0) epage[r] = a.e_new[bh];
+  if (lane == 0) epage[r] = e_new;
 }
 
 // L lanes per sub-block (see score_kernel).  ROPE: packed table, scoring
-// only, nsub >= 4.
-template <int D, int L, bool ROPE = false>
+// only, nsub >= 4.  QKV: the appended token and the query from the fused
+// projection rows.
+template <int D, int L, bool ROPE = false, bool QKV = false>
 __global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const FusedArgs a) {
   constexpr int NQ = D / 4;
   constexpr int QL = NQ / L;
@@ -199,7 +210,22 @@ __global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const Fused
   const int MB = t.max_blocks, CS = MB * nsub, cap = MB * bs;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
 
-  const bool want_append = a.k_new != nullptr;
+  // the new token's k and v, and the group's query: separate inputs, or
+  // slices of the sequence's projection row
+  const uint16_t* kn;
+  const uint16_t* vn;
+  const uint16_t* qbase;
+  if constexpr (QKV) {
+    const uint16_t* row = a.qkv + (int64_t)b * (a.Hq + 2 * Hkv) * D;
+    qbase = row + (int64_t)h * G * D;
+    kn = row + ((int64_t)a.Hq + h) * D;
+    vn = row + ((int64_t)a.Hq + Hkv + h) * D;
+  } else {
+    qbase = a.q + ((int64_t)b * a.Hq + (int64_t)h * G) * D;
+    kn = a.k_new + (int64_t)bh * D;
+    vn = a.v_new + (int64_t)bh * D;
+  }
+  const bool want_append = QKV || a.k_new != nullptr;
   const int c = (int)gridDim.x - 1 - (int)blockIdx.x;  // chunks last to first
   const int s0 = c * SPG;
   // Issued together, before any of them is needed: the length, the pages of
@@ -213,7 +239,7 @@ __global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const Fused
     spec_page = page_of_any(t, bh, c * bpc + lane, doc);
   }
   const int dq = threadIdx.x < D ? threadIdx.x : 0;
-  const uint16_t* qh = a.q + ((int64_t)b * a.Hq + (int64_t)h * G) * D + dq;
+  const uint16_t* qh = qbase + dq;
   uint16_t qraw[16];
 #pragma unroll
   for (int g = 0; g < 16; ++g) qraw[g] = qh[(int64_t)min(g, G - 1) * D];
@@ -254,11 +280,32 @@ __global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const Fused
     sh.qbar[threadIdx.x] = acc / (double)G;
   }
   __syncthreads();  // have_new cleared before the append sets it
+  if constexpr (QKV) {  // the split query, for the decode (one workgroup per pair)
+    if (blockIdx.x == 0) {
+      for (int u = threadIdx.x; u < G * D / 8; u += kFusedThreads)
+        reinterpret_cast<uint4*>(a.q_out + ((int64_t)b * a.Hq + (int64_t)h * G) * D)[u] =
+            reinterpret_cast<const uint4*>(qbase)[u];
+    }
+  }
   if (lead) {  // the page of the new token's block, from this wave's lookups
     const int idx = raw / bs - c * bpc;
     const int64_t page = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(spec_page >> 32), idx) << 32) |
                                    (uint32_t)__builtin_amdgcn_readlane((int)spec_page, idx));
-    append_token<D>(a, sh, bh, raw, page);
+    float e_new;
+    if constexpr (QKV) {  // the eviction head: w_h . v in float64, one rounding
+      const float* wh = a.w_evict + (int64_t)h * D;
+      double acc = 0;
+#pragma unroll
+      for (int jd = 0; jd < D / kWave; ++jd) {
+        const int d = lane + jd * kWave;
+        acc = fma((double)bf16_to_f32(vn[d]), (double)wh[d], acc);
+      }
+      acc = xor_reduce<1, kWave>(acc, [](double x, double y) { return x + y; });
+      e_new = (float)acc;
+    } else {
+      e_new = a.e_new[bh];
+    }
+    append_token<D>(a, sh, bh, raw, page, kn, vn, e_new);
     load_summary();
   }
   __syncthreads();  // qbar, and the append's summary
@@ -338,11 +385,52 @@ __global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const Fused
   }
 }
 
+hipError_t launch_append_score_qkv(const nosa_dims& d, const nosa_kv& kv, const uint16_t* qkv, const float* w_evict,
+                                   const int32_t* seq_lens_in, int32_t* seq_lens_out, float* k_summary,
+                                   float* e_summary, uint16_t* q_out, float* score_q, float* score_e,
+                                   hipStream_t stream) {
+  FusedArgs a = {};
+  a.t = make_table(d, kv);
+  a.Hq = d.n_q_heads;
+  a.bs = d.block_size;
+  a.ss = d.sub_block;
+  a.k_pages = kv.k_pages;
+  a.v_pages = kv.v_pages;
+  a.e_pages = kv.e_pages;
+  a.seq_in = seq_lens_in;
+  a.seq_out = seq_lens_out;
+  a.k_summary = k_summary;
+  a.e_summary = e_summary;
+  a.score_q = score_q;
+  a.score_e = score_e;
+  a.qkv = qkv;
+  a.w_evict = w_evict;
+  a.q_out = q_out;
+  const int nsub = d.block_size / d.sub_block;
+  const int CS = d.max_blocks * nsub;
+  const int L = nsub <= 16 ? 4 : (nsub <= 32 ? 2 : 1);
+  const int spg = (kWave / L) * (kFusedThreads / kWave);
+  const dim3 grid((CS + spg - 1) / spg, d.batch * d.n_kv_heads);
+#define NOSA_APPEND_SCORE_QKV(DD, LL) \
+  append_score_kernel<DD, LL, false, true><<<grid, kFusedThreads, 0, stream>>>(a)
+  if (d.head_dim == 128) {
+    if (L == 4) NOSA_APPEND_SCORE_QKV(128, 4);
+    else if (L == 2) NOSA_APPEND_SCORE_QKV(128, 2);
+    else NOSA_APPEND_SCORE_QKV(128, 1);
+  } else {
+    if (L == 4) NOSA_APPEND_SCORE_QKV(64, 4);
+    else if (L == 2) NOSA_APPEND_SCORE_QKV(64, 2);
+    else NOSA_APPEND_SCORE_QKV(64, 1);
+  }
+#undef NOSA_APPEND_SCORE_QKV
+  return hipGetLastError();
+}
+
 hipError_t launch_append_score(const nosa_dims& d, const nosa_kv& kv, const uint16_t* k_new,
                                const uint16_t* v_new, const float* e_new, const int32_t* seq_lens_in,
                                int32_t* seq_lens_out, float* k_summary, float* e_summary, const uint16_t* q,
                                float* score_q, float* score_e, hipStream_t stream) {
-  FusedArgs a;
+  FusedArgs a = {};
   a.t = make_table(d, kv);
   a.Hq = d.n_q_heads;
   a.bs = d.block_size;

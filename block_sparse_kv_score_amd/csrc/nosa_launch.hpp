@@ -88,6 +88,11 @@ hipError_t launch_decode_alibi(const nosa_dims& d, const uint16_t* q, const nosa
                                float* part_m, float* part_l, int32_t* counters, float* o, float* m, float* l,
                                hipStream_t stream);
 
+hipError_t launch_append_score_qkv(const nosa_dims& d, const nosa_kv& kv, const uint16_t* qkv, const float* w_evict,
+                                   const int32_t* seq_lens_in, int32_t* seq_lens_out, float* k_summary,
+                                   float* e_summary, uint16_t* q_out, float* score_q, float* score_e,
+                                   hipStream_t stream);
+
 hipError_t launch_combine(const nosa_dims& d, int32_t num_splits, const float* part_o,
                           const float* part_m, const float* part_l, float* o, float* m, float* l,
                           hipStream_t stream);

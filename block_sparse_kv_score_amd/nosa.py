@@ -37,6 +37,7 @@ ENTRY_POINTS = [
     "nosa_sparse_decode",
     "nosa_sparse_decode_combine",
     "nosa_select_decode",
+    "nosa_append_score_qkv",
     "nosa_sparse_decode_mass",
     "nosa_sparse_decode_alibi",
     "nosa_combine",
@@ -110,6 +111,7 @@ _SIGNATURES = {
                                 _P],
     "nosa_sparse_decode_alibi": [_DIMS, _P, _KV, _P, _P, _I32, _P, _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P],
+    "nosa_append_score_qkv": [_DIMS, _KV, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "nosa_combine": [_DIMS, _I32, _P, _P, _P, _P, _P, _P, _P],
     "nosa_retrieve": [_DIMS, _KV, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P],
     "nosa_retrieve_buffered": [_DIMS, _KV, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P],
@@ -340,6 +342,18 @@ def nosa_sparse_decode_alibi(dims, q, kv, sel, sel_count, seq_lens, num_splits, 
           _dev(part_m, "part_m", (torch.float32,)), _dev(part_l, "part_l", (torch.float32,)),
           _dev(counters, "counters", (torch.int32,)), _dev(o, "o", (torch.float32,)),
           _dev(m, "m", (torch.float32,)), _dev(l, "l", (torch.float32,)), _stream(stream))
+
+
+def nosa_append_score_qkv(dims, kv, qkv, w_evict, seq_lens_in, seq_lens_out, k_summary, e_summary, q_out,
+                          score_q, score_e, stream=None):
+    """Append + score from the fused projection rows (qkv: bf16 [B, (Hq + 2 Hkv) D];
+    w_evict: fp32 [Hkv, D]; q_out: bf16 [B, Hq, D])."""
+    _call("nosa_append_score_qkv", ctypes.byref(dims), ctypes.byref(kv), _dev(qkv, "qkv", _BF16_LIKE),
+          _dev(w_evict, "w_evict", (torch.float32,)), _dev(seq_lens_in, "seq_lens_in", (torch.int32,)),
+          _dev(seq_lens_out, "seq_lens_out", (torch.int32,)),
+          _dev(k_summary, "k_summary", (torch.float32,)), _dev(e_summary, "e_summary", (torch.float32,)),
+          _dev(q_out, "q_out", _BF16_LIKE), _dev(score_q, "score_q", (torch.float32,)),
+          _dev(score_e, "score_e", (torch.float32,)), _stream(stream))
 
 
 SELECT_DECODE_MAX_BLOCKS = 1024

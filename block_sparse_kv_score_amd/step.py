@@ -31,7 +31,10 @@ they leave the selection and a bucketed LRU frees slots for misses.
 With `mass` the decode is nosa_sparse_decode_mass (after nosa_select_swap):
 the softmax score step adds each selected block's softmax mass per query
 head (`mass`) to O, m, l.  With `alibi` it is nosa_sparse_decode_alibi,
-with the slopes of the synthetic inputs.
+with the slopes of the synthetic inputs.  With `qkv` the append is
+nosa_append_score_qkv: the step's input is each sequence's fused projection
+row, the eviction logit comes from the eviction head, and the decode reads
+the query that call split out.
 """
 
 from __future__ import annotations
@@ -60,7 +63,7 @@ class DecodeSession:
     def __init__(self, w: Workload, inp: Inputs, splits: int | None = None, device: str = "cuda",
                  poison: bool = True, stream: torch.cuda.Stream | None = None, fused: bool = True,
                  offload: bool = False, buffer_slots: int | None = None, bucket_width: int = 1,
-                 mass: bool = False, alibi: bool = False):
+                 mass: bool = False, alibi: bool = False, qkv: bool = False):
         self.w, self.inp = w, inp
         self.buffered = buffer_slots is not None
         self.buffer_slots, self.bucket_width = buffer_slots, int(bucket_width)
@@ -68,6 +71,9 @@ class DecodeSession:
         self.mass_on = mass
         if mass and (w.table == TABLE_PACKED_ROPE or not fused):
             raise ValueError("the softmax score step runs in the fused decode over flat or two-level tables")
+        self.qkv_on = qkv
+        if qkv and (w.table == TABLE_PACKED_ROPE or not fused or not w.append or offload):
+            raise ValueError("the QKV-row append runs in the fused step over flat or two-level tables, in HBM")
         self.alibi_on = alibi
         if alibi and (w.table == TABLE_PACKED_ROPE or not fused or mass):
             raise ValueError("ALiBi runs in the fused decode over flat or two-level tables, without the mass step")
@@ -130,6 +136,11 @@ class DecodeSession:
         self.m = torch.full((B, Hq), fill, dtype=torch.float32, device=dev)
         self.l = torch.full_like(self.m, fill)
         self.counters = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)  # fused combine arrivals
+        if qkv:  # fused projection rows per step, the eviction head, the split query
+            self.qkv_all = torch.from_numpy(np.stack([synth.qkv_rows(w, inp, t).view(np.int16)
+                                                      for t in range(1, w.n_append + 1)])).to(dev)
+            self.w_evict = torch.from_numpy(synth.eviction_head_weights(w, inp.seed)).to(dev)
+            self.q_out = torch.zeros((B, Hq, D), dtype=torch.int16, device=dev)
         if alibi:  # per query head slopes
             self.alibi_slopes = torch.from_numpy(synth.alibi_slopes(Hq)).to(dev)
         if mass:  # softmax score step: per-tile workspace and the block masses
@@ -212,6 +223,8 @@ class DecodeSession:
         del k_src, v_src, e_src
 
     def q(self, t: int) -> torch.Tensor:
+        if self.qkv_on:  # the query the fused append split out of this step's rows
+            return self.q_out
         return self.q_all[t - 1]
 
     # ------------------------------------------------------------------
@@ -246,6 +259,12 @@ class DecodeSession:
         """Fused append + score; afterwards seq_lens is the other buffer."""
         w = self.w
         out = self.seq_bufs[1] if self.seq_lens is self.seq_bufs[0] else self.seq_bufs[0]
+        if self.qkv_on:
+            nosa.nosa_append_score_qkv(self.dims, self.kv, self.qkv_all[t - 1], self.w_evict, self.seq_lens, out,
+                                       self.k_summary, self.e_summary, self.q_out, self.score_q, self.score_e,
+                                       self.stream)
+            self.seq_lens = out
+            return
         if w.append:
             k_new, v_new, e_new, seq_out = self.k_new[t - 1], self.v_new[t - 1], self.e_new[t - 1], out
         else:

@@ -24,6 +24,7 @@ Recipe (per workload ``w`` and base seed ``seed``):
 
 from __future__ import annotations
 
+import math
 import os
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
@@ -38,6 +39,7 @@ S_K, S_V, S_E, S_HEAVY = 1, 2, 3, 4
 S_K_APP, S_V_APP, S_E_APP, S_HEAVY_APP = 11, 12, 13, 14
 S_Q = 20
 S_PAGES, S_SEGS, S_DOCS = 30, 31, 32
+S_EHEAD = 40
 
 PACK_PAGE_BITS = 20   # packed word: page id in bits 0..19
 PACK_PAGE_MASK = (1 << PACK_PAGE_BITS) - 1
@@ -105,6 +107,25 @@ def alibi_slopes(n_heads: int) -> np.ndarray:
     """Per-head ALiBi slopes for the synthetic runs (an input of the
     ALiBi decode, like the queries): 2^(-8 (j + 1) / n_heads), float32."""
     return np.power(2.0, -8.0 * (np.arange(n_heads) + 1.0) / n_heads).astype(np.float32)
+
+
+def eviction_head_weights(w: Workload, seed: int) -> np.ndarray:
+    """Random-init eviction-head weights, fp32 [Hkv, D] ~ N(0, 1/D) (an
+    input of the fused QKV append, like the projection rows)."""
+    g = rng_for(seed, w, S_EHEAD)
+    return (g.standard_normal((w.Hkv, w.D), dtype=np.float32) / np.float32(math.sqrt(w.D))).astype(np.float32)
+
+
+def qkv_rows(w: Workload, inp: "Inputs", step: int) -> np.ndarray:
+    """The fused projection rows of decode step ``step``: per sequence
+    [q heads | k heads | v heads] of the appended token, bf16 bits
+    [B, (Hq + 2 Hkv) D] (the same query and appended k, v as the separate
+    inputs)."""
+    pos = w.T0 + step - 1
+    q = inp.q(step).reshape(w.B, w.Hq * w.D)
+    k = inp.K[:, :, pos].reshape(w.B, w.Hkv * w.D)
+    v = inp.V[:, :, pos].reshape(w.B, w.Hkv * w.D)
+    return np.ascontiguousarray(np.concatenate([q, k, v], axis=1))
 
 
 def page_ids(w: Workload, seed: int) -> np.ndarray:

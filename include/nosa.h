@@ -196,6 +196,23 @@ nosa_status nosa_select(const nosa_dims* dims, const float* score_q, const float
                         const int32_t* seq_lens, int32_t k_e, int32_t k_q, uint32_t* evicted,
                         int32_t* sel, int32_t sel_cap, int32_t* sel_count, hipStream_t stream);
 
+/* nosa_append_score from the token's fused projection row [NOSA, NOSI
+ * kernel fusion: the eviction head, the QKV split and pooling in one
+ * kernel]:
+ *   qkv bf16 [B][(Hq + 2 Hkv) D]: per sequence the new token's row
+ *     [q heads | k heads | v heads];
+ *   w_evict fp32 [Hkv][D]: the eviction head, e = w_h . v (float64 sum,
+ *     one rounding to fp32), no exponent [NOSA, ED-DMA];
+ *   q_out bf16 [B][Hq][D]: receives the query part (the decode's q).
+ * The token's k, v and e are appended and the blocks scored with the row's
+ * query exactly as nosa_append_score does with k_new, v_new, e_new and q
+ * (seq_lens_in / seq_lens_out, k_summary .. score_e as there).  Flat and
+ * two-level tables (NOSA_ERR_UNSUPPORTED for the packed RoPE kind).       */
+nosa_status nosa_append_score_qkv(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* qkv,
+                                  const float* w_evict, const int32_t* seq_lens_in, int32_t* seq_lens_out,
+                                  float* k_summary, float* e_summary, uint16_t* q_out, float* score_q,
+                                  float* score_e, hipStream_t stream);
+
 /* nosa_select and nosa_swap_diff in one launch: the selection is made as
  * by nosa_select, then load / evict are formed against prev exactly as
  * nosa_swap_diff(prev, sel) would, from the selection still in registers

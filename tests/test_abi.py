@@ -155,6 +155,14 @@ def test_host_checks_reject_bad_arguments():
                                           fake, fake, fake, fake, None)
     assert adec(kv, slopes=None) == nosa.NOSA_ERR_ARG
     assert adec(rope) == nosa.NOSA_ERR_UNSUPPORTED
+    # append from fused projection rows: weights and split-query output required
+    def qkv_app(kvd, w_e=fake, q_out=fake, seq_out=P(768)):
+        return L.nosa_append_score_qkv(D(d), D(kvd), fake, w_e, P(512), seq_out, fake, fake, q_out, fake, fake,
+                                       None)
+    assert qkv_app(kv, w_e=None) == nosa.NOSA_ERR_ARG
+    assert qkv_app(kv, q_out=None) == nosa.NOSA_ERR_ARG
+    assert qkv_app(kv, seq_out=P(512)) == nosa.NOSA_ERR_ARG  # lengths in place
+    assert qkv_app(rope) == nosa.NOSA_ERR_UNSUPPORTED
     # host-tier retrieve: slot count bounds, required lists
     def retr(slots, load=fake):
         return L.nosa_retrieve(D(d), D(kv), P(4096), P(8192), P(12288), slots, fake, fake, load, fake, fake, fake,

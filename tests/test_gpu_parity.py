@@ -96,16 +96,21 @@ def force_slots(sess, b: int, h: int, owner: list, last_use: list | None = None)
 
 
 def run_trajectory(w, seed=0, pairs=None, steps=None, splits=None, check_scores=True, fused=True, inp=None,
-                   offload=False, buffer_slots=None, bucket_width=1, mass=False, alibi=False):
+                   offload=False, buffer_slots=None, bucket_width=1, mass=False, alibi=False, qkv=False):
     announce(f"trajectory {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T0={w.T0} k={w.k_e}/{w.k_q} "
              f"steps={steps or w.steps} P={splits or w.splits} pairs={'all' if pairs is None else pairs} "
              f"seed={seed} fused={fused} offload={offload} buffer={buffer_slots}/{bucket_width} mass={mass} "
-             f"alibi={alibi}")
+             f"alibi={alibi} qkv={qkv}")
     inp = inp if inp is not None else synth.generate(w, seed)
     sess = session(w, inp, splits=splits, fused=fused, offload=offload, buffer_slots=buffer_slots,
-                   bucket_width=bucket_width, mass=mass, alibi=alibi)
+                   bucket_width=bucket_width, mass=mass, alibi=alibi, qkv=qkv)
     pairs = pairs or [(b, h) for b in range(w.B) for h in range(w.Hkv)]
     lgs = {p: logical_pair(inp, *p) for p in pairs}
+    if qkv:  # appended tokens' logits come from the eviction head (the oracle's)
+        w_e = synth.eviction_head_weights(w, inp.seed)
+        for (b, h), lg in lgs.items():
+            lg.e = lg.e.copy()
+            lg.e[w.T0:] = oracle.eviction_head(lg.V[w.T0:], w_e[h]).astype(np.float64)
     states = {p: PairState() for p in pairs}
     owners = {p: [-1] * sess.slots for p in pairs} if offload else None
     stamps = {p: [0] * sess.slots for p in pairs} if offload else None
@@ -560,6 +565,48 @@ def test_alibi_full_size_sampled():
     sampled pairs against the oracle."""
     w = WORKLOADS["llama3_8b_32k"]
     run_trajectory(w, seed=38, steps=2, alibi=True, pairs=[(0, 0), (9, 4), (31, 7)])
+
+
+QKV_CASES = [
+    ("tiny_nosa", {}, 2),
+    ("llama3_8b_32k", dict(B=2, Hq=8, Hkv=2, T0=4096 + 61), 1),
+    ("llama31_70b_256k", dict(B=2, Hq=16, Hkv=2, T0=16384 + 100, dir_entries=64), 4),
+]
+
+
+@pytest.mark.parametrize("name,scale,splits", QKV_CASES, ids=[f"{c[0]}-P{c[2]}" for c in QKV_CASES])
+def test_qkv_append_trajectory(name, scale, splits):
+    """The append from fused projection rows (QKV split + eviction head +
+    pooling in one launch) against the oracle along a trajectory."""
+    w = WORKLOADS[name].scaled(**scale) if scale else WORKLOADS[name]
+    run_trajectory(w, seed=41, splits=splits, steps=min(w.steps, 6), qkv=True)
+
+
+def test_qkv_append_pages_and_split_query():
+    """The split query is the row's query bit for bit, the appended K and V
+    land exactly as with separate inputs, and each appended logit is the
+    oracle's eviction head of the token's value vector."""
+    w = WORKLOADS["llama3_8b_32k"].scaled(B=2, Hq=8, Hkv=2, T0=4096 + 61)
+    announce("qkv append: split query, pages, eviction logits")
+    inp = synth.generate(w, 42)
+    a = session(w, inp, splits=1, qkv=True)
+    s = session(w, inp, splits=1)
+    w_e = synth.eviction_head_weights(w, inp.seed)
+    for t in range(1, 4):
+        a.step(t)
+        s.step(t)
+        torch.cuda.synchronize()
+        assert int(a.err.item()) == 0
+        assert np.array_equal(a.q_out.cpu().numpy().view(np.uint16), inp.q(t))
+        assert torch.equal(a.k_pages, s.k_pages) and torch.equal(a.v_pages, s.v_pages)
+        assert torch.equal(a.seq_lens, s.seq_lens)
+        pos = w.T0 + t - 1
+        ep = a.e_pages.cpu().numpy()
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                page = host_page(w, inp, b, h, pos // w.bs)
+                want = oracle.eviction_head(oracle.bf16_to_f64(inp.V[b, h, pos]), w_e[h])
+                assert ep[page, pos % w.bs] == want, (t, b, h)
 
 
 def test_offload_more_loads_than_slots_flags():
