@@ -78,6 +78,7 @@ __all__ = [
     "rope_inv_freq",
     "rope_rotate",
     "decode_step_bh",
+    "prefill_attention_bh",
 ]
 
 
@@ -523,3 +524,44 @@ def decode_step_bh(q_group, K, V, e, T, bs, ss, k_e, k_q, evicted, prev_sel,
     if alibi is None:
         out["mass"] = softmax_block_mass(qt, Kt, gamma, T, bs, scale)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Prefill over reused documents  [LAZY, 1. Prefilling + mathematical
+# equivalence]
+# ---------------------------------------------------------------------------
+
+def prefill_attention_bh(q, K, V, T, q_pos0, block_start, bs, base, scale):
+    """Causal attention of a prompt over a context of reused documents, for
+    one (sequence, KV head).
+
+    q:  (M, G, D) float64 prompt queries (unrotated), query m at position
+        n = q_pos0 + m.
+    K, V: (>=T, D) float64 stored keys / values in logical order; the keys
+        carry only their in-document rotation.
+    block_start: (nb,) absolute start position of the document holding
+        each block.
+
+    Keys are materialised as Rot(doc start) k_stored, queries as Rot(n) q;
+    query m attends the keys at positions t <= n (t < T), by the softmax
+    definition.  READING: the prompt is itself the last document of the
+    context (its keys present in the cache), positions are logical token
+    indices.  Returns O (M, G, D), m (M, G), l (M, G).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    M, G, D = q.shape
+    nb = num_blocks(T, bs)
+    Kt = np.empty((T, D))
+    for i in range(nb):
+        r = block_token_range(i, T, bs)
+        Kt[r.start:r.stop] = rope_rotate(K[r.start:r.stop], float(block_start[i]), base)
+    O = np.zeros((M, G, D))
+    m = np.full((M, G), -np.inf)
+    l = np.zeros((M, G))
+    for mi in range(M):
+        n = q_pos0 + mi
+        qt = rope_rotate(q[mi], n, base)
+        hi = min(n + 1, T)
+        O[mi], m[mi], l[mi] = attend(qt, Kt[:hi], V[:hi], scale)
+    return O, m, l
+

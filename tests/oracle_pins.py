@@ -534,6 +534,41 @@ def check_index_inputs(O, seed=13):
         assert O.eviction_head(V[t], w1) == np.float32(acc)
 
 
+def check_prefill(O, seed=14):
+    """Prefill over reused documents: against torch's float64 SDPA with an
+    explicit causal mask on rotated queries and keys built from the
+    complex-number form, and the last prompt query against the decode
+    step's dense attention at the same position."""
+    rng = np.random.default_rng(seed)
+    G, D, bs, base = 2, 16, 4, 1000.0
+    T, M = 40, 9
+    q_pos0 = T - M
+    q = rng.standard_normal((M, G, D))
+    K = rng.standard_normal((T, D))
+    V = rng.standard_normal((T, D))
+    nb = -(-T // bs)
+    starts = (np.arange(nb) // 2) * 2 * bs * 1.0  # documents of two blocks
+    Ow, mw, lw = O.prefill_attention_bh(q, K, V, T, q_pos0, starts, bs, base, 1 / math.sqrt(D))
+    theta = base ** (-2.0 * np.arange(D // 2) / D)
+    def rot(x, pos):
+        c = (x[..., :D // 2] + 1j * x[..., D // 2:]) * np.exp(1j * pos * theta)
+        return np.concatenate([c.real, c.imag], axis=-1)
+    Kr = np.stack([rot(K[t], starts[t // bs]) for t in range(T)])
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))
+    for g in range(G):
+        Qr = np.stack([rot(q[mi, g], q_pos0 + mi) for mi in range(M)])
+        mask = np.arange(T)[None, :] <= (q_pos0 + np.arange(M))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            t(Qr)[None], t(Kr)[None], t(V)[None], attn_mask=torch.tensor(mask)[None], scale=1 / math.sqrt(D))[0]
+        assert np.abs(Ow[:, g] - ref.numpy()).max() <= 1e-12
+        s = t(Qr) @ t(Kr).T / math.sqrt(D)
+        lse = torch.logsumexp(s.masked_fill(~torch.tensor(mask), -math.inf), dim=1).numpy()
+        assert np.abs(mw[:, g] + np.log(lw[:, g]) - lse).max() <= 1e-12
+    r = O.decode_step_bh(q[M - 1], K, V, np.zeros(T), T, bs, bs, 0, nb, set(), [], 1, 1 / math.sqrt(D),
+                         select_all=True, rope=dict(q_pos=T - 1, block_start=starts, base=base))
+    assert np.abs(r["O"] - Ow[M - 1]).max() <= 1e-12 and np.abs(r["m"] - mw[M - 1]).max() <= 1e-12
+
+
 # ---------------------------------------------------------------------------
 # rotary embedding and the deferred (lazy) rotation
 # ---------------------------------------------------------------------------
@@ -648,6 +683,6 @@ ALL_CHECKS = [
     check_pool_closed_form, check_pool_linearity, check_eviction_pre_exp,
     check_select_bruteforce, check_select_sizes, check_trajectory_invariants,
     check_swap_lists, check_place_blocks, check_buffer_retrieve, check_rope_complex, check_rope_identities,
-    check_softmax_block_mass, check_alibi, check_rope_scores, check_index_inputs, check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
+    check_softmax_block_mass, check_alibi, check_rope_scores, check_index_inputs, check_prefill, check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
     check_bf16_decode,
 ]

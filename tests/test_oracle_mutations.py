@@ -32,6 +32,7 @@ _abias = O.alibi_bias
 _aslopes = O.alibi_slopes
 _split = O.split_qkv
 _ehead = O.eviction_head
+_prefill = O.prefill_attention_bh
 _qscore = O.query_token_scores
 _freq = O.rope_inv_freq
 
@@ -183,6 +184,11 @@ def _ehead_on_exp(v, w):
     return _ehead(np.exp(np.asarray(v, dtype=np.float64)), w)
 
 
+def _prefill_not_causal(q, K, V, T, q_pos0, block_start, bs, base, scale):
+    # every prompt query placed at the last position: it sees the whole prompt
+    return _prefill(q, K, V, T, T - 1, block_start, bs, base, scale)
+
+
 def _rotate_sign(x, pos, base):
     return _rotate(x, -np.asarray(pos), base)
 
@@ -234,6 +240,7 @@ MUTANTS = [
     ("rope_rotate", _rotate_none, P.check_rope_scores),
     ("split_qkv", _split_kv_swapped, P.check_index_inputs),
     ("eviction_head", _ehead_on_exp, P.check_index_inputs),
+    ("prefill_attention_bh", _prefill_not_causal, P.check_prefill),
     ("rope_rotate", _rotate_sign, P.check_rope_complex),
     ("rope_rotate", _rotate_pairs_adjacent, P.check_rope_complex),
     ("rope_inv_freq", _freq_wrong_exponent, P.check_rope_complex),
