@@ -37,6 +37,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBPS = 8000.0
 PEAK_HOST_LINK_GBPS = 64.0  # PCIe 5.0 x16, one direction
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16 matrix cores
 METRIC = "sparse decode attn tokens/s + achieved HBM GB/s (% peak), 8B shape @32K"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_llama3_8b_32k.json")
 CSRC = os.path.join(ROOT, "block_sparse_kv_score_amd", "csrc")
@@ -161,6 +162,98 @@ def cpu_baseline(w, inp, budget_s: float):
     return out
 
 
+def prefill_flops(w) -> float:
+    """Algorithmic FLOPs of one prefill launch: every prompt query of every
+    head attends its n + 1 visible keys, 2 D for q.k and 2 D for p.v each."""
+    M, p0 = w.prompt, w.T0 - w.prompt
+    keys = sum(p0 + m + 1 for m in range(M))
+    return 4.0 * w.D * keys * w.Hq * w.B
+
+
+def prefill_cpu_baseline(w, inp, budget_s: float):
+    """The oracle's prefill (as it stands) on single prompt rows of random
+    (b, h) pairs until the budget is spent; scaled to the launch."""
+    import numpy as np
+    import oracle
+    from block_sparse_kv_score_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    rng = np.random.default_rng(0)
+    qp = synth.prefill_queries(w, inp.seed)
+    starts = synth.block_doc_start(w) * w.bs
+    p0 = w.T0 - w.prompt
+    done, elapsed = 0, 0.0
+    while elapsed < budget_s:
+        b, h, r = int(rng.integers(w.B)), int(rng.integers(w.Hkv)), int(rng.integers(w.prompt))
+        t0 = time.perf_counter()
+        K = oracle.bf16_to_f64(inp.K[b, h, :w.T0])
+        V = oracle.bf16_to_f64(inp.V[b, h, :w.T0])
+        q = oracle.bf16_to_f64(qp[b, r:r + 1, h * w.G:(h + 1) * w.G])
+        oracle.prefill_attention_bh(q, K, V, w.T0, p0 + r, starts, w.bs, w.rope_base, w.sm_scale)
+        elapsed += time.perf_counter() - t0
+        done += 1
+    launch_s = elapsed / done * w.prompt * w.B * w.Hkv
+    return {"value": w.B * w.prompt / launch_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} prompt rows of random (b, h) pairs ({elapsed:.1f} s), scaled to the launch "
+                      f"({w.B * w.Hkv * w.prompt} rows); float64 NumPy, BLAS threads = {threads}",
+            "sec_per_launch": launch_s}
+
+
+def bench_prefill(args, w) -> int:
+    """Prefill over reused documents: K cold launches (1 GiB read before
+    each), events around each launch on the launch stream."""
+    import numpy as np
+    import torch
+    from block_sparse_kv_score_amd import synth
+    from block_sparse_kv_score_amd.step import DecodeSession
+    K, W = args.steps, args.warmup
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = synth.generate(w, args.seed)
+    sess = DecodeSession(w, inp, poison=False)
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    for _ in range(W):
+        flush_buf.sum()
+        sess.prefill_attention()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for k in range(K):
+        flush_buf.sum()
+        ev[k][0].record(stream)
+        sess.prefill_attention()
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    assert int(sess.err.cpu()[0]) == 0, "device contract flag raised"
+    ms = [a.elapsed_time(b) for a, b in ev]
+    t = float(np.median(ms)) / 1e3
+    flops = prefill_flops(w)
+    tflops = flops / t / 1e12
+    kv_bytes = w.B * w.Hkv * w.T0 * 4 * w.D  # every cached K and V byte once
+    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(w, inp, args.cpu_seconds)
+    out = {
+        "metric": f"prefill tokens/s over reused documents, deferred RoPE ({w.name})",
+        "value": round(w.B * w.prompt / t, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(t * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
+                   "context": w.T0, "prompt": w.prompt, "documents": w.n_docs, "doc_len": w.doc_len,
+                   "block": w.bs, "parallelism": "single GPU"},
+        "step_ms_p10_p90": [round(float(np.percentile(ms, 10)), 4), round(float(np.percentile(ms, 90)), 4)],
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "nosa_prefill_attention (prefill_rope_kernel)",
+                     "algorithmic_flops_per_launch": flops, "avg_launch_us": round(float(np.mean(ms)) * 1e3, 2)},
+        "hbm_gbps_kv_once": round(kv_bytes / t / 1e9, 1),
+        "cpu_baseline": cpu,
+        "seed": args.seed,
+    }
+    print(json.dumps(out))
+    return 0
+
+
 def main(argv=None) -> int:
     args = parse(argv)
     if args.gpus != 1:
@@ -177,6 +270,8 @@ def main(argv=None) -> int:
     w = WORKLOADS[args.workload]
     if args.warmup is None:
         args.warmup = 60 if args.buffer_slots is not None else 5
+    if w.prompt:
+        return bench_prefill(args, w)
     K, W = args.steps, args.warmup
     passes = 3
     if w.append and W + passes * K > w.n_append:

@@ -273,6 +273,22 @@ nosa_status nosa_sparse_decode_alibi(const nosa_dims* dims, const uint16_t* q, c
                                             alibi_slopes, part_o, part_m, part_l, counters, o, m, l, stream));
 }
 
+nosa_status nosa_prefill_attention(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* q, int32_t n_prompt,
+                                   const int32_t* q_pos0, const int32_t* seq_lens, float sm_scale, float* o,
+                                   float* m, float* l, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if ((st = check_kv(dims, kv, false)) != NOSA_OK) return st;
+  if (kv->kind != NOSA_TABLE_PACKED_ROPE) return NOSA_ERR_UNSUPPORTED;
+  if (!(kv->rope_base > 1.f)) return NOSA_ERR_ARG;
+  if (!q || !q_pos0 || !seq_lens || !o || !m || !l || n_prompt < 1 || !aligned16(q)) return NOSA_ERR_ARG;
+  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return NOSA_ERR_ARG;
+  if ((dims->block_size % 64) != 0) return NOSA_ERR_UNSUPPORTED;
+  if ((int64_t)dims->batch * n_prompt * dims->n_q_heads * dims->head_dim > ((int64_t)1 << 40)) return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_prefill_attention(*dims, *kv, q, n_prompt, q_pos0, seq_lens, sm_scale, o, m, l,
+                                                 stream));
+}
+
 nosa_status nosa_select_decode(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* q, const float* score_q,
                                const float* score_e, const int32_t* seq_lens, int32_t k_e, int32_t k_q,
                                const uint32_t* evicted_in, uint32_t* evicted_out, int32_t* sel, int32_t sel_cap,

@@ -93,6 +93,10 @@ hipError_t launch_append_score_qkv(const nosa_dims& d, const nosa_kv& kv, const 
                                    float* e_summary, uint16_t* q_out, float* score_q, float* score_e,
                                    hipStream_t stream);
 
+hipError_t launch_prefill_attention(const nosa_dims& d, const nosa_kv& kv, const uint16_t* q, int32_t n_prompt,
+                                    const int32_t* q_pos0, const int32_t* seq_lens, float sm_scale, float* o,
+                                    float* m, float* l, hipStream_t stream);
+
 hipError_t launch_combine(const nosa_dims& d, int32_t num_splits, const float* part_o,
                           const float* part_m, const float* part_l, float* o, float* m, float* l,
                           hipStream_t stream);

@@ -1,0 +1,345 @@
+// Prefill attention over reused documents with deferred RoPE.
+//
+// LazyAttention summary, Technical implementation, 1. Prefilling: cached KV
+// blocks are loaded while the prompt is processed, and instead of rotating
+// keys twice (back to position 0, then to their new position) the kernel
+// applies a single relative rotation from the offset between the queries
+// and the cached document; Mathematical equivalence: RoPE attention depends
+// only on that offset.  Stored keys carry their in-document rotation, so
+//   Rot(n) q . Rot(st) k_stored = Rot(n - st) q . k_stored
+// for a query at position n and a document starting at st.  The relative
+// rotation is applied to the query, once per (query column, document) --
+// documents span many key tiles, so this is rarer than rotating every K
+// tile -- and the keys stream from their pages untouched.
+//
+// gfx950 mapping.  Workgroup = 4 waves = one (b, KV head) and 64 query
+// columns (a column is a (prompt position, head of the group) pair); wave w
+// owns 16 columns.  Keys stream in 64-token tiles that all four waves share
+// through LDS (loaded with 16-byte loads into registers one tile ahead, then
+// stored to LDS).  Both products run on v_mfma_f32_16x16x32_bf16 as in the
+// decode: S^T = K . Q^T with the key rows as the A operand straight from the
+// K page layout, and O^T += V^T . P with V^T rows from the V page layout and
+// the tile's bf16 probabilities (one LDS round trip) as the B operand.  The
+// rotated query is split into bf16 hi + lo parts (two MFMAs per chunk) so the
+// rotation costs no precision beyond ~2^-16.  Online softmax per column in
+// log2 units; causal mask t <= n; keys past the context are masked and their
+// V entries zeroed (0 * stale NaN would leak through the MFMA).
+
+#include "nosa_launch.hpp"
+
+namespace nosa {
+
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kPfTile = 64;  // keys per tile
+constexpr int kPfCols = 16;  // query columns per wave
+constexpr float kPfLog2e = 1.4426950408889634f;
+constexpr float kPfLn2 = 0.6931471805599453f;
+
+struct PrefillArgs {
+  Table t;
+  int Hq, bs, M;
+  float scale_log2;
+  double rope_base;
+  const uint16_t* q;  // [B][M][Hq][D], unrotated
+  const uint16_t* k_pages;
+  const uint16_t* v_pages;
+  const int32_t* q_pos0;    // [B] position of the first prompt token
+  const int32_t* seq_lens;  // [B]
+  float* o;                 // [B][M][Hq][D]
+  float* m;                 // [B][M][Hq]
+  float* l;
+};
+
+template <int D>
+struct PrefillSmem {
+  uint4 k[D / 8][kPfTile];                     // K tile, page layout [D/8][64][8]
+  uint4 v[kPfTile / 8][D];                     // V tile, page layout [64/8][D][8]
+  uint16_t p[kPfWaves][kPfCols][kPfTile];      // bf16 probabilities, per wave
+  float cs[D / 2][2];                          // cos, sin of st * theta_k
+};
+
+typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float pf_floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ pf_floatx4 pf_mfma(const uint4& a, const uint4& b, const pf_floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pf_bf16x8, a), __builtin_bit_cast(pf_bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 pf_load(const uint4* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Packs 8 fp32 values as bf16 (round to nearest even).
+__device__ __forceinline__ uint4 pack_bf16x8(const float* x) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = (uint32_t)f32_to_bf16(x[2 * j]) | ((uint32_t)f32_to_bf16(x[2 * j + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Column lr of wave w: prompt row m0 + w * (16 / G) + lr / G, head lr % G.
+template <int D, int G>
+__global__ __launch_bounds__(kPfThreads, 2) void prefill_rope_kernel(const PrefillArgs a) {
+  constexpr int NCH = D / 32;      // 32-dim chunks of q.k
+  constexpr int NDT = D / 16;      // 16-dim tiles of P.V
+  constexpr int PPW = kPfCols / G;  // prompt rows per wave
+  constexpr int KU = (D / 8) * kPfTile / kPfThreads;  // K tile units per thread (= NCH)
+  constexpr int VU = (kPfTile / 8) * D / kPfThreads;  // V tile units per thread (= NCH)
+  static_assert(kPfCols % G == 0, "G divides 16");
+  __shared__ PrefillSmem<D> sh;
+
+  const Table& t = a.t;
+  const int bh = blockIdx.y;
+  const int Hkv = t.Hkv;
+  const int b = bh / Hkv, h = bh % Hkv;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int lq = lane >> 4, lr = lane & 15;
+  const int bs = a.bs;
+  const int T = min(max(a.seq_lens[b], 0), t.max_blocks * bs);
+  const int m0 = blockIdx.x * (kPfWaves * PPW);
+  const int mi = m0 + w * PPW + lr / G;
+  const int g = lr % G;
+  const bool col_ok = mi < a.M;
+  const int64_t p0 = a.q_pos0[b];
+  const int64_t n = p0 + min(mi, a.M - 1);  // this column's position (idle columns: the last row)
+  const int mlast = min(m0 + kPfWaves * PPW, a.M) - 1;
+  const int64_t last_key = min(p0 + mlast, (int64_t)T - 1);
+  const int ntile = last_key >= 0 ? (int)(last_key / kPfTile) + 1 : 0;
+
+  // Rot(n) q for this lane's column and dims 32 c + 8 lq + e, in fp32
+  // (float64 angles, once)
+  float qn[NCH][8];
+  {
+    const uint16_t* qp = a.q + (((int64_t)b * a.M + min(mi, a.M - 1)) * a.Hq + (int64_t)h * G + g) * D;
+#pragma unroll
+    for (int c = 0; c < NCH / 2; ++c) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 32 * c + 8 * lq + e;  // < D/2; partner d + D/2 in chunk c + NCH/2
+        const double x1 = bf16_to_f32(qp[d]), x2 = bf16_to_f32(qp[d + D / 2]);
+        const double th = pow(a.rope_base, -2.0 * (double)d / (double)D);
+        double sv, cv;
+        sincos((double)n * th, &sv, &cv);
+        qn[c][e] = (float)(x1 * cv - x2 * sv);
+        qn[c + NCH / 2][e] = (float)(x2 * cv + x1 * sv);
+      }
+    }
+  }
+  const double theta_k = threadIdx.x < D / 2 ? pow(a.rope_base, -2.0 * (double)threadIdx.x / (double)D) : 0.0;
+
+  uint4 qhi[NCH], qlo[NCH];
+  float m_run = -INFINITY, l_run = 0.f;  // column lr, log2 units (l_run: this lane's keys)
+  pf_floatx4 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = pf_floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // tile -> page and document start (tokens); page < 0: unresolvable
+  auto tile_page = [&](int tile, int64_t& page, int64_t& st) {
+    const int i = tile * kPfTile / bs;
+    uint32_t docb = 0;
+    page = page_of<NOSA_TABLE_PACKED_ROPE>(t, bh, i, docb);
+    st = (int64_t)docb * bs;
+  };
+  uint4 kr[KU], vr[VU];
+  auto fetch = [&](int tile, int64_t page) {
+    const int sub = (tile * kPfTile % bs) / kPfTile;
+    const uint4* kp = reinterpret_cast<const uint4*>(a.k_pages + page * (int64_t)bs * D);
+    const uint4* vp = reinterpret_cast<const uint4*>(a.v_pages + page * (int64_t)bs * D);
+#pragma unroll
+    for (int j = 0; j < KU; ++j) {
+      const int u = threadIdx.x + j * kPfThreads;
+      kr[j] = page >= 0 ? pf_load(kp + (int64_t)(u / kPfTile) * bs + sub * kPfTile + u % kPfTile)
+                        : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < VU; ++j) {
+      const int u = threadIdx.x + j * kPfThreads;
+      vr[j] = page >= 0 ? pf_load(vp + (int64_t)(sub * 8 + u / D) * D + u % D) : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  int64_t page = -1, st = 0, cur_st = -1;
+  if (ntile > 0) {
+    tile_page(0, page, st);
+    if (page < 0 && threadIdx.x == 0) flag_error(t.err);
+    fetch(0, page);
+  }
+  for (int tile = 0; tile < ntile; ++tile) {
+    const int key0 = tile * kPfTile;
+    const bool tile_ok = page >= 0;
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int j = 0; j < KU; ++j) {
+      const int u = threadIdx.x + j * kPfThreads;
+      sh.k[u / kPfTile][u % kPfTile] = kr[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VU; ++j) {
+      const int u = threadIdx.x + j * kPfThreads;
+      const int ko = u / D;
+      uint4 x = vr[j];
+      const int nv = min(max(T - (key0 + 8 * ko), 0), 8);  // present keys of this unit
+      if (nv < 8) {
+        uint32_t mk[4];
+#pragma unroll
+        for (int jd = 0; jd < 4; ++jd)
+          mk[jd] = (2 * jd < nv ? 0x0000ffffu : 0u) | (2 * jd + 1 < nv ? 0xffff0000u : 0u);
+        x.x &= mk[0];
+        x.y &= mk[1];
+        x.z &= mk[2];
+        x.w &= mk[3];
+      }
+      sh.v[ko][u % D] = x;
+    }
+    const bool new_doc = st != cur_st;
+    if (new_doc && threadIdx.x < D / 2) {
+      double sv, cv;
+      sincos((double)st * theta_k, &sv, &cv);
+      sh.cs[threadIdx.x][0] = (float)cv;
+      sh.cs[threadIdx.x][1] = (float)sv;
+    }
+    __syncthreads();  // the tile and the document's rotation table
+    const int64_t this_st = st;
+    if (tile + 1 < ntile) {  // the next tile's loads, in flight during this one
+      tile_page(tile + 1, page, st);
+      if (page < 0 && threadIdx.x == 0) flag_error(t.err);
+      fetch(tile + 1, page);
+    }
+    if (new_doc) {  // Rot(n - st) q = Rot(-st) Rot(n) q, split into bf16 hi + lo
+      cur_st = this_st;
+      float hi[NCH][8], lo[NCH][8];
+#pragma unroll
+      for (int c = 0; c < NCH / 2; ++c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 32 * c + 8 * lq + e;
+          const float cv = sh.cs[d][0], sv = sh.cs[d][1];
+          const float x1 = qn[c][e], x2 = qn[c + NCH / 2][e];
+          const float r1 = x1 * cv + x2 * sv, r2 = x2 * cv - x1 * sv;
+          hi[c][e] = bf16_to_f32(f32_to_bf16(r1));
+          hi[c + NCH / 2][e] = bf16_to_f32(f32_to_bf16(r2));
+          lo[c][e] = r1 - hi[c][e];
+          lo[c + NCH / 2][e] = r2 - hi[c + NCH / 2][e];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        qhi[c] = pack_bf16x8(hi[c]);
+        qlo[c] = pack_bf16x8(lo[c]);
+      }
+    }
+
+    // S^T: rows = keys 16 th + 4 lq + e of the tile, column lr
+    float sv[4][4];
+#pragma unroll
+    for (int th = 0; th < 4; ++th) {
+      pf_floatx4 acc = pf_floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint4 ka = sh.k[4 * c + lq][16 * th + lr];
+        acc = pf_mfma(ka, qhi[c], acc);
+        acc = pf_mfma(ka, qlo[c], acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = key0 + 16 * th + 4 * lq + e;
+        const bool ok = tile_ok && key < T && (int64_t)key <= n;
+        sv[th][e] = ok ? acc[e] * a.scale_log2 : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int th = 0; th < 4; ++th)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sv[th][e]);
+    mx = xor_reduce<16, kWave>(mx, [](float x, float y) { return fmaxf(x, y); });
+    const float mn = fmaxf(m_run, mx);
+    const float alpha = mn == -INFINITY ? 1.f : exp2f(m_run - mn);
+    m_run = mn;
+    float psum = 0.f;
+#pragma unroll
+    for (int th = 0; th < 4; ++th) {
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pv[e] = mn == -INFINITY ? 0.f : exp2f(sv[th][e] - mn);
+        psum += pv[e];
+      }
+      const uint32_t w0 = (uint32_t)f32_to_bf16(pv[0]) | ((uint32_t)f32_to_bf16(pv[1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16(pv[2]) | ((uint32_t)f32_to_bf16(pv[3]) << 16);
+      *reinterpret_cast<uint2*>(&sh.p[w][lr][16 * th + 4 * lq]) = make_uint2(w0, w1);
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+    wave_lds_sync();
+
+    // O^T (dims x columns) += V^T (dims x keys) . P (keys x columns)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint4 pb = *reinterpret_cast<const uint4*>(&sh.p[w][lr][32 * ks + 8 * lq]);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] = pf_mfma(sh.v[4 * ks + lq][16 * dt + lr], pb, oacc[dt]);
+    }
+  }
+
+  // column totals: l over the lanes that share the column
+  const float lsum = xor_reduce<16, kWave>(l_run, [](float x, float y) { return x + y; });
+  if (col_ok) {
+    const int64_t row = ((int64_t)b * a.M + mi) * a.Hq + (int64_t)h * G + g;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.o[row * D + 16 * dt + 4 * lq + e] = oacc[dt][e] * inv;
+    if (lq == 0) {
+      a.m[row] = lsum > 0.f ? m_run * kPfLn2 : -INFINITY;
+      a.l[row] = lsum;
+    }
+  }
+}
+
+template <int D>
+static void launch_prefill_d(dim3 grid, const PrefillArgs& a, int G, hipStream_t stream) {
+  switch (G) {
+    case 1: prefill_rope_kernel<D, 1><<<grid, kPfThreads, 0, stream>>>(a); break;
+    case 2: prefill_rope_kernel<D, 2><<<grid, kPfThreads, 0, stream>>>(a); break;
+    case 4: prefill_rope_kernel<D, 4><<<grid, kPfThreads, 0, stream>>>(a); break;
+    case 8: prefill_rope_kernel<D, 8><<<grid, kPfThreads, 0, stream>>>(a); break;
+    default: prefill_rope_kernel<D, 16><<<grid, kPfThreads, 0, stream>>>(a); break;
+  }
+}
+
+hipError_t launch_prefill_attention(const nosa_dims& d, const nosa_kv& kv, const uint16_t* q, int32_t n_prompt,
+                                    const int32_t* q_pos0, const int32_t* seq_lens, float sm_scale, float* o,
+                                    float* m, float* l, hipStream_t stream) {
+  PrefillArgs a;
+  a.t = make_table(d, kv);
+  a.Hq = d.n_q_heads;
+  a.bs = d.block_size;
+  a.M = n_prompt;
+  a.scale_log2 = sm_scale * kPfLog2e;
+  a.rope_base = (double)kv.rope_base;
+  a.q = q;
+  a.k_pages = kv.k_pages;
+  a.v_pages = kv.v_pages;
+  a.q_pos0 = q_pos0;
+  a.seq_lens = seq_lens;
+  a.o = o;
+  a.m = m;
+  a.l = l;
+  const int G = d.n_q_heads / d.n_kv_heads;
+  const int rows_per_wg = kPfWaves * (kPfCols / G);
+  const dim3 grid((n_prompt + rows_per_wg - 1) / rows_per_wg, d.batch * d.n_kv_heads);
+  if (d.head_dim == 128)
+    launch_prefill_d<128>(grid, a, G, stream);
+  else
+    launch_prefill_d<64>(grid, a, G, stream);
+  return hipGetLastError();
+}
+
+}  // namespace nosa

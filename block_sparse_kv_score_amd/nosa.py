@@ -38,6 +38,7 @@ ENTRY_POINTS = [
     "nosa_sparse_decode_combine",
     "nosa_select_decode",
     "nosa_append_score_qkv",
+    "nosa_prefill_attention",
     "nosa_sparse_decode_mass",
     "nosa_sparse_decode_alibi",
     "nosa_combine",
@@ -112,6 +113,7 @@ _SIGNATURES = {
     "nosa_sparse_decode_alibi": [_DIMS, _P, _KV, _P, _P, _I32, _P, _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P],
     "nosa_append_score_qkv": [_DIMS, _KV, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "nosa_prefill_attention": [_DIMS, _KV, _P, _I32, _P, _P, _F32, _P, _P, _P, _P],
     "nosa_combine": [_DIMS, _I32, _P, _P, _P, _P, _P, _P, _P],
     "nosa_retrieve": [_DIMS, _KV, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P],
     "nosa_retrieve_buffered": [_DIMS, _KV, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P],
@@ -354,6 +356,14 @@ def nosa_append_score_qkv(dims, kv, qkv, w_evict, seq_lens_in, seq_lens_out, k_s
           _dev(k_summary, "k_summary", (torch.float32,)), _dev(e_summary, "e_summary", (torch.float32,)),
           _dev(q_out, "q_out", _BF16_LIKE), _dev(score_q, "score_q", (torch.float32,)),
           _dev(score_e, "score_e", (torch.float32,)), _stream(stream))
+
+
+def nosa_prefill_attention(dims, kv, q, q_pos0, seq_lens, sm_scale, o, m, l, stream=None):
+    """Causal prefill of the prompt over reused documents (q: bf16 [B, M, Hq, D])."""
+    _call("nosa_prefill_attention", ctypes.byref(dims), ctypes.byref(kv), _dev(q, "q", _BF16_LIKE),
+          int(q.shape[1]), _dev(q_pos0, "q_pos0", (torch.int32,)), _dev(seq_lens, "seq_lens", (torch.int32,)),
+          float(sm_scale), _dev(o, "o", (torch.float32,)), _dev(m, "m", (torch.float32,)),
+          _dev(l, "l", (torch.float32,)), _stream(stream))
 
 
 SELECT_DECODE_MAX_BLOCKS = 1024

@@ -141,6 +141,13 @@ class DecodeSession:
                                                       for t in range(1, w.n_append + 1)])).to(dev)
             self.w_evict = torch.from_numpy(synth.eviction_head_weights(w, inp.seed)).to(dev)
             self.q_out = torch.zeros((B, Hq, D), dtype=torch.int16, device=dev)
+        if w.prompt:  # prefill over reused documents: the prompt's queries and outputs
+            M = w.prompt
+            self.q_prefill = torch.from_numpy(synth.prefill_queries(w, inp.seed).view(np.int16)).to(dev)
+            self.q_pos0 = torch.full((B,), w.T0 - M, dtype=torch.int32, device=dev)
+            self.pf_o = torch.full((B, M, Hq, D), fill, dtype=torch.float32, device=dev)
+            self.pf_m = torch.full((B, M, Hq), fill, dtype=torch.float32, device=dev)
+            self.pf_l = torch.full_like(self.pf_m, fill)
         if alibi:  # per query head slopes
             self.alibi_slopes = torch.from_numpy(synth.alibi_slopes(Hq)).to(dev)
         if mass:  # softmax score step: per-tile workspace and the block masses
@@ -312,6 +319,12 @@ class DecodeSession:
         nosa.nosa_sparse_decode_combine(self.dims, self.q(t), kv, self.sel, self.sel_count, self.seq_lens,
                                         self.P, self.w.sm_scale, self.part_o, self.part_m, self.part_l,
                                         self.counters, self.o, self.m, self.l, self.stream)
+
+    def prefill_attention(self):
+        """The prompt's causal attention over the reused documents (prefill
+        workloads)."""
+        nosa.nosa_prefill_attention(self.dims, self.kv, self.q_prefill, self.q_pos0, self.seq_lens, self.w.sm_scale,
+                                    self.pf_o, self.pf_m, self.pf_l, self.stream)
 
     def select_decode(self, t: int):
         """Fused select + swap lists + decode + combine; afterwards evicted is

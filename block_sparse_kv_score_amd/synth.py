@@ -40,6 +40,7 @@ S_K_APP, S_V_APP, S_E_APP, S_HEAVY_APP = 11, 12, 13, 14
 S_Q = 20
 S_PAGES, S_SEGS, S_DOCS = 30, 31, 32
 S_EHEAD = 40
+S_QP = 41
 
 PACK_PAGE_BITS = 20   # packed word: page id in bits 0..19
 PACK_PAGE_MASK = (1 << PACK_PAGE_BITS) - 1
@@ -102,6 +103,12 @@ def queries(w: Workload, seed: int, step: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # page tables
 # ---------------------------------------------------------------------------
+
+def prefill_queries(w: Workload, seed: int) -> np.ndarray:
+    """The prompt's queries (unrotated), (B, prompt, Hq, D) bf16 bits."""
+    q = rng_for(seed, w, S_QP).standard_normal((w.B, w.prompt, w.Hq, w.D), dtype=np.float32)
+    return f32_to_bf16_bits(q)
+
 
 def alibi_slopes(n_heads: int) -> np.ndarray:
     """Per-head ALiBi slopes for the synthetic runs (an input of the

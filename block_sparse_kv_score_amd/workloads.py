@@ -43,6 +43,7 @@ class Workload:
     rope_base: float = 0.0
     n_docs: int = 0
     doc_len: int = 0
+    prompt: int = 0          # prefill: the last `prompt` context tokens are the prompt
     seg_log2: int = 10       # two-level table: 1024-entry segments
     dir_entries: int = 256   # two-level table: directory size
 
@@ -116,6 +117,13 @@ WORKLOADS = {
         Workload(6, "lazy_rope_sparse_32k", B=64, Hq=32, Hkv=8, D=128, T0=32768, steps=4,
                  bs=64, ss=16, k_e=32, k_q=32, splits=1, table=TABLE_PACKED_ROPE,
                  append=False, rope_base=500000.0, n_docs=8, doc_len=4096),
+        # 7: prefill over reused documents: 64 retrieved documents of 512
+        # tokens, then a 512-token prompt (the last document) attending
+        # causally over everything before it
+        Workload(7, "lazy_prefill_33k", B=4, Hq=32, Hkv=8, D=128, T0=65 * 512, steps=1,
+                 bs=64, ss=16, k_e=0, k_q=520, splits=1, table=TABLE_PACKED_ROPE,
+                 append=False, select_all=True, rope_base=500000.0, n_docs=65, doc_len=512,
+                 prompt=512),
     ]
 }
 

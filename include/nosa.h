@@ -431,6 +431,26 @@ nosa_status nosa_retrieve_buffered(const nosa_dims* dims, const nosa_kv* host_kv
  * the host tier).  NOSA_ERR_ARG for memory that is not pinned and mapped. */
 nosa_status nosa_host_device_pointer(const void* host_ptr, void** device_ptr);
 
+/* Prefill over reused documents with deferred RoPE [LAZY, 1. Prefilling:
+ * a single relative rotation from the offset between the queries and the
+ * cached document instead of re-encoding the keys; Mathematical
+ * equivalence].  The prompt (n_prompt tokens, query m at position
+ * n = q_pos0[b] + m) attends causally over the context: the keys at
+ * positions t <= n, t < seq_lens[b], with the prompt's own keys already in
+ * the cache as its last document.  Stored keys carry their in-document
+ * rotation (as for nosa_sparse_decode with NOSA_TABLE_PACKED_ROPE), so
+ *   s = sm_scale * Rot(n - st) q_j . k_stored,  st = the document start
+ * of the key's block (from the packed word); every block up to the last
+ * position is read (no selection).
+ *   q bf16 [B][n_prompt][Hq][D] (unrotated);  q_pos0, seq_lens int32 [B];
+ *   o fp32 [B][n_prompt][Hq][D];  m, l fp32 [B][n_prompt][Hq] (natural-log
+ *   units, as nosa_combine).
+ * NOSA_TABLE_PACKED_ROPE descriptors only (rope_base required); block_size
+ * a multiple of 64.                                                       */
+nosa_status nosa_prefill_attention(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* q,
+                                   int32_t n_prompt, const int32_t* q_pos0, const int32_t* seq_lens,
+                                   float sm_scale, float* o, float* m, float* l, hipStream_t stream);
+
 /* Attention, combine [NOVITA: return rowmax and l with O]:
  *   m = max_p part_m (over p with part_l > 0), l = sum_p part_l e^(part_m - m),
  *   O = sum_p part_l e^(part_m - m) part_o / l;  all empty: O = 0, m = -inf, l = 0.

@@ -163,6 +163,12 @@ def test_host_checks_reject_bad_arguments():
     assert qkv_app(kv, q_out=None) == nosa.NOSA_ERR_ARG
     assert qkv_app(kv, seq_out=P(512)) == nosa.NOSA_ERR_ARG  # lengths in place
     assert qkv_app(rope) == nosa.NOSA_ERR_UNSUPPORTED
+    # prefill: packed RoPE descriptors only, a prompt of at least one token
+    def pf(kvd, n_prompt=4, q_pos0=fake):
+        return L.nosa_prefill_attention(D(d), D(kvd), fake, n_prompt, q_pos0, fake, 0.1, fake, fake, fake, None)
+    assert pf(kv) == nosa.NOSA_ERR_UNSUPPORTED
+    assert pf(rope, n_prompt=0) == nosa.NOSA_ERR_ARG
+    assert pf(rope, q_pos0=None) == nosa.NOSA_ERR_ARG
     # host-tier retrieve: slot count bounds, required lists
     def retr(slots, load=fake):
         return L.nosa_retrieve(D(d), D(kv), P(4096), P(8192), P(12288), slots, fake, fake, load, fake, fake, fake,

@@ -609,6 +609,64 @@ def test_qkv_append_pages_and_split_query():
                 assert ep[page, pos % w.bs] == want, (t, b, h)
 
 
+def run_prefill(w, seed, rows=None, pairs=None):
+    """nosa_prefill_attention against the oracle's prefill for the given
+    prompt rows (all by default) of the given pairs (all by default)."""
+    announce(f"prefill {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} T0={w.T0} prompt={w.prompt} "
+             f"docs={w.n_docs}x{w.doc_len} seed={seed} rows={'all' if rows is None else rows}")
+    inp = synth.generate(w, seed)
+    sess = session(w, inp)
+    sess.prefill_attention()
+    torch.cuda.synchronize()
+    assert int(sess.err.item()) == 0
+    O, m, l = sess.pf_o.cpu().numpy(), sess.pf_m.cpu().numpy(), sess.pf_l.cpu().numpy()
+    qp = synth.prefill_queries(w, inp.seed)
+    starts = synth.block_doc_start(w) * w.bs
+    rows = list(range(w.prompt)) if rows is None else rows
+    for (b, h) in pairs or [(b, h) for b in range(w.B) for h in range(w.Hkv)]:
+        lg = logical_pair(inp, b, h)
+        hs = slice(h * w.G, (h + 1) * w.G)
+        q = oracle.bf16_to_f64(qp[b, rows][:, hs])
+        # only the requested rows: the oracle's prefill over a row subset
+        Ow, mw, lw = oracle.prefill_attention_bh(q, lg.K, lg.V, w.T0, w.T0 - w.prompt, starts, w.bs,
+                                                  w.rope_base, w.sm_scale) if rows == list(range(w.prompt)) else \
+            _prefill_rows(q, lg, w, rows, starts)
+        where = f"{w.name} b={b} h={h}"
+        got_o, got_m, got_l = O[b, rows][:, hs], m[b, rows][:, hs], l[b, rows][:, hs]
+        assert np.abs(got_o - Ow).max() <= 1e-2, (where, "O", float(np.abs(got_o - Ow).max()))
+        assert np.abs(got_m + np.log(got_l) - mw - np.log(lw)).max() <= 1e-3, (where, "LSE")
+        assert np.abs(got_m - mw).max() <= 1e-3, (where, "m")
+
+
+def _prefill_rows(q, lg, w, rows, starts):
+    """The oracle's prefill for a subset of prompt rows: each row on its own
+    (a prompt of one query at its position)."""
+    outs = [oracle.prefill_attention_bh(q[j:j + 1], lg.K, lg.V, w.T0, w.T0 - w.prompt + r, starts, w.bs,
+                                        w.rope_base, w.sm_scale) for j, r in enumerate(rows)]
+    return tuple(np.concatenate([o[k] for o in outs]) for k in range(3))
+
+
+PREFILL_CASES = [
+    ("G4", dict(B=2, Hq=8, Hkv=2, T0=9 * 128, n_docs=9, doc_len=128, prompt=128)),
+    ("G4-ragged", dict(B=1, Hq=8, Hkv=2, T0=8 * 128 + 100, n_docs=9, doc_len=128, prompt=100)),
+    ("G8", dict(B=1, Hq=16, Hkv=2, T0=5 * 256, n_docs=5, doc_len=256, prompt=256)),
+    ("G1", dict(B=1, Hq=2, Hkv=2, T0=9 * 128, n_docs=9, doc_len=128, prompt=128)),
+    ("D64-bs128", dict(B=1, Hq=8, Hkv=2, D=64, bs=128, ss=32, T0=5 * 256, n_docs=5, doc_len=256, prompt=200)),
+]
+
+
+@pytest.mark.parametrize("name,scale", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_small(name, scale):
+    run_prefill(WORKLOADS["lazy_prefill_33k"].scaled(**scale), seed=43)
+
+
+def test_prefill_full_size_sampled():
+    """The full prefill workload (64 documents of 512 tokens + a 512-token
+    prompt), sampled rows and pairs against the oracle."""
+    w = WORKLOADS["lazy_prefill_33k"]
+    run_prefill(w, seed=0, rows=[0, 1, 63, 64, 255, 511], pairs=[(0, 0), (3, 7)])
+
+
 def test_offload_more_loads_than_slots_flags():
     from block_sparse_kv_score_amd import nosa
     w = WORKLOADS["tiny_nosa"].scaled(B=1, Hq=4, Hkv=1, T0=1500)
