@@ -33,6 +33,11 @@ constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfTile = 64;  // keys per tile
 constexpr int kPfCols = 16;  // query columns per wave
+// Row pitch of the per-wave probability tile, in bf16: 64 keys + 8 of
+// padding, so the 16 lanes of a row group (one column each) fall on
+// distinct LDS banks (a 128-byte pitch would put every other column on the
+// same banks).
+constexpr int kPfPitch = kPfTile + 8;
 constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr float kPfLn2 = 0.6931471805599453f;
 
@@ -55,7 +60,7 @@ template <int D>
 struct PrefillSmem {
   uint4 k[D / 8][kPfTile];                     // K tile, page layout [D/8][64][8]
   uint4 v[kPfTile / 8][D];                     // V tile, page layout [64/8][D][8]
-  uint16_t p[kPfWaves][kPfCols][kPfTile];      // bf16 probabilities, per wave
+  uint16_t p[kPfWaves][kPfCols][kPfPitch];     // bf16 probabilities, per wave
   float cs[D / 2][2];                          // cos, sin of st * theta_k
 };
 
@@ -73,12 +78,22 @@ __device__ __forceinline__ uint4 pf_load(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Packs 8 fp32 values as bf16 (round to nearest even).
+typedef __bf16 pf_bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values as packed bf16, round to nearest even (one
+// v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1) {
+  const pf_bf16x2 v = {(__bf16)x0, (__bf16)x1};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// fp32 rounded to bf16 (nearest even) and back.
+__device__ __forceinline__ float round_bf16(float x) { return (float)(__bf16)x; }
+
+// Packs 8 fp32 values as bf16.
 __device__ __forceinline__ uint4 pack_bf16x8(const float* x) {
-  uint32_t w[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = (uint32_t)f32_to_bf16(x[2 * j]) | ((uint32_t)f32_to_bf16(x[2 * j + 1]) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                    pack_bf16x2(x[6], x[7]));
 }
 
 // Column lr of wave w: prompt row m0 + w * (16 / G) + lr / G, head lr % G.
@@ -220,8 +235,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_rope_kernel(const Prefi
           const float cv = sh.cs[d][0], sv = sh.cs[d][1];
           const float x1 = qn[c][e], x2 = qn[c + NCH / 2][e];
           const float r1 = x1 * cv + x2 * sv, r2 = x2 * cv - x1 * sv;
-          hi[c][e] = bf16_to_f32(f32_to_bf16(r1));
-          hi[c + NCH / 2][e] = bf16_to_f32(f32_to_bf16(r2));
+          hi[c][e] = round_bf16(r1);
+          hi[c + NCH / 2][e] = round_bf16(r2);
           lo[c][e] = r1 - hi[c][e];
           lo[c + NCH / 2][e] = r2 - hi[c + NCH / 2][e];
         }
@@ -233,7 +248,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_rope_kernel(const Prefi
       }
     }
 
-    // S^T: rows = keys 16 th + 4 lq + e of the tile, column lr
+    // S^T: rows = keys 16 th + 4 lq + e of the tile, column lr.  A tile
+    // inside the context and at or before every column's position (all but
+    // the last few) needs no mask.
+    const bool full = tile_ok && key0 + kPfTile <= T && (int64_t)(key0 + kPfTile - 1) <= p0 + m0;
     float sv[4][4];
 #pragma unroll
     for (int th = 0; th < 4; ++th) {
@@ -247,7 +265,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_rope_kernel(const Prefi
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = key0 + 16 * th + 4 * lq + e;
-        const bool ok = tile_ok && key < T && (int64_t)key <= n;
+        const bool ok = full || (tile_ok && key < T && (int64_t)key <= n);
         sv[th][e] = ok ? acc[e] * a.scale_log2 : -INFINITY;
       }
     }
@@ -269,8 +287,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_rope_kernel(const Prefi
         pv[e] = mn == -INFINITY ? 0.f : exp2f(sv[th][e] - mn);
         psum += pv[e];
       }
-      const uint32_t w0 = (uint32_t)f32_to_bf16(pv[0]) | ((uint32_t)f32_to_bf16(pv[1]) << 16);
-      const uint32_t w1 = (uint32_t)f32_to_bf16(pv[2]) | ((uint32_t)f32_to_bf16(pv[3]) << 16);
+      const uint32_t w0 = pack_bf16x2(pv[0], pv[1]);
+      const uint32_t w1 = pack_bf16x2(pv[2], pv[3]);
       *reinterpret_cast<uint2*>(&sh.p[w][lr][16 * th + 4 * lq]) = make_uint2(w0, w1);
     }
     l_run = l_run * alpha + psum;
