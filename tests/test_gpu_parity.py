@@ -667,6 +667,65 @@ def test_prefill_full_size_sampled():
     run_prefill(w, seed=0, rows=[0, 1, 63, 64, 255, 511], pairs=[(0, 0), (3, 7)])
 
 
+# ---------------------------------------------------------------------------
+# edge cases of the extensions: empty context, zero budgets, the widest
+# capacity, one-token prompts, appends past capacity
+# ---------------------------------------------------------------------------
+
+EXT_MODES = [
+    ("mass", dict(mass=True)),
+    ("alibi", dict(alibi=True)),
+    ("qkv", dict(qkv=True)),
+    ("offload", dict(offload=True)),
+    ("buffer", dict(offload=True, buffer_slots=10, bucket_width=1)),
+]
+
+
+@pytest.mark.parametrize("mode,kw", EXT_MODES, ids=[m[0] for m in EXT_MODES])
+def test_extensions_empty_context(mode, kw):
+    # the first step appends token 0 and attends to it alone
+    w = WORKLOADS["tiny_nosa"].scaled(B=2, Hq=4, Hkv=2, T0=0)
+    run_trajectory(w, seed=44, steps=6, **kw)
+
+
+@pytest.mark.parametrize("mode,kw", EXT_MODES, ids=[m[0] for m in EXT_MODES])
+@pytest.mark.parametrize("k_e,k_q", [(0, 6), (6, 0)])
+def test_extensions_zero_budgets(mode, kw, k_e, k_q):
+    w = WORKLOADS["tiny_nosa"].scaled(B=2, Hq=8, Hkv=2, T0=1500, k_e=k_e, k_q=k_q)
+    run_trajectory(w, seed=45, steps=4, **kw)
+
+
+@pytest.mark.parametrize("mode,kw", [m for m in EXT_MODES if m[0] in ("mass", "buffer")],
+                         ids=["mass", "buffer"])
+def test_extensions_maximum_capacity(mode, kw):
+    # 8192 blocks of capacity
+    w = WORKLOADS["tiny_nosa"].scaled(B=1, Hq=4, Hkv=1, T0=8192 * 64 - 256 - 10, k_e=6, k_q=10)
+    kw = dict(kw, buffer_slots=24) if mode == "buffer" else kw
+    run_trajectory(w, seed=46, steps=3, splits=3, **kw)
+
+
+def test_prefill_one_token_prompt():
+    # a prompt of one token (the last document holds just it), 128-token blocks
+    w = WORKLOADS["lazy_prefill_33k"].scaled(B=1, Hq=8, Hkv=2, bs=128, ss=32, T0=4 * 128 + 1, n_docs=5,
+                                              doc_len=128, prompt=1)
+    run_prefill(w, seed=47)
+
+
+def test_qkv_append_past_capacity_flags_and_keeps_length():
+    from block_sparse_kv_score_amd import nosa
+    w = WORKLOADS["tiny_nosa"].scaled(B=2, Hq=4, Hkv=2, T0=100)
+    announce("qkv append past capacity: error flag, lengths unchanged")
+    inp = synth.generate(w, 48)
+    sess = session(w, inp, qkv=True)
+    cap = w.max_blocks * w.bs
+    full = torch.full((w.B,), cap, dtype=torch.int32, device="cuda")
+    out = torch.zeros_like(full)
+    nosa.nosa_append_score_qkv(sess.dims, sess.kv, sess.qkv_all[0], sess.w_evict, full, out, sess.k_summary,
+                               sess.e_summary, sess.q_out, sess.score_q, sess.score_e)
+    torch.cuda.synchronize()
+    assert int(sess.err.item()) == 1 and out.tolist() == [cap] * w.B
+
+
 def test_offload_more_loads_than_slots_flags():
     from block_sparse_kv_score_amd import nosa
     w = WORKLOADS["tiny_nosa"].scaled(B=1, Hq=4, Hkv=1, T0=1500)
