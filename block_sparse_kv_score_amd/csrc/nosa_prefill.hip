@@ -12,10 +12,12 @@
 // documents span many key tiles, so this is rarer than rotating every K
 // tile -- and the keys stream from their pages untouched.
 //
-// gfx950 mapping.  Workgroup = 4 waves = one (b, KV head) and 64 query
+// gfx950 mapping.  Workgroup = 8 waves = one (b, KV head) and 128 query
 // columns (a column is a (prompt position, head of the group) pair); wave w
-// owns 16 columns.  Keys stream in 64-token tiles that all four waves share
-// through LDS (loaded with 16-byte loads into registers one tile ahead, then
+// owns 16 columns.  Keys stream in 64-token tiles that all eight waves share
+// through LDS (eight waves rather than four halve the tile loads, stores and
+// barriers per column; the register file holds two waves per SIMD, so one
+// workgroup per CU) (loaded with 16-byte loads into registers one tile ahead, then
 // stored to LDS).  Both products run on v_mfma_f32_16x16x32_bf16 as in the
 // decode: S^T = K . Q^T with the key rows as the A operand straight from the
 // K page layout, and O^T += V^T . P with V^T rows from the V page layout and
@@ -29,7 +31,7 @@
 
 namespace nosa {
 
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfTile = 64;  // keys per tile
 constexpr int kPfCols = 16;  // query columns per wave
@@ -98,12 +100,13 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float* x) {
 
 // Column lr of wave w: prompt row m0 + w * (16 / G) + lr / G, head lr % G.
 template <int D, int G>
-__global__ __launch_bounds__(kPfThreads, 2) void prefill_rope_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const PrefillArgs a) {
   constexpr int NCH = D / 32;      // 32-dim chunks of q.k
   constexpr int NDT = D / 16;      // 16-dim tiles of P.V
   constexpr int PPW = kPfCols / G;  // prompt rows per wave
-  constexpr int KU = (D / 8) * kPfTile / kPfThreads;  // K tile units per thread (= NCH)
-  constexpr int VU = (kPfTile / 8) * D / kPfThreads;  // V tile units per thread (= NCH)
+  constexpr int KU = (D / 8) * kPfTile / kPfThreads;  // K tile units per thread
+  constexpr int VU = (kPfTile / 8) * D / kPfThreads;  // V tile units per thread
+  static_assert(KU >= 1 && VU >= 1, "tile units per thread");
   static_assert(kPfCols % G == 0, "G divides 16");
   __shared__ PrefillSmem<D> sh;
 
