@@ -111,6 +111,7 @@ struct DecodeSelSmem {
   SelShared sel;
   int32_t list[kDecSelCap];
   int32_t n;
+  int32_t spec[kDecWaves];  // tile index of each wave's speculative tile, -1: none
 };
 template <>
 struct DecodeSelSmem<0> {};
@@ -277,14 +278,25 @@ __device__ __forceinline__ void finish_mass(const Table& t, int bh, int b, int h
 // SR > 0: the select variant (SR elements per thread of the selection,
 // covering max_blocks <= SR * kSelThreads).  MASS: the softmax score step
 // (SR == 0 with the fused combine only).  ALIBI: ALiBi biases (SR == 0).
+//
+// Speculative first tile (select variant with one split).  The selection
+// keeps the HBM idle for several microseconds at the start of the launch.
+// Meanwhile each wave w loads the first tile of the w-th block (in index
+// order) that the eviction part has not dropped yet: the next eviction part
+// keeps every such block unless a newly created block displaces one of them,
+// so the block is almost always selected.  If it is, the wave decodes it
+// first and the other waves skip it; otherwise the wave discards the tile.
+// Only the order in which the waves visit the selected tiles changes.
 template <int D, int G, int KIND, int SR, bool MASS = false, bool ALIBI = false>
-__global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(const DecodeArgs a) {
   constexpr bool ROPE = KIND == NOSA_TABLE_PACKED_ROPE;
   using S = DecodeShape<D, G, ROPE>;
   constexpr int GE = S::GE, LPS = S::LPS, TPM = S::TPM, TH = S::TH, NDS = S::NDS, NDT = S::NDT;
   __shared__ DecodeSmem<D, G, ROPE> sh;
   __shared__ DecodeSelSmem<SR> ssh;
   static_assert(SR == 0 || kDecThreads == kSelThreads, "the selection runs on the whole workgroup");
+  static_assert(!(MASS && SR > 0) && !(ALIBI && SR > 0), "select variants decode plain scores");
+  static_assert(kDecWaves == 4, "the speculation's sorting network");
 
   const int bh = blockIdx.x, p = blockIdx.y;
   const int Hkv = a.t.Hkv;
@@ -298,46 +310,28 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
 
   const int T = min(max(a.seq_lens[b], 0), a.t.max_blocks * a.bs);
   const int nb = (T + a.bs - 1) / a.bs;
-  int n;
-  const int32_t* selp = a.sel + (int64_t)bh * a.sel_cap;  // global list (SR == 0)
-  if constexpr (SR > 0) {
-    // the pair's selection, into LDS; split 0 also writes the outputs
-    const bool lead = p == 0;
-    {
-      const int words = (a.t.max_blocks + 31) / 32;
-      SwapArgs sw = a.sw;  // a copy (see select_pair)
-      if (!lead) sw.load = nullptr;
-      const int ns = select_pair<SR, true>(ssh.sel, bh, T, a.bs, a.t.max_blocks, a.score_q, a.score_e, a.k_e, a.k_q,
-                                           a.ev_in + (int64_t)bh * words,
-                                           lead ? a.ev_out + (int64_t)bh * words : nullptr, ssh.list, a.sel_cap,
-                                           nullptr, sw);
-      if (threadIdx.x == 0) ssh.n = ns;
-    }
-    __syncthreads();  // the list and its size
-    n = ssh.n;
-    if (lead) {
-      for (int k = threadIdx.x; k < n; k += kDecThreads) a.sel_w[(int64_t)bh * a.sel_cap + k] = ssh.list[k];
-      if (threadIdx.x == 0) a.sel_count_w[bh] = n;
-    }
-  } else {
-    n = min(max(a.sel_count[bh], 0), a.sel_cap);
-  }
-  const int c = (n + a.P - 1) / a.P;
-  const int j0 = min(p * c, n), j1 = min(j0 + c, n);
   const int tpb = a.bs / kTile;
-  const int ntiles = (j1 - j0) * tpb;
   const uint16_t* qg = a.q + ((int64_t)b * a.Hq + (int64_t)h * G) * D;  // heads h*G.. are contiguous
 
-  // query operand of q.k, one 16-byte slice per d-step
+  // query operand of q.k, one 16-byte slice per d-step.  The select variant
+  // parks the query in LDS during the selection (its loads go out before the
+  // selection's inputs, and it holds no registers meanwhile).
   uint4 qreg[NDS];
   double theta = 0.0;
   int64_t qpos = 0;
-  if constexpr (!ROPE) {
+  __shared__ uint4 qstage[SR > 0 ? G * D / 8 : 1];
+  auto query_from = [&](const uint4* src) {
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
       const int o = ds * LPS + dsub;
-      qreg[ds] = qcol ? *reinterpret_cast<const uint4*>(qg + cg * D + 8 * o) : make_uint4(0, 0, 0, 0);
+      qreg[ds] = qcol ? src[(cg * D + 8 * o) / 8] : make_uint4(0, 0, 0, 0);
     }
+  };
+  if constexpr (SR > 0) {
+    static_assert(!ROPE, "select variants read flat or two-level tables");
+    for (int x = threadIdx.x; x < G * D / 8; x += kDecThreads) qstage[x] = reinterpret_cast<const uint4*>(qg)[x];
+  } else if constexpr (!ROPE) {
+    query_from(reinterpret_cast<const uint4*>(qg));
   } else {
     for (int k = threadIdx.x; k < G * D; k += kDecThreads) sh.qf[k / D][k % D] = bf16_to_f32(qg[k]);
     if (lane < D / 2) theta = pow((double)a.rope_base, -2.0 * (double)lane / (double)D);
@@ -346,6 +340,134 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
     for (int ds = 0; ds < NDS; ++ds) qreg[ds] = make_uint4(0, 0, 0, 0);
     __syncthreads();
   }
+
+  // K as the A operand: row lr of token set set_q, octet ds*LPS + dsub;
+  // V^T as the A operand of P.V: dim 16 dt + lr, tokens 32 ks + 8 lq .. +8
+  auto k_ptr = [&](int64_t page, int sub) {
+    return reinterpret_cast<const uint4*>(a.k_pages + page * (int64_t)a.bs * D) + sub * kTile + 16 * set_q + lr +
+           (int64_t)dsub * a.bs;
+  };
+  auto v_ptr = [&](int64_t page, int sub) {
+    return reinterpret_cast<const uint4*>(a.v_pages + page * (int64_t)a.bs * D) + (sub * 8 + lq) * D + lr;
+  };
+  uint4 kr[TH][NDS];
+  uint4 vr[2][NDT];
+  auto load_tile = [&](int64_t page, int sub) {
+    const uint4* kpg = k_ptr(page, sub);
+#pragma unroll
+    for (int th = 0; th < TH; ++th)
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) kr[th][ds] = load_stream(kpg + (int64_t)ds * LPS * a.bs + th * TPM);
+    const uint4* vpg = v_ptr(page, sub);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vr[ks][dt] = load_stream(vpg + ks * 4 * D + dt * 16);
+  };
+
+  int n;
+  const int32_t* selp = a.sel + (int64_t)bh * a.sel_cap;  // global list (SR == 0)
+  // speculation: this wave's block (-1: none), its page, and the selected
+  // tiles the waves took speculatively, ascending (INT_MAX: unused)
+  int spec_blk = -1;
+  int64_t spec_page = -1;
+  uint32_t spec_docb = 0;
+  int skip[kDecWaves] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+  int nskip = 0;
+  if constexpr (SR > 0) {
+    // the pair's selection, into LDS; split 0 also writes the outputs
+    const bool lead = p == 0;
+    const bool spec = a.P == 1;
+    const int words = (a.t.max_blocks + 31) / 32;  // <= 32: one word per lane
+    uint32_t evw = 0xffffffffu;
+    if (spec && lane < words) evw = a.ev_in[(int64_t)bh * words + lane];
+    // once the selection's loads are out: this wave's block is the w-th zero
+    // bit of the eviction bitmap below nb; its page lookup goes out now
+    auto guess = [&]() {
+      if (!spec) return;
+      const int base = lane * 32;
+      uint32_t z = base >= nb ? 0u : (nb - base >= 32 ? ~evw : ~evw & ((1u << (nb - base)) - 1u));
+      const int c = __popc(z);
+      const int excl = wave_scan_incl(c) - c;
+      const bool mine = excl <= w && w < excl + c;
+      const uint64_t m = __ballot(mine);
+      if (m == 0) return;  // fewer than w + 1 such blocks
+      for (int j = mine ? w - excl : 0; j > 0; --j) z &= z - 1u;
+      const int src = __ffsll((unsigned long long)m) - 1;
+      spec_blk = __builtin_amdgcn_readlane(base + __ffs(z) - 1, src);
+      spec_page = page_of<KIND>(a.t, bh, spec_blk, spec_docb);
+    };
+    // once the eviction part is decided: the tile's loads go out
+    auto issue = [&]() {
+      if (spec_blk < 0) return;
+      if (spec_page < 0) {  // unresolvable: no speculation (the decode flags it if selected)
+        spec_blk = -1;
+        return;
+      }
+      load_tile(spec_page, 0);
+    };
+    {
+      SwapArgs sw = a.sw;  // a copy (see select_pair)
+      if (!lead) sw.load = nullptr;
+      const int ns = select_pair<SR, true>(ssh.sel, bh, T, a.bs, a.t.max_blocks, a.score_q, a.score_e, a.k_e, a.k_q,
+                                           a.ev_in + (int64_t)bh * words,
+                                           lead ? a.ev_out + (int64_t)bh * words : nullptr, ssh.list, a.sel_cap,
+                                           nullptr, sw, guess, issue);
+      if (threadIdx.x == 0) ssh.n = ns;
+    }
+    __syncthreads();  // the list and its size
+    n = ssh.n;
+    query_from(qstage);
+    if (lead) {
+      for (int k = threadIdx.x; k < n; k += kDecThreads) a.sel_w[(int64_t)bh * a.sel_cap + k] = ssh.list[k];
+      if (threadIdx.x == 0) a.sel_count_w[bh] = n;
+    }
+    if (spec) {
+      // is this wave's block selected, and at which list position
+      int pos = n;
+      if (spec_blk >= 0) {
+        int below = 0;
+        for (int j0_ = 0; j0_ < n; j0_ += kWave) {
+          const int j = j0_ + lane;
+          below += __popcll(__ballot(j < n && ssh.list[j] < spec_blk));
+        }
+        pos = below < n && ssh.list[below] == spec_blk ? below : n;
+      }
+      if (pos >= n) spec_blk = -1;
+      if (lane == 0) ssh.spec[w] = spec_blk >= 0 ? pos * tpb : -1;
+      __syncthreads();
+#pragma unroll
+      for (int ww = 0; ww < kDecWaves; ++ww) {
+        const int v = ssh.spec[ww];
+        skip[ww] = v < 0 ? INT_MAX : v;
+        nskip += v >= 0;
+      }
+      auto cs = [](int& x, int& y) {
+        const int lo = min(x, y), hi = max(x, y);
+        x = lo;
+        y = hi;
+      };
+      cs(skip[0], skip[1]);
+      cs(skip[2], skip[3]);
+      cs(skip[0], skip[2]);
+      cs(skip[1], skip[3]);
+      cs(skip[1], skip[2]);
+    }
+  } else {
+    n = min(max(a.sel_count[bh], 0), a.sel_cap);
+  }
+  const int c = (n + a.P - 1) / a.P;
+  const int j0 = min(p * c, n), j1 = min(j0 + c, n);
+  const int ntiles = (j1 - j0) * tpb;
+  const int ntu = ntiles - nskip;  // tiles left after the speculative ones
+  // tile index among the split's tiles of entry k of the remaining ones
+  auto full_of = [&](int k) {
+    if constexpr (SR > 0) {
+#pragma unroll
+      for (int s = 0; s < kDecWaves; ++s) k += k >= skip[s];
+    }
+    return k;
+  };
   uint32_t cur_doc = 0xffffffffu;
 
   float m_run = -INFINITY, l_run = 0.f;  // for head slot cg, log2 units
@@ -356,19 +478,21 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Tile k of this split: block sel[j0 + k / tpb], 64-token slice k % tpb.
-  // Returns the next tile >= k with data, skipping (and flagging) entries the
-  // table cannot resolve; ntiles when there is none.
+  // Remaining tile k of this split: tile kf = full_of(k), i.e. block
+  // sel[j0 + kf / tpb], 64-token slice kf % tpb.  Returns the next k with
+  // data, skipping (and flagging) entries the table cannot resolve; ntu when
+  // there is none.
   auto next_tile = [&](int k, int64_t& page, int& ntok, uint32_t& docb, int& sub, int& pos0) -> int {
-    for (; k < ntiles; k += kDecWaves) {
+    for (; k < ntu; k += kDecWaves) {
+      const int kf = full_of(k);
       // the LDS list is read by name (LDS instructions): through a generic
       // pointer every read would also wait for the in-flight tile loads
       int i;
       if constexpr (SR > 0)
-        i = ssh.list[j0 + k / tpb];
+        i = ssh.list[j0 + kf / tpb];
       else
-        i = selp[j0 + k / tpb];
-      sub = k % tpb;
+        i = selp[j0 + kf / tpb];
+      sub = kf % tpb;
       if (i < 0 || i >= nb) {
         if (lane == 0) flag_error(a.t.err);
         continue;
@@ -382,42 +506,29 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
       ntok = min(kTile, T - (i * a.bs + sub * kTile));
       if (ntok > 0) return k;
     }
-    return ntiles;
-  };
-  // K as the A operand: row lr of token set set_q, octet ds*LPS + dsub;
-  // V^T as the A operand of P.V: dim 16 dt + lr, tokens 32 ks + 8 lq .. +8
-  auto k_ptr = [&](int64_t page, int sub) {
-    return reinterpret_cast<const uint4*>(a.k_pages + page * (int64_t)a.bs * D) + sub * kTile + 16 * set_q + lr +
-           (int64_t)dsub * a.bs;
-  };
-  auto v_ptr = [&](int64_t page, int sub) {
-    return reinterpret_cast<const uint4*>(a.v_pages + page * (int64_t)a.bs * D) + (sub * 8 + lq) * D + lr;
+    return ntu;
   };
 
-  uint4 kr[TH][NDS];
-  uint4 vr[2][NDT];
   int64_t page = 0;
   int ntok = 0, sub = 0, pos0 = 0;
   uint32_t docb = 0;
-  int k = next_tile(w, page, ntok, docb, sub, pos0);
-  if (k < ntiles) {
-    const uint4* kpg = k_ptr(page, sub);
-#pragma unroll
-    for (int th = 0; th < TH; ++th)
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) kr[th][ds] = load_stream(kpg + (int64_t)ds * LPS * a.bs + th * TPM);
-    const uint4* vpg = v_ptr(page, sub);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) vr[ks][dt] = load_stream(vpg + ks * 4 * D + dt * 16);
+  int k;  // the current tile: a remaining one, or w - kDecWaves for the speculative one
+  if (spec_blk >= 0) {  // its loads are in flight; the wave's remaining tiles follow
+    k = w - kDecWaves;
+    page = spec_page;
+    docb = spec_docb;
+    ntok = min(kTile, T - spec_blk * a.bs);
+    pos0 = spec_blk * a.bs;
+  } else {
+    k = next_tile(w, page, ntok, docb, sub, pos0);
+    if (k < ntu) load_tile(page, sub);
   }
 
   // Software pipeline: once q.k has consumed this tile's keys the key
   // registers receive the next tile's keys, and once P.V has consumed the
   // values they receive the next values, so every wave keeps a tile of
   // loads in flight while it computes.
-  while (k < ntiles) {
+  while (k < ntu) {
     int64_t npage = 0;
     int nntok = 0, nsub = 0, npos0 = 0;
     uint32_t ndocb = 0;
@@ -483,7 +594,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (nk < ntiles) {  // prefetch the next tile's keys
+    if (nk < ntu) {  // prefetch the next tile's keys
       const uint4* kpg = k_ptr(npage, nsub);
 #pragma unroll
       for (int th = 0; th < TH; ++th)
@@ -557,7 +668,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(const DecodeArgs
     }
     wave_lds_sync();
     __builtin_amdgcn_sched_barrier(0);
-    if (nk < ntiles) {  // prefetch the next tile's values
+    if (nk < ntu) {  // prefetch the next tile's values
       const uint4* vpg = v_ptr(npage, nsub);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)

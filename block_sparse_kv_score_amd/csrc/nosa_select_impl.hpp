@@ -194,11 +194,19 @@ struct SwapArgs {
 //     the previous selection (global memory).  sw is taken by value: a
 //     reference into a kernel's by-value argument would force a stack copy
 //     of the whole argument and turn every global access into a flat one.
-template <int R, bool SWAP>
+//   after_loads / after_eviction: called by every thread once the inputs'
+//     loads are issued, and once the eviction part is decided (a caller's
+//     own memory traffic can go out there without delaying these loads).
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+template <int R, bool SWAP, class H1 = NoHook, class H2 = NoHook>
 __device__ int select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks,
                            const float* __restrict__ score_q, const float* __restrict__ score_e, int k_e,
                            int k_q, const uint32_t* ev_in, uint32_t* ev_out, int32_t* sel_row, int sel_cap,
-                           int32_t* sel_count_slot, const SwapArgs sw) {
+                           int32_t* sel_count_slot, const SwapArgs sw, H1 after_loads = H1(),
+                           H2 after_eviction = H2()) {
   constexpr int NT = kSelThreads;
   static_assert(R <= 32, "selection shape");
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -230,6 +238,7 @@ __device__ int select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks,
     for (int r = 0; r < R; ++r) pv[r] = pl[min(r * NT + (int)threadIdx.x, sel_cap - 1)];
     n_prev = min(max(sw.prev_count[bh], 0), sel_cap);
   }
+  after_loads();
   uint32_t valid = 0, evm = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -252,6 +261,7 @@ __device__ int select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks,
   if (n_e == n_cand) in_e = cand_e;
   else if (n_e > 0) radix_top_k<R>(ke, cand_e, n_e, in_e, phase, sh);
   evm |= cand_e & ~in_e;  // every candidate left out is evicted for good
+  after_eviction();
 
   // --- query part: best of the blocks the eviction part did not take ----
   const uint32_t cand_q = valid & ~in_e;

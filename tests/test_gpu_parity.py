@@ -19,6 +19,7 @@ import oracle
 from block_sparse_kv_score_amd import synth
 from block_sparse_kv_score_amd.workloads import WORKLOADS
 
+import parity
 from parity import (Gpu, PairState, bitmap_set, check_attention, compare_pair, logical_pair)
 
 pytestmark = pytest.mark.gpu
@@ -216,7 +217,11 @@ def test_fused_equals_separate(name, scale, splits):
     give bit-identical results to the separate calls they fuse, step after
     step:
     selections, swap lists, partials, outputs, lengths, summaries, block
-    scores and pages."""
+    scores and pages.  With one split the fused decode takes a speculatively
+    loaded tile first in each wave, so it visits the selected tiles in
+    another order: there its attention outputs are held to the parity bar
+    against the separate calls (the row max, a max over the same scores,
+    stays bit-identical)."""
     w = WORKLOADS[name].scaled(**scale) if scale else WORKLOADS[name]
     announce(f"fused vs separate {name} {scale} P={splits}")
     inp = synth.generate(w, 11)
@@ -245,6 +250,14 @@ def test_fused_equals_separate(name, scale, splits):
                     for h in range(w.Hkv):
                         k = int(cnt[b, h])
                         assert torch.equal(x[b, h, :k], y[b, h, :k]), (n, t, b, h)
+                continue
+            if splits == 1 and n in ("part_o", "o"):
+                assert (x - y).abs().max().item() <= parity.O_TOL, (n, t)
+                continue
+            if splits == 1 and n in ("part_l", "l"):
+                lx, ly = torch.log(x.double()), torch.log(y.double())
+                assert torch.equal(x > 0, y > 0), (n, t)
+                assert not (x > 0).any() or (lx - ly)[x > 0].abs().max().item() <= parity.LSE_TOL, (n, t)
                 continue
             assert torch.equal(x.view(torch.int32) if x.dtype == torch.float32 else x,
                                y.view(torch.int32) if y.dtype == torch.float32 else y), (n, t)
@@ -525,12 +538,13 @@ def test_softmax_mass_trajectory(name, scale, splits):
 @pytest.mark.parametrize("name,scale,splits", MASS_CASES[1:3], ids=[f"{c[0]}-P{c[2]}" for c in MASS_CASES[1:3]])
 def test_softmax_mass_keeps_attention_bits(name, scale, splits):
     """With the score step the attention outputs are the same bits as the
-    plain fused decode, and every head's masses sum to 1."""
+    plain decode's (the separate calls, which visit the tiles in the same
+    order), and every head's masses sum to 1."""
     w = WORKLOADS[name].scaled(**scale)
     announce(f"mass vs plain decode bits {name} {scale} P={splits}")
     inp = synth.generate(w, 36)
     a = session(w, inp, splits=splits, mass=True)
-    s = session(w, inp, splits=splits)
+    s = session(w, inp, splits=splits, fused=False)
     for t in range(1, 5):
         a.step(t)
         s.step(t)
