@@ -329,7 +329,6 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
   };
   if constexpr (SR > 0) {
     static_assert(!ROPE, "select variants read flat or two-level tables");
-    for (int x = threadIdx.x; x < G * D / 8; x += kDecThreads) qstage[x] = reinterpret_cast<const uint4*>(qg)[x];
   } else if constexpr (!ROPE) {
     query_from(reinterpret_cast<const uint4*>(qg));
   } else {
@@ -397,8 +396,12 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
       spec_blk = __builtin_amdgcn_readlane(base + __ffs(z) - 1, src);
       spec_page = page_of<KIND>(a.t, bh, spec_blk, spec_docb);
     };
-    // once the eviction part is decided: the tile's loads go out
+    // once the eviction part is decided: the tile's loads go out.  Every
+    // input load of the selection is complete first (an explicit wait), so
+    // no later wait of the selection, at a join after this conditional
+    // issue, has to cover the tile.
     auto issue = [&]() {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       if (spec_blk < 0) return;
       if (spec_page < 0) {  // unresolvable: no speculation (the decode flags it if selected)
         spec_blk = -1;
@@ -406,16 +409,28 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
       }
       load_tile(spec_page, 0);
     };
+    // Once the selection's input loads are issued: the query (one 16-byte
+    // piece per thread, loaded with them) is parked in LDS and the guess's
+    // page-table read goes out.
+    auto after_loads = [&]() {
+      constexpr int kQPieces = G * D / 8;
+      static_assert(kQPieces <= kDecThreads, "one query piece per thread");
+      const bool has_piece = (int)threadIdx.x < kQPieces;
+      uint4 qp = make_uint4(0, 0, 0, 0);
+      if (has_piece) qp = reinterpret_cast<const uint4*>(qg)[threadIdx.x];
+      guess();
+      if (has_piece) qstage[threadIdx.x] = qp;
+    };
     {
       SwapArgs sw = a.sw;  // a copy (see select_pair)
       if (!lead) sw.load = nullptr;
       const int ns = select_pair<SR, true>(ssh.sel, bh, T, a.bs, a.t.max_blocks, a.score_q, a.score_e, a.k_e, a.k_q,
                                            a.ev_in + (int64_t)bh * words,
                                            lead ? a.ev_out + (int64_t)bh * words : nullptr, ssh.list, a.sel_cap,
-                                           nullptr, sw, guess, issue);
+                                           nullptr, sw, after_loads, issue);
       if (threadIdx.x == 0) ssh.n = ns;
     }
-    __syncthreads();  // the list and its size
+    __syncthreads();  // the list and its size, the query
     n = ssh.n;
     query_from(qstage);
     if (lead) {

@@ -216,17 +216,18 @@ __device__ int select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks,
   const bool swap_lists = SWAP && sw.load != nullptr;
 
   // every load up front, over the whole capacity so they need not wait for
-  // seq_lens; blocks >= nb are masked out afterwards
+  // seq_lens; blocks >= nb are masked out afterwards.  The loads are
+  // unconditional (indices clamped into the table, max_blocks >= 1) so all
+  // of them are in flight together: under a branch each group of three
+  // would wait for its data before the next group went out.
   uint32_t ke[R], kq[R], ew[R];
+  float fe[R], fq[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int i = r * NT + threadIdx.x;
-    ke[r] = kq[r] = ew[r] = 0u;
-    if (i < max_blocks) {
-      ke[r] = order_key(se[i]);
-      kq[r] = order_key(sq[i]);
-      ew[r] = ev_in[i >> 5];
-    }
+    const int i = min(r * NT + (int)threadIdx.x, max_blocks - 1);
+    fe[r] = se[i];
+    fq[r] = sq[i];
+    ew[r] = ev_in[i >> 5];
   }
   // fused swap lists: the previous selection (capacity sel_cap <= max_blocks,
   // so R entries per thread cover it), loaded with everything else
@@ -239,6 +240,13 @@ __device__ int select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks,
     n_prev = min(max(sw.prev_count[bh], 0), sel_cap);
   }
   after_loads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool in = r * NT + (int)threadIdx.x < max_blocks;
+    ke[r] = in ? order_key(fe[r]) : 0u;
+    kq[r] = in ? order_key(fq[r]) : 0u;
+    ew[r] = in ? ew[r] : 0u;
+  }
   uint32_t valid = 0, evm = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
