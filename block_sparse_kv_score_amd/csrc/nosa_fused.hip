@@ -190,11 +190,22 @@ __device__ void append_token(const FusedArgs& a, FusedSmem<D>& sh, int bh, int p
   if (lane == 0) epage[r] = e_new;
 }
 
+// Whether the lead workgroup loads its summaries before its append (with the
+// lookups; one memory round trip fewer on the launch's critical path): where
+// a lane's slice is at most 8 quads and the kernel still fits 8 waves per
+// SIMD (64 VGPRs) without spills with them live across the append (not the
+// QKV variants, whose eviction head needs more registers).
+template <int D, int L, bool ROPE, bool QKV>
+constexpr bool kEarlySummary() {
+  return !ROPE && !QKV && D / 4 / L <= 8;
+}
+
 // L lanes per sub-block (see score_kernel).  ROPE: packed table, scoring
 // only, nsub >= 4.  QKV: the appended token and the query from the fused
 // projection rows.
 template <int D, int L, bool ROPE = false, bool QKV = false>
-__global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const FusedArgs a) {
+__global__ __launch_bounds__(kFusedThreads)
+__attribute__((amdgpu_waves_per_eu(kEarlySummary<D, L, ROPE, QKV>() ? 8 : 1))) void append_score_kernel(const FusedArgs a) {
   constexpr int NQ = D / 4;
   constexpr int QL = NQ / L;
   constexpr int SPW = kWave / L;
@@ -270,9 +281,11 @@ __global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const Fused
     for (int u = 0; u < QL; ++u) v[u] = __builtin_nontemporal_load(p + (int64_t)u * CS);
     ev = a.e_summary[(int64_t)bh * CS + min(s, CS - 1)];
   };
-  // the lead loads its summaries after the append (its registers are then
-  // free), every other workgroup right away
-  if (work && !lead) load_summary();
+  // every other workgroup loads right away; the lead too where its
+  // registers allow (its append then adds one memory round trip, the older
+  // tokens, instead of two), else after the append
+  constexpr bool early = kEarlySummary<D, L, ROPE, QKV>();
+  if (work && (early || !lead)) load_summary();
   if (threadIdx.x < D) {
     double acc = 0;
 #pragma unroll
@@ -306,7 +319,7 @@ __global__ __launch_bounds__(kFusedThreads) void append_score_kernel(const Fused
       e_new = a.e_new[bh];
     }
     append_token<D>(a, sh, bh, raw, page, kn, vn, e_new);
-    load_summary();
+    if constexpr (!early) load_summary();
   }
   __syncthreads();  // qbar, and the append's summary
 
