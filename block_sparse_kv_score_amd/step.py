@@ -14,8 +14,9 @@ With `fused` (the default) the step is two launches with the same results:
   nosa_append_score          append + score
   nosa_select_decode         select + swap_diff + decode + combine
 (where nosa_select_decode is not supported -- more than 1024 blocks of
-capacity -- nosa_select_swap then nosa_sparse_decode_combine; with every
-block selected: nosa_swap_diff, then the fused decode).  The fused launches
+capacity -- or by default above two splits, nosa_select_swap then
+nosa_sparse_decode_combine; with every block selected: nosa_swap_diff,
+then the fused decode).  The fused launches
 write the new lengths and the new eviction bitmap to the other of two
 buffers, so `seq_lens` and `evicted` name the current ones.
 
@@ -50,6 +51,7 @@ _KIND = {TABLE_FLAT: nosa.NOSA_TABLE_FLAT, TABLE_TWO_LEVEL: nosa.NOSA_TABLE_TWO_
          TABLE_PACKED_ROPE: nosa.NOSA_TABLE_PACKED_ROPE}
 
 BF16_NAN = -1  # 0xFFFF as int16: a NaN bit pattern for never-written slots
+SELECT_DECODE_AUTO_MAX_SPLITS = 2  # default: nosa_select_decode up to this many splits
 
 
 def _i32(a: np.ndarray) -> torch.Tensor:
@@ -63,7 +65,8 @@ class DecodeSession:
     def __init__(self, w: Workload, inp: Inputs, splits: int | None = None, device: str = "cuda",
                  poison: bool = True, stream: torch.cuda.Stream | None = None, fused: bool = True,
                  offload: bool = False, buffer_slots: int | None = None, bucket_width: int = 1,
-                 mass: bool = False, alibi: bool = False, qkv: bool = False):
+                 mass: bool = False, alibi: bool = False, qkv: bool = False,
+                 select_decode: bool | None = None):
         self.w, self.inp = w, inp
         self.buffered = buffer_slots is not None
         self.buffer_slots, self.bucket_width = buffer_slots, int(bucket_width)
@@ -118,7 +121,16 @@ class DecodeSession:
         self.score_e = torch.full_like(self.score_q, fill)
         self.ev_bufs = [torch.zeros((B, Hkv, (MB + 31) // 32), dtype=torch.int32, device=dev) for _ in range(2)]
         self.evicted = self.ev_bufs[0]
-        self.select_decode_ok = MB <= nosa.SELECT_DECODE_MAX_BLOCKS and w.table != TABLE_PACKED_ROPE
+        # nosa_select_decode where it supports the shape and, by default, at
+        # few splits only: every workgroup of a pair repeats the selection and
+        # the select variant keeps one wave per SIMD, so with many short
+        # workgroups per pair nosa_select_swap + nosa_sparse_decode_combine
+        # is faster.  select_decode=True takes it wherever it is supported.
+        supported = MB <= nosa.SELECT_DECODE_MAX_BLOCKS and w.table != TABLE_PACKED_ROPE
+        if select_decode is None:
+            self.select_decode_ok = supported and self.P <= SELECT_DECODE_AUTO_MAX_SPLITS
+        else:
+            self.select_decode_ok = supported and bool(select_decode)
         # selections ping-pong between two buffers: step t writes buffer t % 2
         # and diffs against buffer (t - 1) % 2 (both start empty)
         self.sel_bufs = [torch.full((B, Hkv, self.cap), -1, dtype=torch.int32, device=dev) for _ in range(2)]

@@ -106,10 +106,10 @@ WORKLOADS = {
                  bs=64, ss=16, k_e=64, k_q=64, splits=16, append=False),
         # 4: Llama-3.1-70B-shaped layer at 256K context, two-level page table
         Workload(4, "llama31_70b_256k", B=8, Hq=64, Hkv=8, D=128, T0=262144, steps=4,
-                 bs=128, ss=32, k_e=96, k_q=32, splits=16, table=TABLE_TWO_LEVEL),
+                 bs=128, ss=32, k_e=96, k_q=32, splits=4, table=TABLE_TWO_LEVEL),
         # 5: deferred RoPE over 8 documents of 4096 tokens, every block
         Workload(5, "lazy_rope_32k", B=64, Hq=32, Hkv=8, D=128, T0=32768, steps=1,
-                 bs=64, ss=16, k_e=0, k_q=512, splits=8, table=TABLE_PACKED_ROPE,
+                 bs=64, ss=16, k_e=0, k_q=512, splits=1, table=TABLE_PACKED_ROPE,
                  append=False, select_all=True, rope_base=500000.0,
                  n_docs=8, doc_len=4096),
         # 6: the same deferred-RoPE cache with NOSA selection (64 of 512

@@ -225,7 +225,7 @@ def test_fused_equals_separate(name, scale, splits):
     w = WORKLOADS[name].scaled(**scale) if scale else WORKLOADS[name]
     announce(f"fused vs separate {name} {scale} P={splits}")
     inp = synth.generate(w, 11)
-    a = session(w, inp, splits=splits, fused=True)
+    a = session(w, inp, splits=splits, fused=True, select_decode=True)
     s = session(w, inp, splits=splits, fused=False)
     names = ["sel", "sel_count", "evicted", "load", "load_count", "evict", "evict_count",
              "part_o", "part_m", "part_l", "o", "m", "l", "seq_lens", "k_summary", "e_summary",
