@@ -98,6 +98,7 @@ static hipError_t launch_select_any(const nosa_dims& d, const float* score_q, co
   if (R <= 2) NOSA_SELECT(2);
   else if (R <= 4) NOSA_SELECT(4);
   else if (R <= 8) NOSA_SELECT(8);
+  else if (R <= 12) NOSA_SELECT(12);
   else if (R <= 16) NOSA_SELECT(16);
   else NOSA_SELECT(32);
 #undef NOSA_SELECT
