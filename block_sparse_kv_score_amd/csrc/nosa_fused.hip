@@ -89,30 +89,31 @@ struct RopeSmem {
 template <int D>
 struct RopeSmem<D, false> {};
 
-template <int D>
+// NST: older tokens staged per pass (1 where the kernel never appends)
+template <int D, int NST>
 struct FusedSmem {
   double qbar[D];
   f4 knew[D / 4];  // the new token's sub-block summary (append workgroup)
-  uint4 kold[kStageTok][D / 8];  // staged older keys of that sub-block
-  float eold[kStageTok];
+  uint4 kold[NST][D / 8];  // staged older keys of that sub-block
+  float eold[NST];
   float enew;
   int have_new;
 };
 
 // The append of pair bh, by the whole append workgroup (uniform call):
 // token position pos (in range), page the page of its block (-1: none).  The older tokens of the new token's
-// sub-block are staged through LDS kStageTok at a time by all threads (one
+// sub-block are staged through LDS NST at a time by all threads (one
 // memory round trip per pass instead of one per batch of a single lane);
 // wave 0 then sums them in ascending token order exactly as sum_key_quad /
 // sum_logits do, adds the new token, and writes the summary (global memory
 // and sh.knew / sh.enew) and the token itself.  Mirrors append_kernel.
-template <int D>
-__device__ void append_token(const FusedArgs& a, FusedSmem<D>& sh, int bh, int pos, int64_t page,
+template <int D, int NST>
+__device__ void append_token(const FusedArgs& a, FusedSmem<D, NST>& sh, int bh, int pos, int64_t page,
                              const uint16_t* kn, const uint16_t* vn, float e_new) {
   constexpr int NQ = D / 4;
   constexpr int NO = D / 8;  // 16-byte octets per key row
   constexpr int VL = D / kWave;
-  constexpr int IPT = (NO * kStageTok + kFusedThreads - 1) / kFusedThreads;  // staged items per thread
+  constexpr int IPT = (NO * NST + kFusedThreads - 1) / kFusedThreads;  // staged items per thread
   const Table& t = a.t;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int bs = a.bs, ss = a.ss, nsub = bs / ss, CS = t.max_blocks * nsub;
@@ -127,8 +128,8 @@ __device__ void append_token(const FusedArgs& a, FusedSmem<D>& sh, int bh, int p
   uint16_t* vpage = a.v_pages + page * (int64_t)bs * D;
   float* epage = a.e_pages + page * bs;
   double a0 = 0, a1 = 0, a2 = 0, a3 = 0, ae = 0;
-  for (int t0 = lo; t0 < r; t0 += kStageTok) {  // uniform trip count
-    const int n = min(kStageTok, r - t0);
+  for (int t0 = lo; t0 < r; t0 += NST) {  // uniform trip count
+    const int n = min(NST, r - t0);
     uint4 kv[IPT];
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
@@ -210,7 +211,7 @@ __attribute__((amdgpu_waves_per_eu(kEarlySummary<D, L, ROPE, QKV>() ? 8 : 1))) v
   constexpr int QL = NQ / L;
   constexpr int SPW = kWave / L;
   constexpr int SPG = SPW * (kFusedThreads / kWave);
-  __shared__ FusedSmem<D> sh;
+  __shared__ FusedSmem<D, ROPE ? 1 : kStageTok> sh;
   __shared__ RopeSmem<D, ROPE> rsh;
   const Table& t = a.t;
   const int bh = blockIdx.y;
@@ -236,7 +237,7 @@ __attribute__((amdgpu_waves_per_eu(kEarlySummary<D, L, ROPE, QKV>() ? 8 : 1))) v
     kn = a.k_new + (int64_t)bh * D;
     vn = a.v_new + (int64_t)bh * D;
   }
-  const bool want_append = QKV || a.k_new != nullptr;
+  const bool want_append = !ROPE && (QKV || a.k_new != nullptr);  // the RoPE variant only scores
   const int c = (int)gridDim.x - 1 - (int)blockIdx.x;  // chunks last to first
   const int s0 = c * SPG;
   // Issued together, before any of them is needed: the length, the pages of
@@ -318,7 +319,7 @@ __attribute__((amdgpu_waves_per_eu(kEarlySummary<D, L, ROPE, QKV>() ? 8 : 1))) v
     } else {
       e_new = a.e_new[bh];
     }
-    append_token<D>(a, sh, bh, raw, page, kn, vn, e_new);
+    append_token(a, sh, bh, raw, page, kn, vn, e_new);
     if constexpr (!early) load_summary();
   }
   __syncthreads();  // qbar, and the append's summary
