@@ -56,6 +56,7 @@ def parse(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the bandwidth probes (practical ceilings)")
     ap.add_argument("--unfused", action="store_true", help="time the six separate entry points")
     ap.add_argument("--offload", action="store_true",
                     help="host tier: pages in pinned host memory, resident slots in HBM, nosa_retrieve per step")
@@ -254,6 +255,59 @@ def bench_prefill(args, w) -> int:
     return 0
 
 
+def practical_ceilings(sess, flush, stream, reps: int = 10) -> dict:
+    """Live HBM read rates of the step's two access patterns with nothing
+    computed on the data (libnosa's bandwidth probes), timed as the step is:
+    after the same cache flush, between events on the step's stream, median
+    of `reps`.  The stream read covers the whole K page pool; the page gather
+    reads the K and V pages of the current selection (flat tables), with the
+    decode's grid.  The stream read runs one workgroup per compute unit (the
+    grid that streams fastest here) over the block-summary buffer -- the bytes
+    the scoring reads -- and over the whole K page pool."""
+    import numpy as np
+    import torch
+    from block_sparse_kv_score_amd import nosa
+
+    def timed(fn) -> float:
+        evs = []
+        for _ in range(reps):
+            flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs])) / 1e3
+
+    out = {}
+    pool = sess.k_pages
+    n_bytes = pool.numel() * pool.element_size()
+    sink = torch.zeros(torch.cuda.get_device_properties(pool.device).multi_processor_count, dtype=torch.int32,
+                       device=pool.device)
+    summ = sess.k_summary
+    s_bytes = summ.numel() * summ.element_size()
+    t = timed(lambda: nosa.nosa_probe_stream_read(summ, sink, stream))
+    out["stream_read_gbps"] = round(s_bytes / t / 1e9, 1)
+    out["stream_read_bytes"] = int(s_bytes)
+    t = timed(lambda: nosa.nosa_probe_stream_read(pool, sink, stream))
+    out["stream_read_large_gbps"] = round(n_bytes / t / 1e9, 1)
+    out["stream_read_large_bytes"] = int(n_bytes)
+    if sess.table is not None and sess.cap <= 256:
+        sel = sess.sel.long()
+        slot = torch.arange(sel.shape[-1], device=sel.device)
+        pages = torch.gather(sess.table.long(), 2, sel.clamp(min=0))
+        pages = torch.where(slot < sess.sel_count.long()[..., None], pages, torch.full_like(pages, -1))
+        pages = pages.reshape(-1, sel.shape[-1]).to(torch.int32).contiguous()
+        page_bytes = n_bytes // pool.shape[0]
+        g_bytes = int((pages >= 0).sum().item()) * 2 * page_bytes
+        g_sink = torch.zeros(pages.shape[0], dtype=torch.int32, device=pool.device)
+        t = timed(lambda: nosa.nosa_probe_page_gather(sess.k_pages, sess.v_pages, pages, g_sink, stream))
+        out["page_gather_gbps"] = round(g_bytes / t / 1e9, 1)
+        out["page_gather_bytes"] = g_bytes
+    return out
+
+
 def main(argv=None) -> int:
     args = parse(argv)
     if args.gpus != 1:
@@ -443,6 +497,18 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    ceiling = None
+    if not args.no_ceiling and not sess.offload:
+        print("[bench] practical ceilings (bandwidth probes)", file=sys.stderr, flush=True)
+        ceiling = practical_ceilings(sess, flush, stream)
+        score_name = "append_score" if "append_score" in kernels_us else ("score" if "score" in kernels_us else None)
+        if score_name is not None:
+            ceiling["scoring_launch_gbps"] = round(sb / (kernels_us[score_name] / 1e6) / 1e9, 1)
+            ceiling["scoring_frac_of_stream_read"] = round(ceiling["scoring_launch_gbps"] / ceiling["stream_read_gbps"], 4)
+        if "page_gather_gbps" in ceiling:
+            ceiling["decode_launch_gbps"] = round(dec_gbps, 1)
+            ceiling["decode_frac_of_page_gather"] = round(dec_gbps / ceiling["page_gather_gbps"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -481,6 +547,7 @@ def main(argv=None) -> int:
         "wall_ms_per_step_incl_flush": round(wall_cold / K * 1e3, 4),
         "kernels_us": {k: round(v, 2) for k, v in kernels_us.items()},
         "roofline": roofline,
+        "practical_ceiling": ceiling,
         "offload": offload,
         "cpu_baseline": cpu,
         "seed": args.seed,

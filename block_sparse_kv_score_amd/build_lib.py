@@ -37,7 +37,7 @@ COMMON = [
 ]
 
 SOURCES = ["nosa_api.cpp", "nosa_index.hip", "nosa_score.hip", "nosa_select.hip", "nosa_fused.hip",
-           "nosa_decode.hip", "nosa_offload.hip", "nosa_prefill.hip"]
+           "nosa_decode.hip", "nosa_offload.hip", "nosa_prefill.hip", "nosa_probe.hip"]
 
 
 def _compile(src: str) -> str:

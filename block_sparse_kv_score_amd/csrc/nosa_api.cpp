@@ -391,6 +391,24 @@ nosa_status nosa_combine(const nosa_dims* dims, int32_t num_splits, const float*
   return from_hip(nosa::launch_combine(*dims, num_splits, part_o, part_m, part_l, o, m, l, stream));
 }
 
+nosa_status nosa_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t n_workgroups,
+                                   hipStream_t stream) {
+  if (!src || !sink || !aligned16(src)) return NOSA_ERR_ARG;
+  if (bytes < 16 || bytes % 16 != 0 || n_workgroups < 1 || n_workgroups > 65536) return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_probe_stream_read(src, bytes, sink, n_workgroups, stream));
+}
+
+nosa_status nosa_probe_page_gather(const void* k_pool, const void* v_pool, int64_t page_bytes,
+                                   int64_t num_pages, const int32_t* pages, int32_t n_lists,
+                                   int32_t pages_per_list, uint32_t* sink, hipStream_t stream) {
+  if (!k_pool || !v_pool || !pages || !sink || !aligned16(k_pool) || !aligned16(v_pool)) return NOSA_ERR_ARG;
+  if (page_bytes != 8192 && page_bytes != 16384 && page_bytes != 32768) return NOSA_ERR_ARG;
+  if (num_pages < 1 || num_pages > ((int64_t)1 << 31) - 1) return NOSA_ERR_ARG;
+  if (n_lists < 1 || pages_per_list < 1 || pages_per_list > 256) return NOSA_ERR_ARG;
+  return from_hip(nosa::launch_probe_page_gather(k_pool, v_pool, page_bytes, num_pages, pages, n_lists,
+                                                 pages_per_list, sink, stream));
+}
+
 const char* nosa_status_string(nosa_status status) {
   switch (status) {
     case NOSA_OK: return "ok";

@@ -101,4 +101,11 @@ hipError_t launch_combine(const nosa_dims& d, int32_t num_splits, const float* p
                           const float* part_m, const float* part_l, float* o, float* m, float* l,
                           hipStream_t stream);
 
+hipError_t launch_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t n_workgroups,
+                                    hipStream_t stream);
+
+hipError_t launch_probe_page_gather(const void* k_pool, const void* v_pool, int64_t page_bytes, int64_t num_pages,
+                                    const int32_t* pages, int32_t n_lists, int32_t pages_per_list, uint32_t* sink,
+                                    hipStream_t stream);
+
 }  // namespace nosa

@@ -45,6 +45,8 @@ ENTRY_POINTS = [
     "nosa_retrieve",
     "nosa_retrieve_buffered",
     "nosa_host_device_pointer",
+    "nosa_probe_stream_read",
+    "nosa_probe_page_gather",
     "nosa_status_string",
 ]
 
@@ -118,6 +120,8 @@ _SIGNATURES = {
     "nosa_retrieve": [_DIMS, _KV, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P],
     "nosa_retrieve_buffered": [_DIMS, _KV, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P],
     "nosa_host_device_pointer": [_P, ctypes.POINTER(ctypes.c_void_p)],
+    "nosa_probe_stream_read": [_P, ctypes.c_int64, _P, _I32, _P],
+    "nosa_probe_page_gather": [_P, _P, ctypes.c_int64, ctypes.c_int64, _P, _I32, _I32, _P, _P],
 }
 
 
@@ -435,3 +439,32 @@ def nosa_combine(dims, num_splits, part_o, part_m, part_l, o, m, l, stream=None)
           _dev(part_o, "part_o", (torch.float32,)), _dev(part_m, "part_m", (torch.float32,)),
           _dev(part_l, "part_l", (torch.float32,)), _dev(o, "o", (torch.float32,)),
           _dev(m, "m", (torch.float32,)), _dev(l, "l", (torch.float32,)), _stream(stream))
+
+
+def nosa_probe_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Read all of `src` (any dtype, contiguous, a multiple of 16 bytes) with
+    the streaming-read probe; sink int32 [n_workgroups] receives the xor of
+    each workgroup's words (the grid is sink's length)."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    _call("nosa_probe_stream_read", ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
+          _dev(sink, "sink", (torch.int32,)), int(sink.numel()), _stream(stream))
+
+
+def nosa_probe_page_gather(k_pool: torch.Tensor, v_pool: torch.Tensor, pages: torch.Tensor, sink: torch.Tensor,
+                           stream=None):
+    """Read the K and V pages listed in pages int32 [n_lists][pages_per_list]
+    from the pools ([num_pages][...], contiguous, same shape) with the
+    page-gather probe; sink int32 [n_lists]."""
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must have the same shape")
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous GPU tensor")
+    if pages.dim() != 2:
+        raise ValueError("pages must be [n_lists][pages_per_list]")
+    num_pages = int(k_pool.shape[0])
+    page_bytes = k_pool.numel() * k_pool.element_size() // num_pages
+    _call("nosa_probe_page_gather", ctypes.c_void_p(k_pool.data_ptr()), ctypes.c_void_p(v_pool.data_ptr()),
+          page_bytes, num_pages, _dev(pages, "pages", (torch.int32,)), int(pages.shape[0]), int(pages.shape[1]),
+          _dev(sink, "sink", (torch.int32,)), _stream(stream))

@@ -459,6 +459,30 @@ nosa_status nosa_combine(const nosa_dims* dims, int32_t num_splits,
                          const float* part_o, const float* part_m, const float* part_l,
                          float* o, float* m, float* l, hipStream_t stream);
 
+/* Bandwidth probes (measurement tools, not part of the step): the HBM read
+ * rate this GPU gives the step's two access patterns with no arithmetic on
+ * the data, to set the step's kernels against.  Each workgroup writes the
+ * xor of every 32-bit word it read to sink[workgroup] (so the xor of the
+ * sink equals the xor of the bytes read, a check that all of them were).
+ *
+ * nosa_probe_stream_read: `bytes` (a multiple of 16, src 16-byte aligned)
+ *   read once, contiguously, with 16-byte non-temporal loads (the pattern
+ *   of the block-summary stream); n_workgroups in [1, 65536] workgroups of
+ *   256 threads; sink uint32 [n_workgroups].
+ * nosa_probe_page_gather: the K page and the V page of every page id in
+ *   pages int32 [n_lists][pages_per_list] read whole from k_pool / v_pool
+ *   (page_bytes 8192, 16384 or 32768; pages [0, num_pages); ids outside are
+ *   skipped): the decode's selected-page gather, one workgroup of four waves
+ *   per list (a (b, h) pair), wave w taking pages w, w + 4, ..., one K page
+ *   and one V page in flight per wave.  pages_per_list in [1, 256];
+ *   sink uint32 [n_lists].
+ * NOSA_ERR_ARG on null or misaligned pointers and sizes out of range.     */
+nosa_status nosa_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t n_workgroups,
+                                   hipStream_t stream);
+nosa_status nosa_probe_page_gather(const void* k_pool, const void* v_pool, int64_t page_bytes,
+                                   int64_t num_pages, const int32_t* pages, int32_t n_lists,
+                                   int32_t pages_per_list, uint32_t* sink, hipStream_t stream);
+
 /* Static description of a status code (never null). Host only.           */
 const char* nosa_status_string(nosa_status status);
 

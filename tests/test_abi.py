@@ -206,3 +206,24 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4)
     with pytest.raises(ValueError):
         nosa.nosa_combine(d, 4, x, x, x, x, x, x)
+
+
+def test_probe_host_checks():
+    """The bandwidth probes refuse bad arguments before any launch."""
+    from block_sparse_kv_score_amd import nosa
+    L = nosa.lib()
+    P = ctypes.c_void_p
+    fake, odd = P(256), P(264)  # never dereferenced
+    E = nosa.NOSA_ERR_ARG
+    assert L.nosa_probe_stream_read(None, 1024, fake, 8, None) == E
+    assert L.nosa_probe_stream_read(odd, 1024, fake, 8, None) == E      # src not 16-byte aligned
+    assert L.nosa_probe_stream_read(fake, 1000, fake, 8, None) == E     # not a multiple of 16
+    assert L.nosa_probe_stream_read(fake, 1024, fake, 0, None) == E
+    assert L.nosa_probe_stream_read(fake, 1024, fake, 65537, None) == E
+    assert L.nosa_probe_stream_read(fake, 1024, None, 8, None) == E
+    assert L.nosa_probe_page_gather(fake, fake, 12288, 10, fake, 4, 16, fake, None) == E  # page size
+    assert L.nosa_probe_page_gather(fake, odd, 16384, 10, fake, 4, 16, fake, None) == E
+    assert L.nosa_probe_page_gather(fake, fake, 16384, 0, fake, 4, 16, fake, None) == E
+    assert L.nosa_probe_page_gather(fake, fake, 16384, 10, fake, 0, 16, fake, None) == E
+    assert L.nosa_probe_page_gather(fake, fake, 16384, 10, fake, 4, 257, fake, None) == E
+    assert L.nosa_probe_page_gather(fake, fake, 16384, 10, None, 4, 16, fake, None) == E
