@@ -57,6 +57,8 @@ def parse(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the bandwidth probes (practical ceilings)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the cold steps as HIP graph replays (the plain HBM-tier step; other passes eager)")
     ap.add_argument("--unfused", action="store_true", help="time the six separate entry points")
     ap.add_argument("--offload", action="store_true",
                     help="host tier: pages in pinned host memory, resident slots in HBM, nosa_retrieve per step")
@@ -351,16 +353,27 @@ def main(argv=None) -> int:
         flush()
         sess.step(next_t())
     torch.cuda.synchronize()
+    if args.graph:
+        if W < 2:
+            raise SystemExit("--graph needs at least two warm-up steps")
+        sess.capture_graphs()
+        torch.cuda.synchronize()
 
-    # pass 1: cold steps, events at the ends only (the headline)
+    # pass 1: cold steps, events at the ends only (the headline); with
+    # --graph each step is one graph replay, its inputs staged before the flush
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     bytes_kv, bytes_sum = [], []
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for k in range(K):
+        if args.graph:
+            sess.graph_step(next_t(), replay=False)
         flush()
         ev[k][0].record(stream)
-        t = sess.step(next_t())
+        if args.graph:
+            sess.next_graph.replay()
+        else:
+            sess.step(next_t())
         ev[k][1].record(stream)
     torch.cuda.synchronize()
     wall_cold = time.perf_counter() - wall0
@@ -535,7 +548,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
                    "context": w.T0, "block": w.bs, "sub_block": w.ss, "k_e": w.k_e, "k_q": w.k_q,
-                   "splits": sess.P, "table": w.table, "fused": fused, "offload": sess.offload,
+                   "splits": sess.P, "table": w.table, "fused": fused, "graph": bool(args.graph), "offload": sess.offload,
                    "buffer_slots": sess.buffer_slots,
                    "parallelism": "single GPU"},
         "hbm_gbps": round(gbps, 1),

@@ -354,6 +354,74 @@ class DecodeSession:
         nosa.nosa_combine(self.dims, self.P, self.part_o, self.part_m, self.part_l, self.o, self.m, self.l,
                           self.stream)
 
+    # ------------------------------------------------------------------
+    # the step as HIP graphs
+    _GRAPH_INPUTS = ("q_all", "k_new", "v_new", "e_new")
+
+    def _state(self) -> tuple:
+        return (self.seq_lens, self.evicted, self.sel, self.sel_count, self.prev, self.prev_count)
+
+    def _set_state(self, st: tuple):
+        self.seq_lens, self.evicted, self.sel, self.sel_count, self.prev, self.prev_count = st
+
+    def capture_graphs(self):
+        """Capture the step as two HIP graphs, one for each parity of the
+        step index: the ping-pong buffers (lengths, eviction bitmaps,
+        selections) repeat every two steps.  The graphs read the step's
+        inputs (query, new key / value / logit) from static buffers that
+        graph_step(t) refills before each replay.  The plain HBM-tier step
+        only (no host tier, softmax mass, ALiBi or QKV rows), on the current
+        stream, after at least one eager step.  Its launches allocate nothing
+        and record no memset."""
+        if self.offload or self.mass_on or self.alibi_on or self.qkv_on or self.stream is not None:
+            raise ValueError("graphs cover the plain HBM-tier step on the current stream")
+        if self.step_index < 1:
+            raise ValueError("run one eager step before capturing")
+        names = [n for n in self._GRAPH_INPUTS if hasattr(self, n) and (n == "q_all" or self.w.append)]
+        self._g_real = {n: getattr(self, n) for n in names}
+        self._g_static = {n: torch.empty_like(t) for n, t in self._g_real.items()}
+        start, t0 = self._state(), self.step_index
+        self.graphs = []
+        self._g_calls = 0
+        # workloads without appends repeat step 1 (their eviction bitmaps
+        # still alternate); the others advance one token per step
+        for t in ((t0 + 1, t0 + 2) if self.w.append else (1, 1)):
+            for n in names:
+                setattr(self, n, self._g_static[n])
+            g = torch.cuda.CUDAGraph()
+            try:
+                with torch.cuda.graph(g):
+                    self.step(t)
+            finally:
+                for n in names:
+                    setattr(self, n, self._g_real[n])
+            self.graphs.append((t, g, self._state()))
+        if any(a is not b for a, b in zip(self._state(), start)):
+            raise RuntimeError("the step's buffers do not repeat every two steps")
+        self._set_state(start)
+        self.step_index = t0
+
+    def graph_step(self, t: int | None = None, replay: bool = True):
+        """The next decode step (t: its index, the next one; workloads
+        without appends repeat step 1) by replaying the captured graph whose
+        buffers it uses: the step's inputs are copied into the graph's static
+        buffers (stream order), then the graph runs.  replay=False stages the
+        inputs and advances the state only; the caller then replays
+        self.next_graph before any other step."""
+        t = (self.step_index + 1 if self.w.append else 1) if t is None else t
+        if self.w.append and t != self.step_index + 1:
+            raise ValueError("graph steps run in order")
+        gt, g, after = self.graphs[self._g_calls % 2]
+        for n, real in self._g_real.items():
+            self._g_static[n][gt - 1].copy_(real[t - 1])
+        self.next_graph = g
+        if replay:
+            g.replay()
+        self._g_calls += 1
+        self._set_state(after)
+        self.step_index = t
+        return t
+
     def use_buffers(self, t: int):
         """Point sel / prev at the buffers of step t."""
         if self.w.select_all:
