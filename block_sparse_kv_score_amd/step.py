@@ -90,6 +90,7 @@ class DecodeSession:
         self.dev = torch.device(device)
         self.stream = stream
         self.step_index = 0
+        self.n_steps = 0  # steps run so far, eager or replayed (the graphs alternate with it)
         B, Hq, Hkv, D, bs, ss, MB = w.B, w.Hq, w.Hkv, w.D, w.bs, w.ss, w.max_blocks
         self.dims = nosa.make_dims(B, Hq, Hkv, D, bs, ss, MB)
         self.cap = MB if w.select_all else min(w.k, MB)
@@ -380,9 +381,9 @@ class DecodeSession:
         names = [n for n in self._GRAPH_INPUTS if hasattr(self, n) and (n == "q_all" or self.w.append)]
         self._g_real = {n: getattr(self, n) for n in names}
         self._g_static = {n: torch.empty_like(t) for n, t in self._g_real.items()}
-        start, t0 = self._state(), self.step_index
+        start, t0, n0 = self._state(), self.step_index, self.n_steps
         self.graphs = []
-        self._g_calls = 0
+        self._g_n0 = n0
         # workloads without appends repeat step 1 (their eviction bitmaps
         # still alternate); the others advance one token per step
         for t in ((t0 + 1, t0 + 2) if self.w.append else (1, 1)):
@@ -399,7 +400,7 @@ class DecodeSession:
         if any(a is not b for a, b in zip(self._state(), start)):
             raise RuntimeError("the step's buffers do not repeat every two steps")
         self._set_state(start)
-        self.step_index = t0
+        self.step_index, self.n_steps = t0, n0
 
     def graph_step(self, t: int | None = None, replay: bool = True):
         """The next decode step (t: its index, the next one; workloads
@@ -407,17 +408,19 @@ class DecodeSession:
         buffers it uses: the step's inputs are copied into the graph's static
         buffers (stream order), then the graph runs.  replay=False stages the
         inputs and advances the state only; the caller then replays
-        self.next_graph before any other step."""
+        self.next_graph before any other step.  Eager steps may come in
+        between: the graph is chosen by the number of steps run since the
+        capture."""
         t = (self.step_index + 1 if self.w.append else 1) if t is None else t
         if self.w.append and t != self.step_index + 1:
             raise ValueError("graph steps run in order")
-        gt, g, after = self.graphs[self._g_calls % 2]
+        gt, g, after = self.graphs[(self.n_steps - self._g_n0) % 2]
         for n, real in self._g_real.items():
             self._g_static[n][gt - 1].copy_(real[t - 1])
         self.next_graph = g
         if replay:
             g.replay()
-        self._g_calls += 1
+        self.n_steps += 1
         self._set_state(after)
         self.step_index = t
         return t
@@ -467,4 +470,5 @@ class DecodeSession:
             self.decode(t)
             self.combine()
         self.step_index = t
+        self.n_steps += 1
         return t
