@@ -9,21 +9,21 @@
 
 namespace nosa {
 
-// One workgroup per (b, h).
-template <int R, bool SWAP>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(int Hkv, int bs, int max_blocks,
+// One workgroup of NT threads per (b, h).
+template <int R, bool SWAP, int NT>
+__global__ __launch_bounds__(NT) void select_kernel(int Hkv, int bs, int max_blocks,
                                                             const float* __restrict__ score_q,
                                                             const float* __restrict__ score_e,
                                                             const int32_t* __restrict__ seq_lens, int k_e, int k_q,
                                                             uint32_t* __restrict__ evicted,
                                                             int32_t* __restrict__ sel, int sel_cap,
                                                             int32_t* __restrict__ sel_count, const SwapArgs sw) {
-  __shared__ SelShared sh;
+  __shared__ SelSharedT<NT> sh;
   const int bh = blockIdx.x;
   const int T = min(max(seq_lens[bh / Hkv], 0), max_blocks * bs);
   uint32_t* ev = evicted + (int64_t)bh * ((max_blocks + 31) / 32);
-  select_pair<R, SWAP>(sh, bh, T, bs, max_blocks, score_q, score_e, k_e, k_q, ev, ev,
-                           sel + (int64_t)bh * sel_cap, sel_cap, sel_count + bh, sw);
+  select_pair<R, SWAP, NoHook, NoHook, NT>(sh, bh, T, bs, max_blocks, score_q, score_e, k_e, k_q, ev, ev,
+                                           sel + (int64_t)bh * sel_cap, sel_cap, sel_count + bh, sw);
 }
 
 // One wave per (b, h); membership through an LDS bitmap, order-preserving
@@ -83,24 +83,29 @@ static hipError_t launch_select_any(const nosa_dims& d, const float* score_q, co
   const dim3 grid(d.batch * d.n_kv_heads);
   const SwapArgs none = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   const SwapArgs args = sw ? *sw : none;
-#define NOSA_SELECT(RR)                                                                                        \
+#define NOSA_SELECT(RR, NT)                                                                                    \
   do {                                                                                                         \
     if (sw)                                                                                                    \
-      select_kernel<RR, true><<<grid, kSelThreads, 0, stream>>>(d.n_kv_heads, d.block_size, d.max_blocks,     \
-                                                                score_q, score_e, seq_lens, k_e, k_q, evicted, \
-                                                                sel, sel_cap, sel_count, args);                \
+      select_kernel<RR, true, NT><<<grid, NT, 0, stream>>>(d.n_kv_heads, d.block_size, d.max_blocks, score_q,  \
+                                                           score_e, seq_lens, k_e, k_q, evicted, sel, sel_cap, \
+                                                           sel_count, args);                                   \
     else                                                                                                       \
-      select_kernel<RR, false><<<grid, kSelThreads, 0, stream>>>(d.n_kv_heads, d.block_size, d.max_blocks,    \
-                                                                 score_q, score_e, seq_lens, k_e, k_q,         \
-                                                                 evicted, sel, sel_cap, sel_count, args);      \
+      select_kernel<RR, false, NT><<<grid, NT, 0, stream>>>(d.n_kv_heads, d.block_size, d.max_blocks,          \
+                                                            score_q, score_e, seq_lens, k_e, k_q, evicted, sel, \
+                                                            sel_cap, sel_count, args);                         \
   } while (0)
-  const int R = (d.max_blocks + kSelThreads - 1) / kSelThreads;  // elements per thread
-  if (R <= 2) NOSA_SELECT(2);
-  else if (R <= 4) NOSA_SELECT(4);
-  else if (R <= 8) NOSA_SELECT(8);
-  else if (R <= 12) NOSA_SELECT(12);
-  else if (R <= 16) NOSA_SELECT(16);
-  else NOSA_SELECT(32);
+  // Up to 2,048 blocks: four waves, R keys per thread.  Beyond, sixteen
+  // waves: the selection's time follows the keys each thread walks (every
+  // pass of the radix select loops over them), so a wider workgroup with
+  // fewer keys per thread is faster there despite its costlier barriers.
+  const int R = (d.max_blocks + kSelThreads - 1) / kSelThreads;  // keys per thread of four waves
+  const int RW = (d.max_blocks + 1023) / 1024;                   // keys per thread of sixteen waves
+  if (R <= 2) NOSA_SELECT(2, 256);
+  else if (R <= 4) NOSA_SELECT(4, 256);
+  else if (R <= 8) NOSA_SELECT(8, 256);
+  else if (RW <= 3) NOSA_SELECT(3, 1024);
+  else if (RW <= 4) NOSA_SELECT(4, 1024);
+  else NOSA_SELECT(8, 1024);
 #undef NOSA_SELECT
   return hipGetLastError();
 }

@@ -15,8 +15,9 @@
 // part only, ties go to the lower block index, and a newly created block
 // starts as an eviction candidate.
 //
-// NT = 256 threads per (b, h); each keeps its blocks' keys in registers
-// (block i = r * NT + thread).  Top-k is a most-significant-digit radix
+// NT threads per (b, h) (256: the four-wave form; 1024 for the widest
+// tables); each keeps its blocks' keys in registers (block i = r * NT +
+// thread).  Top-k is a most-significant-digit radix
 // select over order-preserving 32-bit keys of the fp32 scores (see
 // radix_top_k); exact key ties go to the lowest index.  Outputs are
 // compacted in index order with wave ballots, so they come out ascending
@@ -30,34 +31,39 @@
 namespace nosa {
 
 constexpr int kSelThreads = 256;                // the four-wave form
-constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kMaxBlocks = 8192;
+constexpr int kDigitWaves = 256 / kWave;         // waves that scan the 256 digit bins
 
 // Per-workgroup scratch in LDS; small slots are double-buffered by phase so
 // one barrier per exchange suffices.
-struct SelShared {
-  uint32_t hist[kSelWaves][256];  // per-wave digit histograms
-  int32_t tot[2][kSelWaves];
+template <int NT>
+struct SelSharedT {
+  static constexpr int NW = NT / kWave;
+  uint32_t hist[NW][256];  // per-wave digit histograms
+  int32_t tot[2][NW];
   int32_t bc[2][4];
-  uint32_t mm[2][kSelWaves][2];
-  int32_t pos[32][kSelWaves];
+  uint32_t mm[2][NW][2];
+  int32_t pos[32][NW];
   // fused swap lists: membership bitmaps and per-wave counts
   uint32_t pick_bm[kMaxBlocks / 32];
   uint32_t prev_bm[kMaxBlocks / 32];
-  int32_t pos_load[32][kSelWaves];
-  int32_t pos_evict[32][kSelWaves];
+  int32_t pos_load[32][NW];
+  int32_t pos_evict[32][NW];
 };
+using SelShared = SelSharedT<kSelThreads>;
 
 // Workgroup sum of one int per wave (the same value in every lane); one
 // barrier.
-__device__ __forceinline__ int block_sum(int v, int& phase, SelShared& sh) {
+template <int NT>
+__device__ __forceinline__ int block_sum(int v, int& phase, SelSharedT<NT>& sh) {
+  constexpr int NW = NT / kWave;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int ph = phase++ & 1;
   if (lane == 0) sh.tot[ph][w] = v;
   __syncthreads();
   int t = 0;
 #pragma unroll
-  for (int k = 0; k < kSelWaves; ++k) t += sh.tot[ph][k];
+  for (int k = 0; k < NW; ++k) t += sh.tot[ph][k];
   return t;
 }
 
@@ -72,9 +78,10 @@ __device__ __forceinline__ int block_sum(int v, int& phase, SelShared& sh) {
 // Digits are counted in per-wave LDS histograms; a workgroup scan over the
 // 256 bins finds the bin holding the k-th key; the select stops as soon as
 // that bin is taken whole.
-template <int R>
+template <int R, int NT>
 __device__ void radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k, uint32_t& out, int& phase,
-                            SelShared& sh) {
+                            SelSharedT<NT>& sh) {
+  constexpr int NW = NT / kWave;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   // range of the candidate keys
   uint32_t kmin = 0xffffffffu, kmax = 0u;
@@ -94,7 +101,7 @@ __device__ void radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k, uint
     }
     __syncthreads();
 #pragma unroll
-    for (int ww = 0; ww < kSelWaves; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       kmin = min(kmin, sh.mm[ph][ww][0]);
       kmax = max(kmax, sh.mm[ph][ww][1]);
     }
@@ -116,17 +123,21 @@ __device__ void radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k, uint
       if (((cand >> r) & 1u) && (key[r] & pmask) == prefix) atomicAdd(&sh.hist[w][(key[r] >> lo) & dmask], 1u);
     __syncthreads();
     const int ph = phase++ & 1;
-    // thread t owns digit 255 - t: inclusive scan gives the count of keys
-    // with a digit >= 255 - t
-    const int dg = 255 - (int)threadIdx.x;
+    // thread t < 256 owns digit 255 - t: inclusive scan gives the count of
+    // keys with a digit >= 255 - t (the other threads of a wider workgroup
+    // count nothing)
+    const bool owner = NT == 256 || (int)threadIdx.x < 256;
+    const int dg = owner ? 255 - (int)threadIdx.x : 0;
     int c = 0;
+    if (owner) {
 #pragma unroll
-    for (int ww = 0; ww < kSelWaves; ++ww) c += (int)sh.hist[ww][dg];
+      for (int ww = 0; ww < NW; ++ww) c += (int)sh.hist[ww][dg];
+    }
     int cum = wave_scan_incl(c);
-    if (lane == kWave - 1) sh.tot[ph][w] = cum;
+    if (lane == kWave - 1 && w < kDigitWaves) sh.tot[ph][w] = cum;
     __syncthreads();
 #pragma unroll
-    for (int ww = 0; ww < kSelWaves; ++ww) cum += ww < w ? sh.tot[ph][ww] : 0;
+    for (int ww = 0; ww < kDigitWaves; ++ww) cum += ww < w ? sh.tot[ph][ww] : 0;
     if (c > 0 && cum >= rem && cum - c < rem) {
       sh.bc[ph][0] = dg;
       sh.bc[ph][1] = cum - c;
@@ -161,7 +172,7 @@ __device__ void radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k, uint
   for (int r = 0; r < R; ++r) {
     int rank = before + lanes_below(eqm[r]);
 #pragma unroll
-    for (int ww = 0; ww < kSelWaves; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const int c = sh.pos[r][ww];
       rank += ww < w ? c : 0;
       before += c;
@@ -201,14 +212,14 @@ struct NoHook {
   __device__ void operator()() const {}
 };
 
-template <int R, bool SWAP, class H1 = NoHook, class H2 = NoHook>
-__device__ int select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks,
+template <int R, bool SWAP, class H1 = NoHook, class H2 = NoHook, int NT = kSelThreads>
+__device__ int select_pair(SelSharedT<NT>& sh, int bh, int T, int bs, int max_blocks,
                            const float* __restrict__ score_q, const float* __restrict__ score_e, int k_e,
                            int k_q, const uint32_t* ev_in, uint32_t* ev_out, int32_t* sel_row, int sel_cap,
                            int32_t* sel_count_slot, const SwapArgs sw, H1 after_loads = H1(),
                            H2 after_eviction = H2()) {
-  constexpr int NT = kSelThreads;
-  static_assert(R <= 32, "selection shape");
+  constexpr int NW = NT / kWave;
+  static_assert(R <= 32 && NT % 256 == 0, "selection shape");
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int nb = (T + bs - 1) / bs;
   const float* se = score_e + (int64_t)bh * max_blocks;
@@ -267,7 +278,7 @@ __device__ int select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks,
   const int n_e = min(k_e, n_cand);
   uint32_t in_e = 0;
   if (n_e == n_cand) in_e = cand_e;
-  else if (n_e > 0) radix_top_k<R>(ke, cand_e, n_e, in_e, phase, sh);
+  else if (n_e > 0) radix_top_k<R, NT>(ke, cand_e, n_e, in_e, phase, sh);
   evm |= cand_e & ~in_e;  // every candidate left out is evicted for good
   after_eviction();
 
@@ -277,7 +288,7 @@ __device__ int select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks,
   const int n_q = min(k_q, rest);
   uint32_t in_q = 0;
   if (n_q == rest) in_q = cand_q;
-  else if (n_q > 0) radix_top_k<R>(kq, cand_q, n_q, in_q, phase, sh);
+  else if (n_q > 0) radix_top_k<R, NT>(kq, cand_q, n_q, in_q, phase, sh);
 
   // --- outputs: ascending union via ballots, eviction bitmap words ------
   const uint32_t pick = in_e | in_q;
@@ -311,7 +322,7 @@ __device__ int select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks,
   for (int r = 0; r < R; ++r) {
     int pos = before + lanes_below(pm[r]);
 #pragma unroll
-    for (int ww = 0; ww < kSelWaves; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const int c = sh.pos[r][ww];
       pos += ww < w ? c : 0;
       before += c;
@@ -364,7 +375,7 @@ __device__ int select_pair(SelShared& sh, int bh, int T, int bs, int max_blocks,
     for (int r = 0; r < R; ++r) {
       int pl_ = bl + lanes_below(lm[r]), pe = be + lanes_below(em[r]);
 #pragma unroll
-      for (int ww = 0; ww < kSelWaves; ++ww) {
+      for (int ww = 0; ww < NW; ++ww) {
         const int cl = sh.pos_load[r][ww], ce = sh.pos_evict[r][ww];
         pl_ += ww < w ? cl : 0;
         pe += ww < w ? ce : 0;

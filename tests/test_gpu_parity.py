@@ -370,6 +370,16 @@ def test_maximum_capacity():
     run_trajectory(w, seed=24, steps=3, splits=3)
 
 
+@pytest.mark.parametrize("blocks", [2049, 3500])
+def test_wide_selection_workgroups(blocks):
+    # above 2048 blocks of capacity the selection runs on sixteen waves
+    # (3 and 4 keys per thread here); ties in the eviction logits are likely
+    # at this many blocks, so the budgets are uneven
+    w = WORKLOADS["tiny_nosa"].scaled(B=2, Hq=4, Hkv=2, T0=blocks * 64 - 256 - 30, k_e=40, k_q=9)
+    assert w.max_blocks == blocks
+    run_trajectory(w, seed=26, steps=3, splits=2)
+
+
 def test_append_past_capacity_flags_and_keeps_length():
     from block_sparse_kv_score_amd import nosa
     w = WORKLOADS["tiny_nosa"].scaled(B=2, Hq=4, Hkv=2, T0=100)
