@@ -349,6 +349,11 @@ def test_exact_ties_lowest_index_wins(n_distinct):
     w = WORKLOADS["llama3_8b_32k"].scaled(B=1, Hq=8, Hkv=2, T0=4096 + 7)
     log = run_trajectory(w, seed=21, steps=3, inp=tie_inputs(w, 21, n_distinct))
     assert not log, log
+    # the sixteen-wave selection (above 2048 blocks of capacity)
+    w = WORKLOADS["tiny_nosa"].scaled(B=1, Hq=4, Hkv=2, T0=2600 * 64 - 256 - 5, k_e=20, k_q=12)
+    assert w.max_blocks > 2048
+    log = run_trajectory(w, seed=27, steps=2, inp=tie_inputs(w, 27, n_distinct))
+    assert not log, log
 
 
 def test_empty_context():
