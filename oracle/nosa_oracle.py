@@ -77,6 +77,8 @@ __all__ = [
     "alibi_bias",
     "rope_inv_freq",
     "rope_rotate",
+    "materialise",
+    "attend_blocks",
     "decode_step_bh",
     "prefill_attention_bh",
 ]
@@ -457,6 +459,49 @@ def rope_rotate(x: np.ndarray, pos, base: float) -> np.ndarray:
 # One decode step for one (b, h) pair
 # ---------------------------------------------------------------------------
 
+def materialise(q_group, K, T, bs, rope=None):
+    """Queries and keys as attention sees them.  Without deferred RoPE they
+    are the inputs (the first T keys).  With it (rope = dict(q_pos=n,
+    block_start=(nb,) absolute start of the document holding each block,
+    base=...)) every key is materialised as Rot(doc start) k_stored and the
+    queries as Rot(n) q [LAZY, mathematical equivalence; READING: stored
+    keys carry their in-document rotation].  Returns (q, K), float64."""
+    if rope is None:
+        return q_group, K[:T]
+    nb = num_blocks(T, bs)
+    Kt = np.empty((T, K.shape[1]))
+    starts = np.asarray(rope["block_start"], dtype=np.float64)
+    for i in range(nb):
+        r = block_token_range(i, T, bs)
+        Kt[r.start:r.stop] = rope_rotate(K[r.start:r.stop], starts[i], rope["base"])
+    return rope_rotate(q_group, rope["q_pos"], rope["base"]), Kt
+
+
+def attend_blocks(qt, Kt, V, T, bs, blocks, num_splits, scale, alibi=None):
+    """Attention of the group's query rows over the tokens of the given
+    blocks, split into contiguous chunks of the block list and unsplit
+    [NOVITA, attention modifications]: per-split (o, m, l) partials, the
+    merged (O, m, l) over every listed token, and, without ALiBi, each
+    block's softmax mass per query row.  qt, Kt as materialise() returns
+    them; alibi: None or the group's (G,) slopes, biasing by the distance
+    from the query at position T - 1."""
+    def bias(toks):
+        return None if alibi is None else alibi_bias(alibi, T - 1, toks)
+
+    parts = []
+    for chunk in split_chunks(list(blocks), num_splits):
+        toks = tokens_of_blocks(chunk, T, bs)
+        parts.append(attend(qt, Kt[toks], V[toks], scale, bias(toks)))
+    out = {"part_o": np.stack([p[0] for p in parts], axis=1),   # (G, P, D)
+           "part_m": np.stack([p[1] for p in parts], axis=1),   # (G, P)
+           "part_l": np.stack([p[2] for p in parts], axis=1)}
+    toks = tokens_of_blocks(blocks, T, bs)
+    out["O"], out["m"], out["l"] = attend(qt, Kt[toks], V[toks], scale, bias(toks))
+    if alibi is None:
+        out["mass"] = softmax_block_mass(qt, Kt, list(blocks), T, bs, scale)
+    return out
+
+
 def decode_step_bh(q_group, K, V, e, T, bs, ss, k_e, k_q, evicted, prev_sel,
                    num_splits, scale, select_all=False, rope=None, alibi=None):
     """The whole step for one (sequence, KV head), from already-appended
@@ -484,15 +529,7 @@ def decode_step_bh(q_group, K, V, e, T, bs, ss, k_e, k_q, evicted, prev_sel,
     """
     nb = num_blocks(T, bs)
     out: dict = {"nb": nb}
-    if rope is not None:
-        Kt = np.empty((T, K.shape[1]))
-        starts = np.asarray(rope["block_start"], dtype=np.float64)
-        for i in range(nb):
-            r = block_token_range(i, T, bs)
-            Kt[r.start:r.stop] = rope_rotate(K[r.start:r.stop], starts[i], rope["base"])
-        qt = rope_rotate(q_group, rope["q_pos"], rope["base"])
-    else:
-        Kt, qt = K[:T], q_group
+    qt, Kt = materialise(q_group, K, T, bs, rope)
     if select_all:
         gamma_e, gamma_q, gamma = [], list(range(nb)), list(range(nb))
         evicted_after = set(evicted)
@@ -507,22 +544,7 @@ def decode_step_bh(q_group, K, V, e, T, bs, ss, k_e, k_q, evicted, prev_sel,
     out.update(gamma_e=gamma_e, gamma_q=gamma_q, sel=gamma, evicted=evicted_after,
                load=load, evict=drop)
 
-    def bias(toks):
-        return None if alibi is None else alibi_bias(alibi, T - 1, toks)
-
-    parts = []
-    for chunk in split_chunks(gamma, num_splits):
-        toks = tokens_of_blocks(chunk, T, bs)
-        parts.append(attend(qt, Kt[toks], V[toks], scale, bias(toks)))
-    G, D = qt.shape
-    part_o = np.stack([p[0] for p in parts], axis=1)   # (G, P, D)
-    part_m = np.stack([p[1] for p in parts], axis=1)   # (G, P)
-    part_l = np.stack([p[2] for p in parts], axis=1)
-    toks = tokens_of_blocks(gamma, T, bs)
-    O, m, l = attend(qt, Kt[toks], V[toks], scale, bias(toks))
-    out.update(part_o=part_o, part_m=part_m, part_l=part_l, O=O, m=m, l=l)
-    if alibi is None:
-        out["mass"] = softmax_block_mass(qt, Kt, gamma, T, bs, scale)
+    out.update(attend_blocks(qt, Kt, V, T, bs, gamma, num_splits, scale, alibi))
     return out
 
 

@@ -678,11 +678,39 @@ def check_bf16_decode(O):
     assert O.bf16_to_f64(bits).tolist() == want
 
 
+def check_attend_blocks(O, seed=15):
+    """Attention over an arbitrary block list (not a selection: any order,
+    the ragged tail block included, more splits than blocks) is SDPA over
+    those blocks' tokens, each split partial is SDPA over its chunk's
+    tokens (empty chunks exactly (0, -inf, 0)), and each query row's block
+    masses sum to 1."""
+    rng = np.random.default_rng(seed)
+    G, D, T, bs = 4, 16, 181, 16
+    q, K, V = rng.standard_normal((G, D)), rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    blocks = [11, 3, 0, 7]  # block 11 holds the 5 tokens 176..180
+    P = 6
+    r = O.attend_blocks(q, K, V, T, bs, blocks, P, 0.3)
+    toks = np.concatenate([np.arange(i * bs, min(i * bs + bs, T)) for i in blocks])
+    assert len(toks) == 3 * bs + 5
+    assert np.abs(r["O"] - _sdpa(q, K[toks], V[toks], 0.3)).max() <= 1e-12
+    ref_lse = torch.logsumexp(torch.tensor(q @ K[toks].T * 0.3), dim=1).numpy()
+    assert np.abs(r["m"] + np.log(r["l"]) - ref_lse).max() <= 1e-12
+    for p_, i in enumerate(blocks):  # one block per chunk, then empty chunks
+        t_ = np.arange(i * bs, min(i * bs + bs, T))
+        assert np.abs(r["part_o"][:, p_] - _sdpa(q, K[t_], V[t_], 0.3)).max() <= 1e-12
+    assert np.all(r["part_o"][:, len(blocks):] == 0) and np.all(np.isneginf(r["part_m"][:, len(blocks):]))
+    assert np.all(r["part_l"][:, len(blocks):] == 0)
+    assert np.abs(r["mass"].sum(axis=1) - 1).max() <= 1e-12
+    # materialise without RoPE hands back the inputs (first T keys)
+    qt, Kt = O.materialise(q, np.vstack([K, K[:3]]), T, bs)
+    assert qt is q and Kt.shape == (T, D) and np.array_equal(Kt, K)
+
+
 ALL_CHECKS = [
     check_attend_vs_sdpa, check_merge_vs_sdpa, check_split_chunks,
     check_pool_closed_form, check_pool_linearity, check_eviction_pre_exp,
     check_select_bruteforce, check_select_sizes, check_trajectory_invariants,
     check_swap_lists, check_place_blocks, check_buffer_retrieve, check_rope_complex, check_rope_identities,
     check_softmax_block_mass, check_alibi, check_rope_scores, check_index_inputs, check_prefill, check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
-    check_bf16_decode,
+    check_attend_blocks, check_bf16_decode,
 ]
