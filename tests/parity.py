@@ -6,7 +6,11 @@ Acceptance (per pair and step):
 * selection, eviction set (recovered from the bitmap) and swap lists are
   bit-exact, except where every mismatched pair of blocks is a near-tie:
   |S[a] - S[b]| <= 1e-6 * max(|S[a]|, |S[b]|) on the oracle's float64
-  scores of the stage that chose them;
+  scores of the stage that chose them.  After such a near-tie the swap
+  lists and the attention are compared with the oracle's over the GPU's
+  own selection, so no pair-step goes without an attention check, and a
+  run fails if near-ties exceed MAX_NEAR_TIE_FRAC of its compared
+  pair-steps;
 * O within 1e-2 max-abs, LSE = m + ln l within 1e-3, m within 1e-3, and the
   same for every non-empty split partial; empty splits are exactly
   (m, l, O) = (-inf, 0, 0);
@@ -31,6 +35,11 @@ from block_sparse_kv_score_amd.workloads import TABLE_PACKED_ROPE, Workload
 O_TOL = 1e-2
 LSE_TOL = 1e-3
 TIE_REL = 1e-6
+# near-tie events allowed per run: this fraction of the compared pair-steps
+# (at least one); fp32 scores agree with the float64 ones to ~2^-22
+# relative, so a tie inside 1e-6 is rare on Gaussian inputs, and more than
+# a few would point at a scoring error, not at ties
+MAX_NEAR_TIE_FRAC = 0.01
 # softmax block mass: p = exp(s - LSE), so an LSE error within LSE_TOL moves
 # every probability by that relative amount, and a block's mass (a sum of
 # them) by no more; twice that, plus an absolute floor for fp32 rounding
@@ -118,18 +127,26 @@ def check_attention(r: dict, O: np.ndarray, m: np.ndarray, l: np.ndarray,
 def score_bound(w: Workload, lg: Logical, q: np.ndarray, T: int) -> np.ndarray:
     """Per-block bound on |GPU score_q - oracle S_q|: the sub-block mean keys
     are rounded once to fp32 (relative 2^-24 each) and the block score once
-    more; 2^-22 covers both with margin."""
+    more; 2^-22 covers both with margin.  Computed per sub-block from
+    |qbar| . |kbar| (with deferred RoPE, where the query is rotated, from
+    ||qbar|| ||kbar||: the rotation keeps norms)."""
     qbar = np.abs(q.mean(axis=0))
     nb = -(-T // w.bs)
+    n_sub = -(-T // w.ss)  # non-empty sub-blocks, in token order
+    full = T // w.ss
+    sums = np.zeros((n_sub, lg.K.shape[1]))
+    sums[:full] = lg.K[:full * w.ss].reshape(full, w.ss, -1).mean(axis=1)
+    if n_sub > full:
+        sums[full] = lg.K[full * w.ss:T].mean(axis=0)
+    kbar = np.abs(sums)
+    if w.table == TABLE_PACKED_ROPE:
+        x = np.linalg.norm(qbar) * np.linalg.norm(kbar, axis=1)
+    else:
+        x = kbar @ qbar
+    x = x / math.sqrt(w.D)
+    blk = np.arange(n_sub) * w.ss // w.bs
     out = np.zeros(nb)
-    rope = w.table == TABLE_PACKED_ROPE
-    for i in range(nb):
-        for r in oracle.subblock_token_ranges(i, T, w.bs, w.ss):
-            kbar = np.abs(lg.K[r.start:r.stop].mean(axis=0))
-            # with deferred RoPE the query is rotated: bound its products by
-            # norms (the rotation keeps them), |rq|.|kbar| <= ||qbar|| ||kbar||
-            x = float(np.linalg.norm(qbar) * np.linalg.norm(kbar)) if rope else float(kbar @ qbar)
-            out[i] = max(out[i], x / math.sqrt(w.D))
+    np.maximum.at(out, blk, x)
     return out * 2.0 ** -22
 
 
@@ -158,12 +175,29 @@ class Gpu:
         self.mass = s.mass.cpu().numpy() if getattr(s, "mass_on", False) else None
 
 
+def oracle_over(w: Workload, inp, lg: Logical, b: int, h: int, t: int, prev: list, blocks: list, P: int,
+                alibi: bool = False) -> dict:
+    """The oracle's swap lists and attention for a given selection (the
+    GPU's, after a near-tie): the same stages as oracle_step after the
+    selection, over `blocks`."""
+    T = w.seq_len(t)
+    q = oracle.bf16_to_f64(inp.q(t)[b, h * w.G:(h + 1) * w.G])
+    rope = None
+    if w.table == TABLE_PACKED_ROPE:
+        rope = dict(q_pos=int(inp.q_pos[b]), block_start=synth.block_doc_start(w) * w.bs, base=w.rope_base)
+    slopes = synth.alibi_slopes(w.Hq)[h * w.G:(h + 1) * w.G].astype(np.float64) if alibi else None
+    qt, Kt = oracle.materialise(q, lg.K, T, w.bs, rope)
+    r = oracle.attend_blocks(qt, Kt, lg.V, T, w.bs, list(blocks), P, 1.0 / math.sqrt(w.D), slopes)
+    r["load"], r["evict"] = oracle.swap_lists(prev, blocks)
+    return r
+
+
 def compare_pair(w: Workload, inp, lg: Logical, g: Gpu, b: int, h: int, t: int, st: PairState,
                  P: int, log: list, check_scores: bool = True, alibi: bool = False) -> dict:
     """Compare one pair at step t; returns the oracle result.  Selection
-    mismatches must be near-ties (logged); attention is then not compared
-    for this pair and step because the two sides attend over different
-    blocks."""
+    mismatches must be near-ties (logged); the swap lists and attention are
+    then compared with the oracle's over the GPU's selection (the two sides
+    attend over different blocks, each correctly)."""
     r = oracle_step(w, inp, lg, b, h, t, st, P, alibi)
     where = f"{w.name} t={t} b={b} h={h}"
     nb = r["nb"]
@@ -196,17 +230,17 @@ def compare_pair(w: Workload, inp, lg: Logical, g: Gpu, b: int, h: int, t: int, 
             assert same_sel, (where, "union", sel, r["sel"])
     else:
         assert same_sel, (where, "select_all", sel[:5], r["sel"][:5])
-    if same_sel:
-        nl, ne = int(g.load_count[b, h]), int(g.evict_count[b, h])
-        assert g.load[b, h, :nl].tolist() == r["load"], (where, "load")
-        assert g.evict[b, h, :ne].tolist() == r["evict"], (where, "evict")
-        hs = slice(h * G, (h + 1) * G)
-        check_attention(r, g.o[b, hs], g.m[b, hs], g.l[b, hs], g.part_o[b, hs], g.part_m[b, hs],
-                        g.part_l[b, hs], where)
-        if g.mass is not None:
-            got = g.mass[b, hs, :len(sel)]
-            want = r["mass"]
-            err = np.abs(got - want)
-            assert np.all(err <= MASS_REL * want + MASS_ABS), (where, "mass", float(err.max()))
-            assert np.all(g.mass[b, hs, len(sel):] == 0), (where, "mass past the selection")
+    ra = r if same_sel else oracle_over(w, inp, lg, b, h, t, st.prev, sel, P, alibi)
+    nl, ne = int(g.load_count[b, h]), int(g.evict_count[b, h])
+    assert g.load[b, h, :nl].tolist() == ra["load"], (where, "load")
+    assert g.evict[b, h, :ne].tolist() == ra["evict"], (where, "evict")
+    hs = slice(h * G, (h + 1) * G)
+    check_attention(ra, g.o[b, hs], g.m[b, hs], g.l[b, hs], g.part_o[b, hs], g.part_m[b, hs],
+                    g.part_l[b, hs], where)
+    if g.mass is not None:
+        got = g.mass[b, hs, :len(sel)]
+        want = ra["mass"]
+        err = np.abs(got - want)
+        assert np.all(err <= MASS_REL * want + MASS_ABS), (where, "mass", float(err.max()))
+        assert np.all(g.mass[b, hs, len(sel):] == 0), (where, "mass past the selection")
     return r
