@@ -356,6 +356,61 @@ class DecodeSession:
                           self.stream)
 
     # ------------------------------------------------------------------
+    # checkpoint / resume of the state one step hands to the next
+    def _state_tensors(self) -> dict:
+        """The cross-step state: everything a later step reads that an
+        earlier one wrote.  The eviction bitmap is the strict policy's memory
+        (a block left out once never returns to the eviction part), the
+        previous selection is what the swap lists are taken against, and the
+        pages and summaries hold the appended tokens."""
+        st = {"seq_lens": self.seq_lens, "evicted": self.evicted,
+              "sel0": self.sel_bufs[0], "sel1": self.sel_bufs[1],
+              "count0": self.cnt_bufs[0], "count1": self.cnt_bufs[1],
+              "k_summary": self.k_summary, "e_summary": self.e_summary,
+              "k_pages": self.k_pages, "v_pages": self.v_pages, "e_pages": self.e_pages}
+        if self.offload:
+            st.update(host_k=self.host_k, host_v=self.host_v, host_e=self.host_e, resident=self.resident,
+                      slot_owner=self.slot_owner)
+            if self.buffered:
+                st["last_use"] = self.last_use
+        return st
+
+    def save_state(self, path: str):
+        """Write the cross-step state after the last step to a safetensors
+        file (host copies; the stream is synchronised first)."""
+        from safetensors.torch import save_file
+        torch.cuda.synchronize()
+        tensors = {k: v.detach().cpu().contiguous() for k, v in self._state_tensors().items()}
+        meta = {"workload": self.w.name, "step_index": str(self.step_index), "n_steps": str(self.n_steps),
+                "buffer_clock": str(self.buffer_clock), "splits": str(self.P)}
+        save_file(tensors, str(path), metadata=meta)
+
+    def load_state(self, path: str):
+        """Resume from a file written by save_state for the same workload
+        and inputs: the next step() continues where that session stopped.
+        The current length and bitmap go to the first of their two buffers."""
+        from safetensors import safe_open
+        with safe_open(str(path), framework="pt") as f:
+            meta = f.metadata()
+            if meta.get("workload") != self.w.name or int(meta["splits"]) != self.P:
+                raise ValueError(f"state of {meta.get('workload')} at {meta.get('splits')} splits, "
+                                 f"not {self.w.name} at {self.P}")
+            self.seq_lens, self.evicted = self.seq_bufs[0], self.ev_bufs[0]
+            own = self._state_tensors()
+            if set(f.keys()) != set(own):
+                raise ValueError(f"state holds {sorted(f.keys())}, this session {sorted(own)}")
+            for k, dst in own.items():
+                src = f.get_tensor(k)
+                if src.shape != dst.shape or src.dtype != dst.dtype:
+                    raise ValueError(f"state tensor {k}: {tuple(src.shape)} {src.dtype}, "
+                                     f"expected {tuple(dst.shape)} {dst.dtype}")
+                dst.copy_(src)
+        self.step_index, self.n_steps = int(meta["step_index"]), int(meta["n_steps"])
+        self.buffer_clock = int(meta["buffer_clock"])
+        self.counters.zero_()
+        torch.cuda.synchronize()
+
+    # ------------------------------------------------------------------
     # the step as HIP graphs
     _GRAPH_INPUTS = ("q_all", "k_new", "v_new", "e_new")
 
