@@ -102,17 +102,24 @@ def algorithmic_bytes(w, sel, sel_count, T):
     return kv, summ
 
 
+def host_threads() -> tuple[int, int]:
+    """Host cores this process may run on, and the BLAS threads NumPy uses."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    return cores, int(threads)
+
+
 def cpu_baseline(w, inp, budget_s: float):
     """The oracle as it stands, on (b, h) pairs of decode step 1 until the
     time budget is spent; scaled to the whole batch."""
     import numpy as np
     import oracle
     from block_sparse_kv_score_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    cores, threads = host_threads()
     pairs = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
     rng = np.random.default_rng(0)
     rng.shuffle(pairs)
@@ -156,9 +163,9 @@ def cpu_baseline(w, inp, budget_s: float):
         if elapsed >= budget_s:
             break
     step_s = elapsed / done * len(pairs)
-    out = {"value": w.B / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    out = {"value": w.B / step_s, "unit": "tokens/s", "cores": cores, "blas_threads": threads, "kind": "oracle",
            "sample": f"{done} of {len(pairs)} (b,h) pairs of decode step 1 ({elapsed:.1f} s), "
-                     f"scaled to the batch; float64 NumPy, BLAS threads = {threads}",
+                     f"scaled to the batch; float64 NumPy on {cores} host cores, BLAS threads = {threads}",
            "sec_per_step": step_s}
     if not w.select_all:
         out["stage_sec_per_step"] = {k_: round(v / done * len(pairs), 4) for k_, v in stage.items()}
@@ -179,11 +186,7 @@ def prefill_cpu_baseline(w, inp, budget_s: float):
     import numpy as np
     import oracle
     from block_sparse_kv_score_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    cores, threads = host_threads()
     rng = np.random.default_rng(0)
     qp = synth.prefill_queries(w, inp.seed)
     starts = synth.block_doc_start(w) * w.bs
@@ -199,9 +202,11 @@ def prefill_cpu_baseline(w, inp, budget_s: float):
         elapsed += time.perf_counter() - t0
         done += 1
     launch_s = elapsed / done * w.prompt * w.B * w.Hkv
-    return {"value": w.B * w.prompt / launch_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": w.B * w.prompt / launch_s, "unit": "tokens/s", "cores": cores, "blas_threads": threads,
+            "kind": "oracle",
             "sample": f"{done} prompt rows of random (b, h) pairs ({elapsed:.1f} s), scaled to the launch "
-                      f"({w.B * w.Hkv * w.prompt} rows); float64 NumPy, BLAS threads = {threads}",
+                      f"({w.B * w.Hkv * w.prompt} rows); float64 NumPy on {cores} host cores, "
+                      f"BLAS threads = {threads}",
             "sec_per_launch": launch_s}
 
 
