@@ -135,7 +135,7 @@ def score_bound(w: Workload, lg: Logical, q: np.ndarray, T: int) -> np.ndarray:
     n_sub = -(-T // w.ss)  # non-empty sub-blocks, in token order
     full = T // w.ss
     sums = np.zeros((n_sub, lg.K.shape[1]))
-    sums[:full] = lg.K[:full * w.ss].reshape(full, w.ss, -1).mean(axis=1)
+    sums[:full] = lg.K[:full * w.ss].reshape(full, w.ss, lg.K.shape[1]).mean(axis=1)
     if n_sub > full:
         sums[full] = lg.K[full * w.ss:T].mean(axis=0)
     kbar = np.abs(sums)
