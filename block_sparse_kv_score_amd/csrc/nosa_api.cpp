@@ -319,6 +319,37 @@ nosa_status nosa_select_decode(const nosa_dims* dims, const nosa_kv* kv, const u
                                              counters, o, m, l, stream));
 }
 
+nosa_status nosa_select_decode_noalloc(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* q,
+                                       const float* score_q, const float* score_e, const int32_t* seq_lens,
+                                       int32_t k_e, int32_t k_q, const uint32_t* evicted_in, uint32_t* evicted_out,
+                                       int32_t* sel, int32_t sel_cap, int32_t* sel_count, const int32_t* prev,
+                                       const int32_t* prev_count, int32_t* load, int32_t* load_count, int32_t* evict,
+                                       int32_t* evict_count, int32_t num_splits, float sm_scale, float* o, float* m,
+                                       float* l, hipStream_t stream) {
+  nosa_status st = check_dims(dims);
+  if (st != NOSA_OK) return st;
+  if ((st = check_kv(dims, kv, true)) != NOSA_OK) return st;
+  if (kv->kind == NOSA_TABLE_PACKED_ROPE) return NOSA_ERR_UNSUPPORTED;
+  if (dims->max_blocks > NOSA_SELECT_DECODE_MAX_BLOCKS) return NOSA_ERR_UNSUPPORTED;
+  if (!q || !score_q || !score_e || !seq_lens || !evicted_in || !evicted_out || !sel || !sel_count)
+    return NOSA_ERR_ARG;
+  if (!prev || !prev_count || !load || !load_count || !evict || !evict_count) return NOSA_ERR_ARG;
+  if (!o || !m || !l) return NOSA_ERR_ARG;
+  if (!aligned16(q)) return NOSA_ERR_ARG;
+  if (k_e < 0 || k_q < 0 || sel_cap < 1 || sel_cap > dims->max_blocks) return NOSA_ERR_ARG;
+  const int64_t k = (int64_t)k_e + k_q;
+  if ((int64_t)sel_cap < (k < dims->max_blocks ? k : (int64_t)dims->max_blocks)) return NOSA_ERR_ARG;
+  if (prev == sel || load == sel || evict == sel || load == evict) return NOSA_ERR_ARG;
+  if (num_splits < 1 || num_splits > 256) return NOSA_ERR_ARG;
+  if (num_splits > 1 && evicted_in == evicted_out) return NOSA_ERR_ARG;
+  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return NOSA_ERR_ARG;
+  if (nosa::noalloc_layout(*dims, num_splits).total > nosa::kNoAllocScratchBytes) return NOSA_ERR_SCRATCH;
+  return from_hip(nosa::launch_select_decode_noalloc(*dims, q, *kv, score_q, score_e, seq_lens, k_e, k_q,
+                                                     evicted_in, evicted_out, sel, sel_cap, sel_count, prev,
+                                                     prev_count, load, load_count, evict, evict_count, num_splits,
+                                                     sm_scale, o, m, l, stream));
+}
+
 nosa_status nosa_host_device_pointer(const void* host_ptr, void** device_ptr) {
   if (!host_ptr || !device_ptr) return NOSA_ERR_ARG;
   void* d = nullptr;
@@ -415,6 +446,7 @@ const char* nosa_status_string(nosa_status status) {
     case NOSA_ERR_ARG: return "invalid argument";
     case NOSA_ERR_UNSUPPORTED: return "unsupported configuration";
     case NOSA_ERR_HIP: return "HIP launch failed";
+    case NOSA_ERR_SCRATCH: return "larger than the library's static scratch (NOSA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -54,6 +54,8 @@
 // for key position t and query position n = T - 1, added in the tile loop
 // from the tile's first position; nothing else changes.
 
+#include <mutex>
+
 #include "nosa_launch.hpp"
 #include "nosa_select_impl.hpp"
 
@@ -929,6 +931,71 @@ hipError_t launch_select_decode(const nosa_dims& d, const uint16_t* q, const nos
   a.sel_count_w = sel_count;
   a.sw = SwapArgs{prev, prev_count, load, load_count, evict, evict_count};
   return launch_decode_args(d, a, kv.kind, true, stream);
+}
+
+// ---------------------------------------------------------------------------
+// nosa_select_decode_noalloc: the workspaces of the fused select + decode (the
+// split partials and the per-pair arrival counters of the cross-workgroup
+// combine) in a fixed device array of the library instead of caller memory,
+// for callers that cannot allocate.  Each GPU holds its own copy of the
+// array; host code uses its device address, looked up once per device.  The
+// counters must be zero at the start of a call: the loader zero-fills the
+// array, set-up clears the counter region once more with a kernel (a memset
+// node would misbehave in a captured graph), and every call leaves them
+// zero.  Calls that overlap on one GPU share the array and race.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+
+__global__ void zero_words_kernel(int32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+// Device address of this GPU's scratch array (set up on first use).
+static hipError_t scratch_address(unsigned char** out, hipStream_t stream) {
+  static std::mutex mu;
+  static unsigned char* addr[kMaxScratchDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    unsigned char* base = static_cast<unsigned char*>(p);
+    zero_words_kernel<<<64, 256, 0, stream>>>(reinterpret_cast<int32_t*>(base + kNoAllocCountersOffset),
+                                              kNoAllocCountersBytes / 4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    addr[dev] = base;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_select_decode_noalloc(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv,
+                                        const float* score_q, const float* score_e, const int32_t* seq_lens,
+                                        int32_t k_e, int32_t k_q, const uint32_t* evicted_in, uint32_t* evicted_out,
+                                        int32_t* sel, int32_t sel_cap, int32_t* sel_count, const int32_t* prev,
+                                        const int32_t* prev_count, int32_t* load, int32_t* load_count,
+                                        int32_t* evict, int32_t* evict_count, int32_t num_splits, float sm_scale,
+                                        float* o, float* m, float* l, hipStream_t stream) {
+  const NoAllocLayout lay = noalloc_layout(d, num_splits);
+  if (lay.total > kNoAllocScratchBytes) return hipErrorInvalidValue;  // the C-ABI layer checks first
+  unsigned char* base = nullptr;
+  const hipError_t e = scratch_address(&base, stream);
+  if (e != hipSuccess) return e;
+  return launch_select_decode(d, q, kv, score_q, score_e, seq_lens, k_e, k_q, evicted_in, evicted_out, sel,
+                              sel_cap, sel_count, prev, prev_count, load, load_count, evict, evict_count,
+                              num_splits, sm_scale, reinterpret_cast<float*>(base + lay.part_o),
+                              reinterpret_cast<float*>(base + lay.part_m), reinterpret_cast<float*>(base + lay.part_l),
+                              reinterpret_cast<int32_t*>(base + kNoAllocCountersOffset), o, m, l, stream);
 }
 
 hipError_t launch_decode_mass(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv, const int32_t* sel,

@@ -64,6 +64,37 @@ hipError_t launch_select_decode(const nosa_dims& d, const uint16_t* q, const nos
                                 float sm_scale, float* part_o, float* part_m, float* part_l, int32_t* counters,
                                 float* o, float* m, float* l, hipStream_t stream);
 
+// Layout of the static scratch of nosa_select_decode_noalloc: the arrival
+// counters (one int32 per pair, at most 65535 pairs) first, then the split
+// partials part_m, part_l [B*Hq*P] and part_o [B*Hq*P*D] fp32, each on a
+// 256-byte boundary.
+constexpr int64_t kNoAllocScratchBytes = NOSA_NOALLOC_SCRATCH_BYTES;
+constexpr int64_t kNoAllocCountersOffset = 0;
+constexpr int64_t kNoAllocCountersBytes = 65536 * 4;
+
+struct NoAllocLayout {
+  int64_t part_m, part_l, part_o, total;
+};
+
+inline NoAllocLayout noalloc_layout(const nosa_dims& d, int32_t num_splits) {
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  const int64_t rows = (int64_t)d.batch * d.n_q_heads * num_splits;
+  NoAllocLayout lay;
+  lay.part_m = kNoAllocCountersOffset + kNoAllocCountersBytes;
+  lay.part_l = lay.part_m + up(rows * 4);
+  lay.part_o = lay.part_l + up(rows * 4);
+  lay.total = lay.part_o + up(rows * d.head_dim * 4);
+  return lay;
+}
+
+hipError_t launch_select_decode_noalloc(const nosa_dims& d, const uint16_t* q, const nosa_kv& kv,
+                                        const float* score_q, const float* score_e, const int32_t* seq_lens,
+                                        int32_t k_e, int32_t k_q, const uint32_t* evicted_in, uint32_t* evicted_out,
+                                        int32_t* sel, int32_t sel_cap, int32_t* sel_count, const int32_t* prev,
+                                        const int32_t* prev_count, int32_t* load, int32_t* load_count,
+                                        int32_t* evict, int32_t* evict_count, int32_t num_splits, float sm_scale,
+                                        float* o, float* m, float* l, hipStream_t stream);
+
 hipError_t launch_retrieve(const nosa_dims& d, const nosa_kv& host_kv, const void* host_k, const void* host_v,
                            const void* host_e, uint16_t* dev_k, uint16_t* dev_v, float* dev_e, int32_t slots,
                            int32_t* resident, int32_t* slot_owner, const int32_t* load, const int32_t* load_count,

@@ -19,6 +19,7 @@ NOSA_OK = 0
 NOSA_ERR_ARG = -1
 NOSA_ERR_UNSUPPORTED = -2
 NOSA_ERR_HIP = -3
+NOSA_ERR_SCRATCH = -4
 
 NOSA_TABLE_FLAT = 0
 NOSA_TABLE_TWO_LEVEL = 1
@@ -37,6 +38,7 @@ ENTRY_POINTS = [
     "nosa_sparse_decode",
     "nosa_sparse_decode_combine",
     "nosa_select_decode",
+    "nosa_select_decode_noalloc",
     "nosa_append_score_qkv",
     "nosa_prefill_attention",
     "nosa_sparse_decode_mass",
@@ -110,6 +112,8 @@ _SIGNATURES = {
     "nosa_sparse_decode_combine": [_DIMS, _P, _KV, _P, _P, _I32, _P, _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P],
     "nosa_select_decode": [_DIMS, _KV, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _P,
                            _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P],
+    "nosa_select_decode_noalloc": [_DIMS, _KV, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _I32, _P, _P, _P, _P, _P,
+                                   _P, _P, _I32, _F32, _P, _P, _P, _P],
     "nosa_sparse_decode_mass": [_DIMS, _P, _KV, _P, _P, _I32, _P, _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _P],
     "nosa_sparse_decode_alibi": [_DIMS, _P, _KV, _P, _P, _I32, _P, _I32, _F32, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -392,6 +396,28 @@ def nosa_select_decode(dims, kv, q, score_q, score_e, seq_lens, k_e, k_q, evicte
           int(num_splits), float(sm_scale), _dev(part_o, "part_o", (torch.float32,)),
           _dev(part_m, "part_m", (torch.float32,)), _dev(part_l, "part_l", (torch.float32,)),
           _dev(counters, "counters", (torch.int32,)), _dev(o, "o", (torch.float32,)),
+          _dev(m, "m", (torch.float32,)), _dev(l, "l", (torch.float32,)), _stream(stream))
+
+
+def nosa_select_decode_noalloc(dims, kv, q, score_q, score_e, seq_lens, k_e, k_q, evicted_in, evicted_out, sel,
+                               sel_count, prev, prev_count, load, load_count, evict, evict_count, num_splits,
+                               sm_scale, o, m, l, stream=None):
+    """nosa_select_decode with its workspaces in the library's static
+    scratch: the call allocates nothing."""
+    cap = int(sel.shape[-1])
+    for t, n in ((prev, "prev"), (load, "load"), (evict, "evict")):
+        if int(t.shape[-1]) != cap:
+            raise ValueError(f"{n} must have the same last dimension as sel ({cap})")
+    ev = (torch.int32, torch.uint32)
+    _call("nosa_select_decode_noalloc", ctypes.byref(dims), ctypes.byref(kv), _dev(q, "q", _BF16_LIKE),
+          _dev(score_q, "score_q", (torch.float32,)), _dev(score_e, "score_e", (torch.float32,)),
+          _dev(seq_lens, "seq_lens", (torch.int32,)), int(k_e), int(k_q),
+          _dev(evicted_in, "evicted_in", ev), _dev(evicted_out, "evicted_out", ev),
+          _dev(sel, "sel", (torch.int32,)), cap, _dev(sel_count, "sel_count", (torch.int32,)),
+          _dev(prev, "prev", (torch.int32,)), _dev(prev_count, "prev_count", (torch.int32,)),
+          _dev(load, "load", (torch.int32,)), _dev(load_count, "load_count", (torch.int32,)),
+          _dev(evict, "evict", (torch.int32,)), _dev(evict_count, "evict_count", (torch.int32,)),
+          int(num_splits), float(sm_scale), _dev(o, "o", (torch.float32,)),
           _dev(m, "m", (torch.float32,)), _dev(l, "l", (torch.float32,)), _stream(stream))
 
 

@@ -73,6 +73,7 @@ typedef int32_t nosa_status;
 #define NOSA_ERR_ARG         -1  /* null pointer, bad size or shape          */
 #define NOSA_ERR_UNSUPPORTED -2  /* valid but not built (head_dim, sizes)    */
 #define NOSA_ERR_HIP         -3  /* a HIP launch failed                      */
+#define NOSA_ERR_SCRATCH     -4  /* needs more than the static scratch       */
 
 #define NOSA_TABLE_FLAT        0 /* table[b][h][i] -> page                   */
 #define NOSA_TABLE_TWO_LEVEL   1 /* directory -> segment -> page  [SPIN 2.C] */
@@ -358,6 +359,37 @@ nosa_status nosa_select_decode(const nosa_dims* dims, const nosa_kv* kv, const u
                                int32_t* load, int32_t* load_count, int32_t* evict, int32_t* evict_count,
                                int32_t num_splits, float sm_scale, float* part_o, float* part_m, float* part_l,
                                int32_t* counters, float* o, float* m, float* l, hipStream_t stream);
+
+/* nosa_select_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same launch and results, bit for bit, as
+ * nosa_select_decode, but the split partials and the arrival counters of the
+ * fused combine live in a fixed device array of the library
+ * (NOSA_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends) instead
+ * of caller buffers; the caller passes every input and output, and the call
+ * allocates nothing.
+ *   Arguments: as nosa_select_decode without part_o, part_m, part_l and
+ *     counters.
+ *   Size limit: 256 KiB of counters plus the partials, 4 B * B * Hq * P * (D
+ *     + 2) rounded up, must fit NOSA_NOALLOC_SCRATCH_BYTES (16 MiB: e.g. B =
+ *     32, Hq = 32, D = 128 up to P = 31); larger calls return
+ *     NOSA_ERR_SCRATCH and launch nothing.
+ *   Set-up: the first call on a device looks up that device's copy of the
+ *     array and clears its counters with a small kernel on `stream`; make
+ *     that first call outside graph capture.
+ *   Sharing: every call on a GPU uses that GPU's array, which keeps the
+ *     last call's contents; each call leaves the counters zero.  Calls that
+ *     overlap on one GPU (concurrent streams or threads) race: serialise
+ *     them.                                                               */
+#define NOSA_NOALLOC_SCRATCH_BYTES (16ll << 20)
+nosa_status nosa_select_decode_noalloc(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* q,
+                                       const float* score_q, const float* score_e, const int32_t* seq_lens,
+                                       int32_t k_e, int32_t k_q, const uint32_t* evicted_in, uint32_t* evicted_out,
+                                       int32_t* sel, int32_t sel_cap, int32_t* sel_count,
+                                       const int32_t* prev, const int32_t* prev_count,
+                                       int32_t* load, int32_t* load_count, int32_t* evict, int32_t* evict_count,
+                                       int32_t num_splits, float sm_scale, float* o, float* m, float* l,
+                                       hipStream_t stream);
 
 /* Retrieve: the host tier [NOSA, Methodology 2 (NOSI): block-sized KV
  * units, set differences drive block swapping, a host-to-device transfer

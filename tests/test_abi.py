@@ -227,3 +227,21 @@ def test_probe_host_checks():
     assert L.nosa_probe_page_gather(fake, fake, 16384, 10, fake, 0, 16, fake, None) == E
     assert L.nosa_probe_page_gather(fake, fake, 16384, 10, fake, 4, 257, fake, None) == E
     assert L.nosa_probe_page_gather(fake, fake, 16384, 10, None, 4, 16, fake, None) == E
+
+
+def test_noalloc_refuses_partials_beyond_the_scratch():
+    from block_sparse_kv_score_amd import nosa
+    L = nosa.lib()
+    fake = ctypes.c_void_p(256)  # never dereferenced: the call is refused before any launch
+    d = nosa.make_dims(32, 32, 8, 128, 64, 16, 600)
+    kv = nosa.nosa_kv()
+    kv.k_pages = kv.v_pages = kv.e_pages = fake
+    kv.num_pages = 1 << 16
+    kv.kind = nosa.NOSA_TABLE_FLAT
+    kv.table = fake
+    args = [ctypes.byref(d), ctypes.byref(kv), fake, fake, fake, fake, 32, 32, fake, ctypes.c_void_p(512), fake, 64,
+            fake, ctypes.c_void_p(768), fake, ctypes.c_void_p(1024), fake, ctypes.c_void_p(1280), fake]
+    tail = [0.088, fake, fake, fake, None]
+    assert L.nosa_select_decode_noalloc(*args, 32, *tail) == nosa.NOSA_ERR_SCRATCH
+    assert L.nosa_select_decode_noalloc(*args, 256, *tail) == nosa.NOSA_ERR_SCRATCH
+    assert "scratch" in nosa.status_string(nosa.NOSA_ERR_SCRATCH)
