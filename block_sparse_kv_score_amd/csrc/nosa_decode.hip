@@ -111,10 +111,15 @@ constexpr int kDecSelCap = 4 * kSelThreads;  // capacity of the select variants 
 template <int SR>
 struct DecodeSelSmem {
   SelShared sel;
-  int32_t list[kDecSelCap];
-  int32_t n;
-  int32_t spec[kDecWaves];  // tile index of each wave's speculative tile, -1: none
+  int32_t list[kDecSelCap];  // the blocks to decode
+  int32_t total;             // tiles of the list, once published (-1 before)
 };
+// spins of a wave waiting for the query part's tiles (about 60 ns each; far
+// beyond any selection's duration): past it the wave flags an error and stops
+constexpr int kPublishSpinLimit = 1 << 20;
+// the query selection's duration in tile times of one wave, for sharing the
+// query part's tiles out (one tile: ~4-5 us per wave at the headline)
+constexpr int kSelectTiles = 2;
 template <>
 struct DecodeSelSmem<0> {};
 
@@ -281,14 +286,23 @@ __device__ __forceinline__ void finish_mass(const Table& t, int bh, int b, int h
 // covering max_blocks <= SR * kSelThreads).  MASS: the softmax score step
 // (SR == 0 with the fused combine only).  ALIBI: ALiBi biases (SR == 0).
 //
-// Speculative first tile (select variant with one split).  The selection
-// keeps the HBM idle for several microseconds at the start of the launch.
-// Meanwhile each wave w loads the first tile of the w-th block (in index
-// order) that the eviction part has not dropped yet: the next eviction part
-// keeps every such block unless a newly created block displaces one of them,
-// so the block is almost always selected.  If it is, the wave decodes it
-// first and the other waves skip it; otherwise the wave discards the tile.
-// Only the order in which the waves visit the selected tiles changes.
+// Select variant.  On most steps the eviction part has nothing to choose:
+// the blocks it has never dropped number at most k_e (a new one appears only
+// when the context crosses a block boundary), so it keeps all of them, and
+// they are known from the incoming bitmap at launch [NOSA summary,
+// Methodology 1, locality guarantee: the eviction part changes only by
+// dropping].  With one split the workgroup then lists those blocks at once;
+// wave 0 makes the query part alone (select_query_wave) while waves 1-3
+// already decode the eviction part's tiles, so the selection no longer
+// holds the HBM idle.  The query part's size, min(k_q, nb - n_e), is known
+// at launch too, so the tiles are shared out by a fixed rule: waves 1-3
+// take the eviction part's round-robin, wave 0 takes the first Q0 of the
+// query part's (Q0 balances its selection time) and waves 1-3 the rest.
+// The schedule depends on the inputs only, so results are reproducible bit
+// for bit.  Otherwise (a new block competes, or several splits) all four
+// waves make the whole selection first (select_pair) and take the tiles
+// round-robin.  Only the order in which tiles are visited differs from the
+// separate calls.
 template <int D, int G, int KIND, int SR, bool MASS = false, bool ALIBI = false>
 __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(const DecodeArgs a) {
   constexpr bool ROPE = KIND == NOSA_TABLE_PACKED_ROPE;
@@ -298,7 +312,6 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
   __shared__ DecodeSelSmem<SR> ssh;
   static_assert(SR == 0 || kDecThreads == kSelThreads, "the selection runs on the whole workgroup");
   static_assert(!(MASS && SR > 0) && !(ALIBI && SR > 0), "select variants decode plain scores");
-  static_assert(kDecWaves == 4, "the speculation's sorting network");
 
   const int bh = blockIdx.x, p = blockIdx.y;
   const int Hkv = a.t.Hkv;
@@ -366,125 +379,96 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
       for (int dt = 0; dt < NDT; ++dt) vr[ks][dt] = load_stream(vpg + ks * 4 * D + dt * 16);
   };
 
-  int n;
+  int n = 0;
   const int32_t* selp = a.sel + (int64_t)bh * a.sel_cap;  // global list (SR == 0)
-  // speculation: this wave's block (-1: none), its page, and the selected
-  // tiles the waves took speculatively, ascending (INT_MAX: unused)
-  int spec_blk = -1;
-  int64_t spec_page = -1;
-  uint32_t spec_docb = 0;
-  int skip[kDecWaves] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
-  int nskip = 0;
+  // Tile c of this workgroup is the 64-token slice c % tpb of list entry
+  // lbase + c / tpb; wave w takes tiles w, w + 4, ... of its split's chunk,
+  // except on the fast path of the select variants (tile_of below).
+  int lbase = 0, ntiles = 0;
+  // fast path of the select variants: tiles [0, e_t) are the eviction
+  // part's, [e_t, ntiles) the query part's; wave 0 takes [e_t, e_t + q0)
+  bool fast = false;
+  int e_t = 0, q0 = 0;
+  const float* sq_row = a.score_q + (int64_t)bh * a.t.max_blocks;
+  const float* se_row = a.score_e + (int64_t)bh * a.t.max_blocks;
   if constexpr (SR > 0) {
-    // the pair's selection, into LDS; split 0 also writes the outputs
     const bool lead = p == 0;
-    const bool spec = a.P == 1;
     const int words = (a.t.max_blocks + 31) / 32;  // <= 32: one word per lane
-    uint32_t evw = 0xffffffffu;
-    if (spec && lane < words) evw = a.ev_in[(int64_t)bh * words + lane];
-    // once the selection's loads are out: this wave's block is the w-th zero
-    // bit of the eviction bitmap below nb; its page lookup goes out now
-    auto guess = [&]() {
-      if (!spec) return;
-      const int base = lane * 32;
-      uint32_t z = base >= nb ? 0u : (nb - base >= 32 ? ~evw : ~evw & ((1u << (nb - base)) - 1u));
-      const int c = __popc(z);
-      const int excl = wave_scan_incl(c) - c;
-      const bool mine = excl <= w && w < excl + c;
-      const uint64_t m = __ballot(mine);
-      if (m == 0) return;  // fewer than w + 1 such blocks
-      for (int j = mine ? w - excl : 0; j > 0; --j) z &= z - 1u;
-      const int src = __ffsll((unsigned long long)m) - 1;
-      spec_blk = __builtin_amdgcn_readlane(base + __ffs(z) - 1, src);
-      spec_page = page_of<KIND>(a.t, bh, spec_blk, spec_docb);
-    };
-    // once the eviction part is decided: the tile's loads go out.  Every
-    // input load of the selection is complete first (an explicit wait), so
-    // no later wait of the selection, at a join after this conditional
-    // issue, has to cover the tile.
-    auto issue = [&]() {
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      if (spec_blk < 0) return;
-      if (spec_page < 0) {  // unresolvable: no speculation (the decode flags it if selected)
-        spec_blk = -1;
-        return;
+    // the incoming bitmap (a word per lane) and each thread's piece of the
+    // query, loaded first
+    const uint32_t evw = lane < words ? a.ev_in[(int64_t)bh * words + lane] : 0xffffffffu;
+    constexpr int kQPieces = G * D / 8;
+    static_assert(kQPieces <= kDecThreads, "one query piece per thread");
+    const bool has_piece = (int)threadIdx.x < kQPieces;
+    uint4 qp = make_uint4(0, 0, 0, 0);
+    if (has_piece) qp = reinterpret_cast<const uint4*>(qg)[threadIdx.x];
+    // wave 0's inputs of the one-wave query selection go out at once too,
+    // before the other waves load pages (wasted if the step takes the
+    // four-wave selection: 8 KB)
+    constexpr int RQ = kDecSelCap / kWave;
+    QueryWaveInputs<RQ> qin;
+    if (w == 0 && a.P == 1) load_query_wave<RQ>(qin, bh, a.t.max_blocks, sq_row, a.sel_cap, a.sw);
+    // the blocks below nb the eviction part has never dropped
+    const int base = lane * 32;
+    const uint32_t z = base >= nb ? 0u : (nb - base >= 32 ? ~evw : ~evw & ((1u << (nb - base)) - 1u));
+    const int cz = __popc(z);
+    const int incl = wave_scan_incl(cz);
+    const int n_cand = __builtin_amdgcn_readlane(incl, kWave - 1);
+    fast = a.P == 1 && n_cand <= a.k_e;
+    if (fast) {
+      // the eviction part keeps them all: wave 0 lists them (ascending), then
+      // makes the query part while the other waves decode them
+      if (w == 0) {
+        uint32_t zz = z;
+        for (int j = incl - cz; zz != 0u; ++j) {
+          ssh.list[j] = base + __ffs(zz) - 1;
+          zz &= zz - 1u;
+        }
       }
-      load_tile(spec_page, 0);
-    };
-    // Once the selection's input loads are issued: the query (one 16-byte
-    // piece per thread, loaded with them) is parked in LDS and the guess's
-    // page-table read goes out.
-    auto after_loads = [&]() {
-      constexpr int kQPieces = G * D / 8;
-      static_assert(kQPieces <= kDecThreads, "one query piece per thread");
-      const bool has_piece = (int)threadIdx.x < kQPieces;
-      uint4 qp = make_uint4(0, 0, 0, 0);
-      if (has_piece) qp = reinterpret_cast<const uint4*>(qg)[threadIdx.x];
-      guess();
+      if (threadIdx.x == 0) ssh.total = -1;
+      e_t = n_cand * tpb;
+      const int q_t = max(0, min(a.k_q, nb - n_cand)) * tpb;
+      ntiles = e_t + q_t;
+      q0 = min(max((e_t + q_t - 3 * kSelectTiles) / kDecWaves, 0), q_t);
       if (has_piece) qstage[threadIdx.x] = qp;
-    };
-    {
+      __syncthreads();  // the eviction part's list, the query
+      query_from(qstage);
+      if (w == 0) {
+        n = select_query_wave<RQ>(qin, bh, nb, a.t.max_blocks, a.k_q, evw, n_cand, lead ? a.ev_out : nullptr,
+                                  a.sel_w + (int64_t)bh * a.sel_cap, a.sel_cap, a.sel_count_w + bh, a.sw,
+                                  ssh.sel.hist[0], ssh.sel.pick_bm, ssh.sel.prev_bm, ssh.list + n_cand);
+        // the query part's tiles follow the eviction part's (list written above)
+        if (lane == 0) __hip_atomic_store(&ssh.total, n * tpb, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    } else {
+      // the whole selection, by all four waves, into LDS; split 0 also
+      // writes the outputs.  The query waits in LDS meanwhile.
+      auto after_loads = [&]() {
+        if (has_piece) qstage[threadIdx.x] = qp;
+      };
       SwapArgs sw = a.sw;  // a copy (see select_pair)
       if (!lead) sw.load = nullptr;
-      const int ns = select_pair<SR, true>(ssh.sel, bh, T, a.bs, a.t.max_blocks, a.score_q, a.score_e, a.k_e, a.k_q,
-                                           a.ev_in + (int64_t)bh * words,
-                                           lead ? a.ev_out + (int64_t)bh * words : nullptr, ssh.list, a.sel_cap,
-                                           nullptr, sw, after_loads, issue);
-      if (threadIdx.x == 0) ssh.n = ns;
-    }
-    __syncthreads();  // the list and its size, the query
-    n = ssh.n;
-    query_from(qstage);
-    if (lead) {
-      for (int k = threadIdx.x; k < n; k += kDecThreads) a.sel_w[(int64_t)bh * a.sel_cap + k] = ssh.list[k];
-      if (threadIdx.x == 0) a.sel_count_w[bh] = n;
-    }
-    if (spec) {
-      // is this wave's block selected, and at which list position
-      int pos = n;
-      if (spec_blk >= 0) {
-        int below = 0;
-        for (int j0_ = 0; j0_ < n; j0_ += kWave) {
-          const int j = j0_ + lane;
-          below += __popcll(__ballot(j < n && ssh.list[j] < spec_blk));
-        }
-        pos = below < n && ssh.list[below] == spec_blk ? below : n;
+      n = select_pair<SR, true>(ssh.sel, bh, T, a.bs, a.t.max_blocks, sq_row, se_row, a.k_e, a.k_q,
+                                a.ev_in + (int64_t)bh * words, lead ? a.ev_out + (int64_t)bh * words : nullptr,
+                                ssh.list, a.sel_cap, nullptr, sw, after_loads);
+      const int cc = (n + a.P - 1) / a.P;
+      const int j0 = min(p * cc, n), j1 = min(j0 + cc, n);
+      lbase = j0;
+      ntiles = (j1 - j0) * tpb;
+      __syncthreads();  // the list, the query
+      query_from(qstage);
+      if (lead) {
+        for (int k = threadIdx.x; k < n; k += kDecThreads) a.sel_w[(int64_t)bh * a.sel_cap + k] = ssh.list[k];
+        if (threadIdx.x == 0) a.sel_count_w[bh] = n;
       }
-      if (pos >= n) spec_blk = -1;
-      if (lane == 0) ssh.spec[w] = spec_blk >= 0 ? pos * tpb : -1;
-      __syncthreads();
-#pragma unroll
-      for (int ww = 0; ww < kDecWaves; ++ww) {
-        const int v = ssh.spec[ww];
-        skip[ww] = v < 0 ? INT_MAX : v;
-        nskip += v >= 0;
-      }
-      auto cs = [](int& x, int& y) {
-        const int lo = min(x, y), hi = max(x, y);
-        x = lo;
-        y = hi;
-      };
-      cs(skip[0], skip[1]);
-      cs(skip[2], skip[3]);
-      cs(skip[0], skip[2]);
-      cs(skip[1], skip[3]);
-      cs(skip[1], skip[2]);
     }
   } else {
     n = min(max(a.sel_count[bh], 0), a.sel_cap);
+    const int cc = (n + a.P - 1) / a.P;
+    const int j0 = min(p * cc, n), j1 = min(j0 + cc, n);
+    lbase = j0;
+    ntiles = (j1 - j0) * tpb;
   }
-  const int c = (n + a.P - 1) / a.P;
-  const int j0 = min(p * c, n), j1 = min(j0 + c, n);
-  const int ntiles = (j1 - j0) * tpb;
-  const int ntu = ntiles - nskip;  // tiles left after the speculative ones
-  // tile index among the split's tiles of entry k of the remaining ones
-  auto full_of = [&](int k) {
-    if constexpr (SR > 0) {
-#pragma unroll
-      for (int s = 0; s < kDecWaves; ++s) k += k >= skip[s];
-    }
-    return k;
-  };
   uint32_t cur_doc = 0xffffffffu;
 
   float m_run = -INFINITY, l_run = 0.f;  // for head slot cg, log2 units
@@ -495,20 +479,59 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Remaining tile k of this split: tile kf = full_of(k), i.e. block
-  // sel[j0 + kf / tpb], 64-token slice kf % tpb.  Returns the next k with
-  // data, skipping (and flagging) entries the table cannot resolve; ntu when
-  // there is none.
-  auto next_tile = [&](int k, int64_t& page, int& ntok, uint32_t& docb, int& sub, int& pos0) -> int {
-    for (; k < ntu; k += kDecWaves) {
-      const int kf = full_of(k);
+  // Tile j of this wave's schedule (-1: none left).  Round-robin over the
+  // four waves, except on the fast path (see the kernel's comment).
+  auto tile_of = [&](int j) -> int {
+    int x;
+    if (!fast) {
+      x = w + kDecWaves * j;
+    } else if (w == 0) {
+      x = j < q0 ? e_t + j : ntiles;
+    } else {
+      const int ne = e_t > w - 1 ? (e_t - w + 3) / 3 : 0;  // eviction-part tiles of this wave
+      x = j < ne ? w - 1 + 3 * j : e_t + q0 + w - 1 + 3 * (j - ne);
+    }
+    return x < ntiles ? x : -1;
+  };
+  // Waves 1-3 wait for wave 0 to publish the query part's tiles before the
+  // first of them (bounded: past the limit the wave flags an error and
+  // takes no more tiles).
+  bool published = !fast || w == 0;
+  auto await_query_part = [&]() -> bool {
+    if constexpr (SR > 0) {
+      for (int spin = 0; !published; ++spin) {
+        published = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                        &ssh.total, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) >= 0;
+        if (published) break;
+        if (spin >= kPublishSpinLimit) {
+          if (lane == 0) flag_error(a.t.err);
+          return false;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    return true;
+  };
+
+  // The wave's next tile with data, from position j of its schedule on:
+  // its page, token count, document, slice and first position; entries the
+  // table cannot resolve are skipped and flagged.  Returns the schedule
+  // position after it (jn) and the tile, or kNone when there is none.
+  constexpr int kNone = INT_MAX;
+  int jn = 0;
+  auto next_tile = [&](int j, int64_t& page, int& ntok, uint32_t& docb, int& sub, int& pos0) -> int {
+    for (;; ++j) {
+      const int kf = tile_of(j);
+      if (kf < 0) return kNone;
+      if (kf >= e_t && !await_query_part()) return kNone;
+      jn = j + 1;
       // the LDS list is read by name (LDS instructions): through a generic
       // pointer every read would also wait for the in-flight tile loads
       int i;
       if constexpr (SR > 0)
-        i = ssh.list[j0 + kf / tpb];
+        i = ssh.list[lbase + kf / tpb];
       else
-        i = selp[j0 + kf / tpb];
+        i = selp[lbase + kf / tpb];
       sub = kf % tpb;
       if (i < 0 || i >= nb) {
         if (lane == 0) flag_error(a.t.err);
@@ -521,35 +544,25 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
       }
       if constexpr (ALIBI) pos0 = i * a.bs + sub * kTile;
       ntok = min(kTile, T - (i * a.bs + sub * kTile));
-      if (ntok > 0) return k;
+      if (ntok > 0) return kf;
     }
-    return ntu;
   };
 
   int64_t page = 0;
   int ntok = 0, sub = 0, pos0 = 0;
   uint32_t docb = 0;
-  int k;  // the current tile: a remaining one, or w - kDecWaves for the speculative one
-  if (spec_blk >= 0) {  // its loads are in flight; the wave's remaining tiles follow
-    k = w - kDecWaves;
-    page = spec_page;
-    docb = spec_docb;
-    ntok = min(kTile, T - spec_blk * a.bs);
-    pos0 = spec_blk * a.bs;
-  } else {
-    k = next_tile(w, page, ntok, docb, sub, pos0);
-    if (k < ntu) load_tile(page, sub);
-  }
+  int k = next_tile(0, page, ntok, docb, sub, pos0);  // the current tile
+  if (k != kNone) load_tile(page, sub);
 
   // Software pipeline: once q.k has consumed this tile's keys the key
   // registers receive the next tile's keys, and once P.V has consumed the
   // values they receive the next values, so every wave keeps a tile of
   // loads in flight while it computes.
-  while (k < ntu) {
+  while (k != kNone) {
     int64_t npage = 0;
     int nntok = 0, nsub = 0, npos0 = 0;
     uint32_t ndocb = 0;
-    const int nk = next_tile(k + kDecWaves, npage, nntok, ndocb, nsub, npos0);
+    const int nk = next_tile(jn, npage, nntok, ndocb, nsub, npos0);
 
     // Slots past the end hold stale page data.  A row of the q.k MFMA mixes
     // tokens of every token set (the query is zero outside a set's slots),
@@ -611,7 +624,7 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (nk < ntu) {  // prefetch the next tile's keys
+    if (nk != kNone) {  // prefetch the next tile's keys
       const uint4* kpg = k_ptr(npage, nsub);
 #pragma unroll
       for (int th = 0; th < TH; ++th)
@@ -648,7 +661,7 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
     if constexpr (MASS) {  // the tile's probability sum per head slot
       const float tsum = xor_reduce<GE, kWave>(psum, [](float x, float y) { return x + y; });
       if (real && cset == 0 && lq == 0) {
-        float* st = a.tile_stats + (((int64_t)bh * a.sel_cap * tpb + (int64_t)j0 * tpb + k) * G + cg) * 2;
+        float* st = a.tile_stats + (((int64_t)bh * a.sel_cap * tpb + (int64_t)lbase * tpb + k) * G + cg) * 2;
         store_coherent(st, tsum);
         store_coherent(st + 1, mn);
       }
@@ -685,7 +698,7 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
     }
     wave_lds_sync();
     __builtin_amdgcn_sched_barrier(0);
-    if (nk < ntu) {  // prefetch the next tile's values
+    if (nk != kNone) {  // prefetch the next tile's values
       const uint4* vpg = v_ptr(npage, nsub);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -742,7 +755,7 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
       store_coherent(a.part_m + row, pm);
       store_coherent(a.part_l + row, L);
     }
-    if (a.counters != nullptr && a.P == 1) {  // fused combine of a single split, in registers
+    if (a.o != nullptr && a.P == 1) {  // fused combine of a single split, in registers
       const int64_t orow = (int64_t)b * a.Hq + (int64_t)h * G + g;
       merge_one(pm, L, po, orow, d, D, a.o, a.m, a.l);
     }

@@ -22,7 +22,8 @@ __global__ __launch_bounds__(NT) void select_kernel(int Hkv, int bs, int max_blo
   const int bh = blockIdx.x;
   const int T = min(max(seq_lens[bh / Hkv], 0), max_blocks * bs);
   uint32_t* ev = evicted + (int64_t)bh * ((max_blocks + 31) / 32);
-  select_pair<R, SWAP, NoHook, NoHook, NT>(sh, bh, T, bs, max_blocks, score_q, score_e, k_e, k_q, ev, ev,
+  select_pair<R, SWAP, NoHook, NoHook, NT>(sh, bh, T, bs, max_blocks, score_q + (int64_t)bh * max_blocks,
+                                           score_e + (int64_t)bh * max_blocks, k_e, k_q, ev, ev,
                                            sel + (int64_t)bh * sel_cap, sel_cap, sel_count + bh, sw);
 }
 

@@ -197,6 +197,8 @@ struct SwapArgs {
 // called by all NT threads of a workgroup; returns the selection size (the
 // same value in every thread).  R elements per thread cover max_blocks
 // (R * NT >= max_blocks).
+//   sq_row, se_row: the pair's max_blocks query-aware and eviction scores
+//     (global memory or LDS);
 //   ev_in / ev_out: the pair's eviction bitmap words before / after (may be
 //     the same; ev_out == nullptr: the new bitmap is not written);
 //   sel_row: the pair's list, sel_cap entries (global memory or LDS);
@@ -214,7 +216,7 @@ struct NoHook {
 
 template <int R, bool SWAP, class H1 = NoHook, class H2 = NoHook, int NT = kSelThreads>
 __device__ int select_pair(SelSharedT<NT>& sh, int bh, int T, int bs, int max_blocks,
-                           const float* __restrict__ score_q, const float* __restrict__ score_e, int k_e,
+                           const float* __restrict__ sq_row, const float* __restrict__ se_row, int k_e,
                            int k_q, const uint32_t* ev_in, uint32_t* ev_out, int32_t* sel_row, int sel_cap,
                            int32_t* sel_count_slot, const SwapArgs sw, H1 after_loads = H1(),
                            H2 after_eviction = H2()) {
@@ -222,8 +224,8 @@ __device__ int select_pair(SelSharedT<NT>& sh, int bh, int T, int bs, int max_bl
   static_assert(R <= 32 && NT % 256 == 0, "selection shape");
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int nb = (T + bs - 1) / bs;
-  const float* se = score_e + (int64_t)bh * max_blocks;
-  const float* sq = score_q + (int64_t)bh * max_blocks;
+  const float* se = se_row;
+  const float* sq = sq_row;
   const bool swap_lists = SWAP && sw.load != nullptr;
 
   // every load up front, over the whole capacity so they need not wait for
@@ -386,6 +388,236 @@ __device__ int select_pair(SelSharedT<NT>& sh, int bh, int T, int bs, int max_bl
       if (((em[r] >> lane) & 1u) && pe < sel_cap) eo[pe] = pv[r];
     }
     if (threadIdx.x == 0) {
+      sw.load_count[bh] = min(bl, sel_cap);
+      sw.evict_count[bh] = min(be, sel_cap);
+    }
+  }
+  return n_sel;
+}
+
+// ---------------------------------------------------------------------------
+// The query part of the selection, and the outputs, made by ONE wave for the
+// step where the eviction part has nothing to choose: the never-evicted
+// blocks below nb number n_e <= k_e, so every one of them stays in the
+// eviction part and none is evicted (the incoming bitmap is the outgoing
+// one).  The query part is then the k_q best of the other blocks by
+// (score_q desc, index asc), and the results equal select_pair's bit for
+// bit.  No workgroup barrier: the decode's other waves stream the eviction
+// part's pages meanwhile.
+//
+// Element r of lane l is block i = r * 64 + l (R * 64 >= max_blocks); rows
+// r >= ceil(nb / 64) hold no block and are skipped.  The inputs are loaded
+// first (load_query_wave), as early as the caller can issue them.
+// ---------------------------------------------------------------------------
+template <int R>
+struct QueryWaveInputs {
+  float fq[R];      // score_q of the wave's elements (clamped indices)
+  int32_t pv[R];    // entries of the previous selection
+  int n_prev;
+};
+
+// sq_row: the pair's max_blocks query-aware scores (global memory or LDS).
+template <int R>
+__device__ __forceinline__ void load_query_wave(QueryWaveInputs<R>& in, int bh, int max_blocks,
+                                                const float* __restrict__ sq_row, int sel_cap, const SwapArgs& sw) {
+  const int lane = threadIdx.x % kWave;
+  const float* sq = sq_row;
+#pragma unroll
+  for (int r = 0; r < R; ++r) in.fq[r] = sq[min(r * kWave + lane, max_blocks - 1)];
+  in.n_prev = 0;
+  if (sw.load != nullptr) {
+    const int32_t* pl = sw.prev + (int64_t)bh * sel_cap;
+#pragma unroll
+    for (int r = 0; r < R; ++r) in.pv[r] = pl[min(r * kWave + lane, sel_cap - 1)];
+    in.n_prev = min(max(sw.prev_count[bh], 0), sel_cap);
+  }
+}
+
+// Marks in `out` (bit r) the k best of the elements in `cand` under (key
+// desc, index asc), by one wave: a radix select over 8-bit digits from the
+// highest bit in which the candidates' keys differ, counting digits in an
+// LDS histogram (hist: 256 words of this wave) and finding the bin of the
+// k-th key with a wave prefix sum; exact ties at the end go to the lowest
+// indices.  Requires 0 < k < number of candidates; rows >= nr hold none.
+template <int R>
+__device__ void wave_radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k, int nr, uint32_t* hist,
+                                 uint32_t& out) {
+  const int lane = threadIdx.x % kWave;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (r < nr && ((cand >> r) & 1u)) {
+      kmin = min(kmin, key[r]);
+      kmax = max(kmax, key[r]);
+    }
+  kmin = xor_reduce<1, kWave>(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
+  kmax = xor_reduce<1, kWave>(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
+  int hi = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);  // bits [hi, 32) are shared
+  uint32_t prefix = hi >= 32 ? 0u : kmin & ~((1u << hi) - 1u);
+  uint32_t pmask = hi >= 32 ? 0u : ~((1u << hi) - 1u);
+  int rem = k, n_eq = 0;
+  bool done = false;
+  while (hi > 0 && !done) {
+    const int lo = hi > 8 ? hi - 8 : 0;
+    const uint32_t dmask = (1u << (hi - lo)) - 1u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[lane + kWave * j] = 0u;
+    wave_lds_sync();
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < nr && ((cand >> r) & 1u) && (key[r] & pmask) == prefix) atomicAdd(&hist[(key[r] >> lo) & dmask], 1u);
+    wave_lds_sync();
+    // lane l holds digits 255 - 4l .. 252 - 4l (descending); keys with a
+    // digit above this lane's are counted before it
+    uint32_t c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[e] = hist[255 - 4 * lane - e];
+    const int c4 = (int)(c[0] + c[1] + c[2] + c[3]);
+    int cum = wave_scan_incl(c4) - c4;
+    int dg = -1, above = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (dg < 0 && c[e] > 0 && cum + (int)c[e] >= rem) {
+        dg = 255 - 4 * lane - e;
+        above = cum;
+        eq = (int)c[e];
+      }
+      cum += (int)c[e];
+    }
+    const uint64_t hit = __ballot(dg >= 0);
+    const int src = __ffsll((unsigned long long)hit) - 1;
+    const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane(dg, src);
+    rem -= __builtin_amdgcn_readlane(above, src);
+    n_eq = __builtin_amdgcn_readlane(eq, src);
+    wave_lds_sync();  // the histogram is cleared again by the next pass
+    prefix |= digit << lo;
+    pmask |= dmask << lo;
+    hi = lo;
+    done = rem == n_eq;  // the whole bin is taken: prefix is the threshold
+  }
+  if (rem == n_eq) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < nr && ((cand >> r) & 1u) && (key[r] & pmask) >= prefix) out |= 1u << r;
+    return;
+  }
+  // exact key ties at the threshold: the rem lowest block indices win
+  int before = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < nr) {
+      const bool c_ = (cand >> r) & 1u;
+      const uint64_t eqm = __ballot(c_ && key[r] == prefix);
+      const int rank = before + lanes_below(eqm);
+      before += __popcll(eqm);
+      if (c_ && (key[r] > prefix || (key[r] == prefix && rank < rem))) out |= 1u << r;
+    }
+  }
+}
+
+//   evw: this lane's word of the incoming bitmap (lane < ceil(max_blocks/32));
+//   ev_out: the pairs' outgoing bitmaps (the pair's words < nb are written);
+//   sel_row / sel_count_slot: the ascending union and its size;
+//   sw: swap lists against the previous selection (sw.load == nullptr: none);
+//   hist, pick_bm, prev_bm: LDS scratch of this wave (256 and
+//     ceil(max_blocks/32) words);
+//   qlist: receives the query part's blocks, ascending (LDS).
+// Returns the union's size (capped at sel_cap), the same in every lane.
+template <int R>
+__device__ int select_query_wave(const QueryWaveInputs<R>& in, int bh, int nb, int max_blocks, int k_q,
+                                 uint32_t evw, int n_e, uint32_t* ev_out, int32_t* sel_row, int sel_cap,
+                                 int32_t* sel_count_slot, const SwapArgs& sw, uint32_t* hist, uint32_t* pick_bm,
+                                 uint32_t* prev_bm, int32_t* qlist) {
+  const int lane = threadIdx.x % kWave;
+  const bool swap_lists = sw.load != nullptr;
+  const int nr = min((nb + kWave - 1) / kWave, R);  // rows holding blocks
+  // eviction part = the never-evicted blocks; the query part's candidates
+  uint32_t in_e = 0, cand = 0, key[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = r * kWave + lane;
+    const uint32_t wlo = (uint32_t)__builtin_amdgcn_readlane((int)evw, 2 * r);
+    const uint32_t whi = (uint32_t)__builtin_amdgcn_readlane((int)evw, 2 * r + 1);
+    const uint32_t word = lane < 32 ? wlo : whi;
+    const bool valid = i < nb;
+    const bool e = valid && !((word >> (lane & 31)) & 1u);
+    in_e |= (uint32_t)e << r;
+    cand |= (uint32_t)(valid && !e) << r;
+    key[r] = order_key(in.fq[r]);
+  }
+  const int n_avail = nb - n_e;
+  const int kk = min(k_q, n_avail);
+  uint32_t in_q = 0;
+  if (kk >= n_avail) in_q = cand;
+  else if (kk > 0) wave_radix_top_k<R>(key, cand, kk, nr, hist, in_q);
+
+  // outputs: the ascending union, the query part's list, the bitmap words
+  const uint32_t pick = in_e | in_q;
+  uint64_t pm[R];
+  int n_all = 0, n_q = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    pm[r] = 0;
+    if (r < nr) {
+      const int i = r * kWave + lane;
+      pm[r] = __ballot((pick >> r) & 1u);
+      const int pos = n_all + lanes_below(pm[r]);
+      if (((pick >> r) & 1u) && pos < sel_cap) sel_row[pos] = i;
+      n_all += __popcll(pm[r]);
+      const uint64_t qm = __ballot((in_q >> r) & 1u);
+      if ((in_q >> r) & 1u) qlist[n_q + lanes_below(qm)] = i;
+      n_q += __popcll(qm);
+    }
+  }
+  const int n_sel = min(n_all, sel_cap);
+  if (lane == 0 && sel_count_slot != nullptr) *sel_count_slot = n_sel;
+  const int words = (max_blocks + 31) / 32;
+  if (ev_out != nullptr && lane < words && lane * 32 < nb) ev_out[(int64_t)bh * words + lane] = evw;
+
+  if (swap_lists) {
+    // membership bitmaps of the union and of the previous selection
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (lane == 0 && 2 * r < words) {
+        pick_bm[2 * r] = (uint32_t)pm[r];
+        if (2 * r + 1 < words) pick_bm[2 * r + 1] = (uint32_t)(pm[r] >> 32);
+      }
+    for (int wd = lane; wd < words; wd += kWave) prev_bm[wd] = 0u;
+    wave_lds_sync();
+    const int nrp = (in.n_prev + kWave - 1) / kWave;  // rows holding previous entries
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int k = r * kWave + lane;
+      if (r < nrp && k < in.n_prev && in.pv[r] >= 0 && in.pv[r] < max_blocks)
+        atomicOr(&prev_bm[in.pv[r] >> 5], 1u << (in.pv[r] & 31));
+    }
+    wave_lds_sync();
+    // load = picked and not before (index order); evict = before and not
+    // picked (the previous list's order)
+    int32_t* lo = sw.load + (int64_t)bh * sel_cap;
+    int32_t* eo = sw.evict + (int64_t)bh * sel_cap;
+    int bl = 0, be = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r < nr) {
+        const int i = r * kWave + lane;
+        const bool in_prev = (prev_bm[min(i, max_blocks - 1) >> 5] >> (i & 31)) & 1u;
+        const uint64_t lm = __ballot(((pick >> r) & 1u) && !in_prev);
+        const int pl_ = bl + lanes_below(lm);
+        if (((lm >> lane) & 1u) && pl_ < sel_cap) lo[pl_] = i;
+        bl += __popcll(lm);
+      }
+      if (r < nrp) {
+        const int k = r * kWave + lane;
+        const int x = in.pv[r];
+        const bool live = k < in.n_prev && x >= 0 && x < max_blocks;
+        const uint64_t em = __ballot(live && !((pick_bm[live ? x >> 5 : 0] >> (x & 31)) & 1u));
+        const int pe = be + lanes_below(em);
+        if (((em >> lane) & 1u) && pe < sel_cap) eo[pe] = x;
+        be += __popcll(em);
+      }
+    }
+    if (lane == 0) {
       sw.load_count[bh] = min(bl, sel_cap);
       sw.evict_count[bh] = min(be, sel_cap);
     }

@@ -431,6 +431,33 @@ def test_wide_selection_workgroups(blocks):
     run_trajectory(w, seed=26, steps=3, splits=2)
 
 
+ONE_SPLIT_EDGES = [
+    # (name, scaling, steps): one split, so the fused select + decode takes
+    # its fast path (eviction part fixed, one wave selects while the others
+    # decode) on every step where no new block competes
+    ("zero-k_e", dict(B=2, Hq=8, Hkv=2, T0=1500, k_e=0, k_q=6), 5),
+    ("zero-k_q", dict(B=2, Hq=8, Hkv=2, T0=1500, k_e=6, k_q=0), 5),
+    ("empty-context", dict(B=2, Hq=4, Hkv=2, T0=0), 8),
+    ("fewer-blocks-than-k_e", dict(B=1, T0=100, k_e=4, k_q=4), 4),
+    ("block-creation", dict(B=2, Hq=8, Hkv=2, T0=64 * 20 - 3, k_e=5, k_q=3), 8),
+    ("G16-D64", dict(B=2, Hq=32, Hkv=2, T0=900, k_e=3, k_q=5), 4),
+]
+
+
+@pytest.mark.parametrize("name,scale,steps", ONE_SPLIT_EDGES, ids=[c[0] for c in ONE_SPLIT_EDGES])
+def test_one_split_select_decode_edges(name, scale, steps):
+    w = WORKLOADS["tiny_nosa"].scaled(**scale)
+    run_trajectory(w, seed=28, steps=steps, splits=1)
+
+
+@pytest.mark.parametrize("n_distinct", [1, 3])
+def test_exact_ties_one_split(n_distinct):
+    # exact ties in the one-wave query selection: lowest index first
+    w = WORKLOADS["tiny_nosa"].scaled(B=2, Hq=8, Hkv=2, T0=1500, k_e=3, k_q=5)
+    log = run_trajectory(w, seed=29, steps=6, splits=1, inp=tie_inputs(w, 29, n_distinct))
+    assert not log, log
+
+
 def test_append_past_capacity_flags_and_keeps_length():
     from block_sparse_kv_score_amd import nosa
     w = WORKLOADS["tiny_nosa"].scaled(B=2, Hq=4, Hkv=2, T0=100)
