@@ -60,6 +60,8 @@ def parse(argv=None):
     ap.add_argument("--graph", action="store_true",
                     help="time the cold steps as HIP graph replays (the plain HBM-tier step; other passes eager)")
     ap.add_argument("--unfused", action="store_true", help="time the six separate entry points")
+    ap.add_argument("--separate-select", action="store_true",
+                    help="nosa_select_swap + nosa_sparse_decode_combine where nosa_select_decode would run")
     ap.add_argument("--offload", action="store_true",
                     help="host tier: pages in pinned host memory, resident slots in HBM, nosa_retrieve per step")
     ap.add_argument("--buffer-slots", type=int, default=None,
@@ -343,7 +345,8 @@ def main(argv=None) -> int:
         args.offload = True
     sess = DecodeSession(w, inp, splits=args.splits, poison=False, fused=not args.unfused or args.offload,
                          offload=args.offload, buffer_slots=args.buffer_slots, bucket_width=args.bucket_width,
-                         mass=args.mass, alibi=args.alibi, qkv=args.qkv)
+                         mass=args.mass, alibi=args.alibi, qkv=args.qkv,
+                         select_decode=False if args.separate_select else None)
     stream = torch.cuda.current_stream()
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
 
@@ -395,7 +398,7 @@ def main(argv=None) -> int:
     elif fused:
         if w.select_all:
             names = (["append"] if w.append else []) + ["swap_diff", "decode_combine"]
-        elif sess.select_decode_ok and not sess.mass_on and not sess.alibi_on:
+        elif sess.runs_select_decode:
             names = ["append_score", "select_decode"]
         else:
             names = ["append_score", "select_swap", "decode_combine"]
@@ -553,7 +556,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
                    "context": w.T0, "block": w.bs, "sub_block": w.ss, "k_e": w.k_e, "k_q": w.k_q,
-                   "splits": sess.P, "table": w.table, "fused": fused, "graph": bool(args.graph), "offload": sess.offload,
+                   "splits": sess.P, "table": w.table, "fused": fused, "select_decode": sess.runs_select_decode, "graph": bool(args.graph), "offload": sess.offload,
                    "buffer_slots": sess.buffer_slots,
                    "parallelism": "single GPU"},
         "hbm_gbps": round(gbps, 1),

@@ -299,8 +299,11 @@ nosa_status nosa_select_decode(const nosa_dims* dims, const nosa_kv* kv, const u
   nosa_status st = check_dims(dims);
   if (st != NOSA_OK) return st;
   if ((st = check_kv(dims, kv, true)) != NOSA_OK) return st;
-  if (kv->kind == NOSA_TABLE_PACKED_ROPE) return NOSA_ERR_UNSUPPORTED;
   if (dims->max_blocks > NOSA_SELECT_DECODE_MAX_BLOCKS) return NOSA_ERR_UNSUPPORTED;
+  if (kv->kind == NOSA_TABLE_PACKED_ROPE) {
+    if (!kv->q_pos || !(kv->rope_base > 1.f)) return NOSA_ERR_ARG;
+    if (dims->n_q_heads / dims->n_kv_heads > 8) return NOSA_ERR_UNSUPPORTED;
+  }
   if (!q || !score_q || !score_e || !seq_lens || !evicted_in || !evicted_out || !sel || !sel_count)
     return NOSA_ERR_ARG;
   if (!prev || !prev_count || !load || !load_count || !evict || !evict_count) return NOSA_ERR_ARG;
@@ -329,8 +332,11 @@ nosa_status nosa_select_decode_noalloc(const nosa_dims* dims, const nosa_kv* kv,
   nosa_status st = check_dims(dims);
   if (st != NOSA_OK) return st;
   if ((st = check_kv(dims, kv, true)) != NOSA_OK) return st;
-  if (kv->kind == NOSA_TABLE_PACKED_ROPE) return NOSA_ERR_UNSUPPORTED;
   if (dims->max_blocks > NOSA_SELECT_DECODE_MAX_BLOCKS) return NOSA_ERR_UNSUPPORTED;
+  if (kv->kind == NOSA_TABLE_PACKED_ROPE) {
+    if (!kv->q_pos || !(kv->rope_base > 1.f)) return NOSA_ERR_ARG;
+    if (dims->n_q_heads / dims->n_kv_heads > 8) return NOSA_ERR_UNSUPPORTED;
+  }
   if (!q || !score_q || !score_e || !seq_lens || !evicted_in || !evicted_out || !sel || !sel_count)
     return NOSA_ERR_ARG;
   if (!prev || !prev_count || !load || !load_count || !evict || !evict_count) return NOSA_ERR_ARG;

@@ -105,21 +105,29 @@ struct DecodeArgs {
   const float* alibi;  // [Hq] slopes
 };
 
-constexpr int kDecSelCap = 4 * kSelThreads;  // capacity of the select variants (SR = 4)
+// The select variants hold SR elements per select thread: SR = 4 covers
+// max_blocks <= 1024, SR = 9 max_blocks <= 2304 (a 256K context of
+// 128-token blocks plus appended tokens).  A lane of a wave holds bitmap
+// words lane and, with SR = 9, lane + 64.
+constexpr int kDecSelMaxBlocks = 9 * kSelThreads;
+static_assert(kDecSelMaxBlocks == NOSA_SELECT_DECODE_MAX_BLOCKS, "the C-ABI limit is the kernels' own");
 
 // LDS of the fused selection (SR > 0: elements per select thread).
 template <int SR>
 struct DecodeSelSmem {
   SelShared sel;
-  int32_t list[kDecSelCap];  // the blocks to decode
-  int32_t total;             // tiles of the list, once published (-1 before)
+  int32_t list[SR * kSelThreads];  // the blocks to decode
+  int32_t total;                   // tiles of the list, once published (-1 before)
 };
 // spins of a wave waiting for the query part's tiles (about 60 ns each; far
 // beyond any selection's duration): past it the wave flags an error and stops
 constexpr int kPublishSpinLimit = 1 << 20;
-// the query selection's duration in tile times of one wave, for sharing the
-// query part's tiles out (one tile: ~4-5 us per wave at the headline)
-constexpr int kSelectTiles = 2;
+// the one-wave query selection's duration in tile times of one wave, for
+// sharing the query part's tiles out (one tile: ~4-6 us per wave at one
+// wave per SIMD).  Measured best: 1 for its 16 rows (SR = 4; 0-2 within
+// noise), 6-8 for its 36 rows (SR = 9, 2050 blocks).
+template <int SR>
+constexpr int kSelectTiles = SR <= 4 ? 1 : 7;
 template <>
 struct DecodeSelSmem<0> {};
 
@@ -291,18 +299,21 @@ __device__ __forceinline__ void finish_mass(const Table& t, int bh, int b, int h
 // when the context crosses a block boundary), so it keeps all of them, and
 // they are known from the incoming bitmap at launch [NOSA summary,
 // Methodology 1, locality guarantee: the eviction part changes only by
-// dropping].  With one split the workgroup then lists those blocks at once;
-// wave 0 makes the query part alone (select_query_wave) while waves 1-3
-// already decode the eviction part's tiles, so the selection no longer
-// holds the HBM idle.  The query part's size, min(k_q, nb - n_e), is known
-// at launch too, so the tiles are shared out by a fixed rule: waves 1-3
-// take the eviction part's round-robin, wave 0 takes the first Q0 of the
-// query part's (Q0 balances its selection time) and waves 1-3 the rest.
-// The schedule depends on the inputs only, so results are reproducible bit
-// for bit.  Otherwise (a new block competes, or several splits) all four
-// waves make the whole selection first (select_pair) and take the tiles
-// round-robin.  Only the order in which tiles are visited differs from the
-// separate calls.
+// dropping].  Each workgroup then lists those blocks at once; wave 0 makes
+// the query part alone (select_query_wave) while waves 1-3 already decode
+// eviction-part tiles, so the selection no longer holds the HBM idle.  The
+// query part's size, min(k_q, nb - n_e), is known at launch too, so the
+// work is shared out by a fixed rule: split p takes the p-th of P equal
+// shares (whole blocks) of the eviction part and of the query part; in the
+// workgroup, waves 1-3 take the share's eviction tiles round-robin, wave 0
+// the first Q0 of its query tiles (Q0 balances its selection time) and
+// waves 1-3 the rest.  The schedule depends on the inputs only, so results
+// are reproducible bit for bit.  Otherwise (a new block competes) all four
+// waves make the whole selection first (select_pair), split p takes the
+// p-th contiguous chunk of the ascending list, and the waves take its
+// tiles round-robin.  Against the separate calls, the tiles' visiting
+// order differs, and on the fast path with several splits which blocks
+// each split's partial covers; the merged output is the same attention.
 template <int D, int G, int KIND, int SR, bool MASS = false, bool ALIBI = false>
 __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(const DecodeArgs a) {
   constexpr bool ROPE = KIND == NOSA_TABLE_PACKED_ROPE;
@@ -334,7 +345,7 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
   uint4 qreg[NDS];
   double theta = 0.0;
   int64_t qpos = 0;
-  __shared__ uint4 qstage[SR > 0 ? G * D / 8 : 1];
+  __shared__ uint4 qstage[SR > 0 && !ROPE ? G * D / 8 : 1];
   auto query_from = [&](const uint4* src) {
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
@@ -343,7 +354,12 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
     }
   };
   if constexpr (SR > 0) {
-    static_assert(!ROPE, "select variants read flat or two-level tables");
+    if constexpr (ROPE) {  // the query itself is parked in sh.qf during the selection
+      if (lane < D / 2) theta = pow((double)a.rope_base, -2.0 * (double)lane / (double)D);
+      qpos = a.q_pos[b];
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) qreg[ds] = make_uint4(0, 0, 0, 0);
+    }
   } else if constexpr (!ROPE) {
     query_from(reinterpret_cast<const uint4*>(qg));
   } else {
@@ -385,69 +401,111 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
   // lbase + c / tpb; wave w takes tiles w, w + 4, ... of its split's chunk,
   // except on the fast path of the select variants (tile_of below).
   int lbase = 0, ntiles = 0;
-  // fast path of the select variants: tiles [0, e_t) are the eviction
-  // part's, [e_t, ntiles) the query part's; wave 0 takes [e_t, e_t + q0)
+  // fast path of the select variants: list tiles [0, e_t) are the eviction
+  // part's, from e_t on the query part's; this split's share is le tiles
+  // from e_lo and lqt tiles from e_t + q_lo, and wave 0 takes the first q0
+  // of the latter
   bool fast = false;
-  int e_t = 0, q0 = 0;
+  int e_t = 0, e_lo = 0, le = 0, q_lo = 0, lqt = 0, q0 = 0;
   const float* sq_row = a.score_q + (int64_t)bh * a.t.max_blocks;
   const float* se_row = a.score_e + (int64_t)bh * a.t.max_blocks;
   if constexpr (SR > 0) {
     const bool lead = p == 0;
-    const int words = (a.t.max_blocks + 31) / 32;  // <= 32: one word per lane
-    // the incoming bitmap (a word per lane) and each thread's piece of the
-    // query, loaded first
-    const uint32_t evw = lane < words ? a.ev_in[(int64_t)bh * words + lane] : 0xffffffffu;
+    const int words = (a.t.max_blocks + 31) / 32;  // <= 2 * kWave
+    // the incoming bitmap (words lane and lane + 64; missing words read as
+    // all dropped) and each thread's piece of the query, loaded first
+    const uint32_t* evp = a.ev_in + (int64_t)bh * words;
+    const uint32_t evw = lane < words ? evp[lane] : 0xffffffffu;
+    const uint32_t evw2 = SR > 8 && lane + kWave < words ? evp[lane + kWave] : 0xffffffffu;
     constexpr int kQPieces = G * D / 8;
     static_assert(kQPieces <= kDecThreads, "one query piece per thread");
     const bool has_piece = (int)threadIdx.x < kQPieces;
     uint4 qp = make_uint4(0, 0, 0, 0);
     if (has_piece) qp = reinterpret_cast<const uint4*>(qg)[threadIdx.x];
+    // the query into LDS: bf16 octets to stage (or, with deferred RoPE, as
+    // floats in sh.qf, rotated per document in the tile loop)
+    auto park_query = [&]() {
+      if (!has_piece) return;
+      if constexpr (ROPE) {
+        const int k0 = 8 * (int)threadIdx.x;  // elements k0 .. k0 + 7 of the G x D query
+        const uint32_t wv[4] = {qp.x, qp.y, qp.z, qp.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sh.qf[(k0 + 2 * e) / D][(k0 + 2 * e) % D] = bf16_lo(wv[e]);
+          sh.qf[(k0 + 2 * e + 1) / D][(k0 + 2 * e + 1) % D] = bf16_hi(wv[e]);
+        }
+      } else {
+        qstage[threadIdx.x] = qp;
+      }
+    };
+    // only split 0 writes the selection's outputs (the swap lists too)
+    SwapArgs sw = a.sw;  // a copy (see select_pair)
+    if (!lead) sw.load = nullptr;
     // wave 0's inputs of the one-wave query selection go out at once too,
     // before the other waves load pages (wasted if the step takes the
-    // four-wave selection: 8 KB)
-    constexpr int RQ = kDecSelCap / kWave;
+    // four-wave selection: 4 * SR KB)
+    constexpr int RQ = SR * kSelThreads / kWave;
     QueryWaveInputs<RQ> qin;
-    if (w == 0 && a.P == 1) load_query_wave<RQ>(qin, bh, a.t.max_blocks, sq_row, a.sel_cap, a.sw);
-    // the blocks below nb the eviction part has never dropped
-    const int base = lane * 32;
-    const uint32_t z = base >= nb ? 0u : (nb - base >= 32 ? ~evw : ~evw & ((1u << (nb - base)) - 1u));
-    const int cz = __popc(z);
+    if (w == 0) load_query_wave<RQ>(qin, bh, a.t.max_blocks, sq_row, a.sel_cap, sw);
+    // the blocks below nb the eviction part has never dropped: bits of
+    // word lane (blocks from base), then of word lane + 64 (from base2)
+    auto never_dropped = [&](uint32_t word, int from) -> uint32_t {
+      return from >= nb ? 0u : (nb - from >= 32 ? ~word : ~word & ((1u << (nb - from)) - 1u));
+    };
+    const int base = lane * 32, base2 = base + 32 * kWave;
+    const uint32_t z = never_dropped(evw, base);
+    const uint32_t z2 = SR > 8 ? never_dropped(evw2, base2) : 0u;
+    const int cz = __popc(z), cz2 = __popc(z2);
     const int incl = wave_scan_incl(cz);
-    const int n_cand = __builtin_amdgcn_readlane(incl, kWave - 1);
-    fast = a.P == 1 && n_cand <= a.k_e;
+    const int n_lo = __builtin_amdgcn_readlane(incl, kWave - 1);  // in words 0 .. 63
+    int incl2 = 0, n_cand = n_lo;
+    if constexpr (SR > 8) {
+      incl2 = wave_scan_incl(cz2);
+      n_cand += __builtin_amdgcn_readlane(incl2, kWave - 1);
+    }
+    fast = n_cand <= a.k_e;
     if (fast) {
       // the eviction part keeps them all: wave 0 lists them (ascending), then
-      // makes the query part while the other waves decode them
+      // makes the query part while the other waves decode its share of them
       if (w == 0) {
         uint32_t zz = z;
         for (int j = incl - cz; zz != 0u; ++j) {
           ssh.list[j] = base + __ffs(zz) - 1;
           zz &= zz - 1u;
         }
+        if constexpr (SR > 8) {
+          zz = z2;
+          for (int j = n_lo + incl2 - cz2; zz != 0u; ++j) {
+            ssh.list[j] = base2 + __ffs(zz) - 1;
+            zz &= zz - 1u;
+          }
+        }
       }
       if (threadIdx.x == 0) ssh.total = -1;
+      const int n_q = max(0, min(a.k_q, nb - n_cand));
+      const int e0 = (int)((int64_t)p * n_cand / a.P), e1 = (int)((int64_t)(p + 1) * n_cand / a.P);
+      const int qa = (int)((int64_t)p * n_q / a.P), qb = (int)((int64_t)(p + 1) * n_q / a.P);
       e_t = n_cand * tpb;
-      const int q_t = max(0, min(a.k_q, nb - n_cand)) * tpb;
-      ntiles = e_t + q_t;
-      q0 = min(max((e_t + q_t - 3 * kSelectTiles) / kDecWaves, 0), q_t);
-      if (has_piece) qstage[threadIdx.x] = qp;
+      e_lo = e0 * tpb;
+      le = (e1 - e0) * tpb;
+      q_lo = qa * tpb;
+      lqt = (qb - qa) * tpb;
+      q0 = min(max((le + lqt - 3 * kSelectTiles<SR>) / kDecWaves, 0), lqt);
+      park_query();
       __syncthreads();  // the eviction part's list, the query
-      query_from(qstage);
+      if constexpr (!ROPE) query_from(qstage);
       if (w == 0) {
-        n = select_query_wave<RQ>(qin, bh, nb, a.t.max_blocks, a.k_q, evw, n_cand, lead ? a.ev_out : nullptr,
-                                  a.sel_w + (int64_t)bh * a.sel_cap, a.sel_cap, a.sel_count_w + bh, a.sw,
-                                  ssh.sel.hist[0], ssh.sel.pick_bm, ssh.sel.prev_bm, ssh.list + n_cand);
+        n = select_query_wave<RQ>(qin, bh, nb, a.t.max_blocks, a.k_q, evw, evw2, n_cand, lead ? a.ev_out : nullptr,
+                                  lead ? a.sel_w + (int64_t)bh * a.sel_cap : nullptr, a.sel_cap,
+                                  lead ? a.sel_count_w + bh : nullptr, sw, ssh.sel.hist[0], ssh.sel.pick_bm,
+                                  ssh.sel.prev_bm, ssh.list + n_cand);
         // the query part's tiles follow the eviction part's (list written above)
         if (lane == 0) __hip_atomic_store(&ssh.total, n * tpb, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     } else {
       // the whole selection, by all four waves, into LDS; split 0 also
       // writes the outputs.  The query waits in LDS meanwhile.
-      auto after_loads = [&]() {
-        if (has_piece) qstage[threadIdx.x] = qp;
-      };
-      SwapArgs sw = a.sw;  // a copy (see select_pair)
-      if (!lead) sw.load = nullptr;
+      auto after_loads = [&]() { park_query(); };
       n = select_pair<SR, true>(ssh.sel, bh, T, a.bs, a.t.max_blocks, sq_row, se_row, a.k_e, a.k_q,
                                 a.ev_in + (int64_t)bh * words, lead ? a.ev_out + (int64_t)bh * words : nullptr,
                                 ssh.list, a.sel_cap, nullptr, sw, after_loads);
@@ -456,7 +514,7 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
       lbase = j0;
       ntiles = (j1 - j0) * tpb;
       __syncthreads();  // the list, the query
-      query_from(qstage);
+      if constexpr (!ROPE) query_from(qstage);
       if (lead) {
         for (int k = threadIdx.x; k < n; k += kDecThreads) a.sel_w[(int64_t)bh * a.sel_cap + k] = ssh.list[k];
         if (threadIdx.x == 0) a.sel_count_w[bh] = n;
@@ -482,16 +540,20 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
   // Tile j of this wave's schedule (-1: none left).  Round-robin over the
   // four waves, except on the fast path (see the kernel's comment).
   auto tile_of = [&](int j) -> int {
-    int x;
     if (!fast) {
-      x = w + kDecWaves * j;
-    } else if (w == 0) {
-      x = j < q0 ? e_t + j : ntiles;
-    } else {
-      const int ne = e_t > w - 1 ? (e_t - w + 3) / 3 : 0;  // eviction-part tiles of this wave
-      x = j < ne ? w - 1 + 3 * j : e_t + q0 + w - 1 + 3 * (j - ne);
+      const int x = w + kDecWaves * j;
+      return x < ntiles ? x : -1;
     }
-    return x < ntiles ? x : -1;
+    // position x in this split's share: eviction tiles [0, le), query [le, le + lqt)
+    int x;
+    if (w == 0) {
+      x = j < q0 ? le + j : le + lqt;
+    } else {
+      const int ne = le > w - 1 ? (le - w + 3) / 3 : 0;  // eviction-part tiles of this wave
+      x = j < ne ? w - 1 + 3 * j : le + q0 + w - 1 + 3 * (j - ne);
+    }
+    if (x >= le + lqt) return -1;
+    return x < le ? e_lo + x : e_t + q_lo + (x - le);
   };
   // Waves 1-3 wait for wave 0 to publish the query part's tiles before the
   // first of them (bounded: past the limit the wave flags an error and
@@ -828,6 +890,22 @@ __global__ void combine_kernel(int P, int D, const float* __restrict__ part_o, c
   merge_splits<false>(P, D, blockIdx.x, threadIdx.x, part_o, part_m, part_l, o, m, l);
 }
 
+// The select variants: SR = 4 up to 1024 blocks, SR = 9 up to 2304.
+template <int D, int G, int SR>
+static void launch_select_dg(dim3 grid, const DecodeArgs& a, int kind, hipStream_t stream) {
+  switch (kind) {
+    case NOSA_TABLE_FLAT:
+      decode_kernel<D, G, NOSA_TABLE_FLAT, SR><<<grid, kDecThreads, 0, stream>>>(a);
+      break;
+    case NOSA_TABLE_TWO_LEVEL:
+      decode_kernel<D, G, NOSA_TABLE_TWO_LEVEL, SR><<<grid, kDecThreads, 0, stream>>>(a);
+      break;
+    default:
+      if constexpr (G <= 8) decode_kernel<D, G, NOSA_TABLE_PACKED_ROPE, SR><<<grid, kDecThreads, 0, stream>>>(a);
+      break;
+  }
+}
+
 template <int D, int G>
 static void launch_decode_dg(dim3 grid, const DecodeArgs& a, int kind, bool select, hipStream_t stream) {
   if (a.alibi != nullptr) {  // ALiBi: flat and two-level tables
@@ -844,11 +922,11 @@ static void launch_decode_dg(dim3 grid, const DecodeArgs& a, int kind, bool sele
       decode_kernel<D, G, NOSA_TABLE_TWO_LEVEL, 0, true><<<grid, kDecThreads, 0, stream>>>(a);
     return;
   }
-  if (select) {  // flat and two-level tables, max_blocks <= kDecSelCap
-    if (kind == NOSA_TABLE_FLAT)
-      decode_kernel<D, G, NOSA_TABLE_FLAT, 4><<<grid, kDecThreads, 0, stream>>>(a);
+  if (select) {  // max_blocks <= kDecSelMaxBlocks
+    if (a.t.max_blocks <= 4 * kSelThreads)
+      launch_select_dg<D, G, 4>(grid, a, kind, stream);
     else
-      decode_kernel<D, G, NOSA_TABLE_TWO_LEVEL, 4><<<grid, kDecThreads, 0, stream>>>(a);
+      launch_select_dg<D, G, 9>(grid, a, kind, stream);
     return;
   }
   switch (kind) {

@@ -26,6 +26,8 @@
 // measured slower for 516 blocks.)
 #pragma once
 
+#include <type_traits>
+
 #include "nosa_device.hpp"
 
 namespace nosa {
@@ -79,7 +81,7 @@ __device__ __forceinline__ int block_sum(int v, int& phase, SelSharedT<NT>& sh) 
 // 256 bins finds the bin holding the k-th key; the select stops as soon as
 // that bin is taken whole.
 template <int R, int NT>
-__device__ void radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k, uint32_t& out, int& phase,
+__device__ __forceinline__ void radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k, uint32_t& out, int& phase,
                             SelSharedT<NT>& sh) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -214,8 +216,10 @@ struct NoHook {
   __device__ void operator()() const {}
 };
 
+// Inlined at every call: a call would pass the hooks' captures, and the
+// caller's registers around it, through scratch memory.
 template <int R, bool SWAP, class H1 = NoHook, class H2 = NoHook, int NT = kSelThreads>
-__device__ int select_pair(SelSharedT<NT>& sh, int bh, int T, int bs, int max_blocks,
+__device__ __forceinline__ int select_pair(SelSharedT<NT>& sh, int bh, int T, int bs, int max_blocks,
                            const float* __restrict__ sq_row, const float* __restrict__ se_row, int k_e,
                            int k_q, const uint32_t* ev_in, uint32_t* ev_out, int32_t* sel_row, int sel_cap,
                            int32_t* sel_count_slot, const SwapArgs sw, H1 after_loads = H1(),
@@ -409,6 +413,10 @@ __device__ int select_pair(SelSharedT<NT>& sh, int bh, int T, int bs, int max_bl
 // r >= ceil(nb / 64) hold no block and are skipped.  The inputs are loaded
 // first (load_query_wave), as early as the caller can issue them.
 // ---------------------------------------------------------------------------
+// Bit r of a row mask is row r of a lane (R <= 64 rows).
+template <int R>
+using RowMask = typename std::conditional<(R > 32), uint64_t, uint32_t>::type;
+
 template <int R>
 struct QueryWaveInputs {
   float fq[R];      // score_q of the wave's elements (clamped indices)
@@ -440,8 +448,8 @@ __device__ __forceinline__ void load_query_wave(QueryWaveInputs<R>& in, int bh, 
 // k-th key with a wave prefix sum; exact ties at the end go to the lowest
 // indices.  Requires 0 < k < number of candidates; rows >= nr hold none.
 template <int R>
-__device__ void wave_radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k, int nr, uint32_t* hist,
-                                 uint32_t& out) {
+__device__ __forceinline__ void wave_radix_top_k(const uint32_t (&key)[R], RowMask<R> cand, int k, int nr,
+                                                 uint32_t* hist, RowMask<R>& out) {
   const int lane = threadIdx.x % kWave;
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
@@ -498,7 +506,7 @@ __device__ void wave_radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k,
   if (rem == n_eq) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (r < nr && ((cand >> r) & 1u) && (key[r] & pmask) >= prefix) out |= 1u << r;
+      if (r < nr && ((cand >> r) & 1u) && (key[r] & pmask) >= prefix) out |= RowMask<R>(1) << r;
     return;
   }
   // exact key ties at the threshold: the rem lowest block indices win
@@ -510,49 +518,54 @@ __device__ void wave_radix_top_k(const uint32_t (&key)[R], uint32_t cand, int k,
       const uint64_t eqm = __ballot(c_ && key[r] == prefix);
       const int rank = before + lanes_below(eqm);
       before += __popcll(eqm);
-      if (c_ && (key[r] > prefix || (key[r] == prefix && rank < rem))) out |= 1u << r;
+      if (c_ && (key[r] > prefix || (key[r] == prefix && rank < rem))) out |= RowMask<R>(1) << r;
     }
   }
 }
 
-//   evw: this lane's word of the incoming bitmap (lane < ceil(max_blocks/32));
+//   evw, evw2: this lane's words lane and lane + 64 of the incoming bitmap
+//     (words past ceil(max_blocks/32) all ones; evw2 is read for R > 32);
 //   ev_out: the pairs' outgoing bitmaps (the pair's words < nb are written);
-//   sel_row / sel_count_slot: the ascending union and its size;
+//   sel_row / sel_count_slot: the ascending union and its size (nullptr:
+//     not written);
 //   sw: swap lists against the previous selection (sw.load == nullptr: none);
 //   hist, pick_bm, prev_bm: LDS scratch of this wave (256 and
 //     ceil(max_blocks/32) words);
 //   qlist: receives the query part's blocks, ascending (LDS).
 // Returns the union's size (capped at sel_cap), the same in every lane.
 template <int R>
-__device__ int select_query_wave(const QueryWaveInputs<R>& in, int bh, int nb, int max_blocks, int k_q,
-                                 uint32_t evw, int n_e, uint32_t* ev_out, int32_t* sel_row, int sel_cap,
+__device__ __forceinline__ int select_query_wave(const QueryWaveInputs<R>& in, int bh, int nb, int max_blocks, int k_q,
+                                 uint32_t evw, uint32_t evw2, int n_e, uint32_t* ev_out, int32_t* sel_row, int sel_cap,
                                  int32_t* sel_count_slot, const SwapArgs& sw, uint32_t* hist, uint32_t* pick_bm,
                                  uint32_t* prev_bm, int32_t* qlist) {
+  static_assert(R <= 64, "rows of a lane: at most two bitmap words per lane");
   const int lane = threadIdx.x % kWave;
   const bool swap_lists = sw.load != nullptr;
   const int nr = min((nb + kWave - 1) / kWave, R);  // rows holding blocks
   // eviction part = the never-evicted blocks; the query part's candidates
-  uint32_t in_e = 0, cand = 0, key[R];
+  RowMask<R> in_e = 0, cand = 0;
+  uint32_t key[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int i = r * kWave + lane;
-    const uint32_t wlo = (uint32_t)__builtin_amdgcn_readlane((int)evw, 2 * r);
-    const uint32_t whi = (uint32_t)__builtin_amdgcn_readlane((int)evw, 2 * r + 1);
+    const uint32_t src = r < 32 ? evw : evw2;  // rows 32.. hold words 64..
+    const uint32_t wlo = (uint32_t)__builtin_amdgcn_readlane((int)src, (2 * r) & 63);
+    const uint32_t whi = (uint32_t)__builtin_amdgcn_readlane((int)src, (2 * r + 1) & 63);
     const uint32_t word = lane < 32 ? wlo : whi;
     const bool valid = i < nb;
     const bool e = valid && !((word >> (lane & 31)) & 1u);
-    in_e |= (uint32_t)e << r;
-    cand |= (uint32_t)(valid && !e) << r;
+    in_e |= RowMask<R>(e) << r;
+    cand |= RowMask<R>(valid && !e) << r;
     key[r] = order_key(in.fq[r]);
   }
   const int n_avail = nb - n_e;
   const int kk = min(k_q, n_avail);
-  uint32_t in_q = 0;
+  RowMask<R> in_q = 0;
   if (kk >= n_avail) in_q = cand;
   else if (kk > 0) wave_radix_top_k<R>(key, cand, kk, nr, hist, in_q);
 
   // outputs: the ascending union, the query part's list, the bitmap words
-  const uint32_t pick = in_e | in_q;
+  const RowMask<R> pick = in_e | in_q;
   uint64_t pm[R];
   int n_all = 0, n_q = 0;
 #pragma unroll
@@ -562,7 +575,7 @@ __device__ int select_query_wave(const QueryWaveInputs<R>& in, int bh, int nb, i
       const int i = r * kWave + lane;
       pm[r] = __ballot((pick >> r) & 1u);
       const int pos = n_all + lanes_below(pm[r]);
-      if (((pick >> r) & 1u) && pos < sel_cap) sel_row[pos] = i;
+      if (sel_row != nullptr && ((pick >> r) & 1u) && pos < sel_cap) sel_row[pos] = i;
       n_all += __popcll(pm[r]);
       const uint64_t qm = __ballot((in_q >> r) & 1u);
       if ((in_q >> r) & 1u) qlist[n_q + lanes_below(qm)] = i;
@@ -573,6 +586,8 @@ __device__ int select_query_wave(const QueryWaveInputs<R>& in, int bh, int nb, i
   if (lane == 0 && sel_count_slot != nullptr) *sel_count_slot = n_sel;
   const int words = (max_blocks + 31) / 32;
   if (ev_out != nullptr && lane < words && lane * 32 < nb) ev_out[(int64_t)bh * words + lane] = evw;
+  if (R > 32 && ev_out != nullptr && lane + kWave < words && (lane + kWave) * 32 < nb)
+    ev_out[(int64_t)bh * words + kWave + lane] = evw2;
 
   if (swap_lists) {
     // membership bitmaps of the union and of the previous selection

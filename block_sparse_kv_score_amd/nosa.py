@@ -374,7 +374,7 @@ def nosa_prefill_attention(dims, kv, q, q_pos0, seq_lens, sm_scale, o, m, l, str
           _dev(l, "l", (torch.float32,)), _stream(stream))
 
 
-SELECT_DECODE_MAX_BLOCKS = 1024
+SELECT_DECODE_MAX_BLOCKS = 2304
 
 
 def nosa_select_decode(dims, kv, q, score_q, score_e, seq_lens, k_e, k_q, evicted_in, evicted_out, sel, sel_count,

@@ -13,8 +13,9 @@ Call sequence of decode step t (1-based):
 With `fused` (the default) the step is two launches with the same results:
   nosa_append_score          append + score
   nosa_select_decode         select + swap_diff + decode + combine
-(where nosa_select_decode is not supported -- more than 1024 blocks of
-capacity -- or by default above two splits, nosa_select_swap then
+(where nosa_select_decode is not supported -- more than 2304 blocks of
+capacity, or deferred RoPE with more than 8 query heads per KV head -- or
+by default above four splits, nosa_select_swap then
 nosa_sparse_decode_combine; with every block selected: nosa_swap_diff,
 then the fused decode).  The fused launches
 write the new lengths and the new eviction bitmap to the other of two
@@ -51,7 +52,7 @@ _KIND = {TABLE_FLAT: nosa.NOSA_TABLE_FLAT, TABLE_TWO_LEVEL: nosa.NOSA_TABLE_TWO_
          TABLE_PACKED_ROPE: nosa.NOSA_TABLE_PACKED_ROPE}
 
 BF16_NAN = -1  # 0xFFFF as int16: a NaN bit pattern for never-written slots
-SELECT_DECODE_AUTO_MAX_SPLITS = 2  # default: nosa_select_decode up to this many splits
+SELECT_DECODE_AUTO_MAX_SPLITS = 4  # default: nosa_select_decode up to this many splits
 
 
 def _i32(a: np.ndarray) -> torch.Tensor:
@@ -127,7 +128,7 @@ class DecodeSession:
         # the select variant keeps one wave per SIMD, so with many short
         # workgroups per pair nosa_select_swap + nosa_sparse_decode_combine
         # is faster.  select_decode=True takes it wherever it is supported.
-        supported = MB <= nosa.SELECT_DECODE_MAX_BLOCKS and w.table != TABLE_PACKED_ROPE
+        supported = MB <= nosa.SELECT_DECODE_MAX_BLOCKS and (w.table != TABLE_PACKED_ROPE or w.G <= 8)
         if select_decode is None:
             self.select_decode_ok = supported and self.P <= SELECT_DECODE_AUTO_MAX_SPLITS
         else:
@@ -480,6 +481,13 @@ class DecodeSession:
         self.step_index = t
         return t
 
+    @property
+    def runs_select_decode(self) -> bool:
+        """Whether step() makes the selection and the decode in one launch
+        (nosa_select_decode)."""
+        return (self.fused and not self.offload and not self.w.select_all and self.select_decode_ok
+                and not self.mass_on and not self.alibi_on)
+
     def use_buffers(self, t: int):
         """Point sel / prev at the buffers of step t."""
         if self.w.select_all:
@@ -508,7 +516,7 @@ class DecodeSession:
                     self.append(t)
                 self.swap_diff()
                 self.decode_combine(t)
-            elif self.select_decode_ok and not self.mass_on and not self.alibi_on:
+            elif self.runs_select_decode:
                 self.append_score(t)
                 self.select_decode(t)
             else:

@@ -338,19 +338,33 @@ nosa_status nosa_sparse_decode_alibi(const nosa_dims* dims, const uint16_t* q, c
  * a (b, h) pair makes the pair's selection from score_q / score_e into
  * on-chip memory, exactly as nosa_select_swap, and decodes its split of it;
  * the workgroup of split 0 also writes the selection, the new eviction
- * bitmap and the swap lists.  Results are bit-identical to
- * nosa_select_swap followed by nosa_sparse_decode_combine, except that the
- * bitmap is read from evicted_in and written to evicted_out:
+ * bitmap and the swap lists.  The selection, bitmap and swap lists are
+ * bit-identical to nosa_select_swap's, except that the bitmap is read from
+ * evicted_in and written to evicted_out; o, m, l are the same attention as
+ * nosa_sparse_decode_combine's over that selection, up to the order in
+ * which tiles are accumulated (m bit-identical).  How the splits divide
+ * the selection:
+ *   - when the eviction part keeps every block it has not dropped (all
+ *     steps but those where a new block competes [NOSA summary,
+ *     Methodology 1, locality guarantee]), split p takes the p-th of P
+ *     equal shares, in whole blocks, of the eviction part and of the query
+ *     part: eviction blocks [p n_e / P, (p+1) n_e / P) of its ascending
+ *     list and query blocks [p n_q / P, (p+1) n_q / P) of its own, where
+ *     n_e is the number of blocks below ceil(seq_len / block_size) clear in
+ *     evicted_in and n_q = min(k_q, nb - n_e) (integer division);
+ *   - otherwise split p takes the p-th contiguous chunk of the ascending
+ *     list, as nosa_sparse_decode_combine;
+ *   part_o / part_m / part_l then hold those splits' partials.
  *   evicted_in, evicted_out: uint32 [B][Hkv][ceil(max_blocks / 32)]; the
  *     same buffer is allowed only with num_splits == 1;
  *   score_q, score_e, seq_lens, k_e, k_q, sel .. evict_count: as
  *     nosa_select_swap (sel_cap <= max_blocks);
  *   q, num_splits, sm_scale, part_* , counters, o, m, l: as
- *     nosa_sparse_decode_combine.
- * Supported for the flat and two-level tables with
- * max_blocks <= NOSA_SELECT_DECODE_MAX_BLOCKS (NOSA_ERR_UNSUPPORTED
- * otherwise: make the two calls).                                         */
-#define NOSA_SELECT_DECODE_MAX_BLOCKS 1024
+ *     nosa_sparse_decode_combine (packed RoPE kind: q_pos and rope_base
+ *     in kv, and at most 8 query heads per KV head).
+ * Supported with max_blocks <= NOSA_SELECT_DECODE_MAX_BLOCKS
+ * (NOSA_ERR_UNSUPPORTED otherwise: make the two calls).                   */
+#define NOSA_SELECT_DECODE_MAX_BLOCKS 2304
 nosa_status nosa_select_decode(const nosa_dims* dims, const nosa_kv* kv, const uint16_t* q,
                                const float* score_q, const float* score_e, const int32_t* seq_lens,
                                int32_t k_e, int32_t k_q, const uint32_t* evicted_in, uint32_t* evicted_out,

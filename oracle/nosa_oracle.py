@@ -69,7 +69,7 @@ __all__ = [
     "recency_bucket",
     "buffer_retrieve",
     "tokens_of_blocks",
-    "split_chunks",
+    "split_chunks", "share_chunks",
     "attend",
     "merge_partials",
     "softmax_block_mass",
@@ -342,6 +342,20 @@ def split_chunks(sel: list[int], P: int) -> list[list[int]]:
     return [list(sel[p * c:(p + 1) * c]) if c else [] for p in range(P)]
 
 
+def share_chunks(gamma_e: list[int], gamma_q: list[int], P: int) -> list[list[int]]:
+    """Another split layout: chunk p holds the p-th of P equal shares, in
+    whole blocks, of each part of the selection, eviction blocks
+    gamma_e[p n_e / P : (p+1) n_e / P] then query blocks
+    gamma_q[p n_q / P : (p+1) n_q / P] (integer division).  READING: as for
+    split_chunks, the pages fix no layout; the fused select + decode uses
+    this one on steps where the eviction part keeps every block it has not
+    dropped, so that each split can start on its eviction share before the
+    query part is known."""
+    ne, nq = len(gamma_e), len(gamma_q)
+    return [list(gamma_e[p * ne // P:(p + 1) * ne // P]) + list(gamma_q[p * nq // P:(p + 1) * nq // P])
+            for p in range(P)]
+
+
 def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, bias: np.ndarray | None = None):
     """Softmax attention of each query row over the given keys/values.
 
@@ -477,19 +491,24 @@ def materialise(q_group, K, T, bs, rope=None):
     return rope_rotate(q_group, rope["q_pos"], rope["base"]), Kt
 
 
-def attend_blocks(qt, Kt, V, T, bs, blocks, num_splits, scale, alibi=None):
+def attend_blocks(qt, Kt, V, T, bs, blocks, num_splits, scale, alibi=None, chunks=None):
     """Attention of the group's query rows over the tokens of the given
-    blocks, split into contiguous chunks of the block list and unsplit
-    [NOVITA, attention modifications]: per-split (o, m, l) partials, the
-    merged (O, m, l) over every listed token, and, without ALiBi, each
-    block's softmax mass per query row.  qt, Kt as materialise() returns
-    them; alibi: None or the group's (G,) slopes, biasing by the distance
-    from the query at position T - 1."""
+    blocks, split into contiguous chunks of the block list (or the given
+    partition `chunks` of it: num_splits lists) and unsplit [NOVITA,
+    attention modifications]: per-split (o, m, l) partials, the merged
+    (O, m, l) over every listed token, and, without ALiBi, each block's
+    softmax mass per query row.  qt, Kt as materialise() returns them;
+    alibi: None or the group's (G,) slopes, biasing by the distance from the
+    query at position T - 1."""
     def bias(toks):
         return None if alibi is None else alibi_bias(alibi, T - 1, toks)
 
+    if chunks is None:
+        chunks = split_chunks(list(blocks), num_splits)
+    assert len(chunks) == num_splits and sorted(b for c in chunks for b in c) == sorted(blocks), \
+        "chunks must partition the block list"
     parts = []
-    for chunk in split_chunks(list(blocks), num_splits):
+    for chunk in chunks:
         toks = tokens_of_blocks(chunk, T, bs)
         parts.append(attend(qt, Kt[toks], V[toks], scale, bias(toks)))
     out = {"part_o": np.stack([p[0] for p in parts], axis=1),   # (G, P, D)

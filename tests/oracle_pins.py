@@ -706,11 +706,44 @@ def check_attend_blocks(O, seed=15):
     assert qt is q and Kt.shape == (T, D) and np.array_equal(Kt, K)
 
 
+def check_share_chunks(O, seed=16):
+    """The share layout, worked by hand: 5 eviction and 3 query blocks over
+    2 splits give eviction blocks [0, 2) and [2, 5) of the eviction list
+    and query blocks [0, 1) and [1, 3) of the query list; one block over 4
+    splits lands in the last.  attend_blocks over an explicit partition:
+    each partial is SDPA over its chunk's tokens, the merged result is the
+    unsplit one, and a list that is not a partition is refused."""
+    assert O.share_chunks([1, 4, 6, 9, 12], [2, 3, 20], 2) == [[1, 4, 2], [6, 9, 12, 3, 20]]
+    assert O.share_chunks([5], [], 4) == [[], [], [], [5]]
+    assert O.share_chunks([], [7, 8, 9], 3) == [[7], [8], [9]]
+    rng = np.random.default_rng(seed)
+    G, D, T, bs = 2, 8, 150, 16
+    q, K, V = rng.standard_normal((G, D)), rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    e, qq = [0, 2, 5, 9], [1, 7]  # block 9 holds the 6 tokens 144..149
+    blocks = sorted(e + qq)
+    chunks = O.share_chunks(e, qq, 3)
+    assert chunks == [[0], [2, 1], [5, 9, 7]]
+    r = O.attend_blocks(q, K, V, T, bs, blocks, 3, 0.4, chunks=chunks)
+    for p_, c in enumerate(chunks):
+        t_ = np.concatenate([np.arange(i * bs, min(i * bs + bs, T)) for i in c])
+        assert np.abs(r["part_o"][:, p_] - _sdpa(q, K[t_], V[t_], 0.4)).max() <= 1e-12
+    toks = np.concatenate([np.arange(i * bs, min(i * bs + bs, T)) for i in blocks])
+    for g in range(G):  # the share partials merge to attention over every listed token
+        Om, mm, lm = O.merge_partials(r["part_o"][g], r["part_m"][g], r["part_l"][g])
+        assert np.abs(Om - _sdpa(q[g:g + 1], K[toks], V[toks], 0.4)[0]).max() <= 1e-12
+    try:
+        O.attend_blocks(q, K, V, T, bs, blocks, 2, 0.4, chunks=[[0, 1], [2, 5]])
+    except AssertionError:
+        pass
+    else:
+        raise AssertionError("a partial cover was accepted")
+
+
 ALL_CHECKS = [
     check_attend_vs_sdpa, check_merge_vs_sdpa, check_split_chunks,
     check_pool_closed_form, check_pool_linearity, check_eviction_pre_exp,
     check_select_bruteforce, check_select_sizes, check_trajectory_invariants,
     check_swap_lists, check_place_blocks, check_buffer_retrieve, check_rope_complex, check_rope_identities,
     check_softmax_block_mass, check_alibi, check_rope_scores, check_index_inputs, check_prefill, check_step_dense_equivalence, check_step_sparse_subset, check_step_lazy_rope,
-    check_attend_blocks, check_bf16_decode,
+    check_attend_blocks, check_share_chunks, check_bf16_decode,
 ]

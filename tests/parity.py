@@ -176,10 +176,11 @@ class Gpu:
 
 
 def oracle_over(w: Workload, inp, lg: Logical, b: int, h: int, t: int, prev: list, blocks: list, P: int,
-                alibi: bool = False) -> dict:
+                alibi: bool = False, chunks: list | None = None) -> dict:
     """The oracle's swap lists and attention for a given selection (the
-    GPU's, after a near-tie): the same stages as oracle_step after the
-    selection, over `blocks`."""
+    GPU's, after a near-tie) and split layout (chunks: None for contiguous
+    chunks): the same stages as oracle_step after the selection, over
+    `blocks`."""
     T = w.seq_len(t)
     q = oracle.bf16_to_f64(inp.q(t)[b, h * w.G:(h + 1) * w.G])
     rope = None
@@ -187,17 +188,20 @@ def oracle_over(w: Workload, inp, lg: Logical, b: int, h: int, t: int, prev: lis
         rope = dict(q_pos=int(inp.q_pos[b]), block_start=synth.block_doc_start(w) * w.bs, base=w.rope_base)
     slopes = synth.alibi_slopes(w.Hq)[h * w.G:(h + 1) * w.G].astype(np.float64) if alibi else None
     qt, Kt = oracle.materialise(q, lg.K, T, w.bs, rope)
-    r = oracle.attend_blocks(qt, Kt, lg.V, T, w.bs, list(blocks), P, 1.0 / math.sqrt(w.D), slopes)
+    r = oracle.attend_blocks(qt, Kt, lg.V, T, w.bs, list(blocks), P, 1.0 / math.sqrt(w.D), slopes, chunks)
     r["load"], r["evict"] = oracle.swap_lists(prev, blocks)
     return r
 
 
 def compare_pair(w: Workload, inp, lg: Logical, g: Gpu, b: int, h: int, t: int, st: PairState,
-                 P: int, log: list, check_scores: bool = True, alibi: bool = False) -> dict:
+                 P: int, log: list, check_scores: bool = True, alibi: bool = False, shares: bool = False) -> dict:
     """Compare one pair at step t; returns the oracle result.  Selection
     mismatches must be near-ties (logged); the swap lists and attention are
     then compared with the oracle's over the GPU's selection (the two sides
-    attend over different blocks, each correctly)."""
+    attend over different blocks, each correctly).  shares: the step ran
+    the fused select + decode, whose splits take equal shares of the
+    eviction and query parts (oracle.share_chunks) on steps where the
+    eviction part keeps every block it has not dropped."""
     r = oracle_step(w, inp, lg, b, h, t, st, P, alibi)
     where = f"{w.name} t={t} b={b} h={h}"
     nb = r["nb"]
@@ -230,7 +234,12 @@ def compare_pair(w: Workload, inp, lg: Logical, g: Gpu, b: int, h: int, t: int, 
             assert same_sel, (where, "union", sel, r["sel"])
     else:
         assert same_sel, (where, "select_all", sel[:5], r["sel"][:5])
-    ra = r if same_sel else oracle_over(w, inp, lg, b, h, t, st.prev, sel, P, alibi)
+    chunks = None
+    if shares and P > 1 and not w.select_all:
+        cand = [i for i in range(nb) if i not in st.evicted]
+        if len(cand) <= w.k_e:  # the fast path: every candidate stays, in ascending order
+            chunks = oracle.share_chunks(cand, sorted(set(sel) - set(cand)), P)
+    ra = r if same_sel and chunks is None else oracle_over(w, inp, lg, b, h, t, st.prev, sel, P, alibi, chunks)
     nl, ne = int(g.load_count[b, h]), int(g.evict_count[b, h])
     assert g.load[b, h, :nl].tolist() == ra["load"], (where, "load")
     assert g.evict[b, h, :ne].tolist() == ra["evict"], (where, "evict")

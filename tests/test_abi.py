@@ -135,12 +135,17 @@ def test_host_checks_reject_bad_arguments():
                                     counters, fake, fake, fake, None)
     assert sdec(kv, ev_in=P(256), ev_out=P(256), splits=2) == nosa.NOSA_ERR_ARG  # shared bitmap, 2 splits
     assert sdec(kv, counters=None) == nosa.NOSA_ERR_ARG
-    big = nosa.make_dims(2, 8, 2, 128, 64, 16, 1025)
+    big = nosa.make_dims(2, 8, 2, 128, 64, 16, 2305)
     assert sdec(kv, dims=big) == nosa.NOSA_ERR_UNSUPPORTED  # capacity above the fused selection's
     rope = nosa.nosa_kv()
     rope.k_pages = rope.v_pages = rope.e_pages = ctypes.c_void_p(4096)
     rope.num_pages, rope.kind, rope.packed = 10, nosa.NOSA_TABLE_PACKED_ROPE, ctypes.c_void_p(4096)
-    assert sdec(rope) == nosa.NOSA_ERR_UNSUPPORTED
+    assert sdec(rope) == nosa.NOSA_ERR_ARG  # deferred RoPE without query positions
+    rope_g16 = nosa.nosa_kv()
+    rope_g16.k_pages = rope_g16.v_pages = rope_g16.e_pages = ctypes.c_void_p(4096)
+    rope_g16.num_pages, rope_g16.kind, rope_g16.packed = 10, nosa.NOSA_TABLE_PACKED_ROPE, ctypes.c_void_p(4096)
+    rope_g16.q_pos, rope_g16.rope_base = ctypes.c_void_p(4096), 10000.0
+    assert sdec(rope_g16, dims=nosa.make_dims(2, 32, 2, 128, 64, 16, 40)) == nosa.NOSA_ERR_UNSUPPORTED  # G = 16
     # softmax score step: workspace and output required, no packed RoPE kind
     def mdec(kvd, stats=fake, mass=fake):
         return L.nosa_sparse_decode_mass(D(d), fake, D(kvd), fake, fake, 8, fake, 1, 0.1, fake, fake, fake, fake,
