@@ -75,6 +75,9 @@ def parse(argv=None):
     ap.add_argument("--qkv", action="store_true",
                     help="the step's input is each sequence's fused projection row: nosa_append_score_qkv "
                          "(QKV split + eviction head + pooling + scoring in one launch)")
+    ap.add_argument("--probe-matrix", action="store_true",
+                    help="after the warm-up, run the page-gather probe matrix over the current selection and "
+                         "print it as one JSON line (no step timing)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with one plain 1 GiB device copy, a known-size kernel for counter calibration")
     return ap.parse_args(argv)
@@ -317,6 +320,59 @@ def practical_ceilings(sess, flush, stream, reps: int = 10) -> dict:
     return out
 
 
+def probe_matrix(sess, flush, stream, reps: int = 10) -> list:
+    """The page-gather probe over the current selection's pages (flat
+    tables, selections of at most 256 pages) in several arrangements, to
+    tell what bounds the decode's gather: the same pages with 4, 8 and 16
+    waves per CU (one K and one V page in flight per wave, so 4, 8 or 16
+    page pairs in flight per CU: each pair's list cut into 1, 2 or 4
+    lists); each list in ascending page order; and a compact pool (the
+    selected pages renumbered 0, 1, ... in list order, then in a random
+    order), which reads the same number of pages from a region the size of
+    the selection instead of the whole pool.  Median of `reps` cold runs."""
+    import numpy as np
+    import torch
+    from block_sparse_kv_score_amd import nosa
+
+    sel = sess.sel.long()
+    if sess.table is None or sel.shape[-1] > 256 or not bool((sess.sel_count == sel.shape[-1]).all()):
+        raise SystemExit("--probe-matrix needs a flat table and full selections of at most 256 blocks")
+    pages = torch.gather(sess.table.long(), 2, sel).reshape(-1, sel.shape[-1])
+    K, V = sess.k_pages, sess.v_pages
+    page_bytes = K.shape[1] * K.element_size()
+
+    def gather(plist, label):
+        plist = plist.to(torch.int32).contiguous()
+        assert int(plist.min()) >= 0 and int(plist.max()) < K.shape[0]
+        sink = torch.zeros(plist.shape[0], dtype=torch.int32, device=K.device)
+        evs = []
+        for _ in range(reps):
+            flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            nosa.nosa_probe_page_gather(K, V, plist, sink, stream)
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        t = float(np.median([a.elapsed_time(b) for a, b in evs])) / 1e3
+        nbytes = plist.numel() * 2 * page_bytes
+        print(f"[bench] probe {label}: {nbytes / t / 1e9:.1f} GB/s", file=sys.stderr, flush=True)
+        return {"arrangement": label, "lists": list(plist.shape), "us": round(t * 1e6, 2),
+                "gbps": round(nbytes / t / 1e9, 1), "bytes": int(nbytes)}
+
+    n_pairs, n_sel = pages.shape
+    out = []
+    for cut in (1, 2, 4):
+        if n_sel % cut == 0:
+            out.append(gather(pages.reshape(n_pairs * cut, n_sel // cut), f"selection, {4 * cut} waves/CU"))
+    out.append(gather(pages.sort(dim=1).values, "selection, each list ascending, 4 waves/CU"))
+    compact = torch.arange(pages.numel(), device=K.device).reshape(pages.shape)
+    out.append(gather(compact, "compact pool, list order, 4 waves/CU"))
+    perm = torch.randperm(pages.numel(), device=K.device, generator=torch.Generator(device=K.device).manual_seed(1))
+    out.append(gather(perm.reshape(pages.shape), "compact pool, random order, 4 waves/CU"))
+    return out
+
+
 def main(argv=None) -> int:
     args = parse(argv)
     if args.gpus != 1:
@@ -361,6 +417,9 @@ def main(argv=None) -> int:
         flush()
         sess.step(next_t())
     torch.cuda.synchronize()
+    if args.probe_matrix:
+        print(json.dumps({"workload": w.name, "probe_matrix": probe_matrix(sess, flush, stream)}))
+        return 0
     if args.graph:
         if W < 2:
             raise SystemExit("--graph needs at least two warm-up steps")

@@ -93,12 +93,26 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// Data that other workgroups of the same launch read back.  Device-scope
-// (agent) atomic stores are made visible across every XCD's L2 before they
-// complete, and device-scope atomic loads never hit a stale L2 line, so a
-// producer needs only to wait for its stores to complete (s_waitcnt
-// vmcnt(0)) before it signals, and no L2 write-back or invalidate is
-// needed on either side.
+// Data that other workgroups of the same launch read back (the split
+// partials of the fused combine, the tile statistics of the softmax score
+// step).  The rule this relies on, in ISA terms: the compiler's AMDGPU
+// memory model for the gfx942 family (gfx950 included) lowers a relaxed
+// agent-scope atomic store or load to a single global_store / global_load
+// with the sc1 (agent-scope coherence) bit set and no cache maintenance
+// around it -- the sc1 bit alone makes that location's accesses coherent
+// across the device's L1s and the L2s of all XCDs.  The decode's code is
+// `global_store_dword ... sc1` for the partials, `global_atomic_add ...
+// sc0` (old value returned) for the arrival counter and `global_load_dword
+// ... sc1` for the read-back.  The protocol: every wave of a producer waits
+// for vmcnt(0), i.e. until its sc1 stores have completed, then the
+// workgroup barrier, then one thread adds to the counter; the workgroup
+// that gets P - 1 back issues its sc1 loads only after that atomic has
+// returned (its value decides the branch).  A completed sc1 store is seen
+// by every later sc1 load of the same location anywhere on the device, so
+// the last workgroup reads every partial.  The C++ orderings are relaxed
+// on purpose: the wait orders the accesses; a release / acquire pair would
+// add an L2 write-back (buffer_wbl2 sc1) and invalidate (buffer_inv sc1)
+// that data written and read only through sc1 accesses does not need.
 __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
