@@ -27,6 +27,9 @@ struct Table {
   int32_t* err;
 };
 
+// The table descriptor of a call (defined with the index kernels).
+Table make_table(const nosa_dims& d, const nosa_kv& kv);
+
 __device__ __forceinline__ void flag_error(int32_t* err) {
   if (err) atomicOr(err, 1);
 }

@@ -1,19 +1,18 @@
 // Internal launchers, one per kernel family.  Arguments are already checked
 // by the C-ABI layer (nosa_api.cpp); each launcher only picks the template
-// instance and enqueues the kernel on `stream`.
+// instance and enqueues the kernel on `stream`.  Host-only declarations (the
+// HIP runtime API, no device code), so the C-ABI layer also builds as plain
+// C++ with a host compiler.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 #include "nosa.h"
-#include "nosa_device.hpp"
 
 namespace nosa {
 
 constexpr int kMaxRetrieveSlots = 1024;  // resident slots per (b, h) in the host-tier retrieve
-
-Table make_table(const nosa_dims& d, const nosa_kv& kv);
 
 hipError_t launch_prefill(const nosa_dims& d, const nosa_kv& kv, const uint16_t* k_src,
                           const uint16_t* v_src, const float* e_src, int32_t src_tokens,

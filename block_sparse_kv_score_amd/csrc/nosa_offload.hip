@@ -26,6 +26,7 @@
 //      in host memory since the previous retrieve get those tokens copied
 //      (or, without the previous lengths, the tail block whole).
 
+#include "nosa_device.hpp"
 #include "nosa_launch.hpp"
 
 namespace nosa {

@@ -27,6 +27,7 @@
 // log2 units; causal mask t <= n; keys past the context are masked and their
 // V entries zeroed (0 * stale NaN would leak through the MFMA).
 
+#include "nosa_device.hpp"
 #include "nosa_launch.hpp"
 
 namespace nosa {

@@ -14,6 +14,7 @@
 // words), written to sink[workgroup], so no load can be dropped and the host
 // can check that every byte was read.
 
+#include "nosa_device.hpp"
 #include "nosa_launch.hpp"
 
 namespace nosa {

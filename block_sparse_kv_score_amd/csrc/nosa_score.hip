@@ -23,6 +23,7 @@
 // block max is a DPP max over the nsub lanes of a block.  The kernel
 // is bound by HBM bandwidth: 4 * D bytes per sub-block plus 4 bytes of logit.
 
+#include "nosa_device.hpp"
 #include "nosa_launch.hpp"
 
 namespace nosa {
