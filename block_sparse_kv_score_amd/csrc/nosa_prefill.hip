@@ -15,10 +15,13 @@
 // gfx950 mapping.  Workgroup = 8 waves = one (b, KV head) and 128 query
 // columns (a column is a (prompt position, head of the group) pair); wave w
 // owns 16 columns.  Keys stream in 64-token tiles that all eight waves share
-// through LDS (eight waves rather than four halve the tile loads, stores and
-// barriers per column; the register file holds two waves per SIMD, so one
-// workgroup per CU) (loaded with 16-byte loads into registers one tile ahead, then
-// stored to LDS).  Both products run on v_mfma_f32_16x16x32_bf16 as in the
+// through a double-buffered LDS tile (eight waves rather than four halve the
+// tile loads and stores per column; the register file holds two waves per
+// SIMD, so one workgroup per CU): tile t + 1, loaded into registers while
+// tile t - 1 was used, is stored into the other buffer after tile t's
+// products, one workgroup barrier per tile.  Workgroups are placed
+// XCD-aware: the workgroups of one (b, KV head) run on one XCD, so its K and
+// V stream from that XCD's L2 after the first reader.  Both products run on v_mfma_f32_16x16x32_bf16 as in the
 // decode: S^T = K . Q^T with the key rows as the A operand straight from the
 // K page layout, and O^T += V^T . P with V^T rows from the V page layout and
 // the tile's bf16 probabilities (one LDS round trip) as the B operand.  The
@@ -41,12 +44,14 @@ constexpr int kPfCols = 16;  // query columns per wave
 // distinct LDS banks (a 128-byte pitch would put every other column on the
 // same banks).
 constexpr int kPfPitch = kPfTile + 8;
+constexpr int kPfXcds = 8;  // XCDs: consecutive workgroups go to consecutive XCDs
 constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr float kPfLn2 = 0.6931471805599453f;
 
 struct PrefillArgs {
   Table t;
   int Hq, bs, M;
+  int n_pairs, n_chunks;  // (b, KV head) pairs and 128-column chunks per pair
   float scale_log2;
   double rope_base;
   const uint16_t* q;  // [B][M][Hq][D], unrotated
@@ -61,10 +66,10 @@ struct PrefillArgs {
 
 template <int D>
 struct PrefillSmem {
-  uint4 k[D / 8][kPfTile];                     // K tile, page layout [D/8][64][8]
-  uint4 v[kPfTile / 8][D];                     // V tile, page layout [64/8][D][8]
+  uint4 k[2][D / 8][kPfTile];                  // K tiles, page layout [D/8][64][8]
+  uint4 v[2][kPfTile / 8][D];                  // V tiles, page layout [64/8][D][8]
   uint16_t p[kPfWaves][kPfCols][kPfPitch];     // bf16 probabilities, per wave
-  float cs[D / 2][2];                          // cos, sin of st * theta_k
+  float cs[2][D / 2][2];                       // cos, sin of st * theta_k, per buffer
 };
 
 typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
@@ -90,6 +95,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// 2^x with the hardware's v_exp_f32 alone: results below 2^-126 flush to
+// zero (probabilities that small are nothing beside the row's sum), where
+// exp2f spends four more instructions on keeping them.
+__device__ __forceinline__ float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // fp32 rounded to bf16 (nearest even) and back.
 __device__ __forceinline__ float round_bf16(float x) { return (float)(__bf16)x; }
 
@@ -112,14 +122,20 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
   __shared__ PrefillSmem<D> sh;
 
   const Table& t = a.t;
-  const int bh = blockIdx.y;
+  // XCD-aware placement: workgroup i runs on XCD i % 8; the workgroups of
+  // one XCD take consecutive (pair, chunk) slots, so a pair's chunks share
+  // an L2.  Slots past the last return at once (the whole workgroup).
+  const int total = a.n_pairs * a.n_chunks, per_xcd = (total + kPfXcds - 1) / kPfXcds;
+  const int slot = (int)(blockIdx.x % kPfXcds) * per_xcd + (int)(blockIdx.x / kPfXcds);
+  if (slot >= total) return;
+  const int bh = slot / a.n_chunks, chunk = slot % a.n_chunks;
   const int Hkv = t.Hkv;
   const int b = bh / Hkv, h = bh % Hkv;
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int lq = lane >> 4, lr = lane & 15;
   const int bs = a.bs;
   const int T = min(max(a.seq_lens[b], 0), t.max_blocks * bs);
-  const int m0 = blockIdx.x * (kPfWaves * PPW);
+  const int m0 = chunk * (kPfWaves * PPW);
   const int mi = m0 + w * PPW + lr / G;
   const int g = lr % G;
   const bool col_ok = mi < a.M;
@@ -130,7 +146,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
   const int ntile = last_key >= 0 ? (int)(last_key / kPfTile) + 1 : 0;
 
   // Rot(n) q for this lane's column and dims 32 c + 8 lq + e, in fp32
-  // (float64 angles, once)
+  // (float64 angles, once), times the score scale in log2 units: the
+  // rotation is linear, so q.k then comes out in the softmax's units
   float qn[NCH][8];
   {
     const uint16_t* qp = a.q + (((int64_t)b * a.M + min(mi, a.M - 1)) * a.Hq + (int64_t)h * G + g) * D;
@@ -143,8 +160,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
         const double th = pow(a.rope_base, -2.0 * (double)d / (double)D);
         double sv, cv;
         sincos((double)n * th, &sv, &cv);
-        qn[c][e] = (float)(x1 * cv - x2 * sv);
-        qn[c + NCH / 2][e] = (float)(x2 * cv + x1 * sv);
+        qn[c][e] = (float)((x1 * cv - x2 * sv) * (double)a.scale_log2);
+        qn[c + NCH / 2][e] = (float)((x2 * cv + x1 * sv) * (double)a.scale_log2);
       }
     }
   }
@@ -181,20 +198,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
     }
   };
 
-  int64_t page = -1, st = 0, cur_st = -1;
-  if (ntile > 0) {
-    tile_page(0, page, st);
-    if (page < 0 && threadIdx.x == 0) flag_error(t.err);
-    fetch(0, page);
-  }
-  for (int tile = 0; tile < ntile; ++tile) {
+  // the registers of tile `tile` into LDS buffer `buf` (V past the context zeroed)
+  auto stage = [&](int tile, int buf) {
     const int key0 = tile * kPfTile;
-    const bool tile_ok = page >= 0;
-    __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int j = 0; j < KU; ++j) {
       const int u = threadIdx.x + j * kPfThreads;
-      sh.k[u / kPfTile][u % kPfTile] = kr[j];
+      sh.k[buf][u / kPfTile][u % kPfTile] = kr[j];
     }
 #pragma unroll
     for (int j = 0; j < VU; ++j) {
@@ -212,31 +222,54 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
         x.z &= mk[2];
         x.w &= mk[3];
       }
-      sh.v[ko][u % D] = x;
+      sh.v[buf][ko][u % D] = x;
     }
-    const bool new_doc = st != cur_st;
-    if (new_doc && threadIdx.x < D / 2) {
+  };
+  // cos, sin of st * theta_k into table `buf` (threads < D/2)
+  auto rotation_table = [&](int64_t st, int buf) {
+    if (threadIdx.x < D / 2) {
       double sv, cv;
       sincos((double)st * theta_k, &sv, &cv);
-      sh.cs[threadIdx.x][0] = (float)cv;
-      sh.cs[threadIdx.x][1] = (float)sv;
+      sh.cs[buf][threadIdx.x][0] = (float)cv;
+      sh.cs[buf][threadIdx.x][1] = (float)sv;
     }
-    __syncthreads();  // the tile and the document's rotation table
-    const int64_t this_st = st;
-    if (tile + 1 < ntile) {  // the next tile's loads, in flight during this one
-      tile_page(tile + 1, page, st);
+  };
+
+  // prologue: tile 0 in buffer 0 with its rotation table, tile 1 in flight
+  int64_t page = -1, st = 0;         // the tile in the registers
+  int64_t st_cur = -1, st_next = 0;  // document starts of tiles t and t + 1
+  bool ok_next = false;              // tile t + 1 resolvable
+  if (ntile > 0) {
+    tile_page(0, page, st);
+    if (page < 0 && threadIdx.x == 0) flag_error(t.err);
+    fetch(0, page);
+    stage(0, 0);
+    rotation_table(st, 0);
+    st_next = st;
+    ok_next = page >= 0;
+    if (ntile > 1) {
+      tile_page(1, page, st);
       if (page < 0 && threadIdx.x == 0) flag_error(t.err);
-      fetch(tile + 1, page);
+      fetch(1, page);
     }
-    if (new_doc) {  // Rot(n - st) q = Rot(-st) Rot(n) q, split into bf16 hi + lo
-      cur_st = this_st;
+  }
+  __syncthreads();
+
+  int64_t rot_st = -1;  // the document start qhi / qlo are rotated for
+  for (int tile = 0; tile < ntile; ++tile) {
+    const int buf = tile & 1;
+    const int key0 = tile * kPfTile;
+    const bool tile_ok = ok_next;
+    st_cur = st_next;
+    if (st_cur != rot_st) {  // Rot(n - st) q = Rot(-st) Rot(n) q, split into bf16 hi + lo
+      rot_st = st_cur;
       float hi[NCH][8], lo[NCH][8];
 #pragma unroll
       for (int c = 0; c < NCH / 2; ++c) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int d = 32 * c + 8 * lq + e;
-          const float cv = sh.cs[d][0], sv = sh.cs[d][1];
+          const float cv = sh.cs[buf][d][0], sv = sh.cs[buf][d][1];
           const float x1 = qn[c][e], x2 = qn[c + NCH / 2][e];
           const float r1 = x1 * cv + x2 * sv, r2 = x2 * cv - x1 * sv;
           hi[c][e] = round_bf16(r1);
@@ -256,22 +289,33 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
     // inside the context and at or before every column's position (all but
     // the last few) needs no mask.
     const bool full = tile_ok && key0 + kPfTile <= T && (int64_t)(key0 + kPfTile - 1) <= p0 + m0;
+    // chunk-major order: the four key slices' accumulators are independent,
+    // so consecutive MFMAs do not wait on each other's results
+    pf_floatx4 acc[4];
+#pragma unroll
+    for (int th = 0; th < 4; ++th) acc[th] = pf_floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      uint4 ka[4];
+#pragma unroll
+      for (int th = 0; th < 4; ++th) ka[th] = sh.k[buf][4 * c + lq][16 * th + lr];
+#pragma unroll
+      for (int th = 0; th < 4; ++th) acc[th] = pf_mfma(ka[th], qhi[c], acc[th]);
+#pragma unroll
+      for (int th = 0; th < 4; ++th) acc[th] = pf_mfma(ka[th], qlo[c], acc[th]);
+    }
     float sv[4][4];
 #pragma unroll
-    for (int th = 0; th < 4; ++th) {
-      pf_floatx4 acc = pf_floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int th = 0; th < 4; ++th)
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const uint4 ka = sh.k[4 * c + lq][16 * th + lr];
-        acc = pf_mfma(ka, qhi[c], acc);
-        acc = pf_mfma(ka, qlo[c], acc);
-      }
+      for (int e = 0; e < 4; ++e) sv[th][e] = acc[th][e];
+    if (!full) {  // (uniform) key 16 th + 4 lq + e is visible iff 16 th + e <= lim
+      const int64_t lim64 = min((int64_t)T - 1, n) - (key0 + 4 * lq);
+      const int lim = tile_ok ? (int)max(min(lim64, (int64_t)kPfTile), (int64_t)-1) : -1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = key0 + 16 * th + 4 * lq + e;
-        const bool ok = full || (tile_ok && key < T && (int64_t)key <= n);
-        sv[th][e] = ok ? acc[e] * a.scale_log2 : -INFINITY;
-      }
+      for (int th = 0; th < 4; ++th)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[th][e] = 16 * th + e <= lim ? sv[th][e] : -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -280,7 +324,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
       for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sv[th][e]);
     mx = xor_reduce<16, kWave>(mx, [](float x, float y) { return fmaxf(x, y); });
     const float mn = fmaxf(m_run, mx);
-    const float alpha = mn == -INFINITY ? 1.f : exp2f(m_run - mn);
+    // a column with every key so far masked has mn = -inf: exponents are then
+    // taken against 0 (masked scores are -inf, so they still give 0 and no
+    // NaN arises; alpha = 0 scales an all-zero accumulator)
+    const float mz = mn == -INFINITY ? 0.f : mn;
+    const float alpha = pf_exp2(m_run - mz);
     m_run = mn;
     float psum = 0.f;
 #pragma unroll
@@ -288,7 +336,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
       float pv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pv[e] = mn == -INFINITY ? 0.f : exp2f(sv[th][e] - mn);
+        pv[e] = pf_exp2(sv[th][e] - mz);
         psum += pv[e];
       }
       const uint32_t w0 = pack_bf16x2(pv[0], pv[1]);
@@ -296,8 +344,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
       *reinterpret_cast<uint2*>(&sh.p[w][lr][16 * th + 4 * lq]) = make_uint2(w0, w1);
     }
     l_run = l_run * alpha + psum;
+    if (__ballot(alpha != 1.f) != 0) {  // (a product with 1 changes nothing)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+    }
     wave_lds_sync();
 
     // O^T (dims x columns) += V^T (dims x keys) . P (keys x columns)
@@ -305,8 +355,24 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
     for (int ks = 0; ks < 2; ++ks) {
       const uint4 pb = *reinterpret_cast<const uint4*>(&sh.p[w][lr][32 * ks + 8 * lq]);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) oacc[dt] = pf_mfma(sh.v[4 * ks + lq][16 * dt + lr], pb, oacc[dt]);
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] = pf_mfma(sh.v[buf][4 * ks + lq][16 * dt + lr], pb, oacc[dt]);
     }
+
+    // tile + 1 (in the registers) into the other buffer, with its rotation
+    // table where its document differs from tile's (read only there, as
+    // every wave's rotation); tile + 2's loads go out
+    if (tile + 1 < ntile) {
+      ok_next = page >= 0;
+      stage(tile + 1, buf ^ 1);
+      st_next = st;
+      if (st_next != st_cur) rotation_table(st_next, buf ^ 1);
+      if (tile + 2 < ntile) {
+        tile_page(tile + 2, page, st);
+        if (page < 0 && threadIdx.x == 0) flag_error(t.err);
+        fetch(tile + 2, page);
+      }
+    }
+    __syncthreads();  // buffer buf ^ 1 and its table complete; buffer buf free
   }
 
   // column totals: l over the lanes that share the column
@@ -356,7 +422,10 @@ hipError_t launch_prefill_attention(const nosa_dims& d, const nosa_kv& kv, const
   a.l = l;
   const int G = d.n_q_heads / d.n_kv_heads;
   const int rows_per_wg = kPfWaves * (kPfCols / G);
-  const dim3 grid((n_prompt + rows_per_wg - 1) / rows_per_wg, d.batch * d.n_kv_heads);
+  a.n_chunks = (n_prompt + rows_per_wg - 1) / rows_per_wg;
+  a.n_pairs = d.batch * d.n_kv_heads;
+  const int64_t total = (int64_t)a.n_chunks * a.n_pairs;
+  const dim3 grid((unsigned)((total + kPfXcds - 1) / kPfXcds * kPfXcds));
   if (d.head_dim == 128)
     launch_prefill_d<128>(grid, a, G, stream);
   else
