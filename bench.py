@@ -43,6 +43,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_llama3_8b_32k.json
 CSRC = os.path.join(ROOT, "block_sparse_kv_score_amd", "csrc")
 # the sources the decode kernel (and its select variant) is built from
 DECODE_SRCS = [os.path.join(CSRC, f) for f in ("nosa_decode.hip", "nosa_select_impl.hpp", "nosa_device.hpp")]
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic_lazy_prefill_33k.json")
+# the sources the prefill kernel is built from
+PREFILL_SRCS = [os.path.join(CSRC, f) for f in ("nosa_prefill.hip", "nosa_device.hpp")]
 
 
 def parse(argv=None):
@@ -245,7 +248,19 @@ def bench_prefill(args, w) -> int:
     flops = prefill_flops(w)
     tflops = flops / t / 1e12
     kv_bytes = w.B * w.Hkv * w.T0 * 4 * w.D  # every cached K and V byte once
+    if args.copy_calibration:  # a plain 1 GiB device copy, to scale memory counters by
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(w, inp, args.cpu_seconds)
+    traffic = None  # counter bytes per launch, while the kernel is the one they were taken on
+    if os.path.exists(PREFILL_TRAFFIC_FILE):
+        tr = json.load(open(PREFILL_TRAFFIC_FILE))
+        if tr.get("prefill_sources_sha256_16") == source_hash(PREFILL_SRCS) and tr.get("workload") == w.name:
+            traffic = tr.get("bytes_per_launch")
     out = {
         "metric": f"prefill tokens/s over reused documents, deferred RoPE ({w.name})",
         "value": round(w.B * w.prompt / t, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -256,7 +271,7 @@ def bench_prefill(args, w) -> int:
                    "block": w.bs, "parallelism": "single GPU"},
         "step_ms_p10_p90": [round(float(np.percentile(ms, 10)), 4), round(float(np.percentile(ms, 90)), 4)],
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "nosa_prefill_attention (prefill_rope_kernel)",
                      "algorithmic_flops_per_launch": flops, "avg_launch_us": round(float(np.mean(ms)) * 1e3, 2)},
         "hbm_gbps_kv_once": round(kv_bytes / t / 1e9, 1),
