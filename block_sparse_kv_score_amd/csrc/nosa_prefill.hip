@@ -15,20 +15,24 @@
 // gfx950 mapping.  Workgroup = 8 waves = one (b, KV head) and 128 query
 // columns (a column is a (prompt position, head of the group) pair); wave w
 // owns 16 columns.  Keys stream in 64-token tiles that all eight waves share
-// through a double-buffered LDS tile (eight waves rather than four halve the
-// tile loads and stores per column; the register file holds two waves per
-// SIMD, so one workgroup per CU): tile t + 1, loaded into registers while
-// tile t - 1 was used, is stored into the other buffer after tile t's
-// products, one workgroup barrier per tile.  Workgroups are placed
-// XCD-aware: the workgroups of one (b, KV head) run on one XCD, so its K and
-// V stream from that XCD's L2 after the first reader.  Both products run on v_mfma_f32_16x16x32_bf16 as in the
-// decode: S^T = K . Q^T with the key rows as the A operand straight from the
-// K page layout, and O^T += V^T . P with V^T rows from the V page layout and
-// the tile's bf16 probabilities (one LDS round trip) as the B operand.  The
-// rotated query is split into bf16 hi + lo parts (two MFMAs per chunk) so the
-// rotation costs no precision beyond ~2^-16.  Online softmax per column in
-// log2 units; causal mask t <= n; keys past the context are masked and their
-// V entries zeroed (0 * stale NaN would leak through the MFMA).
+// through LDS (eight waves rather than four halve the tile loads per column;
+// the register file holds two waves per SIMD, so one workgroup per CU).
+// Tile t + 1 goes from memory straight into the other of two LDS buffers
+// (global_load_lds, no registers and no LDS stores) while tile t is
+// computed, and is waited for just before the one barrier per tile; the
+// pages of a run of 512 tiles are looked up together into LDS beforehand, so
+// no tile waits on a table lookup.  Workgroups are placed XCD-aware: the
+// workgroups of one (b, KV head) run on one XCD, so its K and V stream from
+// that XCD's L2 after the first reader.  Both products run on
+// v_mfma_f32_16x16x32_bf16 as in the decode: S^T = K . Q^T with the key rows
+// as the A operand straight from the K page layout, and O^T += V^T . P with
+// V^T rows from the V page layout and the tile's bf16 probabilities as the B
+// operand, moved from the S^T accumulator layout into the operand layout by
+// lane swaps in registers.  The rotated query is split into bf16 hi + lo
+// parts (two MFMAs per chunk) so the rotation costs no precision beyond
+// ~2^-16.  Online softmax per column in log2 units; causal mask t <= n; keys
+// past the context are masked and their V entries zeroed (0 * stale NaN
+// would leak through the MFMA).
 
 #include "nosa_device.hpp"
 #include "nosa_launch.hpp"
@@ -39,12 +43,9 @@ constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfTile = 64;  // keys per tile
 constexpr int kPfCols = 16;  // query columns per wave
-// Row pitch of the per-wave probability tile, in bf16: 64 keys + 8 of
-// padding, so the 16 lanes of a row group (one column each) fall on
-// distinct LDS banks (a 128-byte pitch would put every other column on the
-// same banks).
-constexpr int kPfPitch = kPfTile + 8;
 constexpr int kPfXcds = 8;  // XCDs: consecutive workgroups go to consecutive XCDs
+// s_waitcnt vmcnt(0) alone (expcnt and lgkmcnt at their maxima)
+constexpr int kVmcntZero = 0x0F70;
 constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr float kPfLn2 = 0.6931471805599453f;
 
@@ -65,12 +66,32 @@ struct PrefillArgs {
 };
 
 template <int D>
-struct PrefillSmem {
-  uint4 k[2][D / 8][kPfTile];                  // K tiles, page layout [D/8][64][8]
-  uint4 v[2][kPfTile / 8][D];                  // V tiles, page layout [64/8][D][8]
-  uint16_t p[kPfWaves][kPfCols][kPfPitch];     // bf16 probabilities, per wave
-  float cs[2][D / 2][2];                       // cos, sin of st * theta_k, per buffer
+struct PrefillShared {
+  float cs[2][D / 2][2];                    // cos, sin of st * theta_k, per tile buffer
+  int2 pt[kPfThreads];                      // (page, document start in blocks) of a run of tiles
 };
+// One K and one V tile buffer.  Each buffer is a __shared__ variable of its
+// own, so the compiler can tell the direct loads into one buffer from the
+// reads of the other and does not wait for those loads before the reads.
+template <int D>
+struct PrefillKTile {
+  uint4 u[D / 8][kPfTile];  // page layout [D/8][64][8]
+};
+template <int D>
+struct PrefillVTile {
+  uint4 u[kPfTile / 8][D];  // page layout [64/8][D][8]
+};
+template <int B>
+struct PfBuf {
+  static constexpr int value = B;
+};
+template <int B, class X>
+__device__ __forceinline__ X& pf_pick(X& x0, X& x1) {
+  if constexpr (B == 0)
+    return x0;
+  else
+    return x1;
+}
 
 typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float pf_floatx4 __attribute__((ext_vector_type(4)));
@@ -78,12 +99,6 @@ typedef float pf_floatx4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ pf_floatx4 pf_mfma(const uint4& a, const uint4& b, const pf_floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pf_bf16x8, a), __builtin_bit_cast(pf_bf16x8, b),
                                                  c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint4 pf_load(const uint4* p) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 typedef __bf16 pf_bf16x2 __attribute__((ext_vector_type(2)));
@@ -119,7 +134,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
   constexpr int VU = (kPfTile / 8) * D / kPfThreads;  // V tile units per thread
   static_assert(KU >= 1 && VU >= 1, "tile units per thread");
   static_assert(kPfCols % G == 0, "G divides 16");
-  __shared__ PrefillSmem<D> sh;
+  __shared__ PrefillShared<D> sh;
+  __shared__ PrefillKTile<D> k0, k1;
+  __shared__ PrefillVTile<D> v0, v1;
 
   const Table& t = a.t;
   // XCD-aware placement: workgroup i runs on XCD i % 8; the workgroups of
@@ -173,46 +190,73 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = pf_floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // tile -> page and document start (tokens); page < 0: unresolvable
+  // Page and document start of tiles [c kPfThreads, (c + 1) kPfThreads),
+  // one tile per thread, into the LDS run table: one memory round trip per
+  // kPfThreads tiles instead of a dependent lookup per tile.  An
+  // unresolvable tile raises the error flag and gets page -1.
+  auto resolve_run = [&](int c) {
+    const int tile = c * kPfThreads + (int)threadIdx.x;
+    int2 e = make_int2(-1, 0);
+    if (tile < ntile) {
+      uint32_t docb = 0;
+      const int64_t pg = page_of<NOSA_TABLE_PACKED_ROPE>(t, bh, tile * kPfTile / bs, docb);
+      if (pg < 0) flag_error(t.err);
+      e = make_int2((int)pg, (int)docb);
+    }
+    sh.pt[threadIdx.x] = e;
+  };
+  // tile -> page and document start (tokens) from the run table; page < 0:
+  // unresolvable
   auto tile_page = [&](int tile, int64_t& page, int64_t& st) {
-    const int i = tile * kPfTile / bs;
-    uint32_t docb = 0;
-    page = page_of<NOSA_TABLE_PACKED_ROPE>(t, bh, i, docb);
-    st = (int64_t)docb * bs;
+    const int2 e = sh.pt[tile % kPfThreads];
+    page = e.x;
+    st = (int64_t)(uint32_t)e.y * bs;
   };
-  uint4 kr[KU], vr[VU];
-  auto fetch = [&](int tile, int64_t page) {
+  // Tile `tile` of page `page` straight from memory into the tile buffers
+  // kd, vd (global_load_lds: lane l of a wave writes the 16 bytes at the
+  // wave's LDS base + 16 l, so the 64 units of one wave-instruction,
+  // consecutive in the page layout, land consecutively); an unresolvable
+  // tile is zero-filled.  The data is in LDS once this wave's vector-memory
+  // count reaches zero.
+  auto fetch_lds = [&](int tile, int64_t page, PrefillKTile<D>& kd, PrefillVTile<D>& vd) {
     const int sub = (tile * kPfTile % bs) / kPfTile;
-    const uint4* kp = reinterpret_cast<const uint4*>(a.k_pages + page * (int64_t)bs * D);
-    const uint4* vp = reinterpret_cast<const uint4*>(a.v_pages + page * (int64_t)bs * D);
+    uint4* kdu = &kd.u[0][0];
+    uint4* vdu = &vd.u[0][0];
+    if (page >= 0) {
+      const uint4* kp = reinterpret_cast<const uint4*>(a.k_pages + page * (int64_t)bs * D);
+      const uint4* vp = reinterpret_cast<const uint4*>(a.v_pages + page * (int64_t)bs * D);
 #pragma unroll
-    for (int j = 0; j < KU; ++j) {
-      const int u = threadIdx.x + j * kPfThreads;
-      kr[j] = page >= 0 ? pf_load(kp + (int64_t)(u / kPfTile) * bs + sub * kPfTile + u % kPfTile)
-                        : make_uint4(0, 0, 0, 0);
-    }
+      for (int j = 0; j < KU; ++j) {
+        const int u = threadIdx.x + j * kPfThreads;
+        __builtin_amdgcn_global_load_lds(kp + (int64_t)(u / kPfTile) * bs + sub * kPfTile + u % kPfTile,
+                                         (__attribute__((address_space(3))) void*)(kdu + (u - lane)), 16, 0, 0);
+      }
 #pragma unroll
-    for (int j = 0; j < VU; ++j) {
-      const int u = threadIdx.x + j * kPfThreads;
-      vr[j] = page >= 0 ? pf_load(vp + (int64_t)(sub * 8 + u / D) * D + u % D) : make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < VU; ++j) {
+        const int u = threadIdx.x + j * kPfThreads;
+        __builtin_amdgcn_global_load_lds(vp + (int64_t)(sub * 8 + u / D) * D + u % D,
+                                         (__attribute__((address_space(3))) void*)(vdu + (u - lane)), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KU; ++j) kdu[threadIdx.x + j * kPfThreads] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < VU; ++j) vdu[threadIdx.x + j * kPfThreads] = make_uint4(0, 0, 0, 0);
     }
   };
-
-  // the registers of tile `tile` into LDS buffer `buf` (V past the context zeroed)
-  auto stage = [&](int tile, int buf) {
+  // After the wait: V of keys past the context zeroed (0 * stale NaN would
+  // leak through the MFMA), in the units this thread loaded; only a tile
+  // that reaches past the context has any.
+  auto mask_tail = [&](int tile, PrefillVTile<D>& vd) {
     const int key0 = tile * kPfTile;
-#pragma unroll
-    for (int j = 0; j < KU; ++j) {
-      const int u = threadIdx.x + j * kPfThreads;
-      sh.k[buf][u / kPfTile][u % kPfTile] = kr[j];
-    }
+    if (key0 + kPfTile <= T) return;  // (uniform)
 #pragma unroll
     for (int j = 0; j < VU; ++j) {
       const int u = threadIdx.x + j * kPfThreads;
       const int ko = u / D;
-      uint4 x = vr[j];
       const int nv = min(max(T - (key0 + 8 * ko), 0), 8);  // present keys of this unit
       if (nv < 8) {
+        uint4 x = vd.u[ko][u % D];
         uint32_t mk[4];
 #pragma unroll
         for (int jd = 0; jd < 4; ++jd)
@@ -221,8 +265,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
         x.y &= mk[1];
         x.z &= mk[2];
         x.w &= mk[3];
+        vd.u[ko][u % D] = x;
       }
-      sh.v[buf][ko][u % D] = x;
     }
   };
   // cos, sin of st * theta_k into table `buf` (threads < D/2)
@@ -234,30 +278,36 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
       sh.cs[buf][threadIdx.x][1] = (float)sv;
     }
   };
+  auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(kVmcntZero); };
 
-  // prologue: tile 0 in buffer 0 with its rotation table, tile 1 in flight
-  int64_t page = -1, st = 0;         // the tile in the registers
+  // prologue: tile 0 in buffer 0 with its rotation table
+  int64_t page = -1, st = 0;         // page and document start of the tile being loaded
   int64_t st_cur = -1, st_next = 0;  // document starts of tiles t and t + 1
   bool ok_next = false;              // tile t + 1 resolvable
+  resolve_run(0);
+  __syncthreads();
   if (ntile > 0) {
     tile_page(0, page, st);
-    if (page < 0 && threadIdx.x == 0) flag_error(t.err);
-    fetch(0, page);
-    stage(0, 0);
+    fetch_lds(0, page, k0, v0);
     rotation_table(st, 0);
     st_next = st;
     ok_next = page >= 0;
-    if (ntile > 1) {
-      tile_page(1, page, st);
-      if (page < 0 && threadIdx.x == 0) flag_error(t.err);
-      fetch(1, page);
-    }
+    wait_loads();
+    mask_tail(0, v0);
   }
   __syncthreads();
 
   int64_t rot_st = -1;  // the document start qhi / qlo are rotated for
-  for (int tile = 0; tile < ntile; ++tile) {
-    const int buf = tile & 1;
+
+  // Tile `tile`, in buffer B: tile + 1's loads go out into the other buffer
+  // first (its last reader finished before the barrier that ended the
+  // previous tile) and are waited for at the end, before the barrier.
+  auto tile_step = [&](int tile, auto bufc) {
+    constexpr int B = decltype(bufc)::value;
+    PrefillKTile<D>& kc = pf_pick<B>(k0, k1);
+    PrefillVTile<D>& vc = pf_pick<B>(v0, v1);
+    PrefillKTile<D>& kn = pf_pick<B>(k1, k0);
+    PrefillVTile<D>& vn = pf_pick<B>(v1, v0);
     const int key0 = tile * kPfTile;
     const bool tile_ok = ok_next;
     st_cur = st_next;
@@ -269,7 +319,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int d = 32 * c + 8 * lq + e;
-          const float cv = sh.cs[buf][d][0], sv = sh.cs[buf][d][1];
+          const float cv = sh.cs[B][d][0], sv = sh.cs[B][d][1];
           const float x1 = qn[c][e], x2 = qn[c + NCH / 2][e];
           const float r1 = x1 * cv + x2 * sv, r2 = x2 * cv - x1 * sv;
           hi[c][e] = round_bf16(r1);
@@ -283,6 +333,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
         qhi[c] = pack_bf16x8(hi[c]);
         qlo[c] = pack_bf16x8(lo[c]);
       }
+    }
+    if (tile + 1 < ntile) {
+      tile_page(tile + 1, page, st);
+      fetch_lds(tile + 1, page, kn, vn);
     }
 
     // S^T: rows = keys 16 th + 4 lq + e of the tile, column lr.  A tile
@@ -298,7 +352,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
     for (int c = 0; c < NCH; ++c) {
       uint4 ka[4];
 #pragma unroll
-      for (int th = 0; th < 4; ++th) ka[th] = sh.k[buf][4 * c + lq][16 * th + lr];
+      for (int th = 0; th < 4; ++th) ka[th] = kc.u[4 * c + lq][16 * th + lr];
 #pragma unroll
       for (int th = 0; th < 4; ++th) acc[th] = pf_mfma(ka[th], qhi[c], acc[th]);
 #pragma unroll
@@ -311,7 +365,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
       for (int e = 0; e < 4; ++e) sv[th][e] = acc[th][e];
     if (!full) {  // (uniform) key 16 th + 4 lq + e is visible iff 16 th + e <= lim
       const int64_t lim64 = min((int64_t)T - 1, n) - (key0 + 4 * lq);
-      const int lim = tile_ok ? (int)max(min(lim64, (int64_t)kPfTile), (int64_t)-1) : -1;
+      const int lim = (int)max(min(lim64, (int64_t)kPfTile), (int64_t)-1) | -(int)!tile_ok;
 #pragma unroll
       for (int th = 0; th < 4; ++th)
 #pragma unroll
@@ -331,6 +385,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
     const float alpha = pf_exp2(m_run - mz);
     m_run = mn;
     float psum = 0.f;
+    uint32_t pa[4], pb2[4];  // bf16 pairs: keys 16 th + 4 lq + (0, 1) and (2, 3), column lr
 #pragma unroll
     for (int th = 0; th < 4; ++th) {
       float pv[4];
@@ -339,40 +394,54 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
         pv[e] = pf_exp2(sv[th][e] - mz);
         psum += pv[e];
       }
-      const uint32_t w0 = pack_bf16x2(pv[0], pv[1]);
-      const uint32_t w1 = pack_bf16x2(pv[2], pv[3]);
-      *reinterpret_cast<uint2*>(&sh.p[w][lr][16 * th + 4 * lq]) = make_uint2(w0, w1);
+      pa[th] = pack_bf16x2(pv[0], pv[1]);
+      pb2[th] = pack_bf16x2(pv[2], pv[3]);
     }
     l_run = l_run * alpha + psum;
     if (__ballot(alpha != 1.f) != 0) {  // (a product with 1 changes nothing)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
     }
-    wave_lds_sync();
 
-    // O^T (dims x columns) += V^T (dims x keys) . P (keys x columns)
+    // O^T (dims x columns) += V^T (dims x keys) . P (keys x columns).  The B
+    // operand of keys 32 ks .. 32 ks + 31 wants keys 32 ks + 8 lq + (0..7) of
+    // column lr in lane (lq, lr): those sit in rows 2 (lq % 2) and
+    // 2 (lq % 2) + 1 of slice th = 2 ks + lq / 2.  Swapping rows 2, 3 of
+    // slice 2 ks with rows 0, 1 of slice 2 ks + 1, then the odd rows of the
+    // first result with the even rows of the second, leaves the first
+    // register with rows (0, 2) of each slice and the second with rows
+    // (1, 3): the operand's dwords 0 and 2 (dwords 1 and 3 from the (2, 3)
+    // pairs).
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const uint4 pb = *reinterpret_cast<const uint4*>(&sh.p[w][lr][32 * ks + 8 * lq]);
+      const auto a32 = __builtin_amdgcn_permlane32_swap(pa[2 * ks], pa[2 * ks + 1], false, false);
+      const auto a16 = __builtin_amdgcn_permlane16_swap(a32[0], a32[1], false, false);
+      const auto b32 = __builtin_amdgcn_permlane32_swap(pb2[2 * ks], pb2[2 * ks + 1], false, false);
+      const auto b16 = __builtin_amdgcn_permlane16_swap(b32[0], b32[1], false, false);
+      const uint4 pb = make_uint4(a16[0], b16[0], a16[1], b16[1]);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) oacc[dt] = pf_mfma(sh.v[buf][4 * ks + lq][16 * dt + lr], pb, oacc[dt]);
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] = pf_mfma(vc.u[4 * ks + lq][16 * dt + lr], pb, oacc[dt]);
     }
 
-    // tile + 1 (in the registers) into the other buffer, with its rotation
-    // table where its document differs from tile's (read only there, as
-    // every wave's rotation); tile + 2's loads go out
+    // tile + 1 complete in the other buffer, with its rotation table where
+    // its document differs from tile's (read only there, as every wave's
+    // rotation); the next run of tile pages before its first lookup
     if (tile + 1 < ntile) {
       ok_next = page >= 0;
-      stage(tile + 1, buf ^ 1);
       st_next = st;
-      if (st_next != st_cur) rotation_table(st_next, buf ^ 1);
-      if (tile + 2 < ntile) {
-        tile_page(tile + 2, page, st);
-        if (page < 0 && threadIdx.x == 0) flag_error(t.err);
-        fetch(tile + 2, page);
+      if (st_next != st_cur) rotation_table(st_next, 1 - B);
+      wait_loads();
+      mask_tail(tile + 1, vn);
+      if ((tile + 2) % kPfThreads == 0 && tile + 2 < ntile) {  // (uniform)
+        __syncthreads();  // every lookup in the current run done
+        resolve_run((tile + 2) / kPfThreads);
       }
     }
-    __syncthreads();  // buffer buf ^ 1 and its table complete; buffer buf free
+    __syncthreads();  // tile + 1 and its table complete; this tile's buffer free
+  };
+  for (int tile = 0; tile < ntile; tile += 2) {
+    tile_step(tile, PfBuf<0>{});
+    if (tile + 1 < ntile) tile_step(tile + 1, PfBuf<1>{});
   }
 
   // column totals: l over the lanes that share the column

@@ -832,6 +832,34 @@ def test_prefill_one_token_prompt():
     run_prefill(w, seed=47)
 
 
+def test_prefill_unresolvable_page_flags_and_stays_finite():
+    # one context block's packed word names a page past the pool: the kernel
+    # flags the error, loads nothing from it (its tile is zero-filled and
+    # masked), and every other pair still matches the oracle
+    w = WORKLOADS["lazy_prefill_33k"].scaled(B=1, Hq=8, Hkv=2, T0=9 * 128, n_docs=9, doc_len=128, prompt=128)
+    announce("prefill with an unresolvable page: error flag, finite outputs")
+    inp = synth.generate(w, 49)
+    sess = session(w, inp)
+    bad_pair, bad_block = 1, 3  # (b, KV head) pair 1 = (0, 1)
+    packed = sess.packed.view(w.B * w.Hkv, w.max_blocks)
+    packed[bad_pair, bad_block] = (1 << 20) - 1  # page id 2^20 - 1 >= num_pages, document start 0
+    assert (1 << 20) - 1 >= w.num_pages
+    sess.prefill_attention()
+    torch.cuda.synchronize()
+    assert int(sess.err.item()) == 1
+    O, m, l = sess.pf_o.cpu().numpy(), sess.pf_m.cpu().numpy(), sess.pf_l.cpu().numpy()
+    assert np.isfinite(O).all() and np.isfinite(m).all() and np.isfinite(l).all()
+    # pair 0 never reads the bad entry: it matches the oracle as usual
+    qp = synth.prefill_queries(w, inp.seed)
+    starts = synth.block_doc_start(w) * w.bs
+    lg = logical_pair(inp, 0, 0)
+    q = oracle.bf16_to_f64(qp[0][:, 0:w.G])
+    Ow, mw, lw = oracle.prefill_attention_bh(q, lg.K, lg.V, w.T0, w.T0 - w.prompt, starts, w.bs,
+                                              w.rope_base, w.sm_scale)
+    assert np.abs(O[0][:, 0:w.G] - Ow).max() <= 1e-2
+    assert np.abs(m[0][:, 0:w.G] - mw).max() <= 1e-3
+
+
 def test_qkv_append_past_capacity_flags_and_keeps_length():
     from block_sparse_kv_score_amd import nosa
     w = WORKLOADS["tiny_nosa"].scaled(B=2, Hq=4, Hkv=2, T0=100)
