@@ -30,9 +30,12 @@
 // operand, moved from the S^T accumulator layout into the operand layout by
 // lane swaps in registers.  The rotated query is split into bf16 hi + lo
 // parts (two MFMAs per chunk) so the rotation costs no precision beyond
-// ~2^-16.  Online softmax per column in log2 units; causal mask t <= n; keys
-// past the context are masked and their V entries zeroed (0 * stale NaN
-// would leak through the MFMA).
+// ~2^-16.  Online softmax per column in log2 units: the q.k accumulators
+// start at minus the running max, so the scores arrive shifted and only a
+// tile that moves some column's max pays for a rescale; the column sums come
+// from the P.V product itself, with an all-ones operand in place of V^T.
+// Causal mask t <= n; keys past the context are masked and their V entries
+// zeroed (0 * stale NaN would leak through the MFMA).
 
 #include "nosa_device.hpp"
 #include "nosa_launch.hpp"
@@ -185,10 +188,15 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
   const double theta_k = threadIdx.x < D / 2 ? pow(a.rope_base, -2.0 * (double)threadIdx.x / (double)D) : 0.0;
 
   uint4 qhi[NCH], qlo[NCH];
-  float m_run = -INFINITY, l_run = 0.f;  // column lr, log2 units (l_run: this lane's keys)
+  float m_run = -INFINITY;  // column lr's running max, log2 units
   pf_floatx4 oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = pf_floatx4{0.f, 0.f, 0.f, 0.f};
+  // column lr's running sum of the bf16 probabilities, every element: the
+  // P.V product with an all-ones A operand sums each column over the keys
+  pf_floatx4 lacc = pf_floatx4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t one2 = 0x3F803F80u;  // bf16 (1, 1)
+  const uint4 ones = make_uint4(one2, one2, one2, one2);
 
   // Page and document start of tiles [c kPfThreads, (c + 1) kPfThreads),
   // one tile per thread, into the LDS run table: one memory round trip per
@@ -345,9 +353,12 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
     const bool full = tile_ok && key0 + kPfTile <= T && (int64_t)(key0 + kPfTile - 1) <= p0 + m0;
     // chunk-major order: the four key slices' accumulators are independent,
     // so consecutive MFMAs do not wait on each other's results
+    // The accumulators start at -ref, ref = the running max (0 before the
+    // column's first key), so the scores come out relative to it.
+    const float ref = m_run == -INFINITY ? 0.f : m_run;
     pf_floatx4 acc[4];
 #pragma unroll
-    for (int th = 0; th < 4; ++th) acc[th] = pf_floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int th = 0; th < 4; ++th) acc[th] = pf_floatx4{-ref, -ref, -ref, -ref};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       uint4 ka[4];
@@ -377,30 +388,31 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
 #pragma unroll
       for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sv[th][e]);
     mx = xor_reduce<16, kWave>(mx, [](float x, float y) { return fmaxf(x, y); });
-    const float mn = fmaxf(m_run, mx);
-    // a column with every key so far masked has mn = -inf: exponents are then
-    // taken against 0 (masked scores are -inf, so they still give 0 and no
-    // NaN arises; alpha = 0 scales an all-zero accumulator)
-    const float mz = mn == -INFINITY ? 0.f : mn;
-    const float alpha = pf_exp2(m_run - mz);
-    m_run = mn;
-    float psum = 0.f;
+    // The column's max moved when a key lies above ref, or at its first
+    // visible keys.  Only then (rare after the first tiles) are the scores
+    // shifted by d and the accumulators scaled by 2^-d (by 0 at the first
+    // keys: they hold nothing yet).
+    const bool moved = mx > 0.f || (m_run == -INFINITY && mx != -INFINITY);
+    if (__ballot(moved) != 0) {  // (uniform)
+      const float d = moved ? mx : 0.f;
+      const float alpha = m_run == -INFINITY ? 0.f : pf_exp2(-d);
+      if (moved) m_run = ref + d;
+#pragma unroll
+      for (int th = 0; th < 4; ++th)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[th][e] -= d;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+      lacc *= alpha;
+    }
     uint32_t pa[4], pb2[4];  // bf16 pairs: keys 16 th + 4 lq + (0, 1) and (2, 3), column lr
 #pragma unroll
     for (int th = 0; th < 4; ++th) {
       float pv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pv[e] = pf_exp2(sv[th][e] - mz);
-        psum += pv[e];
-      }
+      for (int e = 0; e < 4; ++e) pv[e] = pf_exp2(sv[th][e]);
       pa[th] = pack_bf16x2(pv[0], pv[1]);
       pb2[th] = pack_bf16x2(pv[2], pv[3]);
-    }
-    l_run = l_run * alpha + psum;
-    if (__ballot(alpha != 1.f) != 0) {  // (a product with 1 changes nothing)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
     }
 
     // O^T (dims x columns) += V^T (dims x keys) . P (keys x columns).  The B
@@ -421,6 +433,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
       const uint4 pb = make_uint4(a16[0], b16[0], a16[1], b16[1]);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) oacc[dt] = pf_mfma(vc.u[4 * ks + lq][16 * dt + lr], pb, oacc[dt]);
+      lacc = pf_mfma(ones, pb, lacc);
     }
 
     // tile + 1 complete in the other buffer, with its rotation table where
@@ -444,8 +457,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
     if (tile + 1 < ntile) tile_step(tile + 1, PfBuf<1>{});
   }
 
-  // column totals: l over the lanes that share the column
-  const float lsum = xor_reduce<16, kWave>(l_run, [](float x, float y) { return x + y; });
+  // column totals
+  const float lsum = lacc[0];
   if (col_ok) {
     const int64_t row = ((int64_t)b * a.M + mi) * a.Hq + (int64_t)h * G + g;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
