@@ -226,30 +226,39 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
   // consecutive in the page layout, land consecutively); an unresolvable
   // tile is zero-filled.  The data is in LDS once this wave's vector-memory
   // count reaches zero.
+  // This thread's units of a tile: K unit u = tid + 512 j is row u / 64 =
+  // w + 8 j, key u % 64 = lane of the page's [D/8][bs][8] layout; V unit u
+  // sits u units into the tile's slice of the [bs/8][D][8] layout.  The byte
+  // offsets do not change from tile to tile; only the page base does.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  uint32_t koff[KU], voff[VU];
+#pragma unroll
+  for (int j = 0; j < KU; ++j) koff[j] = (uint32_t)(((wu + (kPfThreads / kPfTile) * j) * bs + lane) * 16);
+#pragma unroll
+  for (int j = 0; j < VU; ++j) voff[j] = (uint32_t)((threadIdx.x + j * kPfThreads) * 16);
   auto fetch_lds = [&](int tile, int64_t page, PrefillKTile<D>& kd, PrefillVTile<D>& vd) {
     const int sub = (tile * kPfTile % bs) / kPfTile;
-    uint4* kdu = &kd.u[0][0];
-    uint4* vdu = &vd.u[0][0];
+    uint4* kdu = &kd.u[0][0] + kWave * wu;  // this wave's 64 units, then every 512
+    uint4* vdu = &vd.u[0][0] + kWave * wu;
     if (page >= 0) {
-      const uint4* kp = reinterpret_cast<const uint4*>(a.k_pages + page * (int64_t)bs * D);
-      const uint4* vp = reinterpret_cast<const uint4*>(a.v_pages + page * (int64_t)bs * D);
+      const char* kb =
+          reinterpret_cast<const char*>(a.k_pages + page * (int64_t)bs * D) + (int64_t)sub * kPfTile * 16;
+      const char* vb = reinterpret_cast<const char*>(a.v_pages + page * (int64_t)bs * D) + (int64_t)sub * 8 * D * 16;
+      // (the source address goes in as a uint4 pointer: given a char
+      // pointer, the host pass drops the kernel's launch stub without a word)
 #pragma unroll
-      for (int j = 0; j < KU; ++j) {
-        const int u = threadIdx.x + j * kPfThreads;
-        __builtin_amdgcn_global_load_lds(kp + (int64_t)(u / kPfTile) * bs + sub * kPfTile + u % kPfTile,
-                                         (__attribute__((address_space(3))) void*)(kdu + (u - lane)), 16, 0, 0);
-      }
+      for (int j = 0; j < KU; ++j)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(kb + koff[j]),
+                                         (__attribute__((address_space(3))) void*)(kdu + j * kPfThreads), 16, 0, 0);
 #pragma unroll
-      for (int j = 0; j < VU; ++j) {
-        const int u = threadIdx.x + j * kPfThreads;
-        __builtin_amdgcn_global_load_lds(vp + (int64_t)(sub * 8 + u / D) * D + u % D,
-                                         (__attribute__((address_space(3))) void*)(vdu + (u - lane)), 16, 0, 0);
-      }
+      for (int j = 0; j < VU; ++j)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(vb + voff[j]),
+                                         (__attribute__((address_space(3))) void*)(vdu + j * kPfThreads), 16, 0, 0);
     } else {
 #pragma unroll
-      for (int j = 0; j < KU; ++j) kdu[threadIdx.x + j * kPfThreads] = make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < KU; ++j) kdu[lane + j * kPfThreads] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < VU; ++j) vdu[threadIdx.x + j * kPfThreads] = make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < VU; ++j) vdu[lane + j * kPfThreads] = make_uint4(0, 0, 0, 0);
     }
   };
   // After the wait: V of keys past the context zeroed (0 * stale NaN would
