@@ -31,9 +31,10 @@
 // query-aware score of a block in the document starting at position st is
 // taken with the group's mean query turned by (n - st): by linearity of the
 // rotation and the mean, Rot(n - st) qbar . kbar_stored equals the mean of
-// Rot(n) q_g . Rot(st) k over the sub-block.  Each wave keeps the rotated
-// mean query of each of its blocks in LDS (float64), computing a rotation
-// (one sincos per lane) only where the document changes.
+// Rot(n) q_g . Rot(st) k over the sub-block.  The workgroup turns the mean
+// query once per distinct document among its blocks (float64, one sincos
+// per lane; documents span many blocks, so usually once) and keeps the
+// results in LDS.
 //
 // QKV input (nosa_append_score_qkv; NOSA summary, Methodology 2: NOSI fuses
 // the eviction head, the QKV split and pooling into one kernel).  The new
@@ -80,11 +81,16 @@ struct FusedArgs {
   uint16_t* q_out;       // [B][Hq][D]
 };
 
-// The group's mean query turned by (n - start) for every block of this wave
-// (RoPE scoring): rq[w][bw][d] for block bw of wave w.
+// The group's mean query turned by (n - start) for each distinct document
+// among the workgroup's blocks (RoPE scoring): rq[r] for document r, didx
+// the document of each block, dst each document's start (blocks).
 template <int D, bool ROPE>
 struct RopeSmem {
-  double rq[kFusedThreads / kWave][kRopeBlocksPerWave][D];
+  double rq[kFusedThreads / kWave * kRopeBlocksPerWave][D];
+  uint32_t docb[kFusedThreads / kWave * kRopeBlocksPerWave];
+  int didx[kFusedThreads / kWave * kRopeBlocksPerWave];
+  uint32_t dst[kFusedThreads / kWave * kRopeBlocksPerWave];
+  int ndoc;
 };
 template <int D>
 struct RopeSmem<D, false> {};
@@ -206,7 +212,7 @@ constexpr bool kEarlySummary() {
 // projection rows.
 template <int D, int L, bool ROPE = false, bool QKV = false>
 __global__ __launch_bounds__(kFusedThreads)
-__attribute__((amdgpu_waves_per_eu(kEarlySummary<D, L, ROPE, QKV>() ? 8 : 1))) void append_score_kernel(const FusedArgs a) {
+__attribute__((amdgpu_waves_per_eu(kEarlySummary<D, L, ROPE, QKV>() || ROPE ? 8 : 1))) void append_score_kernel(const FusedArgs a) {
   constexpr int NQ = D / 4;
   constexpr int QL = NQ / L;
   constexpr int SPW = kWave / L;
@@ -286,7 +292,9 @@ __attribute__((amdgpu_waves_per_eu(kEarlySummary<D, L, ROPE, QKV>() ? 8 : 1))) v
   // registers allow (its append then adds one memory round trip, the older
   // tokens, instead of two), else after the append
   constexpr bool early = kEarlySummary<D, L, ROPE, QKV>();
-  if (work && (early || !lead)) load_summary();
+  // (the RoPE variant loads after its rotations, so that the loaded rows are
+  // not held across them)
+  if (!ROPE && work && (early || !lead)) load_summary();
   if (threadIdx.x < D) {
     double acc = 0;
 #pragma unroll
@@ -325,36 +333,42 @@ __attribute__((amdgpu_waves_per_eu(kEarlySummary<D, L, ROPE, QKV>() ? 8 : 1))) v
   __syncthreads();  // qbar, and the append's summary
 
   if constexpr (ROPE) {
-    // rotated mean query of each of this wave's blocks (document starts
-    // from the packed words; one rotation per document change)
-    if (work) {
-      const int nsb = SPW / nsub;  // blocks of this wave (<= kRopeBlocksPerWave)
-      const int blk0 = (s0 + w * SPW) / nsub;
-      uint32_t docw = 0;
-      if (lane < nsb && blk0 + lane < MB) {
-        (void)page_of<NOSA_TABLE_PACKED_ROPE>(t, bh, blk0 + lane, docw);
-      }
-      const double theta = lane < D / 2 ? pow(a.rope_base, -2.0 * (double)lane / (double)D) : 0.0;
-      const int64_t n = a.q_pos[b];
-      int64_t cur = -1;
-      for (int bw = 0; bw < nsb; ++bw) {
-        const int64_t st = (int64_t)__builtin_amdgcn_readlane((int)docw, bw) * bs;
-        if (lane < D / 2) {
-          if (st != cur) {
-            double sv, cv;
-            sincos((double)(n - st) * theta, &sv, &cv);
-            const double x1 = sh.qbar[lane], x2 = sh.qbar[lane + D / 2];
-            rsh.rq[w][bw][lane] = x1 * cv - x2 * sv;
-            rsh.rq[w][bw][lane + D / 2] = x2 * cv + x1 * sv;
-          } else {
-            rsh.rq[w][bw][lane] = rsh.rq[w][bw - 1][lane];
-            rsh.rq[w][bw][lane + D / 2] = rsh.rq[w][bw - 1][lane + D / 2];
-          }
-        }
-        cur = st;
-        wave_lds_sync();
-      }
+    // The rotated mean query once per distinct document among this
+    // workgroup's blocks (documents span many blocks: usually one), wave r %
+    // 4 turning document r, shared through LDS; `work` is uniform over the
+    // workgroup, so every thread meets the barriers.
+    constexpr int NBG = kFusedThreads / kWave * kRopeBlocksPerWave;  // >= SPG / nsub
+    const int nbg = SPG / nsub;
+    const int blkg = s0 / nsub;
+    if (work && w == 0) {
+      uint32_t docw = 0xffffffffu;  // past the table: a document of its own
+      if (lane < nbg && blkg + lane < MB) (void)page_of<NOSA_TABLE_PACKED_ROPE>(t, bh, blkg + lane, docw);
+      if (lane < NBG) rsh.docb[lane] = docw;
+      wave_lds_sync();
+      const bool first = lane < nbg && (lane == 0 || rsh.docb[lane - 1] != docw);
+      const uint64_t starts = __ballot(first);
+      if (lane < nbg) rsh.didx[lane] = __popcll(starts & ((2ull << lane) - 1ull)) - 1;
+      if (first) rsh.dst[__popcll(starts & ((1ull << lane) - 1ull))] = docw;
+      if (lane == 0) rsh.ndoc = __popcll(starts);
     }
+    __syncthreads();
+    if (work) {
+      const int ndoc = rsh.ndoc;
+      const int64_t n = a.q_pos[b];
+      for (int r = w; r < ndoc; r += kFusedThreads / kWave) {  // (uniform per wave)
+        if (lane < D / 2) {
+          const double theta = pow(a.rope_base, -2.0 * (double)lane / (double)D);
+          const int64_t st = (int64_t)rsh.dst[r] * bs;
+          double sv, cv;
+          sincos((double)(n - st) * theta, &sv, &cv);
+          const double x1 = sh.qbar[lane], x2 = sh.qbar[lane + D / 2];
+          rsh.rq[r][lane] = x1 * cv - x2 * sv;
+          rsh.rq[r][lane + D / 2] = x2 * cv + x1 * sv;
+        }
+      }
+      load_summary();
+    }
+    __syncthreads();
   }
 
   if (work) {
@@ -367,7 +381,7 @@ __attribute__((amdgpu_waves_per_eu(kEarlySummary<D, L, ROPE, QKV>() ? 8 : 1))) v
     const bool valid = i < nb && i * bs + j * ss < T;
     double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
     if constexpr (ROPE) {
-      const double* rq = rsh.rq[w][(lane % SPW) / nsub];
+      const double* rq = rsh.rq[rsh.didx[(w * SPW + lane % SPW) / nsub]];
 #pragma unroll
       for (int u = 0; u < QL; ++u) {
         const int d = 4 * (part * QL + u);

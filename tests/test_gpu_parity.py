@@ -323,6 +323,16 @@ def test_lazy_rope_sparse_g8_split():
     run_trajectory(w, seed=40)
 
 
+@pytest.mark.parametrize("doc_len", [64, 128])
+def test_lazy_rope_sparse_short_docs(doc_len):
+    # documents of one or two blocks: a scoring workgroup's 16 blocks span 16
+    # or 8 documents, so its waves turn the mean query for several each
+    n_docs = 2048 // doc_len
+    w = WORKLOADS["lazy_rope_sparse_32k"].scaled(B=2, Hq=8, Hkv=2, T0=2048, doc_len=doc_len, n_docs=n_docs,
+                                                   k_e=4, k_q=8)
+    run_trajectory(w, seed=41)
+
+
 def test_lazy_rope_g8_and_g1():
     for hq in (16, 2):
         w = WORKLOADS["lazy_rope_32k"].scaled(B=1, Hq=hq, Hkv=2, T0=4 * 256, doc_len=256, n_docs=4)
