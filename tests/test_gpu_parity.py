@@ -783,6 +783,8 @@ PREFILL_CASES = [
     ("G8", dict(B=1, Hq=16, Hkv=2, T0=5 * 256, n_docs=5, doc_len=256, prompt=256)),
     ("G1", dict(B=1, Hq=2, Hkv=2, T0=9 * 128, n_docs=9, doc_len=128, prompt=128)),
     ("D64-bs128", dict(B=1, Hq=8, Hkv=2, D=64, bs=128, ss=32, T0=5 * 256, n_docs=5, doc_len=256, prompt=200)),
+    ("G2", dict(B=1, Hq=4, Hkv=2, T0=9 * 128, n_docs=9, doc_len=128, prompt=128)),
+    ("G16-bs256", dict(B=1, Hq=32, Hkv=2, bs=256, ss=64, T0=5 * 256, n_docs=5, doc_len=256, prompt=256)),
 ]
 
 
