@@ -800,6 +800,14 @@ def test_prefill_full_size_sampled():
     run_prefill(w, seed=0, rows=[0, 1, 63, 64, 255, 511], pairs=[(0, 0), (3, 7)])
 
 
+def test_prefill_three_runs_of_tiles():
+    """A context of 1,300 tiles: the kernel looks the pages up in runs of
+    512 tiles, so this crosses two run boundaries (two reloads of the run
+    table), with documents of 640 tokens starting mid-run."""
+    w = WORKLOADS["lazy_prefill_33k"].scaled(B=1, Hq=8, Hkv=2, T0=130 * 640, n_docs=130, doc_len=640, prompt=640)
+    run_prefill(w, seed=50, rows=[0, 1, 300, 639], pairs=[(0, 1)])
+
+
 # ---------------------------------------------------------------------------
 # edge cases of the extensions: empty context, zero budgets, the widest
 # capacity, one-token prompts, appends past capacity
