@@ -391,7 +391,7 @@ def probe_matrix(sess, flush, stream, reps: int = 10) -> list:
 def main(argv=None) -> int:
     args = parse(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the decode path runs on one GPU only (asked for --gpus {args.gpus}); "
               "the per-(b, h) work shards without communication, see the design notes.", file=sys.stderr)
         return 2
 
