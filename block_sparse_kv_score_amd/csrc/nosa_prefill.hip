@@ -17,7 +17,7 @@
 // owns 16 columns.  Keys stream in 64-token tiles that all eight waves share
 // through LDS (eight waves rather than four halve the tile loads per column;
 // the register file holds two waves per SIMD, so one workgroup per CU).
-// Tile t + 1 goes from memory straight into the other of two LDS buffers
+// Tile t + 1 goes from memory straight into the next of three LDS buffers
 // (global_load_lds, no registers and no LDS stores) while tile t is
 // computed, and is waited for just before the one barrier per tile; the
 // pages of a run of 512 tiles are looked up together into LDS beforehand, so
@@ -28,7 +28,9 @@
 // as the A operand straight from the K page layout, and O^T += V^T . P with
 // V^T rows from the V page layout and the tile's bf16 probabilities as the B
 // operand, moved from the S^T accumulator layout into the operand layout by
-// lane swaps in registers.  The rotated query is split into bf16 hi + lo
+// lane swaps in registers.  Waves 4-7 run their P.V one tile late (from the
+// third buffer), so that the two waves sharing a SIMD are in different
+// phases rather than in step.  The rotated query is split into bf16 hi + lo
 // parts (two MFMAs per chunk) so the rotation costs no precision beyond
 // ~2^-16.  Online softmax per column in log2 units: the q.k accumulators
 // start at minus the running max, so the scores arrive shifted and only a
@@ -36,6 +38,8 @@
 // from the P.V product itself, with an all-ones operand in place of V^T.
 // Causal mask t <= n; keys past the context are masked and their V entries
 // zeroed (0 * stale NaN would leak through the MFMA).
+
+#include <type_traits>
 
 #include "nosa_device.hpp"
 #include "nosa_launch.hpp"
@@ -45,6 +49,7 @@ namespace nosa {
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfTile = 64;  // keys per tile
+constexpr int kPfBufs = 3;   // K and V tile buffers
 constexpr int kPfCols = 16;  // query columns per wave
 constexpr int kPfXcds = 8;  // XCDs: consecutive workgroups go to consecutive XCDs
 // s_waitcnt vmcnt(0) alone (expcnt and lgkmcnt at their maxima)
@@ -70,7 +75,7 @@ struct PrefillArgs {
 
 template <int D>
 struct PrefillShared {
-  float cs[2][D / 2][2];                    // cos, sin of st * theta_k, per tile buffer
+  float cs[kPfBufs][D / 2][2];              // cos, sin of st * theta_k, per tile buffer
   int2 pt[kPfThreads];                      // (page, document start in blocks) of a run of tiles
 };
 // One K and one V tile buffer.  Each buffer is a __shared__ variable of its
@@ -89,11 +94,13 @@ struct PfBuf {
   static constexpr int value = B;
 };
 template <int B, class X>
-__device__ __forceinline__ X& pf_pick(X& x0, X& x1) {
+__device__ __forceinline__ X& pf_pick(X& x0, X& x1, X& x2) {
   if constexpr (B == 0)
     return x0;
-  else
+  else if constexpr (B == 1)
     return x1;
+  else
+    return x2;
 }
 
 typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
@@ -138,8 +145,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
   static_assert(KU >= 1 && VU >= 1, "tile units per thread");
   static_assert(kPfCols % G == 0, "G divides 16");
   __shared__ PrefillShared<D> sh;
-  __shared__ PrefillKTile<D> k0, k1;
-  __shared__ PrefillVTile<D> v0, v1;
+  __shared__ PrefillKTile<D> k0, k1, k2;
+  __shared__ PrefillVTile<D> v0, v1, v2;
 
   const Table& t = a.t;
   // XCD-aware placement: workgroup i runs on XCD i % 8; the workgroups of
@@ -316,56 +323,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
 
   int64_t rot_st = -1;  // the document start qhi / qlo are rotated for
 
-  // Tile `tile`, in buffer B: tile + 1's loads go out into the other buffer
-  // first (its last reader finished before the barrier that ended the
-  // previous tile) and are waited for at the end, before the barrier.
-  auto tile_step = [&](int tile, auto bufc) {
-    constexpr int B = decltype(bufc)::value;
-    PrefillKTile<D>& kc = pf_pick<B>(k0, k1);
-    PrefillVTile<D>& vc = pf_pick<B>(v0, v1);
-    PrefillKTile<D>& kn = pf_pick<B>(k1, k0);
-    PrefillVTile<D>& vn = pf_pick<B>(v1, v0);
-    const int key0 = tile * kPfTile;
-    const bool tile_ok = ok_next;
-    st_cur = st_next;
-    if (st_cur != rot_st) {  // Rot(n - st) q = Rot(-st) Rot(n) q, split into bf16 hi + lo
-      rot_st = st_cur;
-      float hi[NCH][8], lo[NCH][8];
-#pragma unroll
-      for (int c = 0; c < NCH / 2; ++c) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 32 * c + 8 * lq + e;
-          const float cv = sh.cs[B][d][0], sv = sh.cs[B][d][1];
-          const float x1 = qn[c][e], x2 = qn[c + NCH / 2][e];
-          const float r1 = x1 * cv + x2 * sv, r2 = x2 * cv - x1 * sv;
-          hi[c][e] = round_bf16(r1);
-          hi[c + NCH / 2][e] = round_bf16(r2);
-          lo[c][e] = r1 - hi[c][e];
-          lo[c + NCH / 2][e] = r2 - hi[c + NCH / 2][e];
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        qhi[c] = pack_bf16x8(hi[c]);
-        qlo[c] = pack_bf16x8(lo[c]);
-      }
-    }
-    if (tile + 1 < ntile) {
-      tile_page(tile + 1, page, st);
-      fetch_lds(tile + 1, page, kn, vn);
-    }
-
-    // S^T: rows = keys 16 th + 4 lq + e of the tile, column lr.  A tile
-    // inside the context and at or before every column's position (all but
-    // the last few) needs no mask.
-    const bool full = tile_ok && key0 + kPfTile <= T && (int64_t)(key0 + kPfTile - 1) <= p0 + m0;
-    // chunk-major order: the four key slices' accumulators are independent,
-    // so consecutive MFMAs do not wait on each other's results
-    // The accumulators start at -ref, ref = the running max (0 before the
-    // column's first key), so the scores come out relative to it.
+  // S^T for one tile: rows = keys 16 th + 4 lq + e, column lr.  Chunk-major
+  // order: the four key slices' accumulators are independent, so
+  // consecutive MFMAs do not wait on each other's results.  The accumulators
+  // start at -ref, ref = the running max (0 before the column's first key),
+  // so the scores come out relative to it.
+  auto qk_tile = [&](PrefillKTile<D>& kc, pf_floatx4* acc) {
     const float ref = m_run == -INFINITY ? 0.f : m_run;
-    pf_floatx4 acc[4];
 #pragma unroll
     for (int th = 0; th < 4; ++th) acc[th] = pf_floatx4{-ref, -ref, -ref, -ref};
 #pragma unroll
@@ -378,6 +342,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
 #pragma unroll
       for (int th = 0; th < 4; ++th) acc[th] = pf_mfma(ka[th], qlo[c], acc[th]);
     }
+  };
+  // Online softmax of one tile's shifted scores: masks (only where `full` is
+  // false), the running max, the rescale of the accumulators when some
+  // column's max moved, and the bf16 probabilities in the P.V operand
+  // layout (pb[ks] for keys 32 ks .. 32 ks + 31).
+  auto softmax_tile = [&](const pf_floatx4* acc, int key0, bool tile_ok, bool full, uint4* pb) {
+    const float ref = m_run == -INFINITY ? 0.f : m_run;
     float sv[4][4];
 #pragma unroll
     for (int th = 0; th < 4; ++th)
@@ -423,10 +394,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
       pa[th] = pack_bf16x2(pv[0], pv[1]);
       pb2[th] = pack_bf16x2(pv[2], pv[3]);
     }
-
-    // O^T (dims x columns) += V^T (dims x keys) . P (keys x columns).  The B
-    // operand of keys 32 ks .. 32 ks + 31 wants keys 32 ks + 8 lq + (0..7) of
-    // column lr in lane (lq, lr): those sit in rows 2 (lq % 2) and
+    // The B operand of keys 32 ks .. 32 ks + 31 wants keys 32 ks + 8 lq +
+    // (0..7) of column lr in lane (lq, lr): those sit in rows 2 (lq % 2) and
     // 2 (lq % 2) + 1 of slice th = 2 ks + lq / 2.  Swapping rows 2, 3 of
     // slice 2 ks with rows 0, 1 of slice 2 ks + 1, then the odd rows of the
     // first result with the even rows of the second, leaves the first
@@ -439,19 +408,92 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
       const auto a16 = __builtin_amdgcn_permlane16_swap(a32[0], a32[1], false, false);
       const auto b32 = __builtin_amdgcn_permlane32_swap(pb2[2 * ks], pb2[2 * ks + 1], false, false);
       const auto b16 = __builtin_amdgcn_permlane16_swap(b32[0], b32[1], false, false);
-      const uint4 pb = make_uint4(a16[0], b16[0], a16[1], b16[1]);
+      pb[ks] = make_uint4(a16[0], b16[0], a16[1], b16[1]);
+    }
+  };
+  // O^T (dims x columns) += V^T (dims x keys) . P (keys x columns), and the
+  // column sums from the same P against an all-ones operand
+  auto pv_tile = [&](const uint4* pb, PrefillVTile<D>& vc) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) oacc[dt] = pf_mfma(vc.u[4 * ks + lq][16 * dt + lr], pb, oacc[dt]);
-      lacc = pf_mfma(ones, pb, lacc);
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] = pf_mfma(vc.u[4 * ks + lq][16 * dt + lr], pb[ks], oacc[dt]);
+      lacc = pf_mfma(ones, pb[ks], lacc);
+    }
+  };
+
+  // Tile `tile`, in buffer B: tile + 1's loads go out into buffer B + 1
+  // first (its last reader finished before the barrier that ended the
+  // previous tile) and are waited for at the end, before the barrier.
+  // Waves 4-7 share SIMDs with waves 0-3 (the dispatcher places waves w and
+  // w + 4 of a workgroup on one SIMD) and run the same steps one P.V behind
+  // (LAG): they start a tile with the previous tile's P.V, from
+  // buffer B - 1, and keep this tile's probabilities for the next.  The two
+  // waves of a SIMD are then in different phases (one's MFMAs beside the
+  // other's softmax) instead of in step.
+  uint4 p_prev[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  auto tile_step = [&](int tile, auto bufc, auto lagc) {
+    constexpr int B = decltype(bufc)::value;
+    constexpr bool LAG = decltype(lagc)::value;
+    PrefillKTile<D>& kc = pf_pick<B>(k0, k1, k2);
+    PrefillVTile<D>& vc = pf_pick<B>(v0, v1, v2);
+    PrefillKTile<D>& kn = pf_pick<(B + 1) % kPfBufs>(k0, k1, k2);
+    PrefillVTile<D>& vn = pf_pick<(B + 1) % kPfBufs>(v0, v1, v2);
+    if constexpr (LAG) {
+      if (tile > 0) pv_tile(p_prev, pf_pick<(B + kPfBufs - 1) % kPfBufs>(v0, v1, v2));
+    }
+    const int key0 = tile * kPfTile;
+    const bool tile_ok = ok_next;
+    st_cur = st_next;
+    if (st_cur != rot_st) {  // Rot(n - st) q = Rot(-st) Rot(n) q, split into bf16 hi + lo
+      rot_st = st_cur;
+      float hi[NCH][8], lo[NCH][8];
+#pragma unroll
+      for (int c = 0; c < NCH / 2; ++c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 32 * c + 8 * lq + e;
+          const float cv = sh.cs[B][d][0], sv = sh.cs[B][d][1];
+          const float x1 = qn[c][e], x2 = qn[c + NCH / 2][e];
+          const float r1 = x1 * cv + x2 * sv, r2 = x2 * cv - x1 * sv;
+          hi[c][e] = round_bf16(r1);
+          hi[c + NCH / 2][e] = round_bf16(r2);
+          lo[c][e] = r1 - hi[c][e];
+          lo[c + NCH / 2][e] = r2 - hi[c + NCH / 2][e];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        qhi[c] = pack_bf16x8(hi[c]);
+        qlo[c] = pack_bf16x8(lo[c]);
+      }
+    }
+    if (tile + 1 < ntile) {
+      tile_page(tile + 1, page, st);
+      fetch_lds(tile + 1, page, kn, vn);
     }
 
-    // tile + 1 complete in the other buffer, with its rotation table where
+    // A tile inside the context and at or before every column's position
+    // (all but the last few) needs no mask.
+    const bool full = tile_ok && key0 + kPfTile <= T && (int64_t)(key0 + kPfTile - 1) <= p0 + m0;
+    pf_floatx4 acc[4];
+    qk_tile(kc, acc);
+    uint4 pb[2];
+    softmax_tile(acc, key0, tile_ok, full, pb);
+    if constexpr (LAG) {
+      p_prev[0] = pb[0];
+      p_prev[1] = pb[1];
+    } else {
+      pv_tile(pb, vc);
+    }
+
+    // tile + 1 complete in the next buffer, with its rotation table where
     // its document differs from tile's (read only there, as every wave's
     // rotation); the next run of tile pages before its first lookup
     if (tile + 1 < ntile) {
       ok_next = page >= 0;
       st_next = st;
-      if (st_next != st_cur) rotation_table(st_next, 1 - B);
+      if (st_next != st_cur) rotation_table(st_next, (B + 1) % kPfBufs);
       wait_loads();
       mask_tail(tile + 1, vn);
       if ((tile + 2) % kPfThreads == 0 && tile + 2 < ntile) {  // (uniform)
@@ -459,11 +501,30 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
         resolve_run((tile + 2) / kPfThreads);
       }
     }
-    __syncthreads();  // tile + 1 and its table complete; this tile's buffer free
+    __syncthreads();  // tile + 1 and its table complete; buffer B - 1 free
   };
-  for (int tile = 0; tile < ntile; tile += 2) {
-    tile_step(tile, PfBuf<0>{});
-    if (tile + 1 < ntile) tile_step(tile + 1, PfBuf<1>{});
+  // the buffers rotate with period three, so each step names its buffers
+  // statically
+  auto run_tiles = [&](auto lagc) {
+    for (int tile = 0; tile < ntile; tile += kPfBufs) {
+      tile_step(tile, PfBuf<0>{}, lagc);
+      if (tile + 1 < ntile) tile_step(tile + 1, PfBuf<1>{}, lagc);
+      if (tile + 2 < ntile) tile_step(tile + 2, PfBuf<2>{}, lagc);
+    }
+  };
+  if (wu >= kPfWaves / 2) {
+    run_tiles(std::true_type{});
+    if (ntile > 0) {  // the last tile's P.V
+      const int lb = (ntile - 1) % kPfBufs;
+      if (lb == 0)
+        pv_tile(p_prev, v0);
+      else if (lb == 1)
+        pv_tile(p_prev, v1);
+      else
+        pv_tile(p_prev, v2);
+    }
+  } else {
+    run_tiles(std::false_type{});
   }
 
   // column totals
