@@ -33,8 +33,10 @@
 // phases rather than in step.  The rotated query is split into bf16 hi + lo
 // parts (two MFMAs per chunk) so the rotation costs no precision beyond
 // ~2^-16.  Online softmax per column in log2 units: the q.k accumulators
-// start at minus the running max, so the scores arrive shifted and only a
-// tile that moves some column's max pays for a rescale; the column sums come
+// start at minus a reference that trails the running max by at most 16
+// (probabilities below 2^16), so the scores arrive shifted and only a tile
+// that moves some column's max past that slack pays for a rescale; the exact
+// max is kept beside it for the outputs.  The column sums come
 // from the P.V product itself, with an all-ones operand in place of V^T.
 // Causal mask t <= n; keys past the context are masked and their V entries
 // zeroed (0 * stale NaN would leak through the MFMA).
@@ -56,6 +58,7 @@ constexpr int kPfXcds = 8;  // XCDs: consecutive workgroups go to consecutive XC
 constexpr int kVmcntZero = 0x0F70;
 constexpr float kPfLog2e = 1.4426950408889634f;
 constexpr float kPfLn2 = 0.6931471805599453f;
+constexpr float kPfShiftSlack = 16.f;  // log2 units
 
 struct PrefillArgs {
   Table t;
@@ -195,7 +198,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
   const double theta_k = threadIdx.x < D / 2 ? pow(a.rope_base, -2.0 * (double)threadIdx.x / (double)D) : 0.0;
 
   uint4 qhi[NCH], qlo[NCH];
-  float m_run = -INFINITY;  // column lr's running max, log2 units
+  // Column lr's reference for the shifted scores (log2 units) and its
+  // exact running max.  The reference moves only when a key lies more than
+  // kPfShiftSlack above it, so the probabilities stay below 2^kPfShiftSlack
+  // (far inside fp32 and bf16 range) and most tiles that raise a column's
+  // max skip the rescale; the exact max and the sum taken against it are
+  // what the column returns.
+  float m_run = -INFINITY;
+  float m_hi = -INFINITY;
   pf_floatx4 oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = pf_floatx4{0.f, 0.f, 0.f, 0.f};
@@ -368,11 +378,12 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
 #pragma unroll
       for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sv[th][e]);
     mx = xor_reduce<16, kWave>(mx, [](float x, float y) { return fmaxf(x, y); });
-    // The column's max moved when a key lies above ref, or at its first
-    // visible keys.  Only then (rare after the first tiles) are the scores
-    // shifted by d and the accumulators scaled by 2^-d (by 0 at the first
-    // keys: they hold nothing yet).
-    const bool moved = mx > 0.f || (m_run == -INFINITY && mx != -INFINITY);
+    // The reference moves when a key lies more than the slack above it, or
+    // at the column's first visible keys.  Only then (rare after the first
+    // tiles) are the scores shifted by d and the accumulators scaled by 2^-d
+    // (by 0 at the first keys: they hold nothing yet).
+    m_hi = fmaxf(m_hi, ref + mx);
+    const bool moved = mx > kPfShiftSlack || (m_run == -INFINITY && mx != -INFINITY);
     if (__ballot(moved) != 0) {  // (uniform)
       const float d = moved ? mx : 0.f;
       const float alpha = m_run == -INFINITY ? 0.f : pf_exp2(-d);
@@ -537,8 +548,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
 #pragma unroll
       for (int e = 0; e < 4; ++e) a.o[row * D + 16 * dt + 4 * lq + e] = oacc[dt][e] * inv;
     if (lq == 0) {
-      a.m[row] = lsum > 0.f ? m_run * kPfLn2 : -INFINITY;
-      a.l[row] = lsum;
+      // the sum against the exact max: m_run trails m_hi by at most the slack
+      a.m[row] = lsum > 0.f ? m_hi * kPfLn2 : -INFINITY;
+      a.l[row] = lsum > 0.f ? lsum * exp2f(m_run - m_hi) : lsum;
     }
   }
 }
