@@ -198,12 +198,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
   const double theta_k = threadIdx.x < D / 2 ? pow(a.rope_base, -2.0 * (double)threadIdx.x / (double)D) : 0.0;
 
   uint4 qhi[NCH], qlo[NCH];
-  // Column lr's reference for the shifted scores (log2 units) and its
-  // exact running max.  The reference moves only when a key lies more than
-  // kPfShiftSlack above it, so the probabilities stay below 2^kPfShiftSlack
-  // (far inside fp32 and bf16 range) and most tiles that raise a column's
-  // max skip the rescale; the exact max and the sum taken against it are
-  // what the column returns.
+  // Column lr's reference for the shifted scores (log2 units), and the
+  // exact running max over this lane's keys (the column's is reduced at the
+  // end).  The reference moves only when a key lies more than kPfShiftSlack
+  // above it, so the probabilities stay below 2^kPfShiftSlack (far inside
+  // fp32 and bf16 range) and most tiles that raise a column's max skip the
+  // rescale; the exact max and the sum taken against it are what the column
+  // returns.
   float m_run = -INFINITY;
   float m_hi = -INFINITY;
   pf_floatx4 oacc[NDT];
@@ -372,20 +373,24 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
 #pragma unroll
         for (int e = 0; e < 4; ++e) sv[th][e] = 16 * th + e <= lim ? sv[th][e] : -INFINITY;
     }
+    // This lane's max over its 16 scores.  The exact max is kept per lane
+    // (the column's is reduced once, at the end).  The reference moves when
+    // a key lies more than the slack above it, or at the column's first
+    // visible keys: a lane that sees either calls for the column maxima
+    // (a cross-lane reduction), and only then (rare after the first tiles)
+    // are the scores shifted by d and the accumulators scaled by 2^-d (by 0
+    // at the first keys: they hold nothing yet).
     float mx = -INFINITY;
 #pragma unroll
     for (int th = 0; th < 4; ++th)
 #pragma unroll
       for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sv[th][e]);
-    mx = xor_reduce<16, kWave>(mx, [](float x, float y) { return fmaxf(x, y); });
-    // The reference moves when a key lies more than the slack above it, or
-    // at the column's first visible keys.  Only then (rare after the first
-    // tiles) are the scores shifted by d and the accumulators scaled by 2^-d
-    // (by 0 at the first keys: they hold nothing yet).
     m_hi = fmaxf(m_hi, ref + mx);
-    const bool moved = mx > kPfShiftSlack || (m_run == -INFINITY && mx != -INFINITY);
-    if (__ballot(moved) != 0) {  // (uniform)
-      const float d = moved ? mx : 0.f;
+    const bool want = mx > kPfShiftSlack || (m_run == -INFINITY && mx != -INFINITY);
+    if (__ballot(want) != 0) {  // (uniform)
+      const float cm = xor_reduce<16, kWave>(mx, [](float x, float y) { return fmaxf(x, y); });
+      const bool moved = cm > kPfShiftSlack || (m_run == -INFINITY && cm != -INFINITY);
+      const float d = moved ? cm : 0.f;
       const float alpha = m_run == -INFINITY ? 0.f : pf_exp2(-d);
       if (moved) m_run = ref + d;
 #pragma unroll
@@ -540,6 +545,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_rope_kernel(const Prefi
 
   // column totals
   const float lsum = lacc[0];
+  m_hi = xor_reduce<16, kWave>(m_hi, [](float x, float y) { return fmaxf(x, y); });  // the column's
   if (col_ok) {
     const int64_t row = ((int64_t)b * a.M + mi) * a.Hq + (int64_t)h * G + g;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
