@@ -70,6 +70,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 struct DecodeArgs {
   Table t;
   int Hq, bs, P, sel_cap;
+  // splits per workgroup (1, or 2 on the plain variant: see split_group)
+  int S;
   float scale_log2;  // sm_scale * log2(e): scores kept in log2 units
   float rope_base;
   const uint16_t* q;
@@ -328,6 +330,11 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
   const int Hkv = a.t.Hkv;
   const int b = bh / Hkv, h = bh % Hkv;
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  // splits per workgroup and waves per split (the select, mass and ALiBi
+  // variants take one split per workgroup)
+  const int spw = SR > 0 || MASS || ALIBI ? 1 : a.S;
+  const int wps = kDecWaves / spw;
+  const int w_s = __builtin_amdgcn_readfirstlane(w);  // the wave index, in a scalar register
   const int lq = lane >> 4, lr = lane & 15;    // lane group, row/column
   const int set_q = lq / LPS, dsub = lq % LPS;  // k slots of this lane group
   const int cset = lr / GE, cg = lr % GE;       // column: token set, head slot
@@ -521,9 +528,12 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
       }
     }
   } else {
+    // this wave's split: workgroup p holds splits p spw .. p spw + spw - 1,
+    // with wps = kDecWaves / spw waves on each
     n = min(max(a.sel_count[bh], 0), a.sel_cap);
     const int cc = (n + a.P - 1) / a.P;
-    const int j0 = min(p * cc, n), j1 = min(j0 + cc, n);
+    const int pw = p * spw + w_s / wps;
+    const int j0 = min(pw * cc, n), j1 = min(j0 + cc, n);
     lbase = j0;
     ntiles = (j1 - j0) * tpb;
   }
@@ -541,7 +551,7 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
   // four waves, except on the fast path (see the kernel's comment).
   auto tile_of = [&](int j) -> int {
     if (!fast) {
-      const int x = w + kDecWaves * j;
+      const int x = w_s % wps + wps * j;
       return x < ntiles ? x : -1;
     }
     // position x in this split's share: eviction tiles [0, le), query [le, le + lqt)
@@ -795,22 +805,22 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
   }
   __syncthreads();
 
-  for (int k = threadIdx.x; k < G * D; k += kDecThreads) {
-    const int g = k / D, d = k % D;
+  // each split's partial: the merge of its waves' totals
+  for (int k = threadIdx.x; k < spw * G * D; k += kDecThreads) {
+    const int sp = k / (G * D), g = (k / D) % G, d = k % D;
+    const int w0 = sp * wps, w1 = w0 + wps;
     float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < kDecWaves; ++ww)
+    for (int ww = w0; ww < w1; ++ww)
       if (sh.lw[ww][g] > 0.f) M = fmaxf(M, sh.mw[ww][g]);
     float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kDecWaves; ++ww) {
+    for (int ww = w0; ww < w1; ++ww) {
       if (sh.lw[ww][g] > 0.f) {
         const float f = exp2f(sh.mw[ww][g] - M);
         L += sh.lw[ww][g] * f;
         O += sh.ow[ww][g][d] * f;
       }
     }
-    const int64_t row = ((int64_t)b * a.Hq + (int64_t)h * G + g) * a.P + p;
+    const int64_t row = ((int64_t)b * a.Hq + (int64_t)h * G + g) * a.P + p * spw + sp;
     const float po = L > 0.f ? O / L : 0.f, pm = L > 0.f ? M * kLn2 : -INFINITY;
     store_coherent(a.part_o + row * D + d, po);
     if (d == 0) {
@@ -853,7 +863,7 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
   // arrival reads the partials back with device-scope loads.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  if (threadIdx.x == 0) sh.last = atomicAdd(&a.counters[bh], 1) == a.P - 1;
+  if (threadIdx.x == 0) sh.last = atomicAdd(&a.counters[bh], spw) == a.P - spw;
   __syncthreads();
   if (!sh.last) return;
   for (int k = threadIdx.x; k < G * D; k += kDecThreads) {
@@ -962,6 +972,7 @@ static DecodeArgs decode_args(const nosa_dims& d, const uint16_t* q, const nosa_
   a.Hq = d.n_q_heads;
   a.bs = d.block_size;
   a.P = num_splits;
+  a.S = 1;
   a.sel_cap = sel_cap;
   a.scale_log2 = sm_scale * kLog2e;
   a.rope_base = kv.rope_base;
@@ -982,9 +993,27 @@ static DecodeArgs decode_args(const nosa_dims& d, const uint16_t* q, const nosa_
   return a;
 }
 
-static hipError_t launch_decode_args(const nosa_dims& d, const DecodeArgs& a, int kind, bool select,
+// Splits per workgroup of the plain decode.  Short splits (at most four
+// 64-token tiles per wave) make short workgroups whose start-up and first
+// loads are a large share of their time; a workgroup then takes two adjacent
+// splits, two waves on each, so each wave streams twice the tiles.  Every
+// split's partial is still its own (the merge of its waves), and the combine
+// merges all P of them.  Kept to one where halving the grid would leave CUs
+// without a workgroup, and on the select, mass and ALiBi variants.
+constexpr int kSplitGroupMinWorkgroups = 256;
+
+static int split_group(const nosa_dims& d, const DecodeArgs& a, bool select) {
+  if (select || a.mass != nullptr || a.alibi != nullptr || a.P % 2 != 0) return 1;
+  const int64_t tiles_per_split = (int64_t)((a.sel_cap + a.P - 1) / a.P) * (a.bs / kTile);
+  const int64_t groups = (int64_t)d.batch * d.n_kv_heads * (a.P / 2);
+  return tiles_per_split <= 4 * kDecWaves && groups >= kSplitGroupMinWorkgroups ? 2 : 1;
+}
+
+static hipError_t launch_decode_args(const nosa_dims& d, const DecodeArgs& args, int kind, bool select,
                                      hipStream_t stream) {
-  const dim3 grid(d.batch * d.n_kv_heads, a.P);
+  DecodeArgs a = args;
+  a.S = split_group(d, a, select);
+  const dim3 grid(d.batch * d.n_kv_heads, a.P / a.S);
   const int G = d.n_q_heads / d.n_kv_heads;
   if (d.head_dim == 128)
     launch_decode_d<128>(grid, a, G, kind, select, stream);
