@@ -190,15 +190,15 @@ struct DecodeSmem {
 // Merge of the P split partials of one output row at dim d [NOVITA, 2.
 // Attention modifications]: M = max of the non-empty splits' row maxima,
 // weights l_p * exp(m_p - M), O = sum_p w_p O_p / sum_p w_p.  The first
-// eight splits are loaded together (clamped, branch-free) so P <= 8 costs
-// one memory round trip.  Thread (row, d); the thread with d == 0 also
+// PRE splits are loaded together (clamped, branch-free) so P <= PRE costs
+// one memory round trip; later splits are loaded one at a time.  Callers
+// take PRE = 8 up to eight splits and 16 above (merge_splits_p).  Thread (row, d); the thread with d == 0 also
 // writes the row's m and l.  COHERENT: the partials come from other
 // workgroups of the same launch (device-scope loads).
-template <bool COHERENT>
+template <bool COHERENT, int PRE>
 __device__ __forceinline__ void merge_splits(int P, int D, int64_t row, int d, const float* __restrict__ part_o,
                                              const float* __restrict__ part_m, const float* __restrict__ part_l,
                                              float* __restrict__ o, float* __restrict__ m, float* __restrict__ l) {
-  constexpr int PRE = 8;
   const float* pm = part_m + row * P;
   const float* pl = part_l + row * P;
   const float* po = part_o + row * P * D + d;
@@ -240,6 +240,18 @@ __device__ __forceinline__ void merge_splits(int P, int D, int64_t row, int d, c
     m[row] = L > 0.f ? M : -INFINITY;
     l[row] = L;
   }
+}
+
+// merge_splits with the prefetch depth for P: the same operations in the
+// same order either way, so the result does not depend on it.
+template <bool COHERENT>
+__device__ __forceinline__ void merge_splits_p(int P, int D, int64_t row, int d, const float* __restrict__ part_o,
+                                               const float* __restrict__ part_m, const float* __restrict__ part_l,
+                                               float* __restrict__ o, float* __restrict__ m, float* __restrict__ l) {
+  if (P > 8)
+    merge_splits<COHERENT, 16>(P, D, row, d, part_o, part_m, part_l, o, m, l);
+  else
+    merge_splits<COHERENT, 8>(P, D, row, d, part_o, part_m, part_l, o, m, l);
 }
 
 // merge_splits for P == 1 with the split's values already in registers:
@@ -869,7 +881,10 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
   for (int k = threadIdx.x; k < G * D; k += kDecThreads) {
     const int g = k / D, d = k % D;
     const int64_t row = (int64_t)b * a.Hq + (int64_t)h * G + g;
-    merge_splits<true>(a.P, D, row, d, a.part_o, a.part_m, a.part_l, a.o, a.m, a.l);
+    if constexpr (SR > 0)  // (up to four splits by default)
+      merge_splits<true, 8>(a.P, D, row, d, a.part_o, a.part_m, a.part_l, a.o, a.m, a.l);
+    else
+      merge_splits_p<true>(a.P, D, row, d, a.part_o, a.part_m, a.part_l, a.o, a.m, a.l);
   }
   if constexpr (MASS) {  // final M (log2 units) and L of each head from the partials
     __shared__ float fm[G], fl[G];
@@ -897,7 +912,7 @@ __global__ __launch_bounds__(kDecThreads, SR > 0 ? 1 : 2) void decode_kernel(con
 __global__ void combine_kernel(int P, int D, const float* __restrict__ part_o, const float* __restrict__ part_m,
                                const float* __restrict__ part_l, float* __restrict__ o, float* __restrict__ m,
                                float* __restrict__ l) {
-  merge_splits<false>(P, D, blockIdx.x, threadIdx.x, part_o, part_m, part_l, o, m, l);
+  merge_splits_p<false>(P, D, blockIdx.x, threadIdx.x, part_o, part_m, part_l, o, m, l);
 }
 
 // The select variants: SR = 4 up to 1024 blocks, SR = 9 up to 2304.
