@@ -299,13 +299,14 @@ def test_fused_equals_separate(name, scale, splits):
         assert not a.counters.any().item()
 
 
-@pytest.mark.parametrize("splits", [16, 18])
-def test_dense_two_splits_per_workgroup(splits):
+@pytest.mark.parametrize("splits,fused", [(16, True), (18, True), (16, False)])
+def test_dense_two_splits_per_workgroup(splits, fused):
     # short splits on enough pairs that a workgroup takes two adjacent
     # splits (two waves on each); at 18 splits over 32 blocks the last two
-    # are empty, and the context ends in a partial block
+    # are empty, and the context ends in a partial block.  Unfused: the
+    # split-only decode and the separate combine.
     w = WORKLOADS["dense_8b_8k"].scaled(B=8, Hq=16, Hkv=4, T0=2000)
-    run_trajectory(w, seed=5, splits=splits)
+    run_trajectory(w, seed=5, splits=splits, fused=fused)
 
 
 def test_dense_small_many_splits():
