@@ -309,6 +309,13 @@ def test_dense_two_splits_per_workgroup(splits, fused):
     run_trajectory(w, seed=5, splits=splits, fused=fused)
 
 
+def test_lazy_rope_two_splits_per_workgroup():
+    # the deferred-RoPE decode with two splits per workgroup: each wave
+    # rotates the query for its own split's documents
+    w = WORKLOADS["lazy_rope_32k"].scaled(B=8, Hq=16, Hkv=4, T0=8 * 256, doc_len=256)
+    run_trajectory(w, seed=6, splits=16)
+
+
 def test_dense_small_many_splits():
     # k = every block, more splits than blocks per split: empty splits
     w = WORKLOADS["dense_8b_8k"].scaled(B=2, Hq=8, Hkv=2, T0=1000)
